@@ -1,0 +1,147 @@
+/*
+ * art_decode.h -- C ABI of the ART paged decode-attention library (gfx950).
+ *
+ * One call computes single-token decode attention for a batch of sequences
+ * over a paged KV cache, with ART run-time termination: for every
+ * (sequence, query head) the KV blocks are folded in a caller-given visit
+ * order into an online-softmax accumulator, and the head stops once its
+ * normalized partial output is stable -- relative change of its L2 norm
+ * below eps_mag AND cosine deviation (1 - cos) below eps_dir -- on
+ * `patience` consecutive blocks, with logical block 0 folded first.
+ * A kv-head stops fetching KV once every query head of its group stopped.
+ *
+ * Method: "ART: Attention Run-time Termination for Efficient Large Language
+ * Model Decoding" (gist.science explainer), Technical Summary 2.1 (streaming
+ * tile-wise accumulation), 2.2 (magnitude and direction statistics, both
+ * under their thresholds on the same block), 2.3 (patience), 2.4 (visit
+ * order, attention sink, RoPE/mask applied before accumulation).
+ *
+ * Conventions shared by every entry point:
+ *  - All pointers except `desc` and `stream` are DEVICE pointers unless
+ *    stated otherwise; the caller owns every buffer.  The library never
+ *    allocates or frees memory and never synchronizes the stream.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = default stream)
+ *    and runs asynchronously.  Argument errors are detected on the host,
+ *    before anything is enqueued, and returned synchronously.
+ *  - Content errors (a block_order row that is not a permutation of
+ *    [0, n_s), a block_table entry outside [0, num_pages), seq_lens[s] >
+ *    max_blocks_per_seq * block_size) are undefined behaviour.
+ *  - Two calls that share a workspace must not overlap in time.
+ */
+#ifndef ART_DECODE_H
+#define ART_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ART_OK = 0,
+  ART_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or scalar   */
+  ART_ERR_UNSUPPORTED = 2, /* valid but outside the supported shape matrix  */
+  ART_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required    */
+  ART_ERR_HIP = 4          /* the HIP runtime refused a launch              */
+} art_status;
+
+typedef enum {
+  ART_DTYPE_F32 = 0,        /* IEEE binary32                                  */
+  ART_DTYPE_BF16 = 1,       /* bfloat16 (upper half of binary32)              */
+  ART_DTYPE_FP8_E4M3FN = 2  /* OCP FP8 E4M3 (bias 7, no inf, S.1111.111 NaN)  */
+} art_dtype;
+
+enum {
+  ART_FLAG_NONE = 0,
+  /* Full attention: every block is folded, stop_block = n.  Selected
+   * automatically when eps_mag == 0 or eps_dir == 0 (a strict "<" test can
+   * then never pass), unless ART_FLAG_KEEP_DETECTOR is set. */
+  ART_FLAG_FULL = 1u,
+  /* Run the terminating kernel (statistics and patience counters) even when
+   * the thresholds make a stop impossible; used to measure detector cost. */
+  ART_FLAG_KEEP_DETECTOR = 2u
+};
+
+/* Shapes and storage types of one call (host memory). */
+typedef struct {
+  int32_t batch;               /* number of sequences, >= 0                    */
+  int32_t num_q_heads;         /* Hq                                           */
+  int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0, g = Hq / Hkv in [1, 16]  */
+  int32_t head_dim;            /* D in {64, 128}                               */
+  int32_t block_size;          /* B (tokens per KV page) in {16, 32}           */
+  int32_t max_blocks_per_seq;  /* row stride of block_table and block_order   */
+  int32_t num_pages;           /* number of physical pages in k_pages/v_pages */
+  int32_t q_dtype;             /* art_dtype of q                               */
+  int32_t kv_dtype;            /* art_dtype of k_pages / v_pages               */
+  uint32_t flags;              /* ART_FLAG_* bits                              */
+} art_decode_desc;
+
+/*
+ * Bytes of device workspace art_decode needs for `desc` (0 = none).  Depends
+ * only on the descriptor.  Returns 0 also for an invalid descriptor.
+ */
+size_t art_decode_workspace_bytes(const art_decode_desc* desc);
+
+/*
+ * Put a workspace into its initial state (zeroes its counters) on `stream`.
+ * Must be called once on a new workspace before its first art_decode call;
+ * art_decode leaves the workspace in that state again when it completes.
+ * Errors: ART_ERR_INVALID_ARG for NULL with bytes > 0, ART_ERR_HIP.
+ */
+art_status art_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ART decode attention, one decode step of one layer.
+ *
+ * q            [batch][Hq][D] in q_dtype (post-RoPE).  16-byte aligned.
+ * k_pages,
+ * v_pages      [num_pages][Hkv][B][D] in kv_dtype; the (page, kv-head) tile
+ *              [B][D] is contiguous.  Row r of logical block b of sequence s
+ *              is token b*B + r.  16-byte aligned.
+ * k_scale,
+ * v_scale      [num_pages][Hkv] float32 per-tile dequantization scales
+ *              (value = scale * decoded byte); required for FP8 KV, must be
+ *              NULL otherwise.
+ * block_table  [batch][max_blocks_per_seq] int32: logical block -> page.
+ * block_order  [batch][max_blocks_per_seq] int32: visit position t ->
+ *              logical block; the first n_s = ceil(seq_lens[s] / B) entries
+ *              of row s are a permutation of [0, n_s).
+ * seq_lens     [batch] int32, 0 <= seq_lens[s] <= max_blocks_per_seq * B.
+ * eps_mag      threshold on |‖O_t‖ - ‖O_{t-1}‖| / ‖O_{t-1}‖ (>= 0, not NaN).
+ * eps_dir      threshold on max(0, 1 - cos(O_t, O_{t-1})) (>= 0, not NaN).
+ * patience     consecutive passing blocks needed to stop (>= 1).
+ * out          [batch][Hq][D] float32: the head's normalized attention output
+ *              over the blocks it folded (0 for an empty sequence).
+ * stop_block   [batch][Hq] int32: number of folded blocks = visit positions
+ *              0 .. stop-1 (n_s when the head never stopped, 0 when empty).
+ * blocks_fetched  optional [batch][Hkv] int32 (NULL to skip): KV blocks the
+ *              kernel actually read for each (sequence, kv-head), speculative
+ *              reads included.
+ * workspace    device scratch of at least art_decode_workspace_bytes(desc)
+ *              bytes, initialized once with art_decode_workspace_init; may be
+ *              NULL when that size is 0.  256-byte aligned.
+ * stream       hipStream_t to enqueue on.
+ *
+ * Supported: D in {64, 128}; B in {16, 32}; g = Hq/Hkv in 1..16;
+ * (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN)}.
+ * Softmax scale is 1/sqrt(D); tokens at positions >= seq_lens[s] are masked
+ * and never read into the result (their rows may hold any bits).
+ */
+art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_pages, const void* v_pages,
+                      const float* k_scale, const float* v_scale, const int32_t* block_table,
+                      const int32_t* block_order, const int32_t* seq_lens, float eps_mag, float eps_dir,
+                      int32_t patience, float* out, int32_t* stop_block, int32_t* blocks_fetched,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a status code (host memory, never NULL). */
+const char* art_status_string(art_status status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t art_decode_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ART_DECODE_H */

@@ -1,0 +1,201 @@
+"""ctypes binding of the C ABI in ``include/art_decode.h`` (argument marshalling only).
+
+Every step of the decode runs in the HIP library ``libart_decode.so``; this
+module only builds the descriptor from tensor shapes/dtypes, passes device
+pointers and the current HIP stream, and turns status codes into exceptions.
+PyTorch is used for device memory and streams.  There is no fallback: if the
+library is missing the functions raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libart_decode.so")
+
+ART_OK, ART_ERR_INVALID_ARG, ART_ERR_UNSUPPORTED, ART_ERR_WORKSPACE, ART_ERR_HIP = range(5)
+ART_DTYPE_F32, ART_DTYPE_BF16, ART_DTYPE_FP8_E4M3FN = range(3)
+ART_FLAG_NONE, ART_FLAG_FULL, ART_FLAG_KEEP_DETECTOR = 0, 1, 2
+
+EXPORTED = ("art_decode_workspace_bytes", "art_decode_workspace_init", "art_decode", "art_status_string",
+            "art_decode_version")
+
+
+class ArtDecodeDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class ArtError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m kv_cache_run_amd.build` "
+                           "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(p)
+    vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
+    lib.art_decode_workspace_bytes.argtypes = [ctypes.POINTER(ArtDecodeDesc)]
+    lib.art_decode_workspace_bytes.restype = sz
+    lib.art_decode_workspace_init.argtypes = [vp, sz, vp]
+    lib.art_decode_workspace_init.restype = ctypes.c_int
+    lib.art_decode.argtypes = [ctypes.POINTER(ArtDecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, f32, f32, i32, vp,
+                               vp, vp, vp, sz, vp]
+    lib.art_decode.restype = ctypes.c_int
+    lib.art_status_string.argtypes = [ctypes.c_int]
+    lib.art_status_string.restype = ctypes.c_char_p
+    lib.art_decode_version.argtypes = []
+    lib.art_decode_version.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def art_status_string(status: int) -> str:
+    return load_library().art_status_string(int(status)).decode()
+
+
+def art_decode_version() -> int:
+    return int(load_library().art_decode_version())
+
+
+def _check(status: int) -> None:
+    if status != ART_OK:
+        raise ArtError(status, art_status_string(status))
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return ART_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return ART_DTYPE_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return ART_DTYPE_FP8_E4M3FN
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def make_desc(q, k_pages, block_table, flags: int = 0) -> ArtDecodeDesc:
+    """Descriptor from q [batch, Hq, D], k_pages [pages, Hkv, B, D], block_table [batch, max_blocks]."""
+    batch, hq, d = q.shape
+    pages, hkv, b, d2 = k_pages.shape
+    if d2 != d:
+        raise ValueError("q and k_pages disagree on head_dim")
+    return ArtDecodeDesc(batch, hq, hkv, d, b, block_table.shape[1], pages, _dtype_code(q), _dtype_code(k_pages),
+                         flags)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) or None
+
+
+def art_decode_workspace_bytes(desc: ArtDecodeDesc) -> int:
+    return int(load_library().art_decode_workspace_bytes(ctypes.byref(desc)))
+
+
+def art_decode_workspace_init(workspace, stream=None) -> None:
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().art_decode_workspace_init(_ptr(workspace), nbytes, _stream(stream)))
+
+
+def art_decode(q, k_pages, v_pages, block_table, block_order, seq_lens, eps_mag: float, eps_dir: float,
+               patience: int, out, stop_block, *, k_scale=None, v_scale=None, blocks_fetched=None, workspace=None,
+               flags: int = 0, stream=None) -> None:
+    """Enqueue one ART decode step (see include/art_decode.h); tensors must be contiguous on the device."""
+    for t in (q, k_pages, v_pages, block_table, block_order, seq_lens, out, stop_block, k_scale, v_scale,
+              blocks_fetched, workspace):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    desc = make_desc(q, k_pages, block_table, flags)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().art_decode(ctypes.byref(desc), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
+                                   _ptr(v_scale), _ptr(block_table), _ptr(block_order), _ptr(seq_lens),
+                                   float(eps_mag), float(eps_dir), int(patience), _ptr(out), _ptr(stop_block),
+                                   _ptr(blocks_fetched), _ptr(workspace), nbytes, _stream(stream))
+    _check(st)
+
+
+class Decoder:
+    """Holds a device workspace for one descriptor shape and calls :func:`art_decode`."""
+
+    def __init__(self, q, k_pages, block_table, device=None):
+        import torch
+
+        self.desc = make_desc(q, k_pages, block_table)
+        nbytes = art_decode_workspace_bytes(self.desc)
+        self.workspace = None
+        if nbytes:
+            self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device or q.device)
+            art_decode_workspace_init(self.workspace)
+
+    def __call__(self, q, k_pages, v_pages, block_table, block_order, seq_lens, eps_mag, eps_dir, patience, *,
+                 k_scale=None, v_scale=None, out=None, stop_block=None, blocks_fetched=None, flags=0, stream=None):
+        import torch
+
+        batch, hq, d = q.shape
+        if out is None:
+            out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
+        if stop_block is None:
+            stop_block = torch.empty((batch, hq), dtype=torch.int32, device=q.device)
+        art_decode(q, k_pages, v_pages, block_table, block_order, seq_lens, eps_mag, eps_dir, patience, out,
+                   stop_block, k_scale=k_scale, v_scale=v_scale, blocks_fetched=blocks_fetched,
+                   workspace=self.workspace, flags=flags, stream=stream)
+        return out, stop_block
+
+
+def case_to_device(case: dict, device="cuda") -> dict:
+    """Copy a generated case (host NumPy storage arrays) to device tensors of the matching dtypes."""
+    import numpy as np
+    import torch
+
+    def kv(a, dtype):
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+        if dtype == "fp8_e4m3fn":
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device).view(torch.float8_e4m3fn)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+    d = {
+        "q": kv(case["q"], case["q_dtype"]),
+        "k_pages": kv(case["k_pages"], case["kv_dtype"]),
+        "v_pages": kv(case["v_pages"], case["kv_dtype"]),
+        "block_table": torch.from_numpy(case["block_table"]).to(device),
+        "block_order": torch.from_numpy(case["block_order"]).to(device),
+        "seq_lens": torch.from_numpy(case["seq_lens"]).to(device),
+        "k_scale": None if case.get("k_scale") is None else torch.from_numpy(case["k_scale"]).to(device),
+        "v_scale": None if case.get("v_scale") is None else torch.from_numpy(case["v_scale"]).to(device),
+    }
+    return d

@@ -1,0 +1,181 @@
+// C-ABI front end: argument validation (host only, before any HIP call),
+// kernel selection, workspace plan and launch.
+#include "../../include/art_decode.h"
+
+#include <math.h>
+#include <string.h>
+
+#include "art_internal.h"
+
+namespace art {
+
+SplitPlan full_split_plan(int batch, int hkv, int max_blocks) {
+  const long streams = (long)batch * hkv;
+  const long target_wgs = 1024;  // about four workgroups per CU on 256 CUs
+  long splits = streams > 0 ? (target_wgs + streams - 1) / streams : 1;
+  const long by_len = (max_blocks + 7) / 8;  // at least 8 blocks (2 per wave) per split
+  if (splits > by_len) splits = by_len;
+  if (splits > 64) splits = 64;
+  if (splits < 1) splits = 1;
+  long per = (max_blocks + splits - 1) / splits;
+  per = (per + 3) / 4 * 4;
+  if (per < 4) per = 4;
+  splits = (max_blocks + per - 1) / per;
+  if (splits < 1) splits = 1;
+  return SplitPlan{(int)splits, (int)per};
+}
+
+}  // namespace art
+
+namespace {
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+// Shape/type checks that need no data.  Returns ART_OK or the error.
+art_status check_desc(const art_decode_desc* d) {
+  if (!d) return ART_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->max_blocks_per_seq < 1 ||
+      d->num_pages < 1)
+    return ART_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return ART_ERR_INVALID_ARG;
+  if (d->flags & ~(uint32_t)(ART_FLAG_FULL | ART_FLAG_KEEP_DETECTOR)) return ART_ERR_INVALID_ARG;
+  const int g = d->num_q_heads / d->num_kv_heads;
+  if (g > 16) return ART_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return ART_ERR_UNSUPPORTED;
+  if (d->block_size != 16 && d->block_size != 32) return ART_ERR_UNSUPPORTED;
+  const bool ok_types = (d->q_dtype == ART_DTYPE_F32 && d->kv_dtype == ART_DTYPE_F32) ||
+                        (d->q_dtype == ART_DTYPE_BF16 && d->kv_dtype == ART_DTYPE_BF16) ||
+                        (d->q_dtype == ART_DTYPE_BF16 && d->kv_dtype == ART_DTYPE_FP8_E4M3FN);
+  if (!ok_types) {
+    const bool known = d->q_dtype >= 0 && d->q_dtype <= 2 && d->kv_dtype >= 0 && d->kv_dtype <= 2;
+    return known ? ART_ERR_UNSUPPORTED : ART_ERR_INVALID_ARG;
+  }
+  // 32-bit limits used inside the kernels
+  if ((long long)d->batch * d->num_kv_heads * 64 > 0x7fffffffLL) return ART_ERR_UNSUPPORTED;
+  if ((long long)d->max_blocks_per_seq * d->block_size > 0x7fffffffLL) return ART_ERR_UNSUPPORTED;
+  return ART_OK;
+}
+
+size_t workspace_for(const art_decode_desc* d) {
+  const art::SplitPlan sp = art::full_split_plan(d->batch, d->num_kv_heads, d->max_blocks_per_seq);
+  if (sp.splits <= 1 || d->batch == 0) return 0;
+  const int gm = art::group_capacity(d->num_q_heads / d->num_kv_heads);
+  const size_t streams = (size_t)d->batch * d->num_kv_heads;
+  size_t part = streams * sp.splits * gm * (size_t)(d->head_dim + 2) * sizeof(float);
+  part = (part + 255) / 256 * 256;
+  const size_t counters = (streams * sizeof(int32_t) + 255) / 256 * 256;
+  return part + counters;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t art_decode_workspace_bytes(const art_decode_desc* desc) {
+  if (check_desc(desc) != ART_OK) return 0;
+  return workspace_for(desc);
+}
+
+art_status art_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace_bytes == 0) return ART_OK;
+  if (!workspace || !aligned(workspace, 256)) return ART_ERR_INVALID_ARG;
+  if (hipMemsetAsync(workspace, 0, workspace_bytes, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ART_ERR_HIP;
+  return ART_OK;
+}
+
+art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_pages, const void* v_pages,
+                      const float* k_scale, const float* v_scale, const int32_t* block_table,
+                      const int32_t* block_order, const int32_t* seq_lens, float eps_mag, float eps_dir,
+                      int32_t patience, float* out, int32_t* stop_block, int32_t* blocks_fetched,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const art_status ds = check_desc(desc);
+  if (ds != ART_OK) return ds;
+  if (!(eps_mag >= 0.f) || !(eps_dir >= 0.f) || patience < 1) return ART_ERR_INVALID_ARG;
+  const bool fp8 = desc->kv_dtype == ART_DTYPE_FP8_E4M3FN;
+  if (!q || !k_pages || !v_pages || !block_table || !block_order || !seq_lens || !out || !stop_block)
+    return ART_ERR_INVALID_ARG;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return ART_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16) ||
+      !aligned(block_table, 4) || !aligned(block_order, 4) || !aligned(seq_lens, 4) || !aligned(stop_block, 4) ||
+      (blocks_fetched && !aligned(blocks_fetched, 4)) || (k_scale && !aligned(k_scale, 4)) ||
+      (v_scale && !aligned(v_scale, 4)))
+    return ART_ERR_INVALID_ARG;
+  const size_t need = workspace_for(desc);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return ART_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return ART_ERR_INVALID_ARG;
+  }
+  if (desc->batch == 0) return ART_OK;
+
+  const bool full = (desc->flags & ART_FLAG_FULL) ||
+                    ((eps_mag == 0.f || eps_dir == 0.f) && !(desc->flags & ART_FLAG_KEEP_DETECTOR));
+  const int g = desc->num_q_heads / desc->num_kv_heads;
+  art::Variant v;
+  v.kv = desc->kv_dtype == ART_DTYPE_F32 ? art::KV_F32 : (fp8 ? art::KV_FP8 : art::KV_BF16);
+  v.d = desc->head_dim;
+  v.b = desc->block_size;
+  v.gm = art::group_capacity(g);
+
+  art::Params p;
+  memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k_pages = k_pages;
+  p.v_pages = v_pages;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_table = block_table;
+  p.block_order = block_order;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.stop_block = stop_block;
+  p.blocks_fetched = blocks_fetched;
+  p.batch = desc->batch;
+  p.hq = desc->num_q_heads;
+  p.hkv = desc->num_kv_heads;
+  p.g = g;
+  p.max_blocks = desc->max_blocks_per_seq;
+  p.eps_mag = eps_mag;
+  p.eps_dir = eps_dir;
+  p.patience = patience;
+  p.qk_log2 = (float)(1.4426950408889634 / sqrt((double)desc->head_dim));
+
+  hipError_t e;
+  if (full) {
+    const art::SplitPlan sp = art::full_split_plan(desc->batch, desc->num_kv_heads, desc->max_blocks_per_seq);
+    p.splits = sp.splits;
+    p.split_blocks = sp.split_blocks;
+    if (sp.splits > 1) {
+      const size_t streams = (size_t)desc->batch * desc->num_kv_heads;
+      size_t part = streams * sp.splits * v.gm * (size_t)(desc->head_dim + 2) * sizeof(float);
+      part = (part + 255) / 256 * 256;
+      p.ws_part = static_cast<float*>(workspace);
+      p.ws_count = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + part);
+    }
+    e = v.kv == art::KV_F32 ? art::launch_full_f32(v, p, static_cast<hipStream_t>(stream))
+        : v.kv == art::KV_BF16 ? art::launch_full_bf16(v, p, static_cast<hipStream_t>(stream))
+                               : art::launch_full_fp8(v, p, static_cast<hipStream_t>(stream));
+  } else {
+    p.splits = 1;
+    p.split_blocks = desc->max_blocks_per_seq;
+    e = v.kv == art::KV_F32 ? art::launch_art_f32(v, p, static_cast<hipStream_t>(stream))
+        : v.kv == art::KV_BF16 ? art::launch_art_bf16(v, p, static_cast<hipStream_t>(stream))
+                               : art::launch_art_fp8(v, p, static_cast<hipStream_t>(stream));
+  }
+  return e == hipSuccess ? ART_OK : ART_ERR_HIP;
+}
+
+const char* art_status_string(art_status s) {
+  switch (s) {
+    case ART_OK: return "ART_OK";
+    case ART_ERR_INVALID_ARG: return "ART_ERR_INVALID_ARG: invalid argument";
+    case ART_ERR_UNSUPPORTED: return "ART_ERR_UNSUPPORTED: shape or type outside the supported matrix";
+    case ART_ERR_WORKSPACE: return "ART_ERR_WORKSPACE: workspace missing or too small";
+    case ART_ERR_HIP: return "ART_ERR_HIP: HIP runtime error";
+  }
+  return "ART: unknown status";
+}
+
+int32_t art_decode_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Internal interface between the C-ABI front end (art_api.cpp) and the
+// gfx950 kernels (art_kernels*.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace art {
+
+enum KvType { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+
+// Everything a kernel needs, passed by value as the kernel argument.
+struct Params {
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_table;
+  const int32_t* block_order;
+  const int32_t* seq_lens;
+  float* out;
+  int32_t* stop_block;
+  int32_t* blocks_fetched;  // may be null
+  float* ws_part;           // full mode with splits: [streams][splits][GM][D + 2]
+  int32_t* ws_count;        // full mode with splits: [streams] arrival counters
+  int32_t batch, hq, hkv, g;
+  int32_t max_blocks;
+  int32_t splits;           // full mode: splits per stream (1 = no merge)
+  int32_t split_blocks;     // full mode: blocks per split
+  float eps_mag, eps_dir;
+  int32_t patience;
+  float qk_log2;            // log2(e) / sqrt(D)
+};
+
+// Kernel variant key.
+struct Variant {
+  int kv;   // KvType
+  int d;    // 64 | 128
+  int b;    // 16 | 32
+  int gm;   // 4 | 8 | 16 (register capacity for the query group)
+};
+
+inline int group_capacity(int g) { return g <= 4 ? 4 : (g <= 8 ? 8 : 16); }
+
+// Full-attention split plan (depends only on the descriptor).
+struct SplitPlan {
+  int splits;
+  int split_blocks;
+};
+SplitPlan full_split_plan(int batch, int hkv, int max_blocks);
+
+// Launchers; return hipSuccess or the launch error.  One translation unit per
+// (kernel, KV storage type): kern_<kernel>_<type>.hip.
+hipError_t launch_art_f32(const Variant& v, const Params& p, hipStream_t stream);
+hipError_t launch_art_bf16(const Variant& v, const Params& p, hipStream_t stream);
+hipError_t launch_art_fp8(const Variant& v, const Params& p, hipStream_t stream);
+hipError_t launch_full_f32(const Variant& v, const Params& p, hipStream_t stream);
+hipError_t launch_full_bf16(const Variant& v, const Params& p, hipStream_t stream);
+hipError_t launch_full_fp8(const Variant& v, const Params& p, hipStream_t stream);
+
+}  // namespace art

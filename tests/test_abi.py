@@ -1,0 +1,97 @@
+"""The C-ABI library: exports, host-side validation (no GPU needed, no device call made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_run_amd import art
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(art.LIB_PATH):
+        from kv_cache_run_amd import build
+
+        build.build()
+    return art.load_library()
+
+
+def _declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for fn in sorted(os.listdir(inc)):
+        if fn.endswith(".h"):
+            text = open(os.path.join(inc, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"\b(art_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_every_declared_function_is_exported(lib):
+    names = _declared_functions()
+    assert "art_decode" in names and len(names) >= 5
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(art.EXPORTED) == set(names)
+
+
+def test_status_strings_and_version(lib):
+    for s in range(5):
+        assert art.art_status_string(s).startswith("ART_")
+    assert "unknown" in art.art_status_string(99)
+    assert art.art_decode_version() >= 100
+
+
+def _desc(**kw):
+    base = dict(batch=2, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, max_blocks_per_seq=64,
+                num_pages=128, q_dtype=art.ART_DTYPE_BF16, kv_dtype=art.ART_DTYPE_BF16, flags=0)
+    base.update(kw)
+    return art.ArtDecodeDesc(**base)
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every case below fails validation first
+
+
+def _call(lib, desc, *, q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, bt=FAKE, bo=FAKE, sl=FAKE, em=1e-3, ed=1e-4, p=4,
+          out=FAKE, stop=FAKE, fetched=None, ws=FAKE, wsb=1 << 30):
+    return lib.art_decode(ctypes.byref(desc) if desc is not None else None, q, k, v, ks, vs, bt, bo, sl, em, ed, p,
+                          out, stop, fetched, ws, wsb, None)
+
+
+def test_validation_errors_return_before_any_device_call(lib):
+    E_ARG, E_UNS, E_WS = art.ART_ERR_INVALID_ARG, art.ART_ERR_UNSUPPORTED, art.ART_ERR_WORKSPACE
+    assert _call(lib, None) == E_ARG
+    assert _call(lib, _desc(num_q_heads=30)) == E_ARG                    # Hq % Hkv
+    assert _call(lib, _desc(num_q_heads=136, num_kv_heads=8)) == E_UNS   # g = 17
+    assert _call(lib, _desc(head_dim=96)) == E_UNS
+    assert _call(lib, _desc(block_size=8)) == E_UNS
+    assert _call(lib, _desc(q_dtype=art.ART_DTYPE_F32)) == E_UNS          # f32 q with bf16 KV
+    assert _call(lib, _desc(kv_dtype=7)) == E_ARG
+    assert _call(lib, _desc(batch=-1)) == E_ARG
+    assert _call(lib, _desc(flags=8)) == E_ARG
+    assert _call(lib, _desc(), em=float("nan")) == E_ARG
+    assert _call(lib, _desc(), ed=-1e-4) == E_ARG
+    assert _call(lib, _desc(), p=0) == E_ARG
+    assert _call(lib, _desc(), q=None) == E_ARG
+    assert _call(lib, _desc(), stop=None) == E_ARG
+    assert _call(lib, _desc(), k=FAKE + 8) == E_ARG                        # 16-byte alignment
+    assert _call(lib, _desc(), ks=FAKE) == E_ARG                           # scales only for fp8
+    assert _call(lib, _desc(kv_dtype=art.ART_DTYPE_FP8_E4M3FN)) == E_ARG   # fp8 needs scales
+    assert _call(lib, _desc(), ws=None) == E_WS
+    assert _call(lib, _desc(), wsb=16) == E_WS
+    assert _call(lib, _desc(), ws=FAKE + 64) == E_ARG                      # 256-byte alignment
+    # an empty batch is valid and enqueues nothing
+    assert _call(lib, _desc(batch=0), ws=None, wsb=0) == art.ART_OK
+
+
+def test_workspace_size_query(lib):
+    assert art.art_decode_workspace_bytes(_desc(head_dim=96)) == 0
+    n = art.art_decode_workspace_bytes(_desc())
+    assert n > 0 and n % 256 == 0
+    assert art.art_decode_workspace_bytes(_desc(batch=0)) == 0
+    assert lib.art_decode_workspace_init(None, 0, None) == art.ART_OK
+    assert lib.art_decode_workspace_init(None, 256, None) == art.ART_ERR_INVALID_ARG

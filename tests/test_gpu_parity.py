@@ -1,0 +1,210 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on one MI355X.
+
+Bars: stop_block bit-exact except where the oracle's statistic lies within
+1e-5 of its threshold (feasible-stop rule, oracle/feasible.py); outputs within
+2e-3 max relative error at the compared stop; full-attention mode within the
+same tolerance.  Reduced sizes compare every head; full sizes compare sampled
+heads plus properties that hold at any size.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_run_amd import synth, workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _device_run(case, eps_mag, eps_dir, patience, flags=0, reps=1):
+    import torch
+
+    from kv_cache_run_amd import art
+
+    dev = art.case_to_device(case)
+    dec = art.Decoder(dev["q"], dev["k_pages"], dev["block_table"])
+    fetched = torch.full((case["batch"], case["num_kv_heads"]), -7, dtype=torch.int32, device="cuda")
+    outs = []
+    for _ in range(reps):
+        out, stop = dec(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"], dev["block_order"],
+                        dev["seq_lens"], eps_mag, eps_dir, patience, k_scale=dev["k_scale"], v_scale=dev["v_scale"],
+                        blocks_fetched=fetched, flags=flags)
+        torch.cuda.synchronize()
+        outs.append((out.cpu().numpy().astype(np.float64), stop.cpu().numpy(), fetched.cpu().numpy()))
+    return outs if reps > 1 else outs[0]
+
+
+def _pairs(case, sample=None, seed=0):
+    allp = [(s, h) for s in range(case["batch"]) for h in range(case["num_q_heads"])]
+    if sample is None or sample >= len(allp):
+        return allp
+    rng = np.random.default_rng(seed)
+    idx = rng.choice(len(allp), size=sample, replace=False)
+    return sorted(allp[i] for i in idx)
+
+
+def _nblocks(case):
+    return (case["seq_lens"].astype(np.int64) + case["block_size"] - 1) // case["block_size"]
+
+
+def check_art(case, eps_mag=None, eps_dir=None, patience=None, sample=None, flags=0):
+    em = case["eps_mag"] if eps_mag is None else eps_mag
+    ed = case["eps_dir"] if eps_dir is None else eps_dir
+    p = case["patience"] if patience is None else patience
+    print(f"[art] {case['workload']} batch={case['batch']} eps=({em},{ed}) p={p}", flush=True)
+    out, stop, fetched = _device_run(case, em, ed, p, flags=flags)
+    pairs = _pairs(case, sample)
+    ref = oracle.art_reference(*synth.oracle_arrays(case), eps_mag=em, eps_dir=ed, patience=p,
+                               pairs=pairs, **synth.oracle_kwargs(case))
+    rep = oracle.compare_with_oracle(out, stop, case, ref, eps_mag=em, eps_dir=ed, patience=p, pairs=pairs)
+    assert rep["bad"] == [], rep
+    assert rep["max_rel_err"] <= TOL, rep
+    # properties at any size: the stream reads at least every block a head of its group folded
+    n = _nblocks(case)
+    g = case["num_q_heads"] // case["num_kv_heads"]
+    grp_max = stop.reshape(case["batch"], case["num_kv_heads"], g).max(axis=2)
+    assert np.all(stop >= 0) and np.all(stop <= n[:, None])
+    assert np.all(fetched >= grp_max) and np.all(fetched <= n[:, None])
+    assert np.all(np.isfinite(out))
+    return rep, out, stop, fetched
+
+
+def check_full(case, sample=None, flags=0):
+    print(f"[full] {case['workload']} batch={case['batch']}", flush=True)
+    out, stop, fetched = _device_run(case, 0.0, 0.0, 1, flags=flags)
+    pairs = _pairs(case, sample)
+    ref = oracle.full_attention(case["q"], case["k_pages"], case["v_pages"], case["block_table"], case["seq_lens"],
+                                pairs=pairs, **synth.oracle_kwargs(case))
+    worst = 0.0
+    for s, h in pairs:
+        worst = max(worst, oracle.feasible.max_rel_err(out[s, h], ref[s, h]))
+    n = _nblocks(case)
+    assert worst <= TOL, worst
+    assert np.array_equal(stop, np.repeat(n[:, None], case["num_q_heads"], axis=1))
+    assert np.array_equal(fetched, np.repeat(n[:, None], case["num_kv_heads"], axis=1))
+    return worst
+
+
+# ---- every head, at sizes the oracle finishes in seconds (ragged tails included) -------------------------
+
+REDUCED = [
+    (W.TINY, dict()),
+    (W.TINY, dict(context=1000)),
+    (W.LLAMA3_8B, dict(batch=2, context=8192 - 5)),
+    (W.RAGGED, dict(batch=4)),
+    (W.LONG, dict(batch=1, context=131072 - 7)),
+    (W.QWEN_FP8, dict(batch=4, context=16384 - 3)),
+]
+
+
+@pytest.mark.parametrize("w,kw", REDUCED, ids=[f"{w.name}-{kw}" for w, kw in REDUCED])
+def test_art_parity_reduced(w, kw):
+    check_art(synth.make_case(w, **kw))
+
+
+@pytest.mark.parametrize("w,kw", REDUCED, ids=[f"{w.name}-{kw}" for w, kw in REDUCED])
+def test_full_parity_reduced(w, kw):
+    check_full(synth.make_case(w, **kw))
+
+
+# ---- shape matrix corners ------------------------------------------------------------------------------
+
+SHAPES = [
+    W.LLAMA3_8B.scaled(name="bf16-d64-gqa4", head_dim=64),
+    W.LLAMA3_8B.scaled(name="bf16-blk32-gqa4", block_size=32),
+    W.LLAMA3_8B.scaled(name="bf16-mha", num_q_heads=8),
+    W.LLAMA3_8B.scaled(name="bf16-gqa16", num_q_heads=128),
+    W.LLAMA3_8B.scaled(name="bf16-gqa2-d64-blk32", num_q_heads=16, head_dim=64, block_size=32),
+    W.QWEN_FP8.scaled(name="fp8-d64-gqa7", head_dim=64),
+    W.QWEN_FP8.scaled(name="fp8-blk32-gqa7", block_size=32),
+    W.TINY.scaled(name="f32-d128-gqa3", head_dim=128, num_q_heads=6, num_kv_heads=2),
+    W.TINY.scaled(name="f32-d64-blk32-gqa12", num_q_heads=12, block_size=32),
+]
+
+
+@pytest.mark.parametrize("w", SHAPES, ids=[w.name for w in SHAPES])
+def test_shape_matrix(w):
+    case = synth.make_case(w, batch=2, context=2000 + 9)
+    check_art(case)
+    check_full(case)
+
+
+# ---- edge cases ----------------------------------------------------------------------------------------
+
+
+def _with_lens(case, lens):
+    c = dict(case)
+    c["seq_lens"] = np.asarray(lens, dtype=np.int32)
+    return c
+
+
+def test_empty_short_and_single_token_sequences():
+    base = synth.make_case(W.LLAMA3_8B, batch=5, context=700)
+    case = _with_lens(base, [0, 1, 15, 16, 17])
+    check_art(case, patience=1, eps_mag=0.5, eps_dir=0.5)
+    check_art(case)
+    check_full(case)
+    out, stop, fetched = _device_run(case, 1e-3, 1e-4, 4)
+    assert np.all(out[0] == 0.0) and np.all(stop[0] == 0) and np.all(fetched[0] == 0)
+
+
+def test_sink_not_first_and_random_orders():
+    case = synth.make_case(W.LLAMA3_8B, batch=3, context=3000)
+    rng = np.random.default_rng(11)
+    n = int(_nblocks(case)[0])
+    order = case["block_order"].copy()
+    order[0, :n] = list(range(n - 1, -1, -1))  # block 0 last: nobody can stop early
+    order[1, :n] = rng.permutation(n)
+    order[2, :n] = [5, 4, 3, 2, 1, 0] + list(range(6, n))
+    case["block_order"] = order
+    rep, out, stop, fetched = check_art(case, eps_mag=1e-2, eps_dir=1e-3, patience=2)
+    assert np.all(stop[0] == n)
+
+
+def test_patience_one_and_loose_thresholds():
+    case = synth.make_case(W.LLAMA3_8B, batch=2, context=4096)
+    rep, out, stop, fetched = check_art(case, eps_mag=10.0, eps_dir=10.0, patience=1)
+    assert np.all(stop == 2)  # every test passes: stop right after the first test
+    check_art(case, eps_mag=10.0, eps_dir=10.0, patience=5)
+
+
+def test_zero_threshold_keeps_detector_and_equals_full():
+    from kv_cache_run_amd import art
+
+    case = synth.make_case(W.LLAMA3_8B, batch=1, context=1024 + 3)
+    rep, out, stop, fetched = check_art(case, eps_mag=0.0, eps_dir=1e-4, flags=art.ART_FLAG_KEEP_DETECTOR)
+    assert np.all(stop == _nblocks(case)[0])
+    check_full(case, flags=art.ART_FLAG_FULL)
+
+
+def test_stop_monotone_in_thresholds_on_device():
+    case = synth.make_case(W.LLAMA3_8B, batch=2, context=8192)
+    prev = None
+    for em, ed in [(1e-4, 1e-5), (5e-4, 5e-5), (1e-3, 1e-4), (4e-3, 4e-4), (1.6e-2, 1.6e-3)]:
+        _, stop, _ = _device_run(case, em, ed, 4)
+        if prev is not None:
+            assert np.all(stop <= prev)
+        prev = stop
+
+
+def test_repeatable_and_workspace_reusable():
+    case = synth.make_case(W.RAGGED, batch=3)
+    runs = _device_run(case, 0.0, 0.0, 1, reps=3)
+    for o, s, f in runs[1:]:
+        assert np.array_equal(o, runs[0][0]) and np.array_equal(s, runs[0][1])
+    runs = _device_run(case, 1e-3, 1e-4, 4, reps=2)
+    assert np.array_equal(runs[0][0], runs[1][0]) and np.array_equal(runs[0][1], runs[1][1])
+
+
+# ---- full sizes (the benchmark shapes): sampled heads ----------------------------------------------------
+
+FULL_SIZES = [W.LLAMA3_8B, W.RAGGED, W.LONG, W.QWEN_FP8]
+
+
+@pytest.mark.parametrize("w", FULL_SIZES, ids=[w.name for w in FULL_SIZES])
+def test_full_size_sampled(w):
+    case = synth.make_case(w)
+    check_art(case, sample=48)
+    check_full(case, sample=24)
