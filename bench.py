@@ -1,0 +1,311 @@
+"""Benchmark: ART paged decode attention on one MI355X.
+
+One step = one ``art_decode`` call over the whole batch (one decode step of
+one attention layer) on the Llama-3-8B-shaped workload (batch 8, 32 q heads /
+8 kv heads, D=128, bf16 K/V, context 8192, KV block 16).  Prints one JSON line.
+
+Timing: inputs are resident in HBM before the timed region.  To keep the
+256 MB MALL and the L2s cold without a flush kernel inside the timed region,
+the page pool holds R copies of the cache and consecutive calls use block
+tables that point into different copies (R chosen so that R-1 calls read more
+than 512 MB).  The K timed calls are captured into one HIP graph (so host
+launch overhead cannot gap the few-µs kernels) and replayed back to back on
+the current stream between two HIP events; µs/step = elapsed / K.
+
+Also reported: full-attention mode, the fraction of KV blocks the kernel read
+(its own counter), the oracle's floor for that fraction, achieved bandwidth on
+algorithmic and on actually-read bytes, and the CPU oracle timed on the host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_GBPS = 8000.0
+METRIC = "decode-attn µs/step + achieved HBM GB/s (frac of peak) + KV fraction read, 1 GPU"
+KERNEL_SOURCES = ["kv_cache_run_amd/csrc/art_kernels_impl.h", "kv_cache_run_amd/csrc/art_api.cpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(case: dict, stop: np.ndarray) -> dict:
+    """Bytes the method itself must move for one call, given the heads' stops.
+
+    Per stream (sequence, kv-head): F = max over the query group of stop_block
+    blocks of K and V tiles (plus two fp32 scales per tile for fp8); per
+    sequence: the order and table entries of its longest-running stream;
+    plus q, seq_lens, out and stop_block.
+    """
+    B, D = case["block_size"], case["head_dim"]
+    es = {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}[case["kv_dtype"]]
+    qes = {"f32": 4, "bf16": 2}[case["q_dtype"]]
+    tile = 2 * B * D * es + (8 if case["kv_dtype"] == "fp8_e4m3fn" else 0)
+    g = case["num_q_heads"] // case["num_kv_heads"]
+    F = stop.reshape(case["batch"], case["num_kv_heads"], g).max(axis=2).astype(np.int64)
+    kv = int(F.sum()) * tile
+    meta = int(F.max(axis=1).sum()) * 8 + case["batch"] * 4
+    q = case["batch"] * case["num_q_heads"] * D * qes
+    outb = case["batch"] * case["num_q_heads"] * (D * 4 + 4)
+    return {"total": kv + meta + q + outb, "kv": kv, "blocks": int(F.sum()), "tile": tile}
+
+
+def _oracle_worker(args):
+    (case, pairs, mode) = args
+    import oracle
+    from kv_cache_run_amd import synth
+
+    t = time.perf_counter()
+    if mode == "art":
+        oracle.art_reference(*synth.oracle_arrays(case), eps_mag=case["eps_mag"], eps_dir=case["eps_dir"],
+                             patience=case["patience"], pairs=pairs, **synth.oracle_kwargs(case))
+    else:
+        oracle.art_reference(*synth.oracle_arrays(case), eps_mag=0.0, eps_dir=0.0, patience=1, pairs=pairs,
+                             **synth.oracle_kwargs(case))
+    return time.perf_counter() - t
+
+
+def cpu_baseline(case: dict, mode: str, max_seconds: float = 12.0) -> dict:
+    """Time the float64 oracle as it stands on the host cores, on whole sequences.
+
+    Sequences are handed to one worker process per core (single-threaded
+    BLAS each).  A bounded prefix of the batch is timed and scaled to one step.
+    """
+    import multiprocessing as mp
+
+    os.environ["OMP_NUM_THREADS"] = "1"
+    os.environ["OPENBLAS_NUM_THREADS"] = "1"
+    os.environ["MKL_NUM_THREADS"] = "1"
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    hq = case["num_q_heads"]
+    # probe one sequence on one core to size the sample
+    t1 = _oracle_worker((case, [(0, h) for h in range(hq)], mode))
+    per_seq = max(t1, 1e-6)
+    nseq = int(min(case["batch"], max(1, math.floor(max_seconds * cores / per_seq))))
+    ctx = mp.get_context("fork")
+    jobs = [(case, [(s, h) for h in range(hq)], mode) for s in range(nseq)]
+    t = time.perf_counter()
+    with ctx.Pool(min(cores, nseq)) as pool:
+        pool.map(_oracle_worker, jobs)
+    wall = time.perf_counter() - t
+    us_step = wall * 1e6 * case["batch"] / nseq
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": us_step, "unit": "us/step", "cores": min(cores, nseq), "kind": "oracle",
+            "sample": f"{mode} mode, {nseq} of {case['batch']} sequences (all {hq} heads each), "
+                      f"scaled to the whole batch; float64 NumPy oracle; host CPU: {model}",
+            "wall_s": wall}
+
+
+def read_traffic(kernel: str, workload: str) -> dict | None:
+    """HBM traffic from the committed counter summary, if it matches the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}--{workload}--counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return {"bytes_per_launch": float(vals["hbm_bytes_per_launch"])}
+    except (KeyError, ValueError):
+        return None
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: the Llama-3-8B-shaped decode)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration under rocprofv3)")
+    ap.add_argument("--modes", default="art,full")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md for how the "
+              "decode would shard across GPUs); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from kv_cache_run_amd import art, synth, workloads
+
+    if not os.path.exists(art.LIB_PATH):
+        from kv_cache_run_amd import build as _b
+
+        _b.build()
+    w = workloads.BY_NAME[args.workload] if args.workload else workloads.LLAMA3_8B
+    torch.cuda.set_device(0)
+    case = synth.make_case(w)
+    dev = art.case_to_device(case)
+    stream = torch.cuda.current_stream()
+    B = case["block_size"]
+    n = (case["seq_lens"].astype(np.int64) + B - 1) // B
+    total_blocks = int(n.sum()) * case["num_kv_heads"]
+    kv_tile = 2 * B * case["head_dim"] * {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}[case["kv_dtype"]]
+    pool_bytes = case["k_pages"].nbytes + case["v_pages"].nbytes
+
+    # one reference call per mode to learn the work (stops, blocks read)
+    def one_call(mode, table, out, stop, fetched, dec, kp, vp, ks, vs):
+        em, ed = (case["eps_mag"], case["eps_dir"]) if mode == "art" else (0.0, 0.0)
+        dec(dev["q"], kp, vp, table, dev["block_order"], dev["seq_lens"], em, ed, case["patience"],
+            k_scale=ks, v_scale=vs, out=out, stop_block=stop, blocks_fetched=fetched)
+
+    results = {}
+    for mode in [m for m in args.modes.split(",") if m]:
+        out = torch.empty((case["batch"], case["num_q_heads"], case["head_dim"]), dtype=torch.float32,
+                          device="cuda")
+        stop = torch.empty((case["batch"], case["num_q_heads"]), dtype=torch.int32, device="cuda")
+        fetched = torch.empty((case["batch"], case["num_kv_heads"]), dtype=torch.int32, device="cuda")
+        dec = art.Decoder(dev["q"], dev["k_pages"], dev["block_table"])
+        one_call(mode, dev["block_table"], out, stop, fetched, dec, dev["k_pages"], dev["v_pages"],
+                 dev["k_scale"], dev["v_scale"])
+        torch.cuda.synchronize()
+        stop_h = stop.cpu().numpy()
+        fetched_h = fetched.cpu().numpy()
+        read_bytes = int(fetched_h.sum()) * kv_tile
+        # page-pool copies so that consecutive calls read cold memory
+        R = int(min(64, max(2, math.ceil(512e6 / max(read_bytes, 1)) + 1),
+                    max(2, (48 << 30) // max(pool_bytes, 1))))
+        def rep(t):
+            if t.dtype == torch.float8_e4m3fn:
+                return t.view(torch.uint8).repeat(R, 1, 1, 1).view(torch.float8_e4m3fn)
+            return t.repeat(R, 1, 1, 1)
+
+        kp = rep(dev["k_pages"])
+        vp = rep(dev["v_pages"])
+        ks = None if dev["k_scale"] is None else dev["k_scale"].repeat(R, 1)
+        vs = None if dev["v_scale"] is None else dev["v_scale"].repeat(R, 1)
+        npages = case["num_pages"]
+        tables = [dev["block_table"] + r * npages for r in range(R)]
+        dec = art.Decoder(dev["q"], kp, dev["block_table"])
+        for i in range(args.warmup):
+            one_call(mode, tables[i % R], out, stop, fetched, dec, kp, vp, ks, vs)
+        torch.cuda.synchronize()
+        # The K timed calls are captured into one HIP graph so that host launch
+        # overhead does not gap the (few-µs) kernels; replays launch back to back.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                one_call(mode, tables[(args.warmup + i) % R], out, stop, fetched, dec, kp, vp, ks, vs)
+        graph.replay()  # first replay uploads the graph; untimed
+        torch.cuda.synchronize()
+        out_first = out.clone()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        graph.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = ev0.elapsed_time(ev1) / args.steps
+        assert np.array_equal(stop.cpu().numpy(), stop_h), "stops changed across page copies / replays"
+        assert torch.equal(out, out_first), "graph replays disagree"
+        del graph
+        alg = algorithmic_bytes(case, stop_h)
+        us = ms * 1e3
+        results[mode] = {
+            "us_per_step": us,
+            "wall_s": wall,
+            "page_copies": R,
+            "alg_bytes": alg["total"],
+            "read_bytes": read_bytes,
+            "achieved_GBps": alg["total"] / (us * 1e-6) / 1e9,
+            "read_GBps": read_bytes / (us * 1e-6) / 1e9,
+            "kv_fraction_read": float(fetched_h.sum()) / total_blocks,
+            "kv_fraction_needed": alg["blocks"] / total_blocks,
+        }
+        del kp, vp, ks, vs, tables, dec
+        torch.cuda.empty_cache()
+
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu and "art" in results:
+        cpu = cpu_baseline(case, "art")
+
+    head = results.get("art") or next(iter(results.values()))
+    head_mode = "art" if "art" in results else next(iter(results))
+    kname = "art_chunk_kernel" if head_mode == "art" else "full_split_kernel"
+    traffic = read_traffic(kname, w.name)
+    roofline = {
+        "bound": "hbm",
+        "kernel": kname,
+        "achieved": round(head["achieved_GBps"], 1),
+        "peak": PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(head["achieved_GBps"] / PEAK_GBPS, 4),
+        "traffic": None if traffic is None else traffic["bytes_per_launch"],
+        "alg_bytes_per_launch": head["alg_bytes"],
+    }
+    line = {
+        "metric": METRIC,
+        "value": round(head["us_per_step"], 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["us_per_step"] / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case["kv_dtype"] + "-in/f32-accum",
+        "data": "synthetic (seeded Gaussian q/K/V with planted heavy keys; no dataset or weights)",
+        "config": {"workload": w.name, "mode": head_mode, "batch": case["batch"], "q_heads": case["num_q_heads"],
+                   "kv_heads": case["num_kv_heads"], "head_dim": case["head_dim"],
+                   "context": int(case["seq_lens"].max()), "block_size": B, "eps_mag": case["eps_mag"],
+                   "eps_dir": case["eps_dir"], "patience": case["patience"]},
+        "achieved_GBps": round(head["achieved_GBps"], 1),
+        "hbm_frac": round(head["achieved_GBps"] / PEAK_GBPS, 4),
+        "read_GBps": round(head["read_GBps"], 1),
+        "kv_fraction_read": round(head["kv_fraction_read"], 5),
+        "kv_fraction_needed": round(head["kv_fraction_needed"], 5),
+        "modes": {m: {k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}
+                  for m, r in results.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

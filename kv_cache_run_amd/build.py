@@ -30,6 +30,9 @@ DEVICE_FLAGS = [
     "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # Run LLVM's machine-code verifier: a register-liveness miscompile then
+    # fails the build instead of producing wrong results.
+    "-mllvm", "-verify-machineinstrs",
 ]
 
 

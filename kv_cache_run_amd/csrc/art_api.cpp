@@ -15,11 +15,11 @@ SplitPlan full_split_plan(int batch, int hkv, int max_blocks) {
   long splits = streams > 0 ? (target_wgs + streams - 1) / streams : 1;
   const long by_len = (max_blocks + 7) / 8;  // at least 8 blocks (2 per wave) per split
   if (splits > by_len) splits = by_len;
-  if (splits > 64) splits = 64;
   if (splits < 1) splits = 1;
   long per = (max_blocks + splits - 1) / splits;
   per = (per + 3) / 4 * 4;
   if (per < 4) per = 4;
+  if (per > 256) per = 256;  // at most 64 blocks per wave (one lane-held page table)
   splits = (max_blocks + per - 1) / per;
   if (splits < 1) splits = 1;
   return SplitPlan{(int)splits, (int)per};

@@ -1,4 +1,5 @@
-// gfx950 kernels for ART paged decode attention.
+// gfx950 kernels for ART paged decode attention (templates; instantiated in
+// kern_<kernel>_<type>.hip).
 //
 // Method: "ART: Attention Run-time Termination for Efficient Large Language
 // Model Decoding" (gist.science explainer), Technical Summary 2.1-2.4.
@@ -6,38 +7,43 @@
 // Two kernels share one per-block datapath (QK on MFMA, block softmax, PV on
 // the VALU in fp32):
 //
-//  * art_chunk_kernel -- the terminating path.  One workgroup (4 waves) owns
-//    one stream = (sequence, kv-head) and walks its visit order in chunks of
-//    C blocks.  All blocks of a chunk are fetched at once (speculatively) and
-//    reduced to per-block partials (m_b, l_b, a_b) in LDS; then one wave per
-//    query head folds the partials in visit order, forms O_t = A_t / L_t for
-//    every t of the chunk, reduces ‖O_t‖² and ‖O_t - O_{t-1}‖² for all t at
-//    once (transposed butterfly), evaluates both statistics for all t in
-//    parallel (one lane per t) and runs the patience counter over the
-//    resulting pass bitmask.  A head that stops writes O_t and is frozen; the
-//    stream stops fetching when every head of its group stopped.
+//  * art_chunk_kernel -- the terminating path.  One workgroup (NWA waves)
+//    owns one stream = (sequence, kv-head) and walks its visit order in
+//    chunks of C blocks.  All blocks of a chunk are fetched at once
+//    (speculatively) and reduced to per-block partials (m_b, l_b, a_b) in
+//    LDS; then one wave per query head folds the partials in visit order,
+//    forms O_t = A_t / L_t for every t of the chunk, reduces ‖O_t‖² and
+//    ‖O_t - O_{t-1}‖² for all t at once (transposed butterfly), evaluates
+//    both statistics for all t in parallel (one lane per t) and runs the
+//    patience counter over the resulting pass bitmask.  A head that stops
+//    writes O_t and is frozen; the stream stops fetching when every head of
+//    its group stopped.  The page entries of chunk c+1 are fetched while
+//    chunk c is computed, so a chunk's KV loads never wait on the table.
 //
 //  * full_split_kernel -- full attention (no detector).  Each workgroup owns
 //    a contiguous slice of one stream's blocks; each wave keeps its own
-//    online-softmax state; waves merge through LDS; slices merge through a
-//    workspace, finished by the last-arriving workgroup of the stream.
+//    online-softmax state with the next block's loads in flight; waves merge
+//    through LDS; slices merge through a workspace, finished by the
+//    last-arriving workgroup of the stream.
 //
 // Data layout (HBM): k_pages/v_pages [page][kv_head][B][D], the (page, kvh)
 // tile contiguous, so one block of one stream is B*D*es contiguous bytes.
 //
 // Lane layouts inside a wave (64 lanes):
 //  * K, MFMA A operand: lane l loads 16 B of token row (l & 15) of each
-//    16-row tile at byte (l >> 4) * 16 + 64 * i.  The d-index <-> k-slot map
-//    is the same for the q operand (B operand, column = head l & 15), so the
-//    dot product is exact in any order.
+//    16-row tile at byte (l >> 4) * 16 + 64 * i.  The q operand (B operand,
+//    column = head l & 15) uses the same byte -> d map, so the dot product
+//    pairs q[d] with k[d] exactly.
 //  * Scores (16x16 MFMA result): lane l holds head (l & 15), tokens
 //    4 * (l >> 4) + r, r = 0..3, of each 16-row tile.
 //  * V and the PV accumulator: lane l owns VB contiguous bytes of a row:
-//    segment (l % LPR) of rows j with j % RPL == l / LPR.
+//    segment (l % LPR) of the rows j with j % RPL == l / LPR.
 #pragma once
-#include "art_internal.h"
-
 #include <math.h>
+
+#include <type_traits>
+
+#include "art_internal.h"
 
 namespace art {
 namespace kern {
@@ -46,9 +52,9 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 
-constexpr int NW = 4;         // waves per workgroup
-constexpr int WG = 64 * NW;   // threads per workgroup
 constexpr float NEG_INF = -__builtin_inff();
+constexpr int NW = 4;        // waves per workgroup, full-attention kernel
+constexpr int WG = 64 * NW;  // threads per workgroup, full-attention kernel
 
 template <int KV> struct ElemSize;
 template <> struct ElemSize<KV_F32> { static constexpr int v = 4; };
@@ -56,6 +62,7 @@ template <> struct ElemSize<KV_BF16> { static constexpr int v = 2; };
 template <> struct ElemSize<KV_FP8> { static constexpr int v = 1; };
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
 
 template <int KV_, int D_, int B_, int GM_>
 struct Cfg {
@@ -70,17 +77,17 @@ struct Cfg {
   static constexpr int EPL = VB / ES;                 // V elements per lane
   static constexpr int VL = B / RPL;                  // V loads per lane per block
   static constexpr int QF = KV == KV_FP8 ? 2 * NKL : NKL;  // 16-B q fragments
-  static constexpr int C0 = 256 / B;
-  static constexpr int C1 = 8192 / (GM * D);
-  static constexpr int C = C0 < C1 ? C0 : C1;         // ART chunk (blocks); partials fit 32 KiB
-  static constexpr int BPW = C / NW;                  // blocks per wave per chunk
-  static constexpr int HPW = (GM + NW - 1) / NW;      // query heads per wave in the scan
+  // ART chunk: C blocks; the per-block partials [C][GM][D] fp32 fit 32 KiB
+  static constexpr int C = cmin(256 / B, 8192 / (GM * D));
+  static constexpr int NWA = cmin(8, C);              // waves per workgroup, ART kernel
+  static constexpr int BPW = C / NWA;                 // blocks per wave per chunk
+  static constexpr int HPW = (GM + NWA - 1) / NWA;    // query heads per wave in the scan
   static constexpr int DPL = D / 64;                  // d per lane in the scan
-  static constexpr int LOG2C2 = ilog2(2 * C);
-  static constexpr int SH = 6 - LOG2C2;               // stat reduction: lane >> SH = value index
-  static_assert(BPW >= 1, "chunk must give every wave a block");
+  static constexpr int SH = 6 - ilog2(2 * C);         // stat reduction: lane >> SH = value index
+  static_assert(BPW >= 1 && BPW * NWA == C, "chunk must split evenly over the waves");
   static_assert(2 * C <= 64, "stat reduction holds at most 64 values");
   static_assert(LPR * EPL == D, "V lanes must tile a row");
+  static_assert(B % (4 * RPL) == 0, "P quads must cover the lane's rows");
 };
 
 template <int VB> struct VWordT;
@@ -93,9 +100,107 @@ struct BlockRegs {
   typename VWordT<Cf::VB>::type v[Cf::VL];
 };
 
-__device__ __forceinline__ float bits_f(uint32_t x) { return __uint_as_float(x); }
+// ---------------------------------------------------------------------------
+// Cross-lane primitives (VALU only: DPP and the gfx950 permlane swaps)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t fbits(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ float bitsf(uint32_t x) { return __uint_as_float(x); }
 
-// 4 fp8 E4M3FN bytes -> 4 floats (exact).
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane ^ 7 within each 8
+constexpr int DPP_ROW_MIRROR = 0x140;   // lane ^ 15 within each 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return bitsf(__builtin_amdgcn_update_dpp(0u, fbits(x), CTRL, 0xF, 0xF, true));
+}
+
+// v_permlane32_swap: lanes 32..63 of a <-> lanes 0..31 of b.
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(fbits(a), fbits(b), false, false);
+  a = bitsf(r[0]);
+  b = bitsf(r[1]);
+}
+// v_permlane16_swap: odd 16-lane rows of a <-> even 16-lane rows of b.
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane16_swap(fbits(a), fbits(b), false, false);
+  a = bitsf(r[0]);
+  b = bitsf(r[1]);
+}
+
+// Reductions over the four 16-lane rows (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float rows_max(float x) {
+  float y = x;
+  swap32(x, y);
+  x = fmaxf(x, y);
+  y = x;
+  swap16(x, y);
+  return fmaxf(x, y);
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  float y = x;
+  swap32(x, y);
+  x += y;
+  y = x;
+  swap16(x, y);
+  return x + y;
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  float y = x;
+  swap32(x, y);
+  return x + y;
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  float y = x;
+  swap16(x, y);
+  return x + y;
+}
+
+// One transposed-butterfly stage inside a 16-lane row: lanes with `up` keep
+// the upper half of the live values, the partner lane (given by CTRL) the lower.
+template <int CTRL, int HALF, int K>
+__device__ __forceinline__ void xstage(float (&v)[K], bool up) {
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) {
+    const float send = up ? v[i] : v[i + HALF];
+    const float keep = up ? v[i + HALF] : v[i];
+    v[i] = keep + dpp<CTRL>(send);
+  }
+}
+
+// Transposed butterfly over 64 lanes: every lane returns the 64-lane sum of
+// v[lane >> (6 - log2 K)].  Pairings per stage: l^32, l^16 (permlane swaps),
+// l^15, l^7 (row / half-row mirrors), l^2, l^1 (quad permutes); together they
+// generate all 64 lanes, so each value is summed over every lane once.
+template <int K>
+__device__ __forceinline__ float xreduce(float (&v)[K], int lane) {
+  constexpr int LOGK = ilog2(K);
+  static_assert((1 << LOGK) == K && K <= 64, "K must be a power of two <= 64");
+  if constexpr (LOGK >= 1) {
+#pragma unroll
+    for (int i = 0; i < K / 2; ++i) { swap32(v[i], v[i + K / 2]); v[i] += v[i + K / 2]; }
+  } else {
+    v[0] = xor32_sum(v[0]);
+  }
+  if constexpr (LOGK >= 2) {
+#pragma unroll
+    for (int i = 0; i < K / 4; ++i) { swap16(v[i], v[i + K / 4]); v[i] += v[i + K / 4]; }
+  } else {
+    v[0] = xor16_sum(v[0]);
+  }
+  if constexpr (LOGK >= 3) xstage<DPP_ROW_MIRROR, K / 8>(v, (lane & 8) != 0); else v[0] += dpp<DPP_ROW_MIRROR>(v[0]);
+  if constexpr (LOGK >= 4) xstage<DPP_HALF_MIRROR, K / 16>(v, (lane & 4) != 0); else v[0] += dpp<DPP_HALF_MIRROR>(v[0]);
+  if constexpr (LOGK >= 5) xstage<DPP_XOR2, K / 32>(v, (lane & 2) != 0); else v[0] += dpp<DPP_XOR2>(v[0]);
+  if constexpr (LOGK >= 6) xstage<DPP_XOR1, K / 64>(v, (lane & 1) != 0); else v[0] += dpp<DPP_XOR1>(v[0]);
+  return v[0];
+}
+
+// ---------------------------------------------------------------------------
+// Per-block datapath
+// ---------------------------------------------------------------------------
+
+// 4 fp8 E4M3FN bytes -> 4 floats (exact; gfx950 converts the OCP format).
 __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float (&o)[4]) {
   f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
   f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
@@ -173,10 +278,10 @@ __device__ __forceinline__ void qk_scores(const BlockRegs<Cf>& r, const uint4 (&
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi),
                                                       __builtin_bit_cast(bf16x8, qf[2 * i + 1]), acc, 0, 0, 0);
       } else {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bits_f(kk.x), bits_f(qf[i].x), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bits_f(kk.y), bits_f(qf[i].y), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bits_f(kk.z), bits_f(qf[i].z), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bits_f(kk.w), bits_f(qf[i].w), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bitsf(kk.x), bitsf(qf[i].x), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bitsf(kk.y), bitsf(qf[i].y), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bitsf(kk.z), bitsf(qf[i].z), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bitsf(kk.w), bitsf(qf[i].w), acc, 0, 0, 0);
       }
     }
     S[t] = acc;
@@ -197,15 +302,33 @@ __device__ __forceinline__ float block_scores(const f32x4 (&S)[Cf::T], int nvali
       x[t][r] = tok < nvalid ? S[t][r] * sl2 : NEG_INF;
       mb = fmaxf(mb, x[t][r]);
     }
-  mb = fmaxf(mb, __shfl_xor(mb, 16));
-  mb = fmaxf(mb, __shfl_xor(mb, 32));
-  return mb;
+  return rows_max(mb);
 }
 
-__device__ __forceinline__ float sum_quads(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+// Store the lane's P values (score layout) into the wave's P rows so that a
+// PV lane reads its own rows contiguously: token j of head h is stored at
+// h*B + (j % RPL) * (B / RPL) + j / RPL.
+template <class Cf>
+__device__ __forceinline__ void store_p(float* pw, int lane, const float (&pv)[Cf::T][4]) {
+  const int c = lane & 15;
+  const int quad = lane >> 4;
+  if (c >= Cf::GM) return;
+  float* row = pw + c * Cf::B;
+  if constexpr (Cf::RPL == 1) {
+#pragma unroll
+    for (int t = 0; t < Cf::T; ++t) {
+      f32x4 q4 = {pv[t][0], pv[t][1], pv[t][2], pv[t][3]};
+      *reinterpret_cast<f32x4*>(row + 16 * t + 4 * quad) = q4;
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < Cf::T; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * t + 4 * quad + r;
+        row[(j % Cf::RPL) * (Cf::B / Cf::RPL) + j / Cf::RPL] = pv[t][r];
+      }
+  }
 }
 
 __device__ __forceinline__ void wave_lds_fence() {
@@ -217,101 +340,83 @@ __device__ __forceinline__ void wave_lds_fence() {
 template <class Cf>
 __device__ __forceinline__ void decode_v(typename VWordT<Cf::VB>::type w, float (&o)[Cf::EPL]) {
   if constexpr (Cf::KV == KV_BF16) {
-    o[0] = bits_f(w << 16);
-    o[1] = bits_f(w & 0xffff0000u);
+    o[0] = bitsf(w << 16);
+    o[1] = bitsf(w & 0xffff0000u);
   } else if constexpr (Cf::KV == KV_FP8) {
     float f[4];
     fp8x4_to_f32(w, f);
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = f[e];
   } else if constexpr (Cf::VB == 4) {
-    o[0] = bits_f(w);
+    o[0] = bitsf(w);
   } else {
-    o[0] = bits_f(w.x);
-    o[1] = bits_f(w.y);
+    o[0] = bitsf(w.x);
+    o[1] = bitsf(w.y);
   }
 }
 
-// acc[h][e] += sum_j P[h][j] * V[j][d(e)] over the lane's rows of one block.
+// acc[h][e] += sum_j P[h][j] * V[j][d(e)] over the lane's rows of one block,
+// for every head slot of the group capacity (slots >= g carry finite junk).
+// Rows past the sequence end may hold any bits, so they are replaced by 0 with
+// a select on every block (no branch: a branch-local redefinition of the
+// decoded values has been miscompiled by the register allocator).
 template <class Cf>
-__device__ __forceinline__ void pv_accumulate(const BlockRegs<Cf>& r, int nvalid, const float* pw, int g, int lane,
+__device__ __forceinline__ void pv_accumulate(const BlockRegs<Cf>& r, int nvalid, const float* pw, int lane,
                                               float (&acc)[Cf::GM][Cf::EPL]) {
   const int rg = lane / Cf::LPR;
+  float v[Cf::VL][Cf::EPL];
 #pragma unroll
   for (int u = 0; u < Cf::VL; ++u) {
-    const int j = u * Cf::RPL + rg;
-    float v[Cf::EPL];
-    decode_v<Cf>(r.v[u], v);
-    if (nvalid < Cf::B) {
-      const bool ok = j < nvalid;
+    decode_v<Cf>(r.v[u], v[u]);
+    const bool ok = u * Cf::RPL + rg < nvalid;
 #pragma unroll
-      for (int e = 0; e < Cf::EPL; ++e) v[e] = ok ? v[e] : 0.f;
-    }
+    for (int e = 0; e < Cf::EPL; ++e) v[u][e] = ok ? v[u][e] : 0.f;
+  }
+  const float* base = pw + rg * (Cf::B / Cf::RPL);
 #pragma unroll
-    for (int h = 0; h < Cf::GM; ++h) {
-      if (h < g) {
-        const float pp = pw[h * Cf::B + j];
+  for (int h = 0; h < Cf::GM; ++h) {
 #pragma unroll
-        for (int e = 0; e < Cf::EPL; ++e) acc[h][e] = fmaf(pp, v[e], acc[h][e]);
-      }
+    for (int k = 0; k < Cf::VL / 4; ++k) {
+      const f32x4 p4 = *reinterpret_cast<const f32x4*>(base + h * Cf::B + 4 * k);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < Cf::EPL; ++e) acc[h][e] = fmaf(p4[m], v[4 * k + m][e], acc[h][e]);
     }
   }
 }
 
 // Sum the PV accumulator over the RPL row groups (lanes sharing a segment).
 template <class Cf>
-__device__ __forceinline__ void reduce_row_groups(float (&acc)[Cf::GM][Cf::EPL], int g) {
+__device__ __forceinline__ void reduce_row_groups(float (&acc)[Cf::GM][Cf::EPL]) {
   if constexpr (Cf::RPL >= 2) {
 #pragma unroll
     for (int h = 0; h < Cf::GM; ++h)
-      if (h < g)
 #pragma unroll
-        for (int e = 0; e < Cf::EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], 32);
+      for (int e = 0; e < Cf::EPL; ++e) acc[h][e] = xor32_sum(acc[h][e]);
   }
   if constexpr (Cf::RPL == 4) {
 #pragma unroll
     for (int h = 0; h < Cf::GM; ++h)
-      if (h < g)
 #pragma unroll
-        for (int e = 0; e < Cf::EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], 16);
+      for (int e = 0; e < Cf::EPL; ++e) acc[h][e] = xor16_sum(acc[h][e]);
   }
 }
 
-// Transposed butterfly: returns, in every lane, the 64-lane sum of
-// v[lane >> (6 - log2 K)].
-template <int K>
-__device__ __forceinline__ float xreduce(float (&v)[K], int lane) {
-  constexpr int LOGK = ilog2(K);
-#pragma unroll
-  for (int st = 0; st < LOGK; ++st) {
-    const int sft = 32 >> st;
-    const int half = K >> (st + 1);
-    const bool up = (lane & sft) != 0;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float send = up ? v[i] : v[i + half];
-      const float keep = up ? v[i + half] : v[i];
-      v[i] = keep + __shfl_xor(send, sft);
-    }
-  }
-  float r = v[0];
-#pragma unroll
-  for (int sft = 32 >> LOGK; sft >= 1; sft >>= 1) r += __shfl_xor(r, sft);
-  return r;
-}
+__device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float readlanef(float v, int l) { return bitsf(__builtin_amdgcn_readlane(fbits(v), l)); }
 
 // ---------------------------------------------------------------------------
 // Terminating kernel
 // ---------------------------------------------------------------------------
 template <int KV, int D, int B, int GM>
-__global__ __launch_bounds__(WG) void art_chunk_kernel(Params p) {
+__global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_chunk_kernel(Params p) {
   using Cf = Cfg<KV, D, B, GM>;
-  constexpr int C = Cf::C, BPW = Cf::BPW, HPW = Cf::HPW, DPL = Cf::DPL, SH = Cf::SH;
+  constexpr int C = Cf::C, NWA = Cf::NWA, BPW = Cf::BPW, HPW = Cf::HPW, DPL = Cf::DPL, SH = Cf::SH;
   __shared__ float part_a[C][GM][D];
   __shared__ float part_m[C][GM];
   __shared__ float part_l[C][GM];
-  __shared__ __attribute__((aligned(16))) float p_lds[NW][GM][B];
-  __shared__ int ord_lds[C];
+  __shared__ __attribute__((aligned(16))) float p_lds[NWA][GM][B];
   __shared__ int alive_lds[GM];
 
   const int lane = threadIdx.x & 63;
@@ -325,7 +430,7 @@ __global__ __launch_bounds__(WG) void art_chunk_kernel(Params p) {
   const size_t head0 = (size_t)s * p.hq + (size_t)kvh * g;
 
   if (n <= 0) {
-    for (int i = threadIdx.x; i < g * D; i += WG) p.out[head0 * D + i] = 0.f;
+    for (int i = threadIdx.x; i < g * D; i += 64 * NWA) p.out[head0 * D + i] = 0.f;
     if (threadIdx.x < g) p.stop_block[head0 + threadIdx.x] = 0;
     if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[stream] = 0;
     return;
@@ -339,12 +444,16 @@ __global__ __launch_bounds__(WG) void art_chunk_kernel(Params p) {
   const char* vbase = static_cast<const char*>(p.v_pages);
   const int32_t* trow = p.block_table + (size_t)s * p.max_blocks;
   const int32_t* orow = p.block_order + (size_t)s * p.max_blocks;
-  const int c = lane & 15;
-  const int quad = lane >> 4;
   const int rg = lane / Cf::LPR;
   const int sg = lane % Cf::LPR;
+  const int slot = lane < C ? lane : C - 1;
 
-  // Per-head streaming state, carried across chunks (head h = w + NW * k).
+  // Chunk entries, one per lane (slot = lane): logical block, page, fp8 scales.
+  int ob_l = orow[min(slot, n - 1)];
+  int pg_l = trow[ob_l];
+  float ks_l = 1.f, vs_l = 1.f;
+
+  // Per-head streaming state, carried across chunks (head h = w + NWA * k).
   float cM[HPW], cL[HPW], cNp[HPW];
   int cCnt[HPW];
   bool cAlive[HPW], cSink[HPW];
@@ -352,7 +461,7 @@ __global__ __launch_bounds__(WG) void art_chunk_kernel(Params p) {
 #pragma unroll
   for (int k = 0; k < HPW; ++k) {
     cM[k] = NEG_INF; cL[k] = 0.f; cNp[k] = 0.f; cCnt[k] = 0; cSink[k] = false;
-    cAlive[k] = (w + NW * k) < g;
+    cAlive[k] = (w + NWA * k) < g;
 #pragma unroll
     for (int j = 0; j < DPL; ++j) { cA[k][j] = 0.f; cOp[k][j] = 0.f; }
   }
@@ -361,76 +470,76 @@ __global__ __launch_bounds__(WG) void art_chunk_kernel(Params p) {
   for (int t0 = 0; t0 < n; t0 += C) {
     const int nt = min(C, n - t0);
 
-    // ---- block phase: fetch the chunk (all of this wave's blocks in flight), then reduce
+    // ---- block phase: every load of the wave's blocks in flight, then reduce.
+    // Slots past the chunk end re-read the last valid slot (an L2 hit), so the
+    // loads are unconditional and the wait counts stay exact.
     BlockRegs<Cf> regs[BPW];
-    int nval[BPW];
-    float ksc[BPW], vsc[BPW];
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
-      const int b = w * BPW + i;
-      nval[i] = 0; ksc[i] = 1.f; vsc[i] = 1.f;
-      if (b < nt) {
-        const int ob = orow[t0 + b];
-        const int pg = trow[ob];
-        nval[i] = min(B, L - ob * B);
-        const size_t off = ((size_t)pg * p.hkv + kvh) * tile;
-        load_block<Cf>(regs[i], kbase + off, vbase + off, lane);
-        if constexpr (KV == KV_FP8) {
-          ksc[i] = p.k_scale[(size_t)pg * p.hkv + kvh];
-          vsc[i] = p.v_scale[(size_t)pg * p.hkv + kvh];
-        }
-        if (lane == 0) ord_lds[b] = ob;
-      }
+      const int b = min(w * BPW + i, nt - 1);
+      const int pg = readlane(pg_l, b);
+      const size_t off = ((size_t)pg * p.hkv + kvh) * tile;
+      load_block<Cf>(regs[i], kbase + off, vbase + off, lane);
     }
+    if constexpr (KV == KV_FP8) {
+      ks_l = p.k_scale[(size_t)pg_l * p.hkv + kvh];
+      vs_l = p.v_scale[(size_t)pg_l * p.hkv + kvh];
+    }
+    // next chunk's order entries (consumed after this chunk's scan)
+    const int ob_n = orow[min(t0 + C + slot, n - 1)];
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
       const int b = w * BPW + i;
       if (b < nt) {
+        const int ob = readlane(ob_l, b);
+        const int nvalid = min(B, L - ob * B);
+        float ksc = 1.f, vsc = 1.f;
+        if constexpr (KV == KV_FP8) { ksc = readlanef(ks_l, b); vsc = readlanef(vs_l, b); }
         f32x4 S[Cf::T];
         qk_scores<Cf>(regs[i], qf, S);
         float x[Cf::T][4];
-        const float mb = block_scores<Cf>(S, nval[i], p.qk_log2 * ksc[i], lane, x);
+        const float mb = block_scores<Cf>(S, nvalid, p.qk_log2 * ksc, lane, x);
         float ls = 0.f;
-        f32x4 pq[Cf::T];
+        float pq[Cf::T][4];
 #pragma unroll
         for (int t = 0; t < Cf::T; ++t)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float e = __builtin_amdgcn_exp2f(x[t][r] - mb);
             ls += e;
-            pq[t][r] = e * vsc[i];
+            pq[t][r] = e * vsc;
           }
-        ls = sum_quads(ls);
-        if (c < g) {
-#pragma unroll
-          for (int t = 0; t < Cf::T; ++t) *reinterpret_cast<f32x4*>(&p_lds[w][c][16 * t + 4 * quad]) = pq[t];
-          if (quad == 0) { part_m[b][c] = mb; part_l[b][c] = ls; }
-        }
+        ls = rows_sum(ls);
+        store_p<Cf>(&p_lds[w][0][0], lane, pq);
+        const int c = lane & 15;
+        if (c < GM && (lane >> 4) == 0) { part_m[b][c] = mb; part_l[b][c] = ls; }
         wave_lds_fence();
         float acc[GM][Cf::EPL];
 #pragma unroll
         for (int h = 0; h < GM; ++h)
 #pragma unroll
           for (int e = 0; e < Cf::EPL; ++e) acc[h][e] = 0.f;
-        pv_accumulate<Cf>(regs[i], nval[i], &p_lds[w][0][0], g, lane, acc);
-        reduce_row_groups<Cf>(acc, g);
+        pv_accumulate<Cf>(regs[i], nvalid, &p_lds[w][0][0], lane, acc);
+        reduce_row_groups<Cf>(acc);
         if (rg == 0) {
 #pragma unroll
           for (int h = 0; h < GM; ++h)
-            if (h < g)
 #pragma unroll
-              for (int e = 0; e < Cf::EPL; ++e) part_a[b][h][sg * Cf::EPL + e] = acc[h][e];
+            for (int e = 0; e < Cf::EPL; ++e) part_a[b][h][sg * Cf::EPL + e] = acc[h][e];
         }
         wave_lds_fence();
       }
     }
+    // next chunk's pages (the order entries have arrived by now)
+    const int pg_n = trow[ob_n];
     fetched += nt;
     __syncthreads();
 
     // ---- scan phase: fold the chunk's partials in visit order, one wave per head
+    const unsigned long long sinkbits = __ballot(lane < nt && ob_l == 0);
 #pragma unroll
     for (int k = 0; k < HPW; ++k) {
-      const int h = w + NW * k;
+      const int h = w + NWA * k;
       if (h < g && cAlive[k]) {
         float st[2 * C];
 #pragma unroll
@@ -447,14 +556,14 @@ __global__ __launch_bounds__(WG) void art_chunk_kernel(Params p) {
             const float rl = 1.0f / cL[k];
 #pragma unroll
             for (int j = 0; j < DPL; ++j) {
-              float* slot = &part_a[t][h][lane + 64 * j];
-              cA[k][j] = fmaf(al, cA[k][j], be * *slot);
+              float* sl = &part_a[t][h][lane + 64 * j];
+              cA[k][j] = fmaf(al, cA[k][j], be * *sl);
               const float o = cA[k][j] * rl;
               const float df = o - cOp[k][j];
               nn = fmaf(o, o, nn);
               ee = fmaf(df, df, ee);
               cOp[k][j] = o;
-              *slot = o;  // keep O_t for the epilogue
+              *sl = o;  // keep O_t for the epilogue
             }
           }
           st[2 * t] = nn;
@@ -480,6 +589,7 @@ __global__ __launch_bounds__(WG) void art_chunk_kernel(Params p) {
           } else {
             const float df = a - bn;
             dm = fabsf(df) / bn;
+            // 1 - cos = (‖O_t - O_{t-1}‖² - (‖O_t‖ - ‖O_{t-1}‖)²) / (2 ‖O_t‖ ‖O_{t-1}‖)
             dd = (a == 0.f) ? 1.f : fmaxf(0.f, (e_t - df * df) / (2.f * a * bn));
           }
           ps = (dm < p.eps_mag) && (dd < p.eps_dir);
@@ -491,7 +601,7 @@ __global__ __launch_bounds__(WG) void art_chunk_kernel(Params p) {
         int stop_t = -1;
         for (int t = 0; t < nt; ++t) {
           if (t0 + t >= 1) cnt = ((pm >> ((2 * t) << SH)) & 1ull) ? cnt + 1 : 0;
-          sink = sink || (ord_lds[t] == 0);
+          sink = sink || ((sinkbits >> t) & 1ull);
           if (cnt >= p.patience && sink) { stop_t = t; break; }
         }
         if (stop_t >= 0) {
@@ -510,8 +620,10 @@ __global__ __launch_bounds__(WG) void art_chunk_kernel(Params p) {
     if (lane == 0) {
 #pragma unroll
       for (int k = 0; k < HPW; ++k)
-        if (w + NW * k < g) alive_lds[w + NW * k] = cAlive[k] ? 1 : 0;
+        if (w + NWA * k < g) alive_lds[w + NWA * k] = cAlive[k] ? 1 : 0;
     }
+    ob_l = ob_n;
+    pg_l = pg_n;
     __syncthreads();
     int any = 0;
     for (int h = 0; h < g; ++h) any |= alive_lds[h];
@@ -521,7 +633,7 @@ __global__ __launch_bounds__(WG) void art_chunk_kernel(Params p) {
   // heads that never stopped: output after all n blocks
 #pragma unroll
   for (int k = 0; k < HPW; ++k) {
-    const int h = w + NW * k;
+    const int h = w + NWA * k;
     if (h < g && cAlive[k]) {
       float* o = p.out + (head0 + h) * D;
 #pragma unroll
@@ -535,23 +647,19 @@ __global__ __launch_bounds__(WG) void art_chunk_kernel(Params p) {
 // ---------------------------------------------------------------------------
 // Full-attention split kernel
 // ---------------------------------------------------------------------------
-template <int KV, int D, int B, int GM>
-__device__ __forceinline__ void full_block(const BlockRegs<Cfg<KV, D, B, GM>>& r, int nvalid, float ksc, float vsc,
-                                           const uint4 (&qf)[Cfg<KV, D, B, GM>::QF], const Params& p, int w,
-                                           int lane, float& m_run, float& l_run,
-                                           float (&acc)[GM][Cfg<KV, D, B, GM>::EPL], float (*p_lds)[GM][B],
-                                           float (*alpha_lds)[GM]) {
-  using Cf = Cfg<KV, D, B, GM>;
-  const int c = lane & 15;
-  const int quad = lane >> 4;
+template <class Cf>
+__device__ __forceinline__ void full_block(const BlockRegs<Cf>& r, int nvalid, float ksc, float vsc,
+                                           const uint4 (&qf)[Cf::QF], float qk_log2, int lane, float& m_run,
+                                           float& l_run, float (&acc)[Cf::GM][Cf::EPL], float* pw,
+                                           float* alpha_w) {
   f32x4 S[Cf::T];
   qk_scores<Cf>(r, qf, S);
   float x[Cf::T][4];
-  const float mb = block_scores<Cf>(S, nvalid, p.qk_log2 * ksc, lane, x);
+  const float mb = block_scores<Cf>(S, nvalid, qk_log2 * ksc, lane, x);
   const float mn = fmaxf(m_run, mb);
   const float al = __builtin_amdgcn_exp2f(m_run - mn);
   float ls = 0.f;
-  f32x4 pq[Cf::T];
+  float pq[Cf::T][4];
 #pragma unroll
   for (int t = 0; t < Cf::T; ++t)
 #pragma unroll
@@ -560,32 +668,27 @@ __device__ __forceinline__ void full_block(const BlockRegs<Cfg<KV, D, B, GM>>& r
       ls += e;
       pq[t][rr] = e * vsc;
     }
-  ls = sum_quads(ls);
+  ls = rows_sum(ls);
   l_run = fmaf(al, l_run, ls);
   m_run = mn;
-  const int g = p.g;
-  if (c < g) {
-#pragma unroll
-    for (int t = 0; t < Cf::T; ++t) *reinterpret_cast<f32x4*>(&p_lds[w][c][16 * t + 4 * quad]) = pq[t];
-    if (quad == 0) alpha_lds[w][c] = al;
-  }
+  store_p<Cf>(pw, lane, pq);
+  const int c = lane & 15;
+  if (c < Cf::GM && (lane >> 4) == 0) alpha_w[c] = al;
   wave_lds_fence();
 #pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    if (h < g) {
-      const float a = alpha_lds[w][h];
+  for (int h = 0; h < Cf::GM; ++h) {
+    const float a = alpha_w[h];
 #pragma unroll
-      for (int e = 0; e < Cf::EPL; ++e) acc[h][e] *= a;
-    }
+    for (int e = 0; e < Cf::EPL; ++e) acc[h][e] *= a;
   }
-  pv_accumulate<Cf>(r, nvalid, &p_lds[w][0][0], g, lane, acc);
+  pv_accumulate<Cf>(r, nvalid, pw, lane, acc);
   wave_lds_fence();
 }
 
 template <int KV, int D, int B, int GM>
 __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
   using Cf = Cfg<KV, D, B, GM>;
-  constexpr int HPW = Cf::HPW, DPL = Cf::DPL, EPL = Cf::EPL;
+  constexpr int HPW = (GM + NW - 1) / NW, DPL = Cf::DPL, EPL = Cf::EPL;
   __shared__ __attribute__((aligned(16))) float p_lds[NW][GM][B];
   __shared__ float alpha_lds[NW][GM];
   __shared__ float mw_a[NW][GM][D];
@@ -605,6 +708,8 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
   const size_t head0 = (size_t)s * p.hq + (size_t)kvh * g;
   const int b0 = split * p.split_blocks;
   const int b1 = min(n, b0 + p.split_blocks);
+  // this wave folds blocks b0 + w + NW * k, k < cnt (cnt <= 64 by the split plan)
+  const int cnt = b0 + w < b1 ? (b1 - b0 - w + NW - 1) / NW : 0;
 
   uint4 qf[Cf::QF];
   load_q<Cf>(p, s, kvh, lane, qf);
@@ -614,6 +719,17 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
   const char* vbase = static_cast<const char*>(p.v_pages);
   const int32_t* trow = p.block_table + (size_t)s * p.max_blocks;
 
+  // lane k holds the page (and fp8 scales) of the wave's k-th block
+  int tab = 0;
+  float ks_t = 1.f, vs_t = 1.f;
+  if (cnt > 0) {
+    tab = trow[b0 + w + NW * min(lane, cnt - 1)];
+    if constexpr (KV == KV_FP8) {
+      ks_t = p.k_scale[(size_t)tab * p.hkv + kvh];
+      vs_t = p.v_scale[(size_t)tab * p.hkv + kvh];
+    }
+  }
+
   float m_run = NEG_INF, l_run = 0.f;
   float acc[GM][EPL];
 #pragma unroll
@@ -621,60 +737,56 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
 
-  // Wave w folds blocks b0 + w, b0 + w + NW, ...; the next block is in flight
-  // while the current one is computed (two register sets, unrolled by two).
-  BlockRegs<Cf> ra, rb;
-  int pa = 0, pb = 0;
-  int b = b0 + w;
-  if (b < b1) {
-    pa = trow[b];
-    load_block<Cf>(ra, kbase + ((size_t)pa * p.hkv + kvh) * tile, vbase + ((size_t)pa * p.hkv + kvh) * tile, lane);
-  }
-  for (; b < b1; b += 2 * NW) {
-    const int bb = b + NW;
-    if (bb < b1) {
-      pb = trow[bb];
-      load_block<Cf>(rb, kbase + ((size_t)pb * p.hkv + kvh) * tile, vbase + ((size_t)pb * p.hkv + kvh) * tile,
-                     lane);
-    }
-    {
-      float ks = 1.f, vs = 1.f;
-      if constexpr (KV == KV_FP8) {
-        ks = p.k_scale[(size_t)pa * p.hkv + kvh];
-        vs = p.v_scale[(size_t)pa * p.hkv + kvh];
+  float* pw = &p_lds[w][0][0];
+  float* aw = &alpha_lds[w][0];
+  auto tile_of = [&](int k) { return ((size_t)readlane(tab, k) * p.hkv + kvh) * tile; };
+  auto fold = [&](const BlockRegs<Cf>& r, int k) {
+    const int b = b0 + w + NW * k;
+    float ks = 1.f, vs = 1.f;
+    if constexpr (KV == KV_FP8) { ks = readlanef(ks_t, k); vs = readlanef(vs_t, k); }
+    full_block<Cf>(r, min(B, L - b * B), ks, vs, qf, p.qk_log2, lane, m_run, l_run, acc, pw, aw);
+  };
+
+  // Two register sets; block k+1 is in flight while block k is folded.  Each
+  // fold site has a fixed number of younger loads outstanding.
+  if (cnt > 0) {
+    BlockRegs<Cf> ra, rb;
+    load_block<Cf>(ra, kbase + tile_of(0), vbase + tile_of(0), lane);
+    int k = 0;
+    for (;;) {
+      if (k + 1 < cnt) {
+        const size_t o = tile_of(k + 1);
+        load_block<Cf>(rb, kbase + o, vbase + o, lane);
+        fold(ra, k);
+      } else {
+        fold(ra, k);
+        break;
       }
-      full_block<KV, D, B, GM>(ra, min(B, L - b * B), ks, vs, qf, p, w, lane, m_run, l_run, acc, p_lds, alpha_lds);
-    }
-    if (bb >= b1) break;
-    const int bc = bb + NW;
-    if (bc < b1) {
-      pa = trow[bc];
-      load_block<Cf>(ra, kbase + ((size_t)pa * p.hkv + kvh) * tile, vbase + ((size_t)pa * p.hkv + kvh) * tile,
-                     lane);
-    }
-    {
-      float ks = 1.f, vs = 1.f;
-      if constexpr (KV == KV_FP8) {
-        ks = p.k_scale[(size_t)pb * p.hkv + kvh];
-        vs = p.v_scale[(size_t)pb * p.hkv + kvh];
+      ++k;
+      if (k + 1 < cnt) {
+        const size_t o = tile_of(k + 1);
+        load_block<Cf>(ra, kbase + o, vbase + o, lane);
+        fold(rb, k);
+      } else {
+        fold(rb, k);
+        break;
       }
-      full_block<KV, D, B, GM>(rb, min(B, L - bb * B), ks, vs, qf, p, w, lane, m_run, l_run, acc, p_lds,
-                               alpha_lds);
+      ++k;
     }
   }
-  reduce_row_groups<Cf>(acc, g);
+  reduce_row_groups<Cf>(acc);
 
   // merge the four waves
-  const int c = lane & 15;
-  const int quad = lane >> 4;
-  if (c < g && quad == 0) { mw_m[w][c] = m_run; mw_l[w][c] = l_run; }
-  if (lane / Cf::LPR == 0) {
-    const int sg = lane % Cf::LPR;
+  {
+    const int c = lane & 15;
+    if (c < g && (lane >> 4) == 0) { mw_m[w][c] = m_run; mw_l[w][c] = l_run; }
+    if (lane / Cf::LPR == 0) {
+      const int sg = lane % Cf::LPR;
 #pragma unroll
-    for (int h = 0; h < GM; ++h)
-      if (h < g)
+      for (int h = 0; h < GM; ++h)
 #pragma unroll
         for (int e = 0; e < EPL; ++e) mw_a[w][h][sg * EPL + e] = acc[h][e];
+    }
   }
   __syncthreads();
 

@@ -7,7 +7,7 @@ namespace {
 
 template <int D, int B, int GM>
 hipError_t go(const Params& p, hipStream_t st) {
-  hipLaunchKernelGGL((kern::art_chunk_kernel<KV_F32, D, B, GM>), dim3(p.batch * p.hkv), dim3(kern::WG), 0, st, p);
+  hipLaunchKernelGGL((kern::art_chunk_kernel<KV_F32, D, B, GM>), dim3(p.batch * p.hkv), dim3(64 * kern::Cfg<KV_F32, D, B, GM>::NWA), 0, st, p);
   return hipGetLastError();
 }
 

@@ -135,8 +135,15 @@ def test_shape_matrix(w):
 
 
 def _with_lens(case, lens):
+    """Shorten sequences; each order row becomes block 0 then newest to oldest of the new length."""
     c = dict(case)
     c["seq_lens"] = np.asarray(lens, dtype=np.int32)
+    order = np.full_like(case["block_order"], -1)
+    for s, L in enumerate(lens):
+        n = (int(L) + case["block_size"] - 1) // case["block_size"]
+        if n:
+            order[s, :n] = [0] + list(range(n - 1, 0, -1))
+    c["block_order"] = order
     return c
 
 
