@@ -62,9 +62,7 @@ size_t workspace_for(const art_decode_desc* d) {
   const int gm = art::group_capacity(d->num_q_heads / d->num_kv_heads);
   const size_t streams = (size_t)d->batch * d->num_kv_heads;
   size_t part = streams * sp.splits * gm * (size_t)(d->head_dim + 2) * sizeof(float);
-  part = (part + 255) / 256 * 256;
-  const size_t counters = (streams * sizeof(int32_t) + 255) / 256 * 256;
-  return part + counters;
+  return (part + 255) / 256 * 256;
 }
 
 }  // namespace
@@ -134,6 +132,7 @@ art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_
   p.hq = desc->num_q_heads;
   p.hkv = desc->num_kv_heads;
   p.g = g;
+  p.block_size = desc->block_size;
   p.max_blocks = desc->max_blocks_per_seq;
   p.eps_mag = eps_mag;
   p.eps_dir = eps_dir;
@@ -145,13 +144,7 @@ art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_
     const art::SplitPlan sp = art::full_split_plan(desc->batch, desc->num_kv_heads, desc->max_blocks_per_seq);
     p.splits = sp.splits;
     p.split_blocks = sp.split_blocks;
-    if (sp.splits > 1) {
-      const size_t streams = (size_t)desc->batch * desc->num_kv_heads;
-      size_t part = streams * sp.splits * v.gm * (size_t)(desc->head_dim + 2) * sizeof(float);
-      part = (part + 255) / 256 * 256;
-      p.ws_part = static_cast<float*>(workspace);
-      p.ws_count = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + part);
-    }
+    if (sp.splits > 1) p.ws_part = static_cast<float*>(workspace);
     e = v.kv == art::KV_F32 ? art::launch_full_f32(v, p, static_cast<hipStream_t>(stream))
         : v.kv == art::KV_BF16 ? art::launch_full_bf16(v, p, static_cast<hipStream_t>(stream))
                                : art::launch_full_fp8(v, p, static_cast<hipStream_t>(stream));

@@ -24,8 +24,8 @@ struct Params {
   int32_t* stop_block;
   int32_t* blocks_fetched;  // may be null
   float* ws_part;           // full mode with splits: [streams][splits][GM][D + 2]
-  int32_t* ws_count;        // full mode with splits: [streams] arrival counters
   int32_t batch, hq, hkv, g;
+  int32_t block_size;
   int32_t max_blocks;
   int32_t splits;           // full mode: splits per stream (1 = no merge)
   int32_t split_blocks;     // full mode: blocks per split

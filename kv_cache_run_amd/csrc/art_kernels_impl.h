@@ -23,8 +23,7 @@
 //  * full_split_kernel -- full attention (no detector).  Each workgroup owns
 //    a contiguous slice of one stream's blocks; each wave keeps its own
 //    online-softmax state with the next block's loads in flight; waves merge
-//    through LDS; slices merge through a workspace, finished by the
-//    last-arriving workgroup of the stream.
+//    through LDS; slices are merged by full_merge_kernel (second launch).
 //
 // Data layout (HBM): k_pages/v_pages [page][kv_head][B][D], the (page, kvh)
 // tile contiguous, so one block of one stream is B*D*es contiguous bytes.
@@ -553,7 +552,7 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_chunk_kerne
             const float be = __builtin_amdgcn_exp2f(mb - Mn);
             cL[k] = fmaf(al, cL[k], be * lb);
             cM[k] = Mn;
-            const float rl = 1.0f / cL[k];
+            const float rl = __builtin_amdgcn_rcpf(cL[k]);  // 1 ulp; statistics need ~1e-6
 #pragma unroll
             for (int j = 0; j < DPL; ++j) {
               float* sl = &part_a[t][h][lane + 64 * j];
@@ -694,7 +693,6 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
   __shared__ float mw_a[NW][GM][D];
   __shared__ float mw_m[NW][GM];
   __shared__ float mw_l[NW][GM];
-  __shared__ int last_flag;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -827,21 +825,27 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
     return;
   }
 
-  // last-arriving workgroup of the stream merges the splits
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(&p.ws_count[stream], 1);
-    last_flag = (prev == p.splits - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
+}
+
+// Merge of the full-attention splits: one workgroup per stream combines the
+// per-split (M, L, A) of each query head (a separate launch, so stream order
+// makes the partials visible without any device-scope fence).
+template <int D, int GM>
+__global__ __launch_bounds__(WG) void full_merge_kernel(Params p) {
+  constexpr int HPW = (GM + NW - 1) / NW, DPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int stream = blockIdx.x;
+  const int s = stream / p.hkv;
+  const int kvh = stream - s * p.hkv;
+  const int g = p.g;
+  const int n = (p.seq_lens[s] + p.block_size - 1) / p.block_size;
+  const size_t head0 = (size_t)s * p.hq + (size_t)kvh * g;
 #pragma unroll
   for (int k = 0; k < HPW; ++k) {
     const int h = w + NW * k;
     if (h >= g) continue;
-    const float* src = part + ((size_t)stream * p.splits * GM + h) * (D + 2);
+    const float* src = p.ws_part + ((size_t)stream * p.splits * GM + h) * (D + 2);
     const size_t sstride = (size_t)GM * (D + 2);
     float M = NEG_INF;
     for (int sp = 0; sp < p.splits; ++sp) M = fmaxf(M, src[sp * sstride + D]);
@@ -862,10 +866,7 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
     for (int j = 0; j < DPL; ++j) p.out[(head0 + h) * D + lane + 64 * j] = A[j] * rl;
     if (lane == 0) p.stop_block[head0 + h] = n;
   }
-  if (threadIdx.x == 0) {
-    p.ws_count[stream] = 0;
-    if (p.blocks_fetched) p.blocks_fetched[stream] = n;
-  }
+  if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[stream] = n;
 }
 
 }  // namespace kern
