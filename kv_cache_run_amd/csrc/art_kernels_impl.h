@@ -4,21 +4,29 @@
 // Method: "ART: Attention Run-time Termination for Efficient Large Language
 // Model Decoding" (gist.science explainer), Technical Summary 2.1-2.4.
 //
-// Two kernels share one per-block datapath (QK on MFMA, block softmax, PV on
-// the VALU in fp32):
+// Both kernels share one per-block datapath, entirely in registers:
+//  * QK: v_mfma_f32_16x16x32_bf16 (fp8 K converted to bf16 exactly; f32 uses
+//    v_mfma_f32_16x16x4_f32) with K tile rows as the A operand and the query
+//    group as the B operand (one head per column);
+//  * block softmax on the 16x16 score tile (row reductions with the gfx950
+//    permlane swaps);
+//  * PV: v_mfma_f32_16x16x4_f32 with V^T as the A operand and P as the B
+//    operand.  Each lane supplies one element of each operand, so P is used
+//    straight from the score registers (column = head, k = token) and V is
+//    loaded with coalesced 16-byte loads in the A-operand layout; products and
+//    sums are fp32.
 //
 //  * art_chunk_kernel -- the terminating path.  One workgroup (NWA waves)
 //    owns one stream = (sequence, kv-head) and walks its visit order in
-//    chunks of C blocks.  All blocks of a chunk are fetched at once
-//    (speculatively) and reduced to per-block partials (m_b, l_b, a_b) in
-//    LDS; then one wave per query head folds the partials in visit order,
-//    forms O_t = A_t / L_t for every t of the chunk, reduces ‖O_t‖² and
-//    ‖O_t - O_{t-1}‖² for all t at once (transposed butterfly), evaluates
-//    both statistics for all t in parallel (one lane per t) and runs the
-//    patience counter over the resulting pass bitmask.  A head that stops
-//    writes O_t and is frozen; the stream stops fetching when every head of
-//    its group stopped.  The page entries of chunk c+1 are fetched while
-//    chunk c is computed, so a chunk's KV loads never wait on the table.
+//    chunks of C blocks.  Each wave turns one block into partials
+//    (m_b, l_b, a_b) in LDS; then one wave per query head folds the partials
+//    in visit order, forms O_t = A_t / L_t for every t of the chunk, reduces
+//    ‖O_t‖² and ‖O_t - O_{t-1}‖² for all t at once (transposed butterfly),
+//    evaluates both statistics and the patience rule for all t in parallel
+//    (one lane per t, bit masks).  A head that stops writes O_t and is frozen;
+//    the stream stops fetching when every head of its group stopped.  The KV
+//    loads of chunk c+1 are issued before chunk c is scanned (speculatively),
+//    and page entries run two chunks ahead.
 //
 //  * full_split_kernel -- full attention (no detector).  Each workgroup owns
 //    a contiguous slice of one stream's blocks; each wave keeps its own
@@ -28,15 +36,14 @@
 // Data layout (HBM): k_pages/v_pages [page][kv_head][B][D], the (page, kvh)
 // tile contiguous, so one block of one stream is B*D*es contiguous bytes.
 //
-// Lane layouts inside a wave (64 lanes):
-//  * K, MFMA A operand: lane l loads 16 B of token row (l & 15) of each
-//    16-row tile at byte (l >> 4) * 16 + 64 * i.  The q operand (B operand,
-//    column = head l & 15) uses the same byte -> d map, so the dot product
-//    pairs q[d] with k[d] exactly.
-//  * Scores (16x16 MFMA result): lane l holds head (l & 15), tokens
-//    4 * (l >> 4) + r, r = 0..3, of each 16-row tile.
-//  * V and the PV accumulator: lane l owns VB contiguous bytes of a row:
-//    segment (l % LPR) of the rows j with j % RPL == l / LPR.
+// Lane layouts inside a wave (64 lanes, q = lane >> 4, c = lane & 15):
+//  * K (QK A operand): 16 B of token row c of each 16-row tile at byte
+//    q * 16 + 64 * i; the q operand uses the same byte -> d map.
+//  * Scores / P: lane holds head c, tokens 16 t + 4 q + r (r = 0..3).
+//  * V (PV A operand): lane holds, for each row 16 t + 4 q + r, the DT = D/16
+//    elements d = DT * c .. DT * c + DT - 1 (R/16 contiguous bytes).
+//  * PV accumulator O^T: lane holds head c, d = DT * (4 q + i) + dt for
+//    i = 0..3, dt = 0..DT-1, i.e. the 4*DT consecutive d from 4*DT*q.
 #pragma once
 #include <math.h>
 
@@ -62,6 +69,7 @@ template <> struct ElemSize<KV_FP8> { static constexpr int v = 1; };
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 template <int KV_, int D_, int B_, int GM_>
 struct Cfg {
@@ -70,14 +78,13 @@ struct Cfg {
   static constexpr int R = D * ES;                    // bytes per token row
   static constexpr int NKL = R / 64;                  // 16-B K chunks per lane per 16-row tile
   static constexpr int T = B / 16;                    // 16-row tiles per block
-  static constexpr int VB = R >= 256 ? R / 64 : 4;    // V bytes per lane per row
-  static constexpr int LPR = R / VB;                  // lanes per V row
-  static constexpr int RPL = 64 / LPR;                // V rows per wave load
-  static constexpr int EPL = VB / ES;                 // V elements per lane
-  static constexpr int VL = B / RPL;                  // V loads per lane per block
+  static constexpr int DT = D / 16;                   // V elements per lane per row (PV d-tiles)
+  static constexpr int VBL = R / 16;                  // V bytes per lane per row
+  static constexpr int VWD = VBL / 4;                 // V dwords per lane per row
   static constexpr int QF = KV == KV_FP8 ? 2 * NKL : NKL;  // 16-B q fragments
-  // ART chunk: C blocks; the per-block partials [C][GM][D] fp32 fit 32 KiB
-  static constexpr int C = cmin(256 / B, 8192 / (GM * D));
+  // ART chunk: C blocks (8, fewer when the per-block partials [C][GM][D]
+  // fp32 would pass 32 KiB)
+  static constexpr int C = cmin(8, 8192 / (GM * D));
   static constexpr int NWA = cmin(8, C);              // waves per workgroup, ART kernel
   static constexpr int BPW = C / NWA;                 // blocks per wave per chunk
   static constexpr int HPW = (GM + NWA - 1) / NWA;    // query heads per wave in the scan
@@ -85,18 +92,13 @@ struct Cfg {
   static constexpr int SH = 6 - ilog2(2 * C);         // stat reduction: lane >> SH = value index
   static_assert(BPW >= 1 && BPW * NWA == C, "chunk must split evenly over the waves");
   static_assert(2 * C <= 64, "stat reduction holds at most 64 values");
-  static_assert(LPR * EPL == D, "V lanes must tile a row");
-  static_assert(B % (4 * RPL) == 0, "P quads must cover the lane's rows");
+  static_assert(VWD >= 1, "a lane reads at least one dword of each V row");
 };
-
-template <int VB> struct VWordT;
-template <> struct VWordT<4> { using type = uint32_t; };
-template <> struct VWordT<8> { using type = uint2; };
 
 template <class Cf>
 struct BlockRegs {
   uint4 k[Cf::T][Cf::NKL];
-  typename VWordT<Cf::VB>::type v[Cf::VL];
+  uint32_t v[Cf::T][4][Cf::VWD];
 };
 
 // ---------------------------------------------------------------------------
@@ -216,21 +218,38 @@ __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
+// Load one block: K in the QK A-operand layout, V in the PV A-operand layout.
+// V rows at or past nvalid are read from the last valid row instead, so that
+// every V value fed to the PV product is finite (their P is exactly 0).
 template <class Cf>
-__device__ __forceinline__ void load_block(BlockRegs<Cf>& r, const char* kt, const char* vt, int lane) {
-  const int krow = lane & 15;
-  const int kcol = (lane >> 4) * 16;
+__device__ __forceinline__ void load_block(BlockRegs<Cf>& r, const char* kt, const char* vt, int lane, int nvalid) {
+  const int c = lane & 15;
+  const int q = lane >> 4;
 #pragma unroll
   for (int t = 0; t < Cf::T; ++t)
 #pragma unroll
     for (int i = 0; i < Cf::NKL; ++i)
-      r.k[t][i] = *reinterpret_cast<const uint4*>(kt + (size_t)(16 * t + krow) * Cf::R + kcol + 64 * i);
-  const int rg = lane / Cf::LPR;
-  const int sg = lane % Cf::LPR;
-  using VW = typename VWordT<Cf::VB>::type;
+      r.k[t][i] = *reinterpret_cast<const uint4*>(kt + (size_t)(16 * t + c) * Cf::R + q * 16 + 64 * i);
 #pragma unroll
-  for (int u = 0; u < Cf::VL; ++u)
-    r.v[u] = *reinterpret_cast<const VW*>(vt + (size_t)(u * Cf::RPL + rg) * Cf::R + sg * Cf::VB);
+  for (int t = 0; t < Cf::T; ++t)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = 16 * t + 4 * q + rr;
+      const char* src = vt + (size_t)min(row, nvalid - 1) * Cf::R + c * Cf::VBL;
+      if constexpr (Cf::VWD == 1) {
+        r.v[t][rr][0] = *reinterpret_cast<const uint32_t*>(src);
+      } else if constexpr (Cf::VWD == 2) {
+        const uint2 x = *reinterpret_cast<const uint2*>(src);
+        r.v[t][rr][0] = x.x; r.v[t][rr][1] = x.y;
+      } else {
+#pragma unroll
+        for (int h = 0; h < Cf::VWD / 4; ++h) {
+          const uint4 x = *reinterpret_cast<const uint4*>(src + 16 * h);
+          r.v[t][rr][4 * h + 0] = x.x; r.v[t][rr][4 * h + 1] = x.y;
+          r.v[t][rr][4 * h + 2] = x.z; r.v[t][rr][4 * h + 3] = x.w;
+        }
+      }
+    }
 }
 
 // q fragments for the MFMA B operand: column (lane & 15) = head of the group.
@@ -304,101 +323,58 @@ __device__ __forceinline__ float block_scores(const f32x4 (&S)[Cf::T], int nvali
   return rows_max(mb);
 }
 
-// Store the lane's P values (score layout) into the wave's P rows so that a
-// PV lane reads its own rows contiguously: token j of head h is stored at
-// h*B + (j % RPL) * (B / RPL) + j / RPL.
+// A lane's V row segment (DT elements) as fp32 (exact for every storage type).
 template <class Cf>
-__device__ __forceinline__ void store_p(float* pw, int lane, const float (&pv)[Cf::T][4]) {
-  const int c = lane & 15;
-  const int quad = lane >> 4;
-  if (c >= Cf::GM) return;
-  float* row = pw + c * Cf::B;
-  if constexpr (Cf::RPL == 1) {
-#pragma unroll
-    for (int t = 0; t < Cf::T; ++t) {
-      f32x4 q4 = {pv[t][0], pv[t][1], pv[t][2], pv[t][3]};
-      *reinterpret_cast<f32x4*>(row + 16 * t + 4 * quad) = q4;
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < Cf::T; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * t + 4 * quad + r;
-        row[(j % Cf::RPL) * (Cf::B / Cf::RPL) + j / Cf::RPL] = pv[t][r];
-      }
-  }
-}
-
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
-// Decode one V word into EPL floats.
-template <class Cf>
-__device__ __forceinline__ void decode_v(typename VWordT<Cf::VB>::type w, float (&o)[Cf::EPL]) {
+__device__ __forceinline__ void v_row(const uint32_t (&w)[Cf::VWD], float (&f)[Cf::DT]) {
   if constexpr (Cf::KV == KV_BF16) {
-    o[0] = bitsf(w << 16);
-    o[1] = bitsf(w & 0xffff0000u);
-  } else if constexpr (Cf::KV == KV_FP8) {
-    float f[4];
-    fp8x4_to_f32(w, f);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = f[e];
-  } else if constexpr (Cf::VB == 4) {
-    o[0] = bitsf(w);
-  } else {
-    o[0] = bitsf(w.x);
-    o[1] = bitsf(w.y);
-  }
-}
-
-// acc[h][e] += sum_j P[h][j] * V[j][d(e)] over the lane's rows of one block,
-// for every head slot of the group capacity (slots >= g carry finite junk).
-// Rows past the sequence end may hold any bits, so they are replaced by 0 with
-// a select on every block (no branch: a branch-local redefinition of the
-// decoded values has been miscompiled by the register allocator).
-template <class Cf>
-__device__ __forceinline__ void pv_accumulate(const BlockRegs<Cf>& r, int nvalid, const float* pw, int lane,
-                                              float (&acc)[Cf::GM][Cf::EPL]) {
-  const int rg = lane / Cf::LPR;
-  float v[Cf::VL][Cf::EPL];
-#pragma unroll
-  for (int u = 0; u < Cf::VL; ++u) {
-    decode_v<Cf>(r.v[u], v[u]);
-    const bool ok = u * Cf::RPL + rg < nvalid;
-#pragma unroll
-    for (int e = 0; e < Cf::EPL; ++e) v[u][e] = ok ? v[u][e] : 0.f;
-  }
-  const float* base = pw + rg * (Cf::B / Cf::RPL);
-#pragma unroll
-  for (int h = 0; h < Cf::GM; ++h) {
-#pragma unroll
-    for (int k = 0; k < Cf::VL / 4; ++k) {
-      const f32x4 p4 = *reinterpret_cast<const f32x4*>(base + h * Cf::B + 4 * k);
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int e = 0; e < Cf::EPL; ++e) acc[h][e] = fmaf(p4[m], v[4 * k + m][e], acc[h][e]);
+    for (int i = 0; i < Cf::VWD; ++i) {
+      f[2 * i] = bitsf(w[i] << 16);
+      f[2 * i + 1] = bitsf(w[i] & 0xffff0000u);
     }
+  } else if constexpr (Cf::KV == KV_FP8) {
+#pragma unroll
+    for (int i = 0; i < Cf::VWD; ++i) {
+      float o[4];
+      fp8x4_to_f32(w[i], o);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[4 * i + e] = o[e];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < Cf::VWD; ++i) f[i] = bitsf(w[i]);
   }
 }
 
-// Sum the PV accumulator over the RPL row groups (lanes sharing a segment).
+// acc += V^T P over the block: acc[dt] is the 16x16 tile of O^T whose rows are
+// d = DT * m + dt (m = 0..15) and whose columns are the heads of the group.
 template <class Cf>
-__device__ __forceinline__ void reduce_row_groups(float (&acc)[Cf::GM][Cf::EPL]) {
-  if constexpr (Cf::RPL >= 2) {
+__device__ __forceinline__ void pv_mfma(const BlockRegs<Cf>& r, const float (&pq)[Cf::T][4], f32x4 (&acc)[Cf::DT]) {
 #pragma unroll
-    for (int h = 0; h < Cf::GM; ++h)
+  for (int t = 0; t < Cf::T; ++t)
 #pragma unroll
-      for (int e = 0; e < Cf::EPL; ++e) acc[h][e] = xor32_sum(acc[h][e]);
-  }
-  if constexpr (Cf::RPL == 4) {
+    for (int rr = 0; rr < 4; ++rr) {
+      float vf[Cf::DT];
+      v_row<Cf>(r.v[t][rr], vf);
 #pragma unroll
-    for (int h = 0; h < Cf::GM; ++h)
+      for (int dt = 0; dt < Cf::DT; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[dt], pq[t][rr], acc[dt], 0, 0, 0);
+    }
+}
+
+// Store a lane's O^T accumulator row (head c) as D-contiguous floats:
+// dst points at [head][0]; the lane writes d = DT*(4q+i) + dt.
+template <class Cf>
+__device__ __forceinline__ void store_acc(float* dst, int lane, const f32x4 (&acc)[Cf::DT], float scale) {
+  const int q = lane >> 4;
 #pragma unroll
-      for (int e = 0; e < Cf::EPL; ++e) acc[h][e] = xor16_sum(acc[h][e]);
+  for (int i = 0; i < 4; ++i) {
+    float* row = dst + Cf::DT * (4 * q + i);
+#pragma unroll
+    for (int dt = 0; dt < Cf::DT; dt += 4) {
+      f32x4 o = {acc[dt][i] * scale, acc[dt + 1][i] * scale, acc[dt + 2][i] * scale, acc[dt + 3][i] * scale};
+      *reinterpret_cast<f32x4*>(row + dt) = o;
+    }
   }
 }
 
@@ -412,10 +388,9 @@ template <int KV, int D, int B, int GM>
 __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_chunk_kernel(Params p) {
   using Cf = Cfg<KV, D, B, GM>;
   constexpr int C = Cf::C, NWA = Cf::NWA, BPW = Cf::BPW, HPW = Cf::HPW, DPL = Cf::DPL, SH = Cf::SH;
-  __shared__ float part_a[C][GM][D];
+  __shared__ __attribute__((aligned(16))) float part_a[C][GM][D];
   __shared__ float part_m[C][GM];
   __shared__ float part_l[C][GM];
-  __shared__ __attribute__((aligned(16))) float p_lds[NWA][GM][B];
   __shared__ int alive_lds[GM];
 
   const int lane = threadIdx.x & 63;
@@ -443,14 +418,33 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_chunk_kerne
   const char* vbase = static_cast<const char*>(p.v_pages);
   const int32_t* trow = p.block_table + (size_t)s * p.max_blocks;
   const int32_t* orow = p.block_order + (size_t)s * p.max_blocks;
-  const int rg = lane / Cf::LPR;
-  const int sg = lane % Cf::LPR;
+  const int c16 = lane & 15;
   const int slot = lane < C ? lane : C - 1;
 
-  // Chunk entries, one per lane (slot = lane): logical block, page, fp8 scales.
-  int ob_l = orow[min(slot, n - 1)];
-  int pg_l = trow[ob_l];
-  float ks_l = 1.f, vs_l = 1.f;
+  // Chunk entries are lane-held (lane = slot): logical block and page of the
+  // current chunk (c) and of the next (n); entries of chunk c+2 are fetched
+  // while chunk c is scanned, so no KV load waits on the tables.
+  int ob_c = orow[min(slot, n - 1)];
+  int ob_n = orow[min(C + slot, n - 1)];
+  int pg_c = trow[ob_c];
+  int pg_n = trow[ob_n];
+  float ks_c = 1.f, vs_c = 1.f;
+
+  BlockRegs<Cf> regs[BPW];
+  auto issue_chunk = [&](int ob_lane, int pg_lane, int nt_chunk) {
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int b = min(w * BPW + i, nt_chunk - 1);  // slots past the end re-read a valid block (cache hit)
+      const int nvalid = min(B, L - readlane(ob_lane, b) * B);
+      const size_t off = ((size_t)readlane(pg_lane, b) * p.hkv + kvh) * tile;
+      load_block<Cf>(regs[i], kbase + off, vbase + off, lane, nvalid);
+    }
+  };
+  issue_chunk(ob_c, pg_c, min(C, n));
+  if constexpr (KV == KV_FP8) {
+    ks_c = p.k_scale[(size_t)pg_c * p.hkv + kvh];
+    vs_c = p.v_scale[(size_t)pg_c * p.hkv + kvh];
+  }
 
   // Per-head streaming state, carried across chunks (head h = w + NWA * k).
   float cM[HPW], cL[HPW], cNp[HPW];
@@ -465,35 +459,19 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_chunk_kerne
     for (int j = 0; j < DPL; ++j) { cA[k][j] = 0.f; cOp[k][j] = 0.f; }
   }
 
-  int fetched = 0;
+  int fetched = min(C, n);
   for (int t0 = 0; t0 < n; t0 += C) {
     const int nt = min(C, n - t0);
 
-    // ---- block phase: every load of the wave's blocks in flight, then reduce.
-    // Slots past the chunk end re-read the last valid slot (an L2 hit), so the
-    // loads are unconditional and the wait counts stay exact.
-    BlockRegs<Cf> regs[BPW];
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const int b = min(w * BPW + i, nt - 1);
-      const int pg = readlane(pg_l, b);
-      const size_t off = ((size_t)pg * p.hkv + kvh) * tile;
-      load_block<Cf>(regs[i], kbase + off, vbase + off, lane);
-    }
-    if constexpr (KV == KV_FP8) {
-      ks_l = p.k_scale[(size_t)pg_l * p.hkv + kvh];
-      vs_l = p.v_scale[(size_t)pg_l * p.hkv + kvh];
-    }
-    // next chunk's order entries (consumed after this chunk's scan)
-    const int ob_n = orow[min(t0 + C + slot, n - 1)];
+    // ---- block phase: per-block partials (m_b, l_b, a_b) into LDS; slots past
+    // the chunk end get neutral partials (m = -inf, l = 0, a = 0).
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
       const int b = w * BPW + i;
       if (b < nt) {
-        const int ob = readlane(ob_l, b);
-        const int nvalid = min(B, L - ob * B);
+        const int nvalid = min(B, L - readlane(ob_c, b) * B);
         float ksc = 1.f, vsc = 1.f;
-        if constexpr (KV == KV_FP8) { ksc = readlanef(ks_l, b); vsc = readlanef(vs_l, b); }
+        if constexpr (KV == KV_FP8) { ksc = readlanef(ks_c, b); vsc = readlanef(vs_c, b); }
         f32x4 S[Cf::T];
         qk_scores<Cf>(regs[i], qf, S);
         float x[Cf::T][4];
@@ -509,77 +487,80 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_chunk_kerne
             pq[t][r] = e * vsc;
           }
         ls = rows_sum(ls);
-        store_p<Cf>(&p_lds[w][0][0], lane, pq);
-        const int c = lane & 15;
-        if (c < GM && (lane >> 4) == 0) { part_m[b][c] = mb; part_l[b][c] = ls; }
-        wave_lds_fence();
-        float acc[GM][Cf::EPL];
+        f32x4 acc[Cf::DT];
 #pragma unroll
-        for (int h = 0; h < GM; ++h)
-#pragma unroll
-          for (int e = 0; e < Cf::EPL; ++e) acc[h][e] = 0.f;
-        pv_accumulate<Cf>(regs[i], nvalid, &p_lds[w][0][0], lane, acc);
-        reduce_row_groups<Cf>(acc);
-        if (rg == 0) {
-#pragma unroll
-          for (int h = 0; h < GM; ++h)
-#pragma unroll
-            for (int e = 0; e < Cf::EPL; ++e) part_a[b][h][sg * Cf::EPL + e] = acc[h][e];
+        for (int dt = 0; dt < Cf::DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        pv_mfma<Cf>(regs[i], pq, acc);
+        if (c16 < GM) {
+          store_acc<Cf>(&part_a[b][c16][0], lane, acc, 1.f);
+          if ((lane >> 4) == 0) { part_m[b][c16] = mb; part_l[b][c16] = ls; }
         }
-        wave_lds_fence();
+      } else {
+        if (c16 < GM && (lane >> 4) == 0) { part_m[b][c16] = NEG_INF; part_l[b][c16] = 0.f; }
+        for (int e = lane; e < GM * D; e += 64) (&part_a[b][0][0])[e] = 0.f;
       }
     }
-    // next chunk's pages (the order entries have arrived by now)
-    const int pg_n = trow[ob_n];
-    fetched += nt;
+
+    // ---- speculative fetch of the next chunk: its loads fly during the scan
+    const bool has_next = t0 + C < n;
+    int ob_nn = 0;
+    float ks_n = 1.f, vs_n = 1.f;
+    if (has_next) {
+      const int nt1 = min(C, n - t0 - C);
+      issue_chunk(ob_n, pg_n, nt1);
+      if constexpr (KV == KV_FP8) {
+        ks_n = p.k_scale[(size_t)pg_n * p.hkv + kvh];
+        vs_n = p.v_scale[(size_t)pg_n * p.hkv + kvh];
+      }
+      ob_nn = orow[min(t0 + 2 * C + slot, n - 1)];
+      fetched += nt1;
+    }
     __syncthreads();
 
     // ---- scan phase: fold the chunk's partials in visit order, one wave per head
-    const unsigned long long sinkbits = __ballot(lane < nt && ob_l == 0);
+    const unsigned long long sinkbits = __ballot(lane < nt && ob_c == 0);
 #pragma unroll
     for (int k = 0; k < HPW; ++k) {
       const int h = w + NWA * k;
       if (h < g && cAlive[k]) {
+        // branch-free over all C slots: neutral slots leave (M, L, A) unchanged
         float st[2 * C];
 #pragma unroll
         for (int t = 0; t < C; ++t) {
+          const float mb = part_m[t][h];
+          const float lb = part_l[t][h];
+          const float Mn = fmaxf(cM[k], mb);
+          const float al = __builtin_amdgcn_exp2f(cM[k] - Mn);
+          const float be = __builtin_amdgcn_exp2f(mb - Mn);
+          cL[k] = fmaf(al, cL[k], be * lb);
+          cM[k] = Mn;
+          const float rl = __builtin_amdgcn_rcpf(cL[k]);  // 1 ulp; the statistics need ~1e-6
           float nn = 0.f, ee = 0.f;
-          if (t < nt) {
-            const float mb = part_m[t][h];
-            const float lb = part_l[t][h];
-            const float Mn = fmaxf(cM[k], mb);
-            const float al = __builtin_amdgcn_exp2f(cM[k] - Mn);
-            const float be = __builtin_amdgcn_exp2f(mb - Mn);
-            cL[k] = fmaf(al, cL[k], be * lb);
-            cM[k] = Mn;
-            const float rl = __builtin_amdgcn_rcpf(cL[k]);  // 1 ulp; statistics need ~1e-6
 #pragma unroll
-            for (int j = 0; j < DPL; ++j) {
-              float* sl = &part_a[t][h][lane + 64 * j];
-              cA[k][j] = fmaf(al, cA[k][j], be * *sl);
-              const float o = cA[k][j] * rl;
-              const float df = o - cOp[k][j];
-              nn = fmaf(o, o, nn);
-              ee = fmaf(df, df, ee);
-              cOp[k][j] = o;
-              *sl = o;  // keep O_t for the epilogue
-            }
+          for (int j = 0; j < DPL; ++j) {
+            float* sl = &part_a[t][h][lane + 64 * j];
+            cA[k][j] = fmaf(al, cA[k][j], be * *sl);
+            const float o = cA[k][j] * rl;
+            const float df = o - cOp[k][j];
+            nn = fmaf(o, o, nn);
+            ee = fmaf(df, df, ee);
+            cOp[k][j] = o;
+            *sl = o;  // keep O_t for the epilogue
           }
           st[2 * t] = nn;
           st[2 * t + 1] = ee;
         }
         const float v0 = xreduce<2 * C>(st, lane);
-        // lane (2t) << SH holds ‖O_t‖², lane (2t+1) << SH holds ‖O_t - O_{t-1}‖²
-        const int idx = lane >> SH;
-        const int tt = idx >> 1;
-        const float e_t = __shfl(v0, (lane + (1 << SH)) & 63);
-        float n_prev = __shfl(v0, (lane - (2 << SH)) & 63);
-        if (tt == 0) n_prev = cNp[k];
-        const bool lead = ((idx & 1) == 0) && ((lane & ((1 << SH) - 1)) == 0);
+        // lane (2t) << SH holds ‖O_t‖², lane (2t+1) << SH holds ‖O_t - O_{t-1}‖²;
+        // gather them so that lane t < C evaluates position t.
+        const float nn_t = __shfl(v0, (2 * slot) << SH);
+        const float ee_t = __shfl(v0, (2 * slot + 1) << SH);
+        float np_t = __shfl(v0, (2 * max(slot - 1, 0)) << SH);
+        if (lane == 0) np_t = cNp[k];
         bool ps = false;
-        if (lead && tt < nt && (t0 + tt) >= 1) {
-          const float a = sqrtf(v0);
-          const float bn = sqrtf(n_prev);
+        if (lane < nt && t0 + lane >= 1) {
+          const float a = __builtin_amdgcn_sqrtf(nn_t);
+          const float bn = __builtin_amdgcn_sqrtf(np_t);
           float dm, dd;
           if (a == 0.f && bn == 0.f) {
             dm = 0.f; dd = 0.f;
@@ -587,32 +568,33 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_chunk_kerne
             dm = __builtin_inff(); dd = 1.f;
           } else {
             const float df = a - bn;
-            dm = fabsf(df) / bn;
+            dm = fabsf(df) * __builtin_amdgcn_rcpf(bn);
             // 1 - cos = (‖O_t - O_{t-1}‖² - (‖O_t‖ - ‖O_{t-1}‖)²) / (2 ‖O_t‖ ‖O_{t-1}‖)
-            dd = (a == 0.f) ? 1.f : fmaxf(0.f, (e_t - df * df) / (2.f * a * bn));
+            dd = (a == 0.f) ? 1.f : fmaxf(0.f, (ee_t - df * df) * __builtin_amdgcn_rcpf(2.f * a * bn));
           }
           ps = (dm < p.eps_mag) && (dd < p.eps_dir);
         }
-        const unsigned long long pm = __ballot(ps);
-        const float n_last = __shfl(v0, ((2 * (nt - 1)) << SH) & 63);
-        int cnt = cCnt[k];
-        bool sink = cSink[k];
-        int stop_t = -1;
-        for (int t = 0; t < nt; ++t) {
-          if (t0 + t >= 1) cnt = ((pm >> ((2 * t) << SH)) & 1ull) ? cnt + 1 : 0;
-          sink = sink || ((sinkbits >> t) & 1ull);
-          if (cnt >= p.patience && sink) { stop_t = t; break; }
-        }
-        if (stop_t >= 0) {
+        // patience rule for every position at once: lane t counts the passes
+        // in a row that end at t (carrying the count from earlier chunks when
+        // every test of this chunk up to t passed) and whether block 0 has
+        // been folded by t.
+        const unsigned long long pass = __ballot(ps);
+        const unsigned long long upto = (2ull << slot) - 1ull;
+        const unsigned long long zeros = ~pass & upto;
+        const int cnt_t = zeros == 0ull ? cCnt[k] + slot + 1 : slot - (63 - __builtin_clzll(zeros));
+        const bool sink_t = cSink[k] || (sinkbits & upto) != 0ull;
+        const unsigned long long fire = __ballot(lane < nt && cnt_t >= p.patience && sink_t);
+        if (fire != 0ull) {
+          const int stop_t = __builtin_ctzll(fire);
           float* o = p.out + (head0 + h) * D;
 #pragma unroll
           for (int j = 0; j < DPL; ++j) o[lane + 64 * j] = part_a[stop_t][h][lane + 64 * j];
           if (lane == 0) p.stop_block[head0 + h] = t0 + stop_t + 1;
           cAlive[k] = false;
         } else {
-          cCnt[k] = cnt;
-          cSink[k] = sink;
-          cNp[k] = n_last;
+          cCnt[k] = readlane(cnt_t, nt - 1);
+          cSink[k] = readlane(sink_t ? 1 : 0, nt - 1) != 0;
+          cNp[k] = readlanef(nn_t, nt - 1);
         }
       }
     }
@@ -621,12 +603,17 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_chunk_kerne
       for (int k = 0; k < HPW; ++k)
         if (w + NWA * k < g) alive_lds[w + NWA * k] = cAlive[k] ? 1 : 0;
     }
-    ob_l = ob_n;
-    pg_l = pg_n;
     __syncthreads();
     int any = 0;
     for (int h = 0; h < g; ++h) any |= alive_lds[h];
-    if (!any) break;
+    if (!any || !has_next) break;
+    // rotate the lane-held entries; the page of chunk c+2 is looked up now
+    ob_c = ob_n;
+    pg_c = pg_n;
+    ob_n = ob_nn;
+    pg_n = trow[ob_nn];
+    ks_c = ks_n;
+    vs_c = vs_n;
   }
 
   // heads that never stopped: output after all n blocks
@@ -641,6 +628,8 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_chunk_kerne
     }
   }
   if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[stream] = fetched;
+  // speculative loads of a chunk that was not needed may still be in flight
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // ---------------------------------------------------------------------------
@@ -649,8 +638,7 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_chunk_kerne
 template <class Cf>
 __device__ __forceinline__ void full_block(const BlockRegs<Cf>& r, int nvalid, float ksc, float vsc,
                                            const uint4 (&qf)[Cf::QF], float qk_log2, int lane, float& m_run,
-                                           float& l_run, float (&acc)[Cf::GM][Cf::EPL], float* pw,
-                                           float* alpha_w) {
+                                           float& l_run, f32x4 (&acc)[Cf::DT]) {
   f32x4 S[Cf::T];
   qk_scores<Cf>(r, qf, S);
   float x[Cf::T][4];
@@ -670,27 +658,17 @@ __device__ __forceinline__ void full_block(const BlockRegs<Cf>& r, int nvalid, f
   ls = rows_sum(ls);
   l_run = fmaf(al, l_run, ls);
   m_run = mn;
-  store_p<Cf>(pw, lane, pq);
-  const int c = lane & 15;
-  if (c < Cf::GM && (lane >> 4) == 0) alpha_w[c] = al;
-  wave_lds_fence();
+  // the lane's accumulator column is its own head: rescale in place
 #pragma unroll
-  for (int h = 0; h < Cf::GM; ++h) {
-    const float a = alpha_w[h];
-#pragma unroll
-    for (int e = 0; e < Cf::EPL; ++e) acc[h][e] *= a;
-  }
-  pv_accumulate<Cf>(r, nvalid, pw, lane, acc);
-  wave_lds_fence();
+  for (int dt = 0; dt < Cf::DT; ++dt) acc[dt] *= al;
+  pv_mfma<Cf>(r, pq, acc);
 }
 
 template <int KV, int D, int B, int GM>
 __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
   using Cf = Cfg<KV, D, B, GM>;
-  constexpr int HPW = (GM + NW - 1) / NW, DPL = Cf::DPL, EPL = Cf::EPL;
-  __shared__ __attribute__((aligned(16))) float p_lds[NW][GM][B];
-  __shared__ float alpha_lds[NW][GM];
-  __shared__ float mw_a[NW][GM][D];
+  constexpr int HPW = (GM + NW - 1) / NW, DPL = Cf::DPL;
+  __shared__ __attribute__((aligned(16))) float mw_a[NW][GM][D];
   __shared__ float mw_m[NW][GM];
   __shared__ float mw_l[NW][GM];
 
@@ -729,32 +707,28 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
   }
 
   float m_run = NEG_INF, l_run = 0.f;
-  float acc[GM][EPL];
+  f32x4 acc[Cf::DT];
 #pragma unroll
-  for (int h = 0; h < GM; ++h)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  for (int dt = 0; dt < Cf::DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  float* pw = &p_lds[w][0][0];
-  float* aw = &alpha_lds[w][0];
+  auto nvalid_of = [&](int k) { return min(B, L - (b0 + w + NW * k) * B); };
   auto tile_of = [&](int k) { return ((size_t)readlane(tab, k) * p.hkv + kvh) * tile; };
   auto fold = [&](const BlockRegs<Cf>& r, int k) {
-    const int b = b0 + w + NW * k;
     float ks = 1.f, vs = 1.f;
     if constexpr (KV == KV_FP8) { ks = readlanef(ks_t, k); vs = readlanef(vs_t, k); }
-    full_block<Cf>(r, min(B, L - b * B), ks, vs, qf, p.qk_log2, lane, m_run, l_run, acc, pw, aw);
+    full_block<Cf>(r, nvalid_of(k), ks, vs, qf, p.qk_log2, lane, m_run, l_run, acc);
   };
 
   // Two register sets; block k+1 is in flight while block k is folded.  Each
   // fold site has a fixed number of younger loads outstanding.
   if (cnt > 0) {
     BlockRegs<Cf> ra, rb;
-    load_block<Cf>(ra, kbase + tile_of(0), vbase + tile_of(0), lane);
+    load_block<Cf>(ra, kbase + tile_of(0), vbase + tile_of(0), lane, nvalid_of(0));
     int k = 0;
     for (;;) {
       if (k + 1 < cnt) {
         const size_t o = tile_of(k + 1);
-        load_block<Cf>(rb, kbase + o, vbase + o, lane);
+        load_block<Cf>(rb, kbase + o, vbase + o, lane, nvalid_of(k + 1));
         fold(ra, k);
       } else {
         fold(ra, k);
@@ -763,7 +737,7 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
       ++k;
       if (k + 1 < cnt) {
         const size_t o = tile_of(k + 1);
-        load_block<Cf>(ra, kbase + o, vbase + o, lane);
+        load_block<Cf>(ra, kbase + o, vbase + o, lane, nvalid_of(k + 1));
         fold(rb, k);
       } else {
         fold(rb, k);
@@ -772,23 +746,17 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
       ++k;
     }
   }
-  reduce_row_groups<Cf>(acc);
 
   // merge the four waves
   {
     const int c = lane & 15;
-    if (c < g && (lane >> 4) == 0) { mw_m[w][c] = m_run; mw_l[w][c] = l_run; }
-    if (lane / Cf::LPR == 0) {
-      const int sg = lane % Cf::LPR;
-#pragma unroll
-      for (int h = 0; h < GM; ++h)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) mw_a[w][h][sg * EPL + e] = acc[h][e];
+    if (c < GM) {
+      store_acc<Cf>(&mw_a[w][c][0], lane, acc, 1.f);
+      if ((lane >> 4) == 0) { mw_m[w][c] = m_run; mw_l[w][c] = l_run; }
     }
   }
   __syncthreads();
 
-  float* part = p.ws_part;
 #pragma unroll
   for (int k = 0; k < HPW; ++k) {
     const int h = w + NW * k;
@@ -814,17 +782,13 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
       for (int j = 0; j < DPL; ++j) p.out[(head0 + h) * D + lane + 64 * j] = A[j] * rl;
       if (lane == 0) p.stop_block[head0 + h] = n;
     } else {
-      float* dst = part + (((size_t)stream * p.splits + split) * GM + h) * (D + 2);
+      float* dst = p.ws_part + (((size_t)stream * p.splits + split) * GM + h) * (D + 2);
 #pragma unroll
       for (int j = 0; j < DPL; ++j) dst[lane + 64 * j] = A[j];
       if (lane == 0) { dst[D] = M; dst[D + 1] = Ls; }
     }
   }
-  if (p.splits == 1) {
-    if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[stream] = n;
-    return;
-  }
-
+  if (p.splits == 1 && threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[stream] = n;
 }
 
 // Merge of the full-attention splits: one workgroup per stream combines the
