@@ -61,6 +61,9 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 constexpr float NEG_INF = -__builtin_inff();
 constexpr int NW = 4;        // waves per workgroup, full-attention kernel
 constexpr int WG = 64 * NW;  // threads per workgroup, full-attention kernel
+#ifndef FULL_PREFETCH
+#define FULL_PREFETCH 3  // blocks in the full kernel's register ring
+#endif
 
 template <int KV> struct ElemSize;
 template <> struct ElemSize<KV_F32> { static constexpr int v = 4; };
@@ -508,6 +511,7 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_chunk_kerne
     if (has_next) {
       const int nt1 = min(C, n - t0 - C);
       issue_chunk(ob_n, pg_n, nt1);
+      __builtin_amdgcn_sched_barrier(0);  // the loads must leave before the scan
       if constexpr (KV == KV_FP8) {
         ks_n = p.k_scale[(size_t)pg_n * p.hkv + kvh];
         vs_n = p.v_scale[(size_t)pg_n * p.hkv + kvh];
@@ -719,31 +723,28 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
     full_block<Cf>(r, nvalid_of(k), ks, vs, qf, p.qk_log2, lane, m_run, l_run, acc);
   };
 
-  // Two register sets; block k+1 is in flight while block k is folded.  Each
-  // fold site has a fixed number of younger loads outstanding.
+  // Register ring of PF block buffers: while block k is folded, blocks
+  // k+1 .. k+PF-1 are in flight.  Loads are unconditional (past the wave's
+  // last block they re-read that block, a cache hit), so every fold site has
+  // the same PF-1 blocks of younger loads outstanding and the waits are exact.
   if (cnt > 0) {
-    BlockRegs<Cf> ra, rb;
-    load_block<Cf>(ra, kbase + tile_of(0), vbase + tile_of(0), lane, nvalid_of(0));
-    int k = 0;
-    for (;;) {
-      if (k + 1 < cnt) {
-        const size_t o = tile_of(k + 1);
-        load_block<Cf>(rb, kbase + o, vbase + o, lane, nvalid_of(k + 1));
-        fold(ra, k);
-      } else {
-        fold(ra, k);
-        break;
+    constexpr int PF = FULL_PREFETCH;
+    BlockRegs<Cf> ring[PF];
+#pragma unroll
+    for (int j = 0; j < PF - 1; ++j) {
+      const int kk = min(j, cnt - 1);
+      const size_t o = tile_of(kk);
+      load_block<Cf>(ring[j], kbase + o, vbase + o, lane, nvalid_of(kk));
+    }
+    for (int k = 0; k < cnt; k += PF) {
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        const int kk = min(k + j + PF - 1, cnt - 1);
+        const size_t o = tile_of(kk);
+        load_block<Cf>(ring[(j + PF - 1) % PF], kbase + o, vbase + o, lane, nvalid_of(kk));
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
+        if (k + j < cnt) fold(ring[j], k + j);
       }
-      ++k;
-      if (k + 1 < cnt) {
-        const size_t o = tile_of(k + 1);
-        load_block<Cf>(ra, kbase + o, vbase + o, lane, nvalid_of(k + 1));
-        fold(rb, k);
-      } else {
-        fold(rb, k);
-        break;
-      }
-      ++k;
     }
   }
 
@@ -791,46 +792,74 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
   if (p.splits == 1 && threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[stream] = n;
 }
 
-// Merge of the full-attention splits: one workgroup per stream combines the
-// per-split (M, L, A) of each query head (a separate launch, so stream order
-// makes the partials visible without any device-scope fence).
+// Merge of the full-attention splits (a separate launch, so stream order
+// makes the partials visible without any device-scope fence).  One 64-lane
+// workgroup per (stream, query head): lanes first read the splits' (M, L) in
+// parallel and reduce the common maximum and the weights; then every lane
+// owns D/64 output elements and sums the weighted split numerators with
+// independent loads in flight.
 template <int D, int GM>
-__global__ __launch_bounds__(WG) void full_merge_kernel(Params p) {
-  constexpr int HPW = (GM + NW - 1) / NW, DPL = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int stream = blockIdx.x;
+__global__ __launch_bounds__(64) void full_merge_kernel(Params p) {
+  constexpr int DPL = D / 64;
+  const int lane = threadIdx.x;
+  const int g = p.g;
+  const int stream = blockIdx.x / g;
+  const int h = blockIdx.x - stream * g;
   const int s = stream / p.hkv;
   const int kvh = stream - s * p.hkv;
-  const int g = p.g;
   const int n = (p.seq_lens[s] + p.block_size - 1) / p.block_size;
-  const size_t head0 = (size_t)s * p.hq + (size_t)kvh * g;
+  const size_t head = (size_t)s * p.hq + (size_t)kvh * g + h;
+  const size_t sstride = (size_t)GM * (D + 2);
+  const float* src = p.ws_part + ((size_t)stream * p.splits * GM + h) * (D + 2);
+  const int S = p.splits;
+
+  // pass 1: common max over splits (lane-parallel, S may exceed 64)
+  float M = NEG_INF;
+  for (int sp = lane; sp < S; sp += 64) M = fmaxf(M, src[sp * sstride + D]);
+  M = rows_max(M);
+  M = fmaxf(M, dpp<DPP_ROW_MIRROR>(M));
+  M = fmaxf(M, dpp<DPP_HALF_MIRROR>(M));
+  M = fmaxf(M, dpp<DPP_XOR2>(M));
+  M = fmaxf(M, dpp<DPP_XOR1>(M));
+  // pass 2: weighted numerators; the weight of split sp is read by every lane
+  float Ls = 0.f;
+  float A[DPL];
 #pragma unroll
-  for (int k = 0; k < HPW; ++k) {
-    const int h = w + NW * k;
-    if (h >= g) continue;
-    const float* src = p.ws_part + ((size_t)stream * p.splits * GM + h) * (D + 2);
-    const size_t sstride = (size_t)GM * (D + 2);
-    float M = NEG_INF;
-    for (int sp = 0; sp < p.splits; ++sp) M = fmaxf(M, src[sp * sstride + D]);
-    float Ls = 0.f;
-    float A[DPL];
+  for (int j = 0; j < DPL; ++j) A[j] = 0.f;
+  int sp = 0;
+  for (; sp + 8 <= S; sp += 8) {
+    float ms[8], ls[8], a[8][DPL];
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) A[j] = 0.f;
-    for (int sp = 0; sp < p.splits; ++sp) {
-      const float* q = src + sp * sstride;
-      const float ms = q[D];
-      const float f = (ms == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-      Ls = fmaf(f, q[D + 1], Ls);
+    for (int u = 0; u < 8; ++u) {
+      const float* q = src + (size_t)(sp + u) * sstride;
+      ms[u] = q[D];
+      ls[u] = q[D + 1];
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) A[j] = fmaf(f, q[lane + 64 * j], A[j]);
+      for (int j = 0; j < DPL; ++j) a[u][j] = q[lane + 64 * j];
     }
-    const float rl = Ls > 0.f ? 1.0f / Ls : 0.f;
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) p.out[(head0 + h) * D + lane + 64 * j] = A[j] * rl;
-    if (lane == 0) p.stop_block[head0 + h] = n;
+    for (int u = 0; u < 8; ++u) {
+      const float f = (ms[u] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - M);
+      Ls = fmaf(f, ls[u], Ls);
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) A[j] = fmaf(f, a[u][j], A[j]);
+    }
   }
-  if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[stream] = n;
+  for (; sp < S; ++sp) {
+    const float* q = src + (size_t)sp * sstride;
+    const float ms = q[D];
+    const float f = (ms == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    Ls = fmaf(f, q[D + 1], Ls);
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) A[j] = fmaf(f, q[lane + 64 * j], A[j]);
+  }
+  const float rl = Ls > 0.f ? 1.0f / Ls : 0.f;
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) p.out[head * D + lane + 64 * j] = A[j] * rl;
+  if (lane == 0) {
+    p.stop_block[head] = n;
+    if (h == 0 && p.blocks_fetched) p.blocks_fetched[stream] = n;
+  }
 }
 
 }  // namespace kern

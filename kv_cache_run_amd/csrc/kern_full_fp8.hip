@@ -10,7 +10,7 @@ hipError_t go(const Params& p, hipStream_t st) {
   hipLaunchKernelGGL((kern::full_split_kernel<KV_FP8, D, B, GM>), dim3(p.batch * p.hkv * p.splits), dim3(kern::WG), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL((kern::full_merge_kernel<D, GM>), dim3(p.batch * p.hkv), dim3(kern::WG), 0, st, p);
+  hipLaunchKernelGGL((kern::full_merge_kernel<D, GM>), dim3(p.batch * p.hkv * p.g), dim3(64), 0, st, p);
   return hipGetLastError();
 }
 
