@@ -84,10 +84,15 @@ typedef struct {
 size_t art_decode_workspace_bytes(const art_decode_desc* desc);
 
 /*
- * Put a workspace into its initial state (zeroes its counters) on `stream`.
- * Must be called once on a new workspace before its first art_decode call;
- * art_decode leaves the workspace in that state again when it completes.
- * Errors: ART_ERR_INVALID_ARG for NULL with bytes > 0, ART_ERR_HIP.
+ * Put a workspace into its initial state (all bytes zero) on `stream`.
+ * Must be called once on a new workspace before its first art_decode call.
+ * The workspace holds the terminating kernel's scheduler words (tagged with
+ * a per-call epoch that the kernel itself advances, so later calls need no
+ * clearing and may be captured in a HIP graph) and the partial results that
+ * helper workgroups hand to the per-stream scanners, or the full-attention
+ * slices before their merge.
+ * Errors: ART_ERR_INVALID_ARG for NULL with bytes > 0 or a pointer that is
+ * not 256-byte aligned, ART_ERR_HIP.
  */
 art_status art_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
@@ -116,8 +121,8 @@ art_status art_decode_workspace_init(void* workspace, size_t workspace_bytes, vo
  * stop_block   [batch][Hq] int32: number of folded blocks = visit positions
  *              0 .. stop-1 (n_s when the head never stopped, 0 when empty).
  * blocks_fetched  optional [batch][Hkv] int32 (NULL to skip): KV blocks the
- *              kernel actually read for each (sequence, kv-head), speculative
- *              reads included.
+ *              kernels actually read for each (sequence, kv-head), speculative
+ *              reads (chunks fetched ahead of the stop) included.
  * workspace    device scratch of at least art_decode_workspace_bytes(desc)
  *              bytes, initialized once with art_decode_workspace_init; may be
  *              NULL when that size is 0.  256-byte aligned.

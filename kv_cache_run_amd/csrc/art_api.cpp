@@ -3,6 +3,7 @@
 #include "../../include/art_decode.h"
 
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "art_internal.h"
@@ -56,13 +57,58 @@ art_status check_desc(const art_decode_desc* d) {
   return ART_OK;
 }
 
-size_t workspace_for(const art_decode_desc* d) {
-  const art::SplitPlan sp = art::full_split_plan(d->batch, d->num_kv_heads, d->max_blocks_per_seq);
-  if (sp.splits <= 1 || d->batch == 0) return 0;
-  const int gm = art::group_capacity(d->num_q_heads / d->num_kv_heads);
+// Scheduler tuning knobs, read from the environment at every call (defaults
+// when unset): ART_RING slots per stream, ART_LOOKAHEAD initial helper
+// window, ART_HELPERS helper workgroups (default 0; -1: enough to reach
+// ART_TARGET_WGS workgroups in total).  The workspace size depends on ART_RING.
+int env_int(const char* name, int def, int lo, int hi) {
+  const char* v = getenv(name);
+  int x = v ? atoi(v) : def;
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+struct Knobs {
+  int ring, lookahead, helpers, target;
+};
+Knobs knobs() {
+  const Knobs k = {env_int("ART_RING", 8, 1, 64), env_int("ART_LOOKAHEAD", 3, 1, 64),
+                          env_int("ART_HELPERS", 0, -1, 1 << 16), env_int("ART_TARGET_WGS", 512, 1, 1 << 16)};
+  return k;
+}
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+art::WorkspacePlan plan_workspace(const art_decode_desc* d) {
+  art::WorkspacePlan w;
+  memset(&w, 0, sizeof(w));
+  if (d->batch == 0) return w;
+  const Knobs k = knobs();
+  const int g = d->num_q_heads / d->num_kv_heads;
+  const int gm = art::group_capacity(g);
   const size_t streams = (size_t)d->batch * d->num_kv_heads;
-  size_t part = streams * sp.splits * gm * (size_t)(d->head_dim + 2) * sizeof(float);
-  return (part + 255) / 256 * 256;
+  const int chunk = art::art_chunk_blocks(gm, d->head_dim);
+  w.ring = k.ring;
+  w.lookahead = k.lookahead < k.ring ? k.lookahead : k.ring;
+  w.slot_floats = (art::art_slot_floats(gm, d->head_dim) + 63) / 64 * 64;
+  const long max_chunks = (d->max_blocks_per_seq + chunk - 1) / chunk;
+  long h = k.helpers >= 0 ? k.helpers : (long)k.target - (long)streams;
+  const long useful = (long)streams * (max_chunks - 1);  // chunks a helper could ever take
+  if (h > useful) h = useful;
+  if (h < 0) h = 0;
+  w.helpers = (int)h;
+  size_t off = 256;  // [0] stored epoch, [1] finished workgroups, [2] error flag
+  w.claim = off;
+  off += round256(streams * 8);
+  w.done = off;
+  off += round256(streams * 8);
+  w.ready = off;
+  off += round256(streams * (size_t)w.ring * 8);
+  w.data = off;
+  const size_t ring_bytes = streams * (size_t)w.ring * w.slot_floats * sizeof(float);
+  const art::SplitPlan sp = art::full_split_plan(d->batch, d->num_kv_heads, d->max_blocks_per_seq);
+  const size_t part = sp.splits > 1 ? streams * sp.splits * gm * (size_t)(d->head_dim + 2) * sizeof(float) : 0;
+  off += round256(ring_bytes > part ? ring_bytes : part);
+  w.total = off;
+  return w;
 }
 
 }  // namespace
@@ -71,7 +117,7 @@ extern "C" {
 
 size_t art_decode_workspace_bytes(const art_decode_desc* desc) {
   if (check_desc(desc) != ART_OK) return 0;
-  return workspace_for(desc);
+  return plan_workspace(desc).total;
 }
 
 art_status art_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
@@ -99,9 +145,9 @@ art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_
       (blocks_fetched && !aligned(blocks_fetched, 4)) || (k_scale && !aligned(k_scale, 4)) ||
       (v_scale && !aligned(v_scale, 4)))
     return ART_ERR_INVALID_ARG;
-  const size_t need = workspace_for(desc);
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need) return ART_ERR_WORKSPACE;
+  const art::WorkspacePlan wp = plan_workspace(desc);
+  if (wp.total > 0) {
+    if (!workspace || workspace_bytes < wp.total) return ART_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return ART_ERR_INVALID_ARG;
   }
   if (desc->batch == 0) return ART_OK;
@@ -144,13 +190,24 @@ art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_
     const art::SplitPlan sp = art::full_split_plan(desc->batch, desc->num_kv_heads, desc->max_blocks_per_seq);
     p.splits = sp.splits;
     p.split_blocks = sp.split_blocks;
-    if (sp.splits > 1) p.ws_part = static_cast<float*>(workspace);
+    if (sp.splits > 1) p.ws_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + wp.data);
     e = v.kv == art::KV_F32 ? art::launch_full_f32(v, p, static_cast<hipStream_t>(stream))
         : v.kv == art::KV_BF16 ? art::launch_full_bf16(v, p, static_cast<hipStream_t>(stream))
                                : art::launch_full_fp8(v, p, static_cast<hipStream_t>(stream));
   } else {
     p.splits = 1;
     p.split_blocks = desc->max_blocks_per_seq;
+    char* ws = static_cast<char*>(workspace);
+    p.sched_ctrl = reinterpret_cast<uint32_t*>(ws);
+    p.sched_claim = reinterpret_cast<unsigned long long*>(ws + wp.claim);
+    p.sched_done = reinterpret_cast<unsigned long long*>(ws + wp.done);
+    p.sched_ready = reinterpret_cast<unsigned long long*>(ws + wp.ready);
+    p.sched_ring = reinterpret_cast<float*>(ws + wp.data);
+    p.ring = wp.ring;
+    p.slot_floats = wp.slot_floats;
+    p.helpers = wp.helpers;
+    p.lookahead = wp.lookahead;
+    p.spin_limit = 1 << 20;
     e = v.kv == art::KV_F32 ? art::launch_art_f32(v, p, static_cast<hipStream_t>(stream))
         : v.kv == art::KV_BF16 ? art::launch_art_bf16(v, p, static_cast<hipStream_t>(stream))
                                : art::launch_art_fp8(v, p, static_cast<hipStream_t>(stream));

@@ -10,6 +10,14 @@ namespace art {
 
 enum KvType { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
+// Blocks per ART chunk: 8, fewer when a chunk's partials [C][GM][D] fp32
+// would pass 32 KiB.
+constexpr int art_chunk_blocks(int gm, int d) { return 8192 / (gm * d) < 8 ? 8192 / (gm * d) : 8; }
+// Floats of one chunk's partials: a[C][GM][D], m[C][GM], l[C][GM].
+constexpr int art_slot_floats(int gm, int d) {
+  return art_chunk_blocks(gm, d) * gm * d + 2 * art_chunk_blocks(gm, d) * gm;
+}
+
 // Everything a kernel needs, passed by value as the kernel argument.
 struct Params {
   const void* q;
@@ -24,6 +32,18 @@ struct Params {
   int32_t* stop_block;
   int32_t* blocks_fetched;  // may be null
   float* ws_part;           // full mode with splits: [streams][splits][GM][D + 2]
+  // ART scheduler (workspace): epoch-tagged control words and the ring of
+  // partial-result slots helpers hand to scanners
+  uint32_t* sched_ctrl;                // [0] stored epoch, [1] finished workgroups, [2] error flag
+  unsigned long long* sched_claim;     // [streams]
+  unsigned long long* sched_done;      // [streams]
+  unsigned long long* sched_ready;     // [streams][ring]
+  float* sched_ring;                   // [streams][ring][slot_floats]
+  int32_t ring;                        // slots per stream
+  int32_t slot_floats;                 // stride of one slot (>= art_slot_floats, multiple of 64)
+  int32_t helpers;                     // helper workgroups launched after the scanners
+  int32_t lookahead;                   // helper window: chunk c is claimable while c < done + min(ring, lookahead + done)
+  int32_t spin_limit;                  // bound of every wait loop
   int32_t batch, hq, hkv, g;
   int32_t block_size;
   int32_t max_blocks;
@@ -50,6 +70,12 @@ struct SplitPlan {
   int split_blocks;
 };
 SplitPlan full_split_plan(int batch, int hkv, int max_blocks);
+
+// Workspace layout (bytes from the workspace base, each region 256-B aligned).
+struct WorkspacePlan {
+  size_t claim, done, ready, data, total;
+  int ring, slot_floats, helpers, lookahead;
+};
 
 // Launchers; return hipSuccess or the launch error.  One translation unit per
 // (kernel, KV storage type): kern_<kernel>_<type>.hip.

@@ -16,17 +16,18 @@
 //    loaded with coalesced 16-byte loads in the A-operand layout; products and
 //    sums are fp32.
 //
-//  * art_chunk_kernel -- the terminating path.  One workgroup (NWA waves)
-//    owns one stream = (sequence, kv-head) and walks its visit order in
-//    chunks of C blocks.  Each wave turns one block into partials
-//    (m_b, l_b, a_b) in LDS; then one wave per query head folds the partials
-//    in visit order, forms O_t = A_t / L_t for every t of the chunk, reduces
-//    ‖O_t‖² and ‖O_t - O_{t-1}‖² for all t at once (transposed butterfly),
-//    evaluates both statistics and the patience rule for all t in parallel
-//    (one lane per t, bit masks).  A head that stops writes O_t and is frozen;
-//    the stream stops fetching when every head of its group stopped.  The KV
-//    loads of chunk c+1 are issued before chunk c is scanned (speculatively),
-//    and page entries run two chunks ahead.
+//  * art_sched_kernel -- the terminating path, one launch.  Scanner
+//    workgroups (one per stream = (sequence, kv-head), NWA waves) fold the
+//    stream's blocks in visit order, C blocks per step: per-block partials
+//    (m_b, l_b, a_b), then one wave per query head folds them, forms
+//    O_t = A_t / L_t for every t of the chunk, reduces ‖O_t‖² and
+//    ‖O_t - O_{t-1}‖² for all t at once (transposed butterfly) and evaluates
+//    both statistics and the patience rule for all t in parallel (one lane per
+//    t, bit masks).  A head that stops writes O_t and is frozen; the stream
+//    stops fetching when every head of its group stopped.  Helper workgroups
+//    compute the partials of chunks ahead of the scanners (see the
+//    scheduler notes below); chunks nobody claimed are computed by the
+//    scanner itself, with their KV loads issued one chunk ahead.
 //
 //  * full_split_kernel -- full attention (no detector).  Each workgroup owns
 //    a contiguous slice of one stream's blocks; each wave keeps its own
@@ -87,13 +88,30 @@ struct Cfg {
   static constexpr int QF = KV == KV_FP8 ? 2 * NKL : NKL;  // 16-B q fragments
   // ART chunk: C blocks (8, fewer when the per-block partials [C][GM][D]
   // fp32 would pass 32 KiB)
-  static constexpr int C = cmin(8, 8192 / (GM * D));
+  static constexpr int C = art_chunk_blocks(GM, D);
   static constexpr int NWA = cmin(8, C);              // waves per workgroup, ART kernel
   static constexpr int BPW = C / NWA;                 // blocks per wave per chunk
   static constexpr int HPW = (GM + NWA - 1) / NWA;    // query heads per wave in the scan
   static constexpr int DPL = D / 64;                  // d per lane in the scan
   static constexpr int SH = 6 - ilog2(2 * C);         // stat reduction: lane >> SH = value index
+  static constexpr int SLOT_A = C * GM * D;           // partials of one chunk: a[C][GM][D], m[C][GM], l[C][GM]
+  static constexpr int SLOT = art_slot_floats(GM, D);
+  // PV on v_mfma_f32_4x4x1_16b_f32 for query groups of up to 8 heads:
+  // V in a lane-owns-d layout (each 256-B load covers RPL token rows, LPR
+  // lanes per row, EPL consecutive d per lane), P broadcast per head from LDS.
+  static constexpr bool PV4 = GM <= 8;
+  static constexpr int RPL = R >= 256 ? 1 : 256 / R;  // token rows per V load
+  static constexpr int BPL = R >= 256 ? R / 64 : 4;   // V bytes per lane per load
+  static constexpr int LPR = 64 / RPL;                // lanes per token row
+  static constexpr int NLD = B / RPL;                 // V loads per block
+  static constexpr int VW = BPL / 4;                  // dwords per lane per load
+  static constexpr int EPL = BPL / ES;                // d per lane per load
+  static constexpr int HG = PV4 ? GM / 4 : 1;         // groups of 4 heads
+  static constexpr int CH = EPL >= 4 ? 1 : 2;         // independent accumulator chains
+  static constexpr int VN = B * R / 256;              // V dwords per lane per block (either layout)
+  static constexpr int NACC = PV4 ? HG * CH * EPL : DT;
   static_assert(BPW >= 1 && BPW * NWA == C, "chunk must split evenly over the waves");
+  static_assert(!PV4 || NLD % 4 == 0, "P is read four tokens at a time");
   static_assert(2 * C <= 64, "stat reduction holds at most 64 values");
   static_assert(VWD >= 1, "a lane reads at least one dword of each V row");
 };
@@ -101,7 +119,14 @@ struct Cfg {
 template <class Cf>
 struct BlockRegs {
   uint4 k[Cf::T][Cf::NKL];
-  uint32_t v[Cf::T][4][Cf::VWD];
+  uint32_t v[Cf::VN];  // PV4: [NLD][VW]; otherwise [T][4][VWD]
+};
+
+// PV accumulator: PV4: [HG][CH][EPL] tiles, lane l holds O[4hg + r][d(l, e)]
+// in component r; otherwise the 16x16 O^T tiles (lane = head column).
+template <class Cf>
+struct PvAcc {
+  f32x4 a[Cf::NACC];
 };
 
 // ---------------------------------------------------------------------------
@@ -233,26 +258,44 @@ __device__ __forceinline__ void load_block(BlockRegs<Cf>& r, const char* kt, con
 #pragma unroll
     for (int i = 0; i < Cf::NKL; ++i)
       r.k[t][i] = *reinterpret_cast<const uint4*>(kt + (size_t)(16 * t + c) * Cf::R + q * 16 + 64 * i);
+  if constexpr (Cf::PV4) {
+    // load u covers token rows u*RPL .. u*RPL+RPL-1; lane: row u*RPL + lane/LPR,
+    // bytes (lane % LPR) * BPL .. +BPL of it
+    const int rg = lane / Cf::LPR;
+    const int cb = (lane % Cf::LPR) * Cf::BPL;
 #pragma unroll
-  for (int t = 0; t < Cf::T; ++t)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int row = 16 * t + 4 * q + rr;
-      const char* src = vt + (size_t)min(row, nvalid - 1) * Cf::R + c * Cf::VBL;
-      if constexpr (Cf::VWD == 1) {
-        r.v[t][rr][0] = *reinterpret_cast<const uint32_t*>(src);
-      } else if constexpr (Cf::VWD == 2) {
-        const uint2 x = *reinterpret_cast<const uint2*>(src);
-        r.v[t][rr][0] = x.x; r.v[t][rr][1] = x.y;
+    for (int u = 0; u < Cf::NLD; ++u) {
+      const int row = u * Cf::RPL + rg;
+      const char* src = vt + (size_t)min(row, nvalid - 1) * Cf::R + cb;
+      if constexpr (Cf::VW == 1) {
+        r.v[u] = *reinterpret_cast<const uint32_t*>(src);
       } else {
-#pragma unroll
-        for (int h = 0; h < Cf::VWD / 4; ++h) {
-          const uint4 x = *reinterpret_cast<const uint4*>(src + 16 * h);
-          r.v[t][rr][4 * h + 0] = x.x; r.v[t][rr][4 * h + 1] = x.y;
-          r.v[t][rr][4 * h + 2] = x.z; r.v[t][rr][4 * h + 3] = x.w;
-        }
+        const uint2 x = *reinterpret_cast<const uint2*>(src);
+        r.v[2 * u] = x.x; r.v[2 * u + 1] = x.y;
       }
     }
+  } else {
+#pragma unroll
+    for (int t = 0; t < Cf::T; ++t)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = 16 * t + 4 * q + rr;
+        const char* src = vt + (size_t)min(row, nvalid - 1) * Cf::R + c * Cf::VBL;
+        uint32_t* dst = &r.v[(t * 4 + rr) * Cf::VWD];
+        if constexpr (Cf::VWD == 1) {
+          dst[0] = *reinterpret_cast<const uint32_t*>(src);
+        } else if constexpr (Cf::VWD == 2) {
+          const uint2 x = *reinterpret_cast<const uint2*>(src);
+          dst[0] = x.x; dst[1] = x.y;
+        } else {
+#pragma unroll
+          for (int h = 0; h < Cf::VWD / 4; ++h) {
+            const uint4 x = *reinterpret_cast<const uint4*>(src + 16 * h);
+            dst[4 * h + 0] = x.x; dst[4 * h + 1] = x.y; dst[4 * h + 2] = x.z; dst[4 * h + 3] = x.w;
+          }
+        }
+      }
+  }
 }
 
 // q fragments for the MFMA B operand: column (lane & 15) = head of the group.
@@ -328,7 +371,7 @@ __device__ __forceinline__ float block_scores(const f32x4 (&S)[Cf::T], int nvali
 
 // A lane's V row segment (DT elements) as fp32 (exact for every storage type).
 template <class Cf>
-__device__ __forceinline__ void v_row(const uint32_t (&w)[Cf::VWD], float (&f)[Cf::DT]) {
+__device__ __forceinline__ void v_row(const uint32_t* w, float (&f)[Cf::DT]) {
   if constexpr (Cf::KV == KV_BF16) {
 #pragma unroll
     for (int i = 0; i < Cf::VWD; ++i) {
@@ -349,26 +392,147 @@ __device__ __forceinline__ void v_row(const uint32_t (&w)[Cf::VWD], float (&f)[C
   }
 }
 
-// acc += V^T P over the block: acc[dt] is the 16x16 tile of O^T whose rows are
-// d = DT * m + dt (m = 0..15) and whose columns are the heads of the group.
+// 16x16 layout (query groups of 9..16 heads): acc[dt] += V^T P over the
+// block, the 16x16 tile of O^T whose rows are d = DT * m + dt (m = 0..15)
+// and whose columns are the heads of the group.
 template <class Cf>
-__device__ __forceinline__ void pv_mfma(const BlockRegs<Cf>& r, const float (&pq)[Cf::T][4], f32x4 (&acc)[Cf::DT]) {
+__device__ __forceinline__ void pv_mfma(const BlockRegs<Cf>& r, const float (&pq)[Cf::T][4], f32x4 (&acc)[Cf::NACC]) {
 #pragma unroll
   for (int t = 0; t < Cf::T; ++t)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       float vf[Cf::DT];
-      v_row<Cf>(r.v[t][rr], vf);
+      v_row<Cf>(&r.v[(t * 4 + rr) * Cf::VWD], vf);
 #pragma unroll
       for (int dt = 0; dt < Cf::DT; ++dt)
         acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[dt], pq[t][rr], acc[dt], 0, 0, 0);
     }
 }
 
-// Store a lane's O^T accumulator row (head c) as D-contiguous floats:
-// dst points at [head][0]; the lane writes d = DT*(4q+i) + dt.
+// The lane's V values of load u (4x4 layout), as fp32 (exact).
 template <class Cf>
-__device__ __forceinline__ void store_acc(float* dst, int lane, const f32x4 (&acc)[Cf::DT], float scale) {
+__device__ __forceinline__ void v4_decode(const BlockRegs<Cf>& r, int u, float (&vf)[Cf::EPL]) {
+  if constexpr (Cf::KV == KV_BF16) {
+#pragma unroll
+    for (int j = 0; j < Cf::VW; ++j) {
+      const uint32_t w = r.v[u * Cf::VW + j];
+      vf[2 * j] = bitsf(w << 16);
+      vf[2 * j + 1] = bitsf(w & 0xffff0000u);
+    }
+  } else if constexpr (Cf::KV == KV_FP8) {
+    fp8x4_to_f32(r.v[u], vf);
+  } else {
+#pragma unroll
+    for (int j = 0; j < Cf::VW; ++j) vf[j] = bitsf(r.v[u * Cf::VW + j]);
+  }
+}
+
+// 4x4 layout: acc += P V over the block on v_mfma_f32_4x4x1_16b_f32.  Output
+// lane l, component r: O[4hg + r][d] with d = (l % LPR) * EPL + e; the A
+// operand (lane m) is P[4hg + m%4][token of lane m's V row], read from this
+// wave's LDS row buffer pbuf [GM][RPL][NLD] (token u*RPL + rg at [rg][u]).
+template <class Cf>
+__device__ __forceinline__ void pv4_mfma(const BlockRegs<Cf>& r, const float (&pq)[Cf::T][4], float* pbuf, int lane,
+                                         f32x4 (&acc)[Cf::NACC]) {
+  const int c16 = lane & 15;
+  const int q = lane >> 4;
+  if (c16 < Cf::GM) {
+    float* row = pbuf + c16 * Cf::B;
+#pragma unroll
+    for (int t = 0; t < Cf::T; ++t) {
+      if constexpr (Cf::RPL == 1) {
+        *reinterpret_cast<f32x4*>(row + 16 * t + 4 * q) = f32x4{pq[t][0], pq[t][1], pq[t][2], pq[t][3]};
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int k = 16 * t + 4 * q + rr;
+          row[(k % Cf::RPL) * Cf::NLD + k / Cf::RPL] = pq[t][rr];
+        }
+      }
+    }
+  }
+  const int rg = lane / Cf::LPR;
+#pragma unroll
+  for (int hg = 0; hg < Cf::HG; ++hg) {
+    const float* src = pbuf + (4 * hg + (lane & 3)) * Cf::B + rg * Cf::NLD;
+#pragma unroll
+    for (int u4 = 0; u4 < Cf::NLD / 4; ++u4) {
+      const f32x4 pp = *reinterpret_cast<const f32x4*>(src + 4 * u4);
+#pragma unroll
+      for (int uu = 0; uu < 4; ++uu) {
+        const int u = 4 * u4 + uu;
+        float vf[Cf::EPL];
+        v4_decode<Cf>(r, u, vf);
+#pragma unroll
+        for (int e = 0; e < Cf::EPL; ++e) {
+          f32x4& a = acc[(hg * Cf::CH + u % Cf::CH) * Cf::EPL + e];
+          a = __builtin_amdgcn_mfma_f32_4x4x1f32(pp[uu], vf[e], a, 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+template <class Cf>
+__device__ __forceinline__ void pv_zero(f32x4 (&acc)[Cf::NACC]) {
+#pragma unroll
+  for (int i = 0; i < Cf::NACC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+template <class Cf>
+__device__ __forceinline__ void pv_block(const BlockRegs<Cf>& r, const float (&pq)[Cf::T][4], float* pbuf, int lane,
+                                         f32x4 (&acc)[Cf::NACC]) {
+  if constexpr (Cf::PV4) pv4_mfma<Cf>(r, pq, pbuf, lane, acc);
+  else pv_mfma<Cf>(r, pq, acc);
+}
+
+// Multiply each head's accumulator by that head's factor; `al` is held by
+// lane h for head h (lanes 0..15 of the score layout).
+template <class Cf>
+__device__ __forceinline__ void pv_rescale(f32x4 (&acc)[Cf::NACC], float al) {
+  if constexpr (Cf::PV4) {
+#pragma unroll
+    for (int hg = 0; hg < Cf::HG; ++hg) {
+      float sc[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) sc[rr] = bitsf(__builtin_amdgcn_readlane(fbits(al), 4 * hg + rr));
+#pragma unroll
+      for (int i = 0; i < Cf::CH * Cf::EPL; ++i) {
+        f32x4& a = acc[hg * Cf::CH * Cf::EPL + i];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) a[rr] *= sc[rr];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < Cf::DT; ++dt) acc[dt] *= al;
+  }
+}
+
+// 4x4 layout: sum the chains into chain 0 and the token-row groups of a V
+// load (lanes l, l + LPR, ...) so that every lane holds the totals.
+template <class Cf>
+__device__ __forceinline__ void pv_finish(f32x4 (&acc)[Cf::NACC]) {
+  if constexpr (Cf::PV4) {
+#pragma unroll
+    for (int hg = 0; hg < Cf::HG; ++hg)
+#pragma unroll
+      for (int e = 0; e < Cf::EPL; ++e) {
+        f32x4& a = acc[(hg * Cf::CH) * Cf::EPL + e];
+        if constexpr (Cf::CH == 2) a += acc[(hg * Cf::CH + 1) * Cf::EPL + e];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          if constexpr (Cf::RPL == 2) a[rr] = xor32_sum(a[rr]);
+          if constexpr (Cf::RPL == 4) a[rr] = rows_sum(a[rr]);
+        }
+      }
+  }
+}
+
+// 16x16 layout: store a lane's O^T accumulator row (head c) as D-contiguous
+// floats: dst points at [head][0]; the lane writes d = DT*(4q+i) + dt.
+template <class Cf>
+__device__ __forceinline__ void store_acc(float* dst, int lane, const f32x4 (&acc)[Cf::NACC], float scale) {
   const int q = lane >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -381,259 +545,703 @@ __device__ __forceinline__ void store_acc(float* dst, int lane, const f32x4 (&ac
   }
 }
 
+// Store the (finished) accumulator as dst[h][d] (head-major, D floats per
+// head) for heads h < GM, scaled by `scale`.
+template <class Cf>
+__device__ __forceinline__ void pv_store(float* dst, int lane, const f32x4 (&acc)[Cf::NACC], float scale) {
+  if constexpr (Cf::PV4) {
+    if (lane < Cf::LPR) {
+#pragma unroll
+      for (int hg = 0; hg < Cf::HG; ++hg)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          float* o = dst + (4 * hg + rr) * Cf::D + lane * Cf::EPL;
+          float v[Cf::EPL];
+#pragma unroll
+          for (int e = 0; e < Cf::EPL; ++e) v[e] = acc[(hg * Cf::CH) * Cf::EPL + e][rr] * scale;
+          if constexpr (Cf::EPL == 4) *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
+          else if constexpr (Cf::EPL == 2) *reinterpret_cast<f32x2*>(o) = f32x2{v[0], v[1]};
+          else o[0] = v[0];
+        }
+    }
+  } else {
+    const int c16 = lane & 15;
+    if (c16 < Cf::GM) store_acc<Cf>(dst + c16 * Cf::D, lane, acc, scale);
+  }
+}
+
 __device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
 __device__ __forceinline__ float readlanef(float v, int l) { return bitsf(__builtin_amdgcn_readlane(fbits(v), l)); }
 
 // ---------------------------------------------------------------------------
-// Terminating kernel
+// Terminating path: one launch = per-stream scanners + helper workgroups
 // ---------------------------------------------------------------------------
-template <int KV, int D, int B, int GM>
-__global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_chunk_kernel(Params p) {
-  using Cf = Cfg<KV, D, B, GM>;
-  constexpr int C = Cf::C, NWA = Cf::NWA, BPW = Cf::BPW, HPW = Cf::HPW, DPL = Cf::DPL, SH = Cf::SH;
-  __shared__ __attribute__((aligned(16))) float part_a[C][GM][D];
-  __shared__ float part_m[C][GM];
-  __shared__ float part_l[C][GM];
-  __shared__ int alive_lds[GM];
+//
+// Workgroups [0, streams) are scanners: scanner s owns stream s, holds the
+// per-head ART state (running max, sum, numerator, previous output, pass
+// count, sink flag) in registers and folds the stream's blocks strictly in
+// visit order, one chunk of C blocks per step.  Workgroups past that are
+// helpers: they claim chunks of still-running streams ahead of the scanner,
+// turn them into per-block partials and publish them through a ring of slots
+// in the workspace.  The scanner folds a helper's chunk from its slot; any
+// chunk nobody claimed it computes itself, so it never waits for work that has
+// not been started.  When a stream stops (every head of the group fired) its
+// claim word is closed and helpers move to the other streams: CUs freed by
+// early-terminated streams go to the ones still running.
+//
+// Control words live in the workspace and carry an epoch in their upper 32
+// bits; a word written by an earlier call reads as its initial value, so no
+// call has to clear them.  The last workgroup to finish advances the epoch.
+//   claim[s]  = FIN | number of chunks claimed (initially 1: chunk 0 is the
+//               scanner's); claims are compare-and-swap, in chunk order.
+//   done[s]   = chunks the scanner has consumed (helpers may claim chunk c
+//               only while c < done + window, window <= ring).
+//   ready[s][c % ring] = c + 1 once chunk c's partials are in its slot.
+// Partials and flags are written and read with device-scope (agent) relaxed
+// atomics, which are coherent across the XCDs' L2s without a cache-wide
+// writeback; a helper waits for its partial stores to complete
+// (s_waitcnt vmcnt(0)) before it stores the ready flag.
 
+typedef unsigned long long u64;
+constexpr uint32_t CLAIM_FIN = 0x80000000u;
+
+__device__ __forceinline__ u64 ld_dev(const u64* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev32(const uint32_t* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(u64* a, u64 v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev32(uint32_t* a, uint32_t v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// compare-and-swap; returns the value found (== expected iff it succeeded)
+__device__ __forceinline__ u64 cas_dev(u64* a, u64 expected, u64 desired) {
+  __hip_atomic_compare_exchange_strong(a, &expected, desired, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return expected;
+}
+__device__ __forceinline__ u64 tag_word(uint32_t E, uint32_t v) { return ((u64)E << 32) | v; }
+__device__ __forceinline__ uint32_t tag_val(u64 w, uint32_t E, uint32_t init) {
+  return (uint32_t)(w >> 32) == E ? (uint32_t)w : init;
+}
+// the epoch of this call from the stored one (never 0, the value of a cleared word)
+__device__ __forceinline__ uint32_t epoch_of(uint32_t stored) { return stored + 1u == 0u ? 1u : stored + 1u; }
+// every memory operation this wave issued so far has completed
+__device__ __forceinline__ void wait_all_memory() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its global loads, so loads issued ahead (the next
+// chunk's KV tiles) stay in flight across it.  (__syncthreads() carries a
+// workgroup-scope fence, which on gfx950 waits for every outstanding load.)
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Lanes of one 16-lane row shifted up by K (lane i reads lane i-K); the
+// first K lanes of the row get `fill`.
+template <int K>
+__device__ __forceinline__ float row_shr(float x, float fill) {
+  return bitsf(__builtin_amdgcn_update_dpp(fbits(fill), fbits(x), 0x110 + K, 0xF, 0xF, false));
+}
+
+// Issue the KV loads of one chunk (BPW blocks per wave).  Slots past the chunk
+// end re-read its last block (a cache hit), so the loads are unconditional.
+template <class Cf>
+__device__ __forceinline__ void issue_chunk(BlockRegs<Cf> (&regs)[Cf::BPW], const Params& p, int kvh, int L,
+                                            int ob_lane, int pg_lane, int nt, int w, int lane) {
+  const size_t tile = (size_t)Cf::B * Cf::R;
+  const char* kbase = static_cast<const char*>(p.k_pages);
+  const char* vbase = static_cast<const char*>(p.v_pages);
+#pragma unroll
+  for (int i = 0; i < Cf::BPW; ++i) {
+    const int b = min(w * Cf::BPW + i, nt - 1);
+    const int nvalid = min(Cf::B, L - readlane(ob_lane, b) * Cf::B);
+    const size_t off = ((size_t)readlane(pg_lane, b) * p.hkv + kvh) * tile;
+    load_block<Cf>(regs[i], kbase + off, vbase + off, lane, nvalid);
+  }
+}
+
+// Block phase: each wave turns its blocks of the chunk into partials
+// (m_b, l_b, a_b) for every head of the group, into `part` (slot layout:
+// a[C][GM][D], then m[C][GM], then l[C][GM]).  Slots past the chunk end get
+// neutral partials (m = -inf, l = 0, a = 0).
+template <class Cf>
+__device__ __forceinline__ void block_phase(const BlockRegs<Cf> (&regs)[Cf::BPW], const uint4 (&qf)[Cf::QF],
+                                            int ob_lane, float ks_lane, float vs_lane, int nt, int L, float qk_log2,
+                                            int w, int lane, float* part, float* pbuf) {
+  const int c16 = lane & 15;
+#pragma unroll
+  for (int i = 0; i < Cf::BPW; ++i) {
+    const int b = w * Cf::BPW + i;
+    float* pa = part + (size_t)b * Cf::GM * Cf::D;
+    float* pm = part + Cf::SLOT_A + b * Cf::GM;
+    float* pl = pm + Cf::C * Cf::GM;
+    if (b < nt) {
+      const int nvalid = min(Cf::B, L - readlane(ob_lane, b) * Cf::B);
+      float ksc = 1.f, vsc = 1.f;
+      if constexpr (Cf::KV == KV_FP8) { ksc = readlanef(ks_lane, b); vsc = readlanef(vs_lane, b); }
+      f32x4 S[Cf::T];
+      qk_scores<Cf>(regs[i], qf, S);
+      float x[Cf::T][4];
+      const float mb = block_scores<Cf>(S, nvalid, qk_log2 * ksc, lane, x);
+      float ls = 0.f;
+      float pq[Cf::T][4];
+#pragma unroll
+      for (int t = 0; t < Cf::T; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(x[t][r] - mb);
+          ls += e;
+          pq[t][r] = e * vsc;
+        }
+      ls = rows_sum(ls);
+      f32x4 acc[Cf::NACC];
+      pv_zero<Cf>(acc);
+      pv_block<Cf>(regs[i], pq, pbuf, lane, acc);
+      pv_finish<Cf>(acc);
+      pv_store<Cf>(pa, lane, acc, 1.f);
+      if (c16 < Cf::GM && (lane >> 4) == 0) { pm[c16] = mb; pl[c16] = ls; }
+    } else {
+      if (c16 < Cf::GM && (lane >> 4) == 0) { pm[c16] = NEG_INF; pl[c16] = 0.f; }
+      for (int e = lane; e < Cf::GM * Cf::D; e += 64) pa[e] = 0.f;
+    }
+  }
+}
+
+// One head's chunk input in registers: lane holds a[t][DPL*lane + j] and, for
+// lane t < C, (m_t, l_t).
+template <class Cf>
+struct ChunkIn {
+  float a[Cf::C][Cf::DPL];
+  float m, l;
+};
+
+template <class Cf>
+__device__ __forceinline__ void gather_lds(ChunkIn<Cf>& in, const float* part, int h, int lane) {
+#pragma unroll
+  for (int t = 0; t < Cf::C; ++t) {
+    const float* src = part + ((size_t)t * Cf::GM + h) * Cf::D + Cf::DPL * lane;
+    if constexpr (Cf::DPL == 2) {
+      const f32x2 v = *reinterpret_cast<const f32x2*>(src);
+      in.a[t][0] = v.x; in.a[t][1] = v.y;
+    } else {
+      in.a[t][0] = src[0];
+    }
+  }
+  const int t = lane < Cf::C ? lane : 0;
+  in.m = lane < Cf::C ? part[Cf::SLOT_A + t * Cf::GM + h] : NEG_INF;
+  in.l = lane < Cf::C ? part[Cf::SLOT_A + Cf::C * Cf::GM + t * Cf::GM + h] : 0.f;
+}
+
+// The same from a ring slot in global memory, with device-scope loads.
+template <class Cf>
+__device__ __forceinline__ void gather_ring(ChunkIn<Cf>& in, const float* slot, int h, int lane) {
+#pragma unroll
+  for (int t = 0; t < Cf::C; ++t) {
+    const float* src = slot + ((size_t)t * Cf::GM + h) * Cf::D + Cf::DPL * lane;
+    if constexpr (Cf::DPL == 2) {
+      const u64 v = ld_dev(reinterpret_cast<const u64*>(src));
+      in.a[t][0] = bitsf((uint32_t)v); in.a[t][1] = bitsf((uint32_t)(v >> 32));
+    } else {
+      in.a[t][0] = bitsf(ld_dev32(reinterpret_cast<const uint32_t*>(src)));
+    }
+  }
+  const int t = lane < Cf::C ? lane : 0;
+  const float m = bitsf(ld_dev32(reinterpret_cast<const uint32_t*>(slot + Cf::SLOT_A + t * Cf::GM + h)));
+  const float l = bitsf(ld_dev32(reinterpret_cast<const uint32_t*>(slot + Cf::SLOT_A + Cf::C * Cf::GM + t * Cf::GM + h)));
+  in.m = lane < Cf::C ? m : NEG_INF;
+  in.l = lane < Cf::C ? l : 0.f;
+}
+
+// Per-head state carried across chunks.
+template <class Cf>
+struct HeadCarry {
+  float M, L, Np;
+  int cnt;
+  bool alive, sink;
+  float A[Cf::DPL], Op[Cf::DPL];
+};
+
+// Fold one chunk into one head and run the detector on every position of it.
+//  * The scalars of the fold are computed lane-parallel (lane t = position
+//    t): running maxima by a prefix max, rescale factors, and the running sums
+//    L_t by a prefix scan of the affine maps L -> al_t L + be_t l_t.
+//  * The vector fold A_t = al_t A_{t-1} + be_t a_t, O_t = A_t / L_t and the
+//    squared norms ‖O_t‖², ‖O_t - O_{t-1}‖² are per lane; the 2C squared norms
+//    are reduced together by one transposed butterfly.
+//  * Lane t then evaluates both statistics and the patience/sink rule.
+// Returns true if the head fired in this chunk (it wrote out/stop).
+template <class Cf>
+__device__ __forceinline__ bool scan_head(HeadCarry<Cf>& hc, const ChunkIn<Cf>& in, int t0, int nt,
+                                          unsigned long long sinkbits, const Params& p, int lane, float* out_row,
+                                          int32_t* stop_ptr) {
+  constexpr int C = Cf::C, DPL = Cf::DPL, SH = Cf::SH;
+  const int slot = lane < C ? lane : C - 1;
+
+  float mx = in.m;
+  if constexpr (C > 1) mx = fmaxf(mx, row_shr<1>(mx, NEG_INF));
+  if constexpr (C > 2) mx = fmaxf(mx, row_shr<2>(mx, NEG_INF));
+  if constexpr (C > 4) mx = fmaxf(mx, row_shr<4>(mx, NEG_INF));
+  mx = fmaxf(mx, hc.M);
+  const float mprev = row_shr<1>(mx, hc.M);
+  const float al = __builtin_amdgcn_exp2f(mprev - mx);
+  const float be = __builtin_amdgcn_exp2f(in.m - mx);
+  float fa = al, fb = be * in.l;
+  if constexpr (C > 1) { const float pa = row_shr<1>(fa, 1.f), pb = row_shr<1>(fb, 0.f); fb = fmaf(fa, pb, fb); fa *= pa; }
+  if constexpr (C > 2) { const float pa = row_shr<2>(fa, 1.f), pb = row_shr<2>(fb, 0.f); fb = fmaf(fa, pb, fb); fa *= pa; }
+  if constexpr (C > 4) { const float pa = row_shr<4>(fa, 1.f), pb = row_shr<4>(fb, 0.f); fb = fmaf(fa, pb, fb); fa *= pa; }
+  const float Lt = fmaf(fa, hc.L, fb);
+  const float rl = __builtin_amdgcn_rcpf(Lt);  // 1 ulp; the statistics need ~1e-6
+
+  float st[2 * C];
+  float oo[C][DPL];
+#pragma unroll
+  for (int t = 0; t < C; ++t) {
+    const float at = readlanef(al, t), bt = readlanef(be, t), rt = readlanef(rl, t);
+    float nn = 0.f, ee = 0.f;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) {
+      hc.A[j] = fmaf(at, hc.A[j], bt * in.a[t][j]);
+      const float o = hc.A[j] * rt;
+      const float df = o - hc.Op[j];
+      nn = fmaf(o, o, nn);
+      ee = fmaf(df, df, ee);
+      hc.Op[j] = o;
+      oo[t][j] = o;
+    }
+    st[2 * t] = nn;
+    st[2 * t + 1] = ee;
+  }
+  const float v0 = xreduce<2 * C>(st, lane);
+  // lane (2t) << SH holds ‖O_t‖², lane (2t+1) << SH holds ‖O_t - O_{t-1}‖²;
+  // gather them so that lane t < C evaluates position t.
+  const float nn_t = __shfl(v0, (2 * slot) << SH);
+  const float ee_t = __shfl(v0, (2 * slot + 1) << SH);
+  float np_t = __shfl(v0, (2 * max(slot - 1, 0)) << SH);
+  if (lane == 0) np_t = hc.Np;
+  bool ps = false;
+  if (lane < nt && t0 + lane >= 1) {
+    const float a = __builtin_amdgcn_sqrtf(nn_t);
+    const float bn = __builtin_amdgcn_sqrtf(np_t);
+    float dm, dd;
+    if (a == 0.f && bn == 0.f) {
+      dm = 0.f; dd = 0.f;
+    } else if (bn == 0.f) {
+      dm = __builtin_inff(); dd = 1.f;
+    } else {
+      const float df = a - bn;
+      dm = fabsf(df) * __builtin_amdgcn_rcpf(bn);
+      // 1 - cos = (‖O_t - O_{t-1}‖² - (‖O_t‖ - ‖O_{t-1}‖)²) / (2 ‖O_t‖ ‖O_{t-1}‖)
+      dd = (a == 0.f) ? 1.f : fmaxf(0.f, (ee_t - df * df) * __builtin_amdgcn_rcpf(2.f * a * bn));
+    }
+    ps = (dm < p.eps_mag) && (dd < p.eps_dir);
+  }
+  // patience rule for every position at once: lane t counts the passes in a
+  // row that end at t (carrying the count from earlier chunks when every test
+  // of this chunk up to t passed) and whether block 0 has been folded by t.
+  const unsigned long long pass = __ballot(ps);
+  const unsigned long long upto = (2ull << slot) - 1ull;
+  const unsigned long long zeros = ~pass & upto;
+  const int cnt_t = zeros == 0ull ? hc.cnt + slot + 1 : slot - (63 - __builtin_clzll(zeros));
+  const bool sink_t = hc.sink || (sinkbits & upto) != 0ull;
+  const unsigned long long fire = __ballot(lane < nt && cnt_t >= p.patience && sink_t);
+  hc.M = readlanef(mx, C - 1);
+  hc.L = readlanef(Lt, C - 1);
+  if (fire != 0ull) {
+    const int stop_t = __builtin_ctzll(fire);
+    float ov[DPL];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) ov[j] = oo[0][j];
+#pragma unroll
+    for (int t = 1; t < C; ++t)
+      if (stop_t == t)
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) ov[j] = oo[t][j];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) out_row[DPL * lane + j] = ov[j];
+    if (lane == 0) *stop_ptr = t0 + stop_t + 1;
+    hc.alive = false;
+    return true;
+  }
+  hc.cnt = readlane(cnt_t, nt - 1);
+  hc.sink = readlane(sink_t ? 1 : 0, nt - 1) != 0;
+  hc.Np = readlanef(nn_t, nt - 1);
+  return false;
+}
+
+// Scheduler workspace views (laid out by the host).
+struct Sched {
+  uint32_t* ctrl;   // [0] stored epoch, [1] finished workgroups, [2] error flag
+  u64* claim;       // [streams]
+  u64* done;        // [streams]
+  u64* ready;       // [streams][ring]
+  float* ring;      // [streams][ring][slot_floats]
+};
+
+template <class Cf>
+__device__ void art_scanner(const Params& p, int stream, uint32_t E, float* part, float* pbuf, int* sh) {
+  constexpr int C = Cf::C, NWA = Cf::NWA, HPW = Cf::HPW, DPL = Cf::DPL;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int stream = blockIdx.x;
   const int s = stream / p.hkv;
   const int kvh = stream - s * p.hkv;
   const int g = p.g;
   const int L = p.seq_lens[s];
-  const int n = (L + B - 1) / B;
+  const int n = (L + Cf::B - 1) / Cf::B;
+  const int nch = (n + C - 1) / C;
   const size_t head0 = (size_t)s * p.hq + (size_t)kvh * g;
+  u64* claimw = p.sched_claim + stream;
+  u64* donew = p.sched_done + stream;
+  u64* readyw = p.sched_ready + (size_t)stream * p.ring;
+  const float* ringb = p.sched_ring + (size_t)stream * p.ring * p.slot_floats;
 
   if (n <= 0) {
-    for (int i = threadIdx.x; i < g * D; i += 64 * NWA) p.out[head0 * D + i] = 0.f;
+    for (int i = threadIdx.x; i < g * Cf::D; i += 64 * NWA) p.out[head0 * Cf::D + i] = 0.f;
     if (threadIdx.x < g) p.stop_block[head0 + threadIdx.x] = 0;
-    if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[stream] = 0;
+    if (threadIdx.x == 0) {
+      u64 cw = ld_dev(claimw);
+      for (int k = 0; k < 64; ++k) {
+        const u64 r = cas_dev(claimw, cw, tag_word(E, CLAIM_FIN | (tag_val(cw, E, 1) & ~CLAIM_FIN)));
+        if (r == cw) break;
+        cw = r;
+      }
+      if (p.blocks_fetched) p.blocks_fetched[stream] = 0;
+    }
     return;
   }
 
   uint4 qf[Cf::QF];
   load_q<Cf>(p, s, kvh, lane, qf);
-
-  const size_t tile = (size_t)B * Cf::R;
-  const char* kbase = static_cast<const char*>(p.k_pages);
-  const char* vbase = static_cast<const char*>(p.v_pages);
   const int32_t* trow = p.block_table + (size_t)s * p.max_blocks;
   const int32_t* orow = p.block_order + (size_t)s * p.max_blocks;
-  const int c16 = lane & 15;
   const int slot = lane < C ? lane : C - 1;
 
-  // Chunk entries are lane-held (lane = slot): logical block and page of the
-  // current chunk (c) and of the next (n); entries of chunk c+2 are fetched
-  // while chunk c is scanned, so no KV load waits on the tables.
-  int ob_c = orow[min(slot, n - 1)];
-  int ob_n = orow[min(C + slot, n - 1)];
-  int pg_c = trow[ob_c];
-  int pg_n = trow[ob_n];
-  float ks_c = 1.f, vs_c = 1.f;
-
-  BlockRegs<Cf> regs[BPW];
-  auto issue_chunk = [&](int ob_lane, int pg_lane, int nt_chunk) {
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const int b = min(w * BPW + i, nt_chunk - 1);  // slots past the end re-read a valid block (cache hit)
-      const int nvalid = min(B, L - readlane(ob_lane, b) * B);
-      const size_t off = ((size_t)readlane(pg_lane, b) * p.hkv + kvh) * tile;
-      load_block<Cf>(regs[i], kbase + off, vbase + off, lane, nvalid);
-    }
+  // Order and page entries in two lane-held windows of 64 visit positions,
+  // [W, W+64) and [W+64, W+128); a chunk's entries (lane = slot) are picked
+  // out with a lane permute.  The next window is fetched 8 chunks before it
+  // is needed, so no KV load waits on the tables.
+  int W = 0;
+  int ob_w0 = orow[min(lane, n - 1)];
+  int ob_w1 = orow[min(64 + lane, n - 1)];
+  int pg_w0 = trow[ob_w0];
+  int pg_w1 = trow[ob_w1];
+  bool pg_w1_due = false;  // ob_w1 was refreshed; its pages are looked up one step later
+  auto entries = [&](int tc, int& ob, int& pg) {
+    const bool in1 = tc >= W + 64;
+    const int idx = tc - W - (in1 ? 64 : 0) + slot;
+    ob = __shfl(in1 ? ob_w1 : ob_w0, idx);
+    pg = __shfl(in1 ? pg_w1 : pg_w0, idx);
   };
-  issue_chunk(ob_c, pg_c, min(C, n));
-  if constexpr (KV == KV_FP8) {
+  int ob_c, pg_c, ob_n, pg_n;
+  entries(0, ob_c, pg_c);
+  float ks_c = 1.f, vs_c = 1.f;
+  BlockRegs<Cf> regs[Cf::BPW];
+  issue_chunk<Cf>(regs, p, kvh, L, ob_c, pg_c, min(C, n), w, lane);
+  if constexpr (Cf::KV == KV_FP8) {
     ks_c = p.k_scale[(size_t)pg_c * p.hkv + kvh];
     vs_c = p.v_scale[(size_t)pg_c * p.hkv + kvh];
   }
 
-  // Per-head streaming state, carried across chunks (head h = w + NWA * k).
-  float cM[HPW], cL[HPW], cNp[HPW];
-  int cCnt[HPW];
-  bool cAlive[HPW], cSink[HPW];
-  float cA[HPW][DPL], cOp[HPW][DPL];
-#pragma unroll
-  for (int k = 0; k < HPW; ++k) {
-    cM[k] = NEG_INF; cL[k] = 0.f; cNp[k] = 0.f; cCnt[k] = 0; cSink[k] = false;
-    cAlive[k] = (w + NWA * k) < g;
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) { cA[k][j] = 0.f; cOp[k][j] = 0.f; }
+  // claim state (thread 0 only): last seen claim word; the attempt for the
+  // chunk after next is issued one step before its result is needed
+  u64 cw = 0, exp_n = 0, ret_n = 0;
+  bool tried_n = false;
+  if (threadIdx.x == 0) {
+    cw = ld_dev(claimw);
+    if (nch > 1 && (tag_val(cw, E, 1) & ~CLAIM_FIN) == 1u) {
+      exp_n = cw;
+      ret_n = cas_dev(claimw, cw, tag_word(E, 2));
+      tried_n = true;
+    }
   }
 
-  int fetched = min(C, n);
-  for (int t0 = 0; t0 < n; t0 += C) {
+  HeadCarry<Cf> hc[HPW];
+#pragma unroll
+  for (int k = 0; k < HPW; ++k) {
+    hc[k].M = NEG_INF; hc[k].L = 0.f; hc[k].Np = 0.f; hc[k].cnt = 0; hc[k].sink = false;
+    hc[k].alive = (w + NWA * k) < g;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) { hc[k].A[j] = 0.f; hc[k].Op[j] = 0.f; }
+  }
+  ChunkIn<Cf> cur[HPW], nxt[HPW];
+  bool cur_loaded = false, nxt_loaded = false;
+  u64 flag_n = 0;           // ready word of chunk c+1, read one step ahead
+  bool local_c = true;      // chunk 0 is always the scanner's
+  int unloaded = -1;        // a chunk this scanner claimed and never loaded
+  bool err = false;
+  int c = 0;
+  for (;; ++c) {
+    const int t0 = c * C;
     const int nt = min(C, n - t0);
+    const bool has_next = c + 1 < nch;
 
-    // ---- block phase: per-block partials (m_b, l_b, a_b) into LDS; slots past
-    // the chunk end get neutral partials (m = -inf, l = 0, a = 0).
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const int b = w * BPW + i;
-      if (b < nt) {
-        const int nvalid = min(B, L - readlane(ob_c, b) * B);
-        float ksc = 1.f, vsc = 1.f;
-        if constexpr (KV == KV_FP8) { ksc = readlanef(ks_c, b); vsc = readlanef(vs_c, b); }
-        f32x4 S[Cf::T];
-        qk_scores<Cf>(regs[i], qf, S);
-        float x[Cf::T][4];
-        const float mb = block_scores<Cf>(S, nvalid, p.qk_log2 * ksc, lane, x);
-        float ls = 0.f;
-        float pq[Cf::T][4];
-#pragma unroll
-        for (int t = 0; t < Cf::T; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float e = __builtin_amdgcn_exp2f(x[t][r] - mb);
-            ls += e;
-            pq[t][r] = e * vsc;
-          }
-        ls = rows_sum(ls);
-        f32x4 acc[Cf::DT];
-#pragma unroll
-        for (int dt = 0; dt < Cf::DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        pv_mfma<Cf>(regs[i], pq, acc);
-        if (c16 < GM) {
-          store_acc<Cf>(&part_a[b][c16][0], lane, acc, 1.f);
-          if ((lane >> 4) == 0) { part_m[b][c16] = mb; part_l[b][c16] = ls; }
-        }
-      } else {
-        if (c16 < GM && (lane >> 4) == 0) { part_m[b][c16] = NEG_INF; part_l[b][c16] = 0.f; }
-        for (int e = lane; e < GM * D; e += 64) (&part_a[b][0][0])[e] = 0.f;
+    if (local_c) block_phase<Cf>(regs, qf, ob_c, ks_c, vs_c, nt, L, p.qk_log2, w, lane, part, pbuf);
+
+    // resolve the claim of chunk c+1, attempt the claim of chunk c+2
+    if (threadIdx.x == 0) {
+      bool loc = false;
+      if (has_next && tried_n) {
+        loc = ret_n == exp_n;
+        cw = loc ? tag_word(E, c + 2) : ret_n;
+      }
+      sh[0] = loc ? 1 : 0;
+      tried_n = false;
+      if (c + 2 < nch && (tag_val(cw, E, 1) & ~CLAIM_FIN) == (uint32_t)(c + 2)) {
+        exp_n = cw;
+        ret_n = cas_dev(claimw, cw, tag_word(E, c + 3));
+        tried_n = true;
       }
     }
+    lds_barrier();
+    const bool local_n = has_next && sh[0] != 0;
 
-    // ---- speculative fetch of the next chunk: its loads fly during the scan
-    const bool has_next = t0 + C < n;
-    int ob_nn = 0;
+    // next chunk's KV loads fly during the scan
     float ks_n = 1.f, vs_n = 1.f;
-    if (has_next) {
-      const int nt1 = min(C, n - t0 - C);
-      issue_chunk(ob_n, pg_n, nt1);
-      __builtin_amdgcn_sched_barrier(0);  // the loads must leave before the scan
-      if constexpr (KV == KV_FP8) {
+    if (has_next) entries(t0 + C, ob_n, pg_n);
+    if (local_n) {
+      issue_chunk<Cf>(regs, p, kvh, L, ob_n, pg_n, min(C, n - t0 - C), w, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (Cf::KV == KV_FP8) {
         ks_n = p.k_scale[(size_t)pg_n * p.hkv + kvh];
         vs_n = p.v_scale[(size_t)pg_n * p.hkv + kvh];
       }
-      ob_nn = orow[min(t0 + 2 * C + slot, n - 1)];
-      fetched += nt1;
     }
-    __syncthreads();
 
-    // ---- scan phase: fold the chunk's partials in visit order, one wave per head
+    // ---- scan waves: this chunk's inputs, next chunk's prefetch, the scan
     const unsigned long long sinkbits = __ballot(lane < nt && ob_c == 0);
+    bool scanning = false;
 #pragma unroll
-    for (int k = 0; k < HPW; ++k) {
-      const int h = w + NWA * k;
-      if (h < g && cAlive[k]) {
-        // branch-free over all C slots: neutral slots leave (M, L, A) unchanged
-        float st[2 * C];
+    for (int k = 0; k < HPW; ++k) scanning |= (w + NWA * k) < g && hc[k].alive;
+    if (scanning && !err) {
+      if (local_c) {
 #pragma unroll
-        for (int t = 0; t < C; ++t) {
-          const float mb = part_m[t][h];
-          const float lb = part_l[t][h];
-          const float Mn = fmaxf(cM[k], mb);
-          const float al = __builtin_amdgcn_exp2f(cM[k] - Mn);
-          const float be = __builtin_amdgcn_exp2f(mb - Mn);
-          cL[k] = fmaf(al, cL[k], be * lb);
-          cM[k] = Mn;
-          const float rl = __builtin_amdgcn_rcpf(cL[k]);  // 1 ulp; the statistics need ~1e-6
-          float nn = 0.f, ee = 0.f;
-#pragma unroll
-          for (int j = 0; j < DPL; ++j) {
-            float* sl = &part_a[t][h][lane + 64 * j];
-            cA[k][j] = fmaf(al, cA[k][j], be * *sl);
-            const float o = cA[k][j] * rl;
-            const float df = o - cOp[k][j];
-            nn = fmaf(o, o, nn);
-            ee = fmaf(df, df, ee);
-            cOp[k][j] = o;
-            *sl = o;  // keep O_t for the epilogue
-          }
-          st[2 * t] = nn;
-          st[2 * t + 1] = ee;
+        for (int k = 0; k < HPW; ++k)
+          if (w + NWA * k < g) gather_lds<Cf>(cur[k], part, w + NWA * k, lane);
+      } else if (!cur_loaded) {
+        const u64* fw = readyw + c % p.ring;
+        int spins = 0;
+        while (tag_val(ld_dev(fw), E, 0) != (uint32_t)(c + 1)) {
+          if (++spins > p.spin_limit) { err = true; break; }
+          __builtin_amdgcn_s_sleep(1);
         }
-        const float v0 = xreduce<2 * C>(st, lane);
-        // lane (2t) << SH holds ‖O_t‖², lane (2t+1) << SH holds ‖O_t - O_{t-1}‖²;
-        // gather them so that lane t < C evaluates position t.
-        const float nn_t = __shfl(v0, (2 * slot) << SH);
-        const float ee_t = __shfl(v0, (2 * slot + 1) << SH);
-        float np_t = __shfl(v0, (2 * max(slot - 1, 0)) << SH);
-        if (lane == 0) np_t = cNp[k];
-        bool ps = false;
-        if (lane < nt && t0 + lane >= 1) {
-          const float a = __builtin_amdgcn_sqrtf(nn_t);
-          const float bn = __builtin_amdgcn_sqrtf(np_t);
-          float dm, dd;
-          if (a == 0.f && bn == 0.f) {
-            dm = 0.f; dd = 0.f;
-          } else if (bn == 0.f) {
-            dm = __builtin_inff(); dd = 1.f;
-          } else {
-            const float df = a - bn;
-            dm = fabsf(df) * __builtin_amdgcn_rcpf(bn);
-            // 1 - cos = (‖O_t - O_{t-1}‖² - (‖O_t‖ - ‖O_{t-1}‖)²) / (2 ‖O_t‖ ‖O_{t-1}‖)
-            dd = (a == 0.f) ? 1.f : fmaxf(0.f, (ee_t - df * df) * __builtin_amdgcn_rcpf(2.f * a * bn));
-          }
-          ps = (dm < p.eps_mag) && (dd < p.eps_dir);
-        }
-        // patience rule for every position at once: lane t counts the passes
-        // in a row that end at t (carrying the count from earlier chunks when
-        // every test of this chunk up to t passed) and whether block 0 has
-        // been folded by t.
-        const unsigned long long pass = __ballot(ps);
-        const unsigned long long upto = (2ull << slot) - 1ull;
-        const unsigned long long zeros = ~pass & upto;
-        const int cnt_t = zeros == 0ull ? cCnt[k] + slot + 1 : slot - (63 - __builtin_clzll(zeros));
-        const bool sink_t = cSink[k] || (sinkbits & upto) != 0ull;
-        const unsigned long long fire = __ballot(lane < nt && cnt_t >= p.patience && sink_t);
-        if (fire != 0ull) {
-          const int stop_t = __builtin_ctzll(fire);
-          float* o = p.out + (head0 + h) * D;
+        const float* sl = ringb + (size_t)(c % p.ring) * p.slot_floats;
 #pragma unroll
-          for (int j = 0; j < DPL; ++j) o[lane + 64 * j] = part_a[stop_t][h][lane + 64 * j];
-          if (lane == 0) p.stop_block[head0 + h] = t0 + stop_t + 1;
-          cAlive[k] = false;
-        } else {
-          cCnt[k] = readlane(cnt_t, nt - 1);
-          cSink[k] = readlane(sink_t ? 1 : 0, nt - 1) != 0;
-          cNp[k] = readlanef(nn_t, nt - 1);
-        }
+        for (int k = 0; k < HPW; ++k)
+          if (w + NWA * k < g) gather_ring<Cf>(cur[k], sl, w + NWA * k, lane);
+      }
+      // helper chunk c+1: if its ready flag (read a step ago) is set, load it now
+      nxt_loaded = false;
+      if (has_next && !local_n && tag_val(flag_n, E, 0) == (uint32_t)(c + 2)) {
+        const float* sl = ringb + (size_t)((c + 1) % p.ring) * p.slot_floats;
+#pragma unroll
+        for (int k = 0; k < HPW; ++k)
+          if (w + NWA * k < g) gather_ring<Cf>(nxt[k], sl, w + NWA * k, lane);
+        nxt_loaded = true;
+      }
+      flag_n = (c + 2 < nch) ? ld_dev(readyw + (c + 2) % p.ring) : 0ull;
+
+#pragma unroll
+      for (int k = 0; k < HPW; ++k) {
+        const int h = w + NWA * k;
+        if (h < g && hc[k].alive && !err)
+          scan_head<Cf>(hc[k], cur[k], t0, nt, sinkbits, p, lane, p.out + (head0 + h) * Cf::D,
+                        p.stop_block + head0 + h);
       }
     }
     if (lane == 0) {
+      int a = 0;
 #pragma unroll
       for (int k = 0; k < HPW; ++k)
-        if (w + NWA * k < g) alive_lds[w + NWA * k] = cAlive[k] ? 1 : 0;
+        if (w + NWA * k < g && hc[k].alive) a = 1;
+      sh[4 + w] = a | (err ? 2 : 0);
     }
-    __syncthreads();
+    lds_barrier();
     int any = 0;
-    for (int h = 0; h < g; ++h) any |= alive_lds[h];
-    if (!any || !has_next) break;
-    // rotate the lane-held entries; the page of chunk c+2 is looked up now
+#pragma unroll
+    for (int ww = 0; ww < NWA; ++ww) any |= sh[4 + ww];
+    if (any & 2) { err = true; break; }
+    if (threadIdx.x == 0) st_dev(donew, tag_word(E, c + 1));
+    if (!(any & 1) || !has_next) break;
+    // rotate: chunk c+1 becomes current
+#pragma unroll
+    for (int k = 0; k < HPW; ++k) cur[k] = nxt[k];
+    cur_loaded = nxt_loaded;
+    local_c = local_n;
     ob_c = ob_n;
     pg_c = pg_n;
-    ob_n = ob_nn;
-    pg_n = trow[ob_nn];
     ks_c = ks_n;
     vs_c = vs_n;
+    if (pg_w1_due) {
+      pg_w1 = trow[ob_w1];
+      pg_w1_due = false;
+    }
+    if (t0 + 2 * C == W + 64) {  // the next chunk opens window 1: slide
+      W += 64;
+      ob_w0 = ob_w1;
+      pg_w0 = pg_w1;
+      ob_w1 = orow[min(W + 64 + lane, n - 1)];
+      pg_w1_due = true;
+    }
   }
 
-  // heads that never stopped: output after all n blocks
+  // heads that never stopped: the output after all n blocks
 #pragma unroll
   for (int k = 0; k < HPW; ++k) {
     const int h = w + NWA * k;
-    if (h < g && cAlive[k]) {
-      float* o = p.out + (head0 + h) * D;
+    if (h < g && hc[k].alive) {
+      float* o = p.out + (head0 + h) * Cf::D;
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) o[lane + 64 * j] = cOp[k][j];
-      if (lane == 0) p.stop_block[head0 + h] = n;
+      for (int j = 0; j < DPL; ++j) o[DPL * lane + j] = err ? __builtin_nanf("") : hc[k].Op[j];
+      if (lane == 0) p.stop_block[head0 + h] = err ? -1 : n;
     }
   }
-  if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[stream] = fetched;
-  // speculative loads of a chunk that was not needed may still be in flight
-  __builtin_amdgcn_s_waitcnt(0);
+  // close the stream: no more claims; KV tiles fetched = every claimed chunk
+  // except one the scanner claimed and then did not need
+  if (threadIdx.x == 0) {
+    if (tried_n) {
+      if (ret_n == exp_n) { cw = tag_word(E, c + 3); unloaded = c + 2; } else { cw = ret_n; }
+    }
+    uint32_t cnt = 0;
+    for (int k = 0; k < (1 << 20); ++k) {
+      cnt = tag_val(cw, E, 1) & ~CLAIM_FIN;
+      const u64 r = cas_dev(claimw, cw, tag_word(E, CLAIM_FIN | cnt));
+      if (r == cw) break;
+      cw = r;
+    }
+    if (err) st_dev32(p.sched_ctrl + 2, 1u);
+    if (p.blocks_fetched) {
+      int f = min(n, (int)cnt * C);
+      if (unloaded >= 0) f -= min(C, n - unloaded * C);
+      p.blocks_fetched[stream] = f;
+    }
+  }
+}
+
+template <class Cf>
+__device__ void art_helper(const Params& p, int hid, uint32_t E, float* part, float* pbuf, int* sh) {
+  constexpr int C = Cf::C, NWA = Cf::NWA;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int streams = p.batch * p.hkv;
+  const int slot = lane < C ? lane : C - 1;
+  int pref = hid % streams;
+  BlockRegs<Cf> regs[Cf::BPW];
+  for (int iter = 0;; ++iter) {
+    // ---- wave 0 looks for a claimable chunk: 64 streams per round
+    if (w == 0) {
+      int got_s = -1, got_c = 0;
+      bool live_any = false;
+      for (int base = 0; base < streams && got_s < 0; base += 64) {
+        const bool valid = base + lane < streams;
+        int st = pref + base + lane;
+        if (st >= streams) st -= streams;
+        u64 cwv = 0, dwv = 0;
+        int nchv = 0;
+        if (valid) {
+          cwv = ld_dev(p.sched_claim + st);
+          dwv = ld_dev(p.sched_done + st);
+          const int nb = (p.seq_lens[st / p.hkv] + Cf::B - 1) / Cf::B;
+          nchv = (nb + C - 1) / C;
+        }
+        const uint32_t cv = tag_val(cwv, E, 1);
+        const uint32_t cnt = cv & ~CLAIM_FIN;
+        const uint32_t dn = tag_val(dwv, E, 0);
+        const bool live = valid && (cv & CLAIM_FIN) == 0u && (int)cnt < nchv;
+        const uint32_t win = min((uint32_t)p.ring, (uint32_t)p.lookahead + dn);
+        const bool ok = live && cnt < dn + win;
+        live_any |= __ballot(live) != 0ull;
+        unsigned long long m = __ballot(ok);
+        while (m != 0ull) {
+          const int l = __builtin_ctzll(m);
+          int won = 0;
+          if (lane == l) won = cas_dev(p.sched_claim + st, cwv, tag_word(E, cnt + 1)) == cwv;
+          if (__ballot(won) != 0ull) {
+            got_s = readlane(st, l);
+            got_c = readlane((int)cnt, l);
+            break;
+          }
+          m &= m - 1ull;
+        }
+      }
+      if (lane == 0) { sh[0] = got_s; sh[1] = got_c; sh[2] = live_any ? 1 : 0; }
+    }
+    lds_barrier();
+    const int st = sh[0], cc = sh[1];
+    const bool live_any = sh[2] != 0;
+    lds_barrier();
+    if (st < 0) {
+      if (!live_any || iter >= p.spin_limit) break;
+      __builtin_amdgcn_s_sleep(4);
+      continue;
+    }
+    pref = st;
+
+    // ---- produce chunk cc of stream st into its ring slot
+    const int s = st / p.hkv;
+    const int kvh = st - s * p.hkv;
+    const int L = p.seq_lens[s];
+    const int n = (L + Cf::B - 1) / Cf::B;
+    const int t0 = cc * C;
+    const int nt = min(C, n - t0);
+    const int32_t* trow = p.block_table + (size_t)s * p.max_blocks;
+    const int32_t* orow = p.block_order + (size_t)s * p.max_blocks;
+    const int ob = orow[min(t0 + slot, n - 1)];
+    const int pg = trow[ob];
+    float ks = 1.f, vs = 1.f;
+    issue_chunk<Cf>(regs, p, kvh, L, ob, pg, nt, w, lane);
+    if constexpr (Cf::KV == KV_FP8) {
+      ks = p.k_scale[(size_t)pg * p.hkv + kvh];
+      vs = p.v_scale[(size_t)pg * p.hkv + kvh];
+    }
+    uint4 qf[Cf::QF];
+    load_q<Cf>(p, s, kvh, lane, qf);
+    block_phase<Cf>(regs, qf, ob, ks, vs, nt, L, p.qk_log2, w, lane, part, pbuf);
+    lds_barrier();
+    u64* dst = reinterpret_cast<u64*>(p.sched_ring + ((size_t)st * p.ring + cc % p.ring) * p.slot_floats);
+    const u64* src = reinterpret_cast<const u64*>(part);
+    for (int i = threadIdx.x; i < Cf::SLOT / 2; i += 64 * NWA) st_dev(dst + i, src[i]);
+    wait_all_memory();
+    lds_barrier();
+    if (threadIdx.x == 0) st_dev(p.sched_ready + (size_t)st * p.ring + cc % p.ring, tag_word(E, cc + 1));
+  }
+}
+
+template <int KV, int D, int B, int GM>
+__global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_sched_kernel(Params p) {
+  using Cf = Cfg<KV, D, B, GM>;
+  __shared__ __attribute__((aligned(16))) float part[Cf::SLOT];
+  __shared__ __attribute__((aligned(16))) float pbuf_all[Cf::NWA][Cf::PV4 ? GM * B : 4];
+  __shared__ int sh[4 + Cf::NWA];
+  __shared__ uint32_t epoch_sh;
+  if (threadIdx.x == 0) epoch_sh = epoch_of(ld_dev32(p.sched_ctrl));
+  lds_barrier();
+  const uint32_t E = epoch_sh;
+  const int streams = p.batch * p.hkv;
+  if ((int)blockIdx.x < streams)
+    art_scanner<Cf>(p, blockIdx.x, E, part, pbuf_all[threadIdx.x >> 6], sh);
+  else
+    art_helper<Cf>(p, blockIdx.x - streams, E, part, pbuf_all[threadIdx.x >> 6], sh);
+  // speculative loads may still be in flight; then count this workgroup out
+  // (the last one advances the epoch for the next call)
+  wait_all_memory();
+  lds_barrier();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(p.sched_ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == gridDim.x - 1) {
+      st_dev32(p.sched_ctrl + 1, 0u);
+      st_dev32(p.sched_ctrl, E);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -642,7 +1250,7 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_chunk_kerne
 template <class Cf>
 __device__ __forceinline__ void full_block(const BlockRegs<Cf>& r, int nvalid, float ksc, float vsc,
                                            const uint4 (&qf)[Cf::QF], float qk_log2, int lane, float& m_run,
-                                           float& l_run, f32x4 (&acc)[Cf::DT]) {
+                                           float& l_run, f32x4 (&acc)[Cf::NACC], float* pbuf) {
   f32x4 S[Cf::T];
   qk_scores<Cf>(r, qf, S);
   float x[Cf::T][4];
@@ -662,10 +1270,8 @@ __device__ __forceinline__ void full_block(const BlockRegs<Cf>& r, int nvalid, f
   ls = rows_sum(ls);
   l_run = fmaf(al, l_run, ls);
   m_run = mn;
-  // the lane's accumulator column is its own head: rescale in place
-#pragma unroll
-  for (int dt = 0; dt < Cf::DT; ++dt) acc[dt] *= al;
-  pv_mfma<Cf>(r, pq, acc);
+  pv_rescale<Cf>(acc, al);
+  pv_block<Cf>(r, pq, pbuf, lane, acc);
 }
 
 template <int KV, int D, int B, int GM>
@@ -675,6 +1281,7 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) float mw_a[NW][GM][D];
   __shared__ float mw_m[NW][GM];
   __shared__ float mw_l[NW][GM];
+  __shared__ __attribute__((aligned(16))) float pbuf_all[NW][Cf::PV4 ? GM * B : 4];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -711,16 +1318,16 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
   }
 
   float m_run = NEG_INF, l_run = 0.f;
-  f32x4 acc[Cf::DT];
-#pragma unroll
-  for (int dt = 0; dt < Cf::DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[Cf::NACC];
+  pv_zero<Cf>(acc);
+  float* pbuf = pbuf_all[w];
 
   auto nvalid_of = [&](int k) { return min(B, L - (b0 + w + NW * k) * B); };
   auto tile_of = [&](int k) { return ((size_t)readlane(tab, k) * p.hkv + kvh) * tile; };
   auto fold = [&](const BlockRegs<Cf>& r, int k) {
     float ks = 1.f, vs = 1.f;
     if constexpr (KV == KV_FP8) { ks = readlanef(ks_t, k); vs = readlanef(vs_t, k); }
-    full_block<Cf>(r, nvalid_of(k), ks, vs, qf, p.qk_log2, lane, m_run, l_run, acc);
+    full_block<Cf>(r, nvalid_of(k), ks, vs, qf, p.qk_log2, lane, m_run, l_run, acc, pbuf);
   };
 
   // Register ring of PF block buffers: while block k is folded, blocks
@@ -751,10 +1358,9 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
   // merge the four waves
   {
     const int c = lane & 15;
-    if (c < GM) {
-      store_acc<Cf>(&mw_a[w][c][0], lane, acc, 1.f);
-      if ((lane >> 4) == 0) { mw_m[w][c] = m_run; mw_l[w][c] = l_run; }
-    }
+    pv_finish<Cf>(acc);
+    pv_store<Cf>(&mw_a[w][0][0], lane, acc, 1.f);
+    if (c < GM && (lane >> 4) == 0) { mw_m[w][c] = m_run; mw_l[w][c] = l_run; }
   }
   __syncthreads();
 

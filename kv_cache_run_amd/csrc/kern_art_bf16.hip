@@ -1,4 +1,4 @@
-// Instantiations of art_chunk_kernel for KV storage BF16 (one translation unit per
+// Instantiations of art_sched_kernel for KV storage BF16 (one translation unit per
 // storage type and kernel so that the build runs in parallel).
 #include "art_kernels_impl.h"
 
@@ -7,7 +7,7 @@ namespace {
 
 template <int D, int B, int GM>
 hipError_t go(const Params& p, hipStream_t st) {
-  hipLaunchKernelGGL((kern::art_chunk_kernel<KV_BF16, D, B, GM>), dim3(p.batch * p.hkv), dim3(64 * kern::Cfg<KV_BF16, D, B, GM>::NWA), 0, st, p);
+  hipLaunchKernelGGL((kern::art_sched_kernel<KV_BF16, D, B, GM>), dim3(p.batch * p.hkv + p.helpers), dim3(64 * kern::Cfg<KV_BF16, D, B, GM>::NWA), 0, st, p);
   return hipGetLastError();
 }
 

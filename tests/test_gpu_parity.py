@@ -215,3 +215,78 @@ def test_full_size_sampled(w):
     case = synth.make_case(w)
     check_art(case, sample=48)
     check_full(case, sample=24)
+
+
+# ---- the workgroup scheduler ----------------------------------------------------------------------------
+#
+# Partials are computed by the same code whichever workgroup (scanner or helper) takes a chunk, and the
+# scanner folds them in visit order, so results must be bit-identical across scheduling configurations.
+
+SCHED_VARIANTS = [
+    dict(ART_HELPERS="0"),                                    # scanners only
+    dict(ART_HELPERS="-1"),                                   # default helper count
+    dict(ART_HELPERS="2000", ART_RING="2", ART_LOOKAHEAD="2"),  # many helpers, tight ring
+    dict(ART_HELPERS="64", ART_RING="1", ART_LOOKAHEAD="1"),    # one slot per stream
+    dict(ART_HELPERS="300", ART_RING="16", ART_LOOKAHEAD="16"),  # deep speculation
+]
+
+
+def _with_env(env, fn):
+    import os
+
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update(env)
+    try:
+        return fn()
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+@pytest.mark.parametrize("w,kw", [(W.LLAMA3_8B, dict(batch=3, context=8192 - 40)),
+                                  (W.RAGGED, dict(batch=3)),
+                                  (W.QWEN_FP8, dict(batch=2, context=16384 - 3))],
+                         ids=["llama", "ragged", "fp8"])
+def test_scheduler_variants_bit_identical(w, kw):
+    case = synth.make_case(w, **kw)
+    em, ed, p = case["eps_mag"], case["eps_dir"], case["patience"]
+    ref = None
+    for env in SCHED_VARIANTS:
+        print(f"[sched] {case['workload']} {env}", flush=True)
+        out, stop, fetched = _with_env(env, lambda: _device_run(case, em, ed, p))
+        if ref is None:
+            rep, ref_out, ref_stop, _ = check_art(case)
+            assert np.array_equal(ref_out, out) and np.array_equal(ref_stop, stop)
+            ref = (out, stop)
+        else:
+            assert np.array_equal(out, ref[0]), env
+            assert np.array_equal(stop, ref[1]), env
+        n = _nblocks(case)
+        g = case["num_q_heads"] // case["num_kv_heads"]
+        grp_max = stop.reshape(case["batch"], case["num_kv_heads"], g).max(axis=2)
+        assert np.all(fetched >= grp_max) and np.all(fetched <= n[:, None]), env
+
+
+def test_scheduler_epoch_advances_and_no_error():
+    import torch
+
+    from kv_cache_run_amd import art
+
+    case = synth.make_case(W.RAGGED, batch=2)
+    dev = art.case_to_device(case)
+    dec = art.Decoder(dev["q"], dev["k_pages"], dev["block_table"])
+    outs = []
+    for i in range(4):
+        out, stop = dec(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"], dev["block_order"],
+                        dev["seq_lens"], case["eps_mag"], case["eps_dir"], case["patience"])
+        torch.cuda.synchronize()
+        ctrl = dec.workspace[:12].view(torch.int32).cpu().numpy()
+        assert ctrl[0] == i + 1, ctrl      # stored epoch
+        assert ctrl[1] == 0, ctrl          # finished-workgroup counter back to 0
+        assert ctrl[2] == 0, ctrl          # no bounded wait ran out
+        outs.append((out.cpu(), stop.cpu()))
+    for o, s in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(s, outs[0][1])
