@@ -89,9 +89,15 @@ struct Cfg {
   // ART chunk: C blocks (8, fewer when the per-block partials [C][GM][D]
   // fp32 would pass 32 KiB)
   static constexpr int C = art_chunk_blocks(GM, D);
-  static constexpr int NWA = cmin(8, C);              // waves per workgroup, ART kernel
-  static constexpr int BPW = C / NWA;                 // blocks per wave per chunk
-  static constexpr int HPW = (GM + NWA - 1) / NWA;    // query heads per wave in the scan
+  static constexpr int NS = 4;                        // scanner: scan waves
+  static constexpr int NBW = C;                       // scanner: block waves (one block of each chunk)
+  static constexpr int NWA = NS + NBW;                // waves per workgroup, ART kernel
+  static constexpr int BPB = 1;                       // blocks per block wave per chunk
+  static constexpr int HPS = (GM + NS - 1) / NS;      // scanner: query heads per scan wave
+  static constexpr int HWV = C;                       // helper: waves computing blocks (one each)
+  // register ring depth of a block wave: two chunks in flight when a block's
+  // K+V tiles take at most 32 VGPRs per lane, else one
+  static constexpr int PFD = 2 * B * R / 64 <= 128 ? 2 : 1;
   static constexpr int DPL = D / 64;                  // d per lane in the scan
   static constexpr int SH = 6 - ilog2(2 * C);         // stat reduction: lane >> SH = value index
   static constexpr int SLOT_A = C * GM * D;           // partials of one chunk: a[C][GM][D], m[C][GM], l[C][GM]
@@ -110,7 +116,7 @@ struct Cfg {
   static constexpr int CH = EPL >= 4 ? 1 : 2;         // independent accumulator chains
   static constexpr int VN = B * R / 256;              // V dwords per lane per block (either layout)
   static constexpr int NACC = PV4 ? HG * CH * EPL : DT;
-  static_assert(BPW >= 1 && BPW * NWA == C, "chunk must split evenly over the waves");
+  static_assert(BPB * NBW == C && HWV <= NWA, "one block wave per block of a chunk");
   static_assert(!PV4 || NLD % 4 == 0, "P is read four tokens at a time");
   static_assert(2 * C <= 64, "stat reduction holds at most 64 values");
   static_assert(VWD >= 1, "a lane reads at least one dword of each V row");
@@ -654,35 +660,36 @@ __device__ __forceinline__ float row_shr(float x, float fill) {
   return bitsf(__builtin_amdgcn_update_dpp(fbits(fill), fbits(x), 0x110 + K, 0xF, 0xF, false));
 }
 
-// Issue the KV loads of one chunk (BPW blocks per wave).  Slots past the chunk
-// end re-read its last block (a cache hit), so the loads are unconditional.
-template <class Cf>
-__device__ __forceinline__ void issue_chunk(BlockRegs<Cf> (&regs)[Cf::BPW], const Params& p, int kvh, int L,
-                                            int ob_lane, int pg_lane, int nt, int w, int lane) {
+// Issue the KV loads of this wave's NB blocks of one chunk (blocks
+// wv*NB .. wv*NB+NB-1).  Slots past the chunk end re-read its last block (a
+// cache hit), so the loads are unconditional.
+template <class Cf, int NB>
+__device__ __forceinline__ void issue_chunk_part(BlockRegs<Cf> (&regs)[NB], const Params& p, int kvh, int L,
+                                                 int ob_lane, int pg_lane, int nt, int wv, int lane) {
   const size_t tile = (size_t)Cf::B * Cf::R;
   const char* kbase = static_cast<const char*>(p.k_pages);
   const char* vbase = static_cast<const char*>(p.v_pages);
 #pragma unroll
-  for (int i = 0; i < Cf::BPW; ++i) {
-    const int b = min(w * Cf::BPW + i, nt - 1);
+  for (int i = 0; i < NB; ++i) {
+    const int b = min(wv * NB + i, nt - 1);
     const int nvalid = min(Cf::B, L - readlane(ob_lane, b) * Cf::B);
     const size_t off = ((size_t)readlane(pg_lane, b) * p.hkv + kvh) * tile;
     load_block<Cf>(regs[i], kbase + off, vbase + off, lane, nvalid);
   }
 }
 
-// Block phase: each wave turns its blocks of the chunk into partials
+// Block phase: each wave turns its NB blocks of the chunk into partials
 // (m_b, l_b, a_b) for every head of the group, into `part` (slot layout:
 // a[C][GM][D], then m[C][GM], then l[C][GM]).  Slots past the chunk end get
 // neutral partials (m = -inf, l = 0, a = 0).
-template <class Cf>
-__device__ __forceinline__ void block_phase(const BlockRegs<Cf> (&regs)[Cf::BPW], const uint4 (&qf)[Cf::QF],
+template <class Cf, int NB>
+__device__ __forceinline__ void block_phase(const BlockRegs<Cf> (&regs)[NB], const uint4 (&qf)[Cf::QF],
                                             int ob_lane, float ks_lane, float vs_lane, int nt, int L, float qk_log2,
-                                            int w, int lane, float* part, float* pbuf) {
+                                            int wv, int lane, float* part, float* pbuf) {
   const int c16 = lane & 15;
 #pragma unroll
-  for (int i = 0; i < Cf::BPW; ++i) {
-    const int b = w * Cf::BPW + i;
+  for (int i = 0; i < NB; ++i) {
+    const int b = wv * NB + i;
     float* pa = part + (size_t)b * Cf::GM * Cf::D;
     float* pm = part + Cf::SLOT_A + b * Cf::GM;
     float* pl = pm + Cf::C * Cf::GM;
@@ -888,11 +895,22 @@ struct Sched {
   float* ring;      // [streams][ring][slot_floats]
 };
 
+// Scanner of one stream.  Waves [0, NS) are scan waves (query heads
+// w, w + NS, ...); waves [NS, NWA) are block waves.  Step c: the scan waves
+// fold chunk c from LDS buffer c % 2 while the block waves turn chunk c+1
+// into partials in buffer (c+1) % 2 (computing it, or copying a helper's slot)
+// with chunk c+2's KV loads already in flight (register ring of two chunks).
+// One LDS barrier per step.  KV loads are issued unconditionally (clamped
+// to valid blocks when there is nothing to fetch), so the waits the compiler
+// places for a chunk's data never include younger loads.
 template <class Cf>
-__device__ void art_scanner(const Params& p, int stream, uint32_t E, float* part, float* pbuf, int* sh) {
-  constexpr int C = Cf::C, NWA = Cf::NWA, HPW = Cf::HPW, DPL = Cf::DPL;
+__device__ void art_scanner(const Params& p, int stream, uint32_t E, float* part2, float* pbuf, int* sh) {
+  constexpr int C = Cf::C, NS = Cf::NS, BPB = Cf::BPB, HPS = Cf::HPS, DPL = Cf::DPL;
+  constexpr int NT = 64 * Cf::NWA;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool scanw = w < NS;
+  const int bw = scanw ? 0 : w - NS;
   const int s = stream / p.hkv;
   const int kvh = stream - s * p.hkv;
   const int g = p.g;
@@ -904,225 +922,270 @@ __device__ void art_scanner(const Params& p, int stream, uint32_t E, float* part
   u64* donew = p.sched_done + stream;
   u64* readyw = p.sched_ready + (size_t)stream * p.ring;
   const float* ringb = p.sched_ring + (size_t)stream * p.ring * p.slot_floats;
+  const bool helped = p.helpers > 0;
+  const bool claimer = w == NS && lane == 0;  // block wave 0, lane 0: the stream's claims
+  int* dec = sh + 16;                         // dec[k % 4]: 1 if chunk k is computed here (sh[0..15]: wave votes)
 
   if (n <= 0) {
-    for (int i = threadIdx.x; i < g * Cf::D; i += 64 * NWA) p.out[head0 * Cf::D + i] = 0.f;
+    for (int i = threadIdx.x; i < g * Cf::D; i += NT) p.out[head0 * Cf::D + i] = 0.f;
     if (threadIdx.x < g) p.stop_block[head0 + threadIdx.x] = 0;
     if (threadIdx.x == 0) {
-      u64 cw = ld_dev(claimw);
-      for (int k = 0; k < 64; ++k) {
-        const u64 r = cas_dev(claimw, cw, tag_word(E, CLAIM_FIN | (tag_val(cw, E, 1) & ~CLAIM_FIN)));
-        if (r == cw) break;
-        cw = r;
+      if (helped) {
+        u64 cw = ld_dev(claimw);
+        for (int k = 0; k < 64; ++k) {
+          const u64 r = cas_dev(claimw, cw, tag_word(E, CLAIM_FIN | (tag_val(cw, E, 1) & ~CLAIM_FIN)));
+          if (r == cw) break;
+          cw = r;
+        }
       }
       if (p.blocks_fetched) p.blocks_fetched[stream] = 0;
     }
     return;
   }
 
-  uint4 qf[Cf::QF];
-  load_q<Cf>(p, s, kvh, lane, qf);
   const int32_t* trow = p.block_table + (size_t)s * p.max_blocks;
   const int32_t* orow = p.block_order + (size_t)s * p.max_blocks;
   const int slot = lane < C ? lane : C - 1;
 
-  // Order and page entries in two lane-held windows of 64 visit positions,
-  // [W, W+64) and [W+64, W+128); a chunk's entries (lane = slot) are picked
-  // out with a lane permute.  The next window is fetched 8 chunks before it
-  // is needed, so no KV load waits on the tables.
-  int W = 0;
-  int ob_w0 = orow[min(lane, n - 1)];
-  int ob_w1 = orow[min(64 + lane, n - 1)];
-  int pg_w0 = trow[ob_w0];
-  int pg_w1 = trow[ob_w1];
-  bool pg_w1_due = false;  // ob_w1 was refreshed; its pages are looked up one step later
-  auto entries = [&](int tc, int& ob, int& pg) {
-    const bool in1 = tc >= W + 64;
-    const int idx = tc - W - (in1 ? 64 : 0) + slot;
-    ob = __shfl(in1 ? ob_w1 : ob_w0, idx);
-    pg = __shfl(in1 ? pg_w1 : pg_w0, idx);
-  };
-  int ob_c, pg_c, ob_n, pg_n;
-  entries(0, ob_c, pg_c);
-  float ks_c = 1.f, vs_c = 1.f;
-  BlockRegs<Cf> regs[Cf::BPW];
-  issue_chunk<Cf>(regs, p, kvh, L, ob_c, pg_c, min(C, n), w, lane);
-  if constexpr (Cf::KV == KV_FP8) {
-    ks_c = p.k_scale[(size_t)pg_c * p.hkv + kvh];
-    vs_c = p.v_scale[(size_t)pg_c * p.hkv + kvh];
-  }
-
-  // claim state (thread 0 only): last seen claim word; the attempt for the
-  // chunk after next is issued one step before its result is needed
-  u64 cw = 0, exp_n = 0, ret_n = 0;
-  bool tried_n = false;
-  if (threadIdx.x == 0) {
-    cw = ld_dev(claimw);
-    if (nch > 1 && (tag_val(cw, E, 1) & ~CLAIM_FIN) == 1u) {
-      exp_n = cw;
-      ret_n = cas_dev(claimw, cw, tag_word(E, 2));
-      tried_n = true;
-    }
-  }
-
-  HeadCarry<Cf> hc[HPW];
-#pragma unroll
-  for (int k = 0; k < HPW; ++k) {
-    hc[k].M = NEG_INF; hc[k].L = 0.f; hc[k].Np = 0.f; hc[k].cnt = 0; hc[k].sink = false;
-    hc[k].alive = (w + NWA * k) < g;
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) { hc[k].A[j] = 0.f; hc[k].Op[j] = 0.f; }
-  }
-  ChunkIn<Cf> cur[HPW], nxt[HPW];
-  bool cur_loaded = false, nxt_loaded = false;
-  u64 flag_n = 0;           // ready word of chunk c+1, read one step ahead
-  bool local_c = true;      // chunk 0 is always the scanner's
-  int unloaded = -1;        // a chunk this scanner claimed and never loaded
-  bool err = false;
-  int c = 0;
-  for (;; ++c) {
-    const int t0 = c * C;
-    const int nt = min(C, n - t0);
-    const bool has_next = c + 1 < nch;
-
-    if (local_c) block_phase<Cf>(regs, qf, ob_c, ks_c, vs_c, nt, L, p.qk_log2, w, lane, part, pbuf);
-
-    // resolve the claim of chunk c+1, attempt the claim of chunk c+2
-    if (threadIdx.x == 0) {
-      bool loc = false;
-      if (has_next && tried_n) {
-        loc = ret_n == exp_n;
-        cw = loc ? tag_word(E, c + 2) : ret_n;
-      }
-      sh[0] = loc ? 1 : 0;
-      tried_n = false;
-      if (c + 2 < nch && (tag_val(cw, E, 1) & ~CLAIM_FIN) == (uint32_t)(c + 2)) {
-        exp_n = cw;
-        ret_n = cas_dev(claimw, cw, tag_word(E, c + 3));
-        tried_n = true;
-      }
-    }
-    lds_barrier();
-    const bool local_n = has_next && sh[0] != 0;
-
-    // next chunk's KV loads fly during the scan
-    float ks_n = 1.f, vs_n = 1.f;
-    if (has_next) entries(t0 + C, ob_n, pg_n);
-    if (local_n) {
-      issue_chunk<Cf>(regs, p, kvh, L, ob_n, pg_n, min(C, n - t0 - C), w, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (Cf::KV == KV_FP8) {
-        ks_n = p.k_scale[(size_t)pg_n * p.hkv + kvh];
-        vs_n = p.v_scale[(size_t)pg_n * p.hkv + kvh];
-      }
-    }
-
-    // ---- scan waves: this chunk's inputs, next chunk's prefetch, the scan
-    const unsigned long long sinkbits = __ballot(lane < nt && ob_c == 0);
-    bool scanning = false;
-#pragma unroll
-    for (int k = 0; k < HPW; ++k) scanning |= (w + NWA * k) < g && hc[k].alive;
-    if (scanning && !err) {
-      if (local_c) {
-#pragma unroll
-        for (int k = 0; k < HPW; ++k)
-          if (w + NWA * k < g) gather_lds<Cf>(cur[k], part, w + NWA * k, lane);
-      } else if (!cur_loaded) {
-        const u64* fw = readyw + c % p.ring;
-        int spins = 0;
-        while (tag_val(ld_dev(fw), E, 0) != (uint32_t)(c + 1)) {
-          if (++spins > p.spin_limit) { err = true; break; }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        const float* sl = ringb + (size_t)(c % p.ring) * p.slot_floats;
-#pragma unroll
-        for (int k = 0; k < HPW; ++k)
-          if (w + NWA * k < g) gather_ring<Cf>(cur[k], sl, w + NWA * k, lane);
-      }
-      // helper chunk c+1: if its ready flag (read a step ago) is set, load it now
-      nxt_loaded = false;
-      if (has_next && !local_n && tag_val(flag_n, E, 0) == (uint32_t)(c + 2)) {
-        const float* sl = ringb + (size_t)((c + 1) % p.ring) * p.slot_floats;
-#pragma unroll
-        for (int k = 0; k < HPW; ++k)
-          if (w + NWA * k < g) gather_ring<Cf>(nxt[k], sl, w + NWA * k, lane);
-        nxt_loaded = true;
-      }
-      flag_n = (c + 2 < nch) ? ld_dev(readyw + (c + 2) % p.ring) : 0ull;
-
-#pragma unroll
-      for (int k = 0; k < HPW; ++k) {
-        const int h = w + NWA * k;
-        if (h < g && hc[k].alive && !err)
-          scan_head<Cf>(hc[k], cur[k], t0, nt, sinkbits, p, lane, p.out + (head0 + h) * Cf::D,
-                        p.stop_block + head0 + h);
-      }
-    }
-    if (lane == 0) {
-      int a = 0;
-#pragma unroll
-      for (int k = 0; k < HPW; ++k)
-        if (w + NWA * k < g && hc[k].alive) a = 1;
-      sh[4 + w] = a | (err ? 2 : 0);
-    }
-    lds_barrier();
-    int any = 0;
-#pragma unroll
-    for (int ww = 0; ww < NWA; ++ww) any |= sh[4 + ww];
-    if (any & 2) { err = true; break; }
-    if (threadIdx.x == 0) st_dev(donew, tag_word(E, c + 1));
-    if (!(any & 1) || !has_next) break;
-    // rotate: chunk c+1 becomes current
-#pragma unroll
-    for (int k = 0; k < HPW; ++k) cur[k] = nxt[k];
-    cur_loaded = nxt_loaded;
-    local_c = local_n;
-    ob_c = ob_n;
-    pg_c = pg_n;
-    ks_c = ks_n;
-    vs_c = vs_n;
-    if (pg_w1_due) {
-      pg_w1 = trow[ob_w1];
-      pg_w1_due = false;
-    }
-    if (t0 + 2 * C == W + 64) {  // the next chunk opens window 1: slide
+  // Order and page entries: scan wave 0 keeps two lane-held windows of 64
+  // visit positions, [W, W+64) and [W+64, W+128), and at step c writes chunk
+  // c+3's entries (lane = slot) into the LDS ring ent[(c+3) % 4]; the other
+  // waves read a chunk's entries from there.  Window 1 is re-read when the
+  // windows slide (its pages one step after its order entries).
+  int* ent = sh + 32;  // [4][2][8]: order entry, page
+  int W = 0, ob_w0 = 0, ob_w1 = 0, pg_w0 = 0, pg_w1 = 0;
+  bool pg_w1_due = false;
+  auto publish_entries = [&](int k) {  // scan wave 0: chunk k (clamped) into ent[k % 4]
+    const int tc = min(k, nch - 1) * C;
+    if (tc >= W + 64) {
       W += 64;
       ob_w0 = ob_w1;
       pg_w0 = pg_w1;
       ob_w1 = orow[min(W + 64 + lane, n - 1)];
       pg_w1_due = true;
     }
+    const int idx = tc - W + slot;
+    const int ob = __shfl(ob_w0, idx);
+    const int pg = __shfl(pg_w0, idx);
+    if (lane < C) { ent[(k & 3) * 16 + lane] = ob; ent[(k & 3) * 16 + 8 + lane] = pg; }
+  };
+  auto entries = [&](int k, int& ob, int& pg) {  // lane-held entries of chunk k
+    ob = ent[(k & 3) * 16 + slot];
+    pg = ent[(k & 3) * 16 + 8 + slot];
+  };
+  if (w == 0) {
+    ob_w0 = orow[min(lane, n - 1)];
+    ob_w1 = orow[min(64 + lane, n - 1)];
+    pg_w0 = trow[ob_w0];
+    pg_w1 = trow[ob_w1];
+    publish_entries(0);
+    publish_entries(1);
+    publish_entries(2);
   }
 
-  // heads that never stopped: the output after all n blocks
-#pragma unroll
-  for (int k = 0; k < HPW; ++k) {
-    const int h = w + NWA * k;
-    if (h < g && hc[k].alive) {
-      float* o = p.out + (head0 + h) * Cf::D;
-#pragma unroll
-      for (int j = 0; j < DPL; ++j) o[DPL * lane + j] = err ? __builtin_nanf("") : hc[k].Op[j];
-      if (lane == 0) p.stop_block[head0 + h] = err ? -1 : n;
+  // claims (helpers only): chunk 0 is the scanner's; chunks 1 and 2 are
+  // claimed before the first step, chunk k >= 3 at step k-3 (attempted one
+  // step earlier); dec[k % 4] = 1 when chunk k is computed here
+  u64 cw = 0, exp3 = 0, ret3 = 0;
+  bool tried3 = false;
+  if (threadIdx.x == 0) {
+    dec[0] = 1; dec[1] = 1; dec[2] = 1; dec[3] = 1;
+  }
+  if (claimer && helped) {
+    cw = ld_dev(claimw);
+    for (int k = 1; k <= 2 && k < nch; ++k) {
+      bool loc = false;
+      if ((tag_val(cw, E, 1) & ~CLAIM_FIN) == (uint32_t)k) {
+        const u64 r = cas_dev(claimw, cw, tag_word(E, k + 1));
+        loc = r == cw;
+        cw = loc ? tag_word(E, k + 1) : r;
+      }
+      dec[k] = loc ? 1 : 0;
+    }
+    if (3 < nch && (tag_val(cw, E, 1) & ~CLAIM_FIN) == 3u) {
+      exp3 = cw;
+      ret3 = cas_dev(claimw, cw, tag_word(E, 4));
+      tried3 = true;
     }
   }
-  // close the stream: no more claims; KV tiles fetched = every claimed chunk
-  // except one the scanner claimed and then did not need
-  if (threadIdx.x == 0) {
-    if (tried_n) {
-      if (ret_n == exp_n) { cw = tag_word(E, c + 3); unloaded = c + 2; } else { cw = ret_n; }
+  lds_barrier();
+
+  bool err = false;
+  int c = 0;
+  // end of a step: vote, barrier, common decision (every wave runs the same
+  // number of barriers)
+  auto end_step = [&](int alive_vote) {
+    if (lane == 0) sh[w] = alive_vote | (err ? 2 : 0);
+    lds_barrier();
+    int any = 0;
+#pragma unroll
+    for (int ww = 0; ww < Cf::NWA; ++ww) any |= sh[ww];
+    if (any & 2) err = true;
+    if (threadIdx.x == 0 && helped) st_dev(donew, tag_word(E, c + 1));
+    return (any & 1) && !(any & 2) && c + 1 < nch;
+  };
+
+  if (scanw) {
+    // ================= scan waves: fold chunk c from buffer c % 2 =================
+    lds_barrier();  // the block waves' prologue
+    HeadCarry<Cf> hc[HPS];
+#pragma unroll
+    for (int k = 0; k < HPS; ++k) {
+      hc[k].M = NEG_INF; hc[k].L = 0.f; hc[k].Np = 0.f; hc[k].cnt = 0; hc[k].sink = false;
+      hc[k].alive = (w + NS * k) < g;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) { hc[k].A[j] = 0.f; hc[k].Op[j] = 0.f; }
     }
-    uint32_t cnt = 0;
-    for (int k = 0; k < (1 << 20); ++k) {
-      cnt = tag_val(cw, E, 1) & ~CLAIM_FIN;
-      const u64 r = cas_dev(claimw, cw, tag_word(E, CLAIM_FIN | cnt));
-      if (r == cw) break;
-      cw = r;
+    for (;; ++c) {
+      const int t0 = c * C;
+      const int nt = min(C, n - t0);
+      const float* cur = part2 + (c & 1) * Cf::SLOT;
+      int ob_c, pg_c;
+      entries(c, ob_c, pg_c);
+      const unsigned long long sinkbits = __ballot(lane < nt && ob_c == 0);
+      if (w == 0) {
+        if (pg_w1_due) { pg_w1 = trow[ob_w1]; pg_w1_due = false; }
+        publish_entries(c + 3);
+      }
+      int a = 0;
+#pragma unroll
+      for (int k = 0; k < HPS; ++k) {
+        const int h = w + NS * k;
+        if (h < g && hc[k].alive) {
+          ChunkIn<Cf> in;
+          gather_lds<Cf>(in, cur, h, lane);
+          scan_head<Cf>(hc[k], in, t0, nt, sinkbits, p, lane, p.out + (head0 + h) * Cf::D, p.stop_block + head0 + h);
+        }
+        if (hc[k].alive) a = 1;
+      }
+      if (!end_step(a)) break;
     }
-    if (err) st_dev32(p.sched_ctrl + 2, 1u);
-    if (p.blocks_fetched) {
-      int f = min(n, (int)cnt * C);
-      if (unloaded >= 0) f -= min(C, n - unloaded * C);
-      p.blocks_fetched[stream] = f;
+    // heads that never stopped: the output after all n blocks
+#pragma unroll
+    for (int k = 0; k < HPS; ++k) {
+      const int h = w + NS * k;
+      if (h < g && hc[k].alive) {
+        float* o = p.out + (head0 + h) * Cf::D;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) o[DPL * lane + j] = err ? __builtin_nanf("") : hc[k].Op[j];
+        if (lane == 0) p.stop_block[head0 + h] = err ? -1 : n;
+      }
+    }
+  } else {
+    // ================= block waves: chunk c+1 into buffer (c+1) % 2 =================
+    uint4 qf[Cf::QF];
+    load_q<Cf>(p, s, kvh, lane, qf);
+    BlockRegs<Cf> ra[BPB], rb[BPB];  // ring: chunk k in (k % 2 ? rb : ra); only ra when PFD == 1
+    float ks_a = 1.f, vs_a = 1.f, ks_b = 1.f, vs_b = 1.f;
+    // issue chunk k's loads for this block wave (k past the end re-reads the last chunk)
+    auto issue = [&](int k, BlockRegs<Cf> (&rr)[BPB], float& ks, float& vs) {
+      int ob, pg;
+      entries(k, ob, pg);
+      const int kc = min(k, nch - 1);
+      issue_chunk_part<Cf, BPB>(rr, p, kvh, L, ob, pg, min(C, n - kc * C), bw, lane);
+      if constexpr (Cf::KV == KV_FP8) {
+        ks = p.k_scale[(size_t)pg * p.hkv + kvh];
+        vs = p.v_scale[(size_t)pg * p.hkv + kvh];
+      }
+    };
+    // prologue: chunk 0 into buffer 0, chunk 1 in flight
+    issue(0, ra, ks_a, vs_a);
+    if constexpr (Cf::PFD == 2) {
+      issue(dec[1] ? 1 : 0, rb, ks_b, vs_b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    {
+      int ob0, pg0;
+      entries(0, ob0, pg0);
+      block_phase<Cf, BPB>(ra, qf, ob0, ks_a, vs_a, min(C, n), L, p.qk_log2, bw, lane, part2, pbuf);
+    }
+    if constexpr (Cf::PFD == 1) issue(dec[1] ? 1 : 0, ra, ks_a, vs_a);
+    lds_barrier();
+
+    // one step: rc holds chunk c+1's tiles, rn receives chunk c+2's
+    auto bstep = [&](BlockRegs<Cf> (&rc)[BPB], float& ksc, float& vsc, BlockRegs<Cf> (&rn)[BPB], float& ksn,
+                     float& vsn) {
+      const int t0 = c * C;
+      float* nxt = part2 + ((c + 1) & 1) * Cf::SLOT;
+      const bool loc2 = dec[(c + 2) & 3] != 0;
+      const int k2 = (c + 2 < nch && loc2) ? c + 2 : c + 1;
+      if constexpr (Cf::PFD == 2) {
+        issue(k2, rn, ksn, vsn);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (c + 1 < nch) {
+        if (dec[(c + 1) & 3]) {
+          int ob1, pg1;
+          entries(c + 1, ob1, pg1);
+          block_phase<Cf, BPB>(rc, qf, ob1, ksc, vsc, min(C, n - t0 - C), L, p.qk_log2, bw, lane, nxt, pbuf);
+        } else {
+          // a helper's chunk: wait for its slot, copy it into the buffer
+          const u64* fw = readyw + (c + 1) % p.ring;
+          int spins = 0;
+          while (tag_val(ld_dev(fw), E, 0) != (uint32_t)(c + 2)) {
+            if (++spins > p.spin_limit) { err = true; break; }
+            __builtin_amdgcn_s_sleep(1);
+          }
+          const u64* src = reinterpret_cast<const u64*>(ringb + (size_t)((c + 1) % p.ring) * p.slot_floats);
+          u64* dst = reinterpret_cast<u64*>(nxt);
+          for (int i = threadIdx.x - 64 * NS; i < Cf::SLOT / 2; i += 64 * Cf::NBW) dst[i] = ld_dev(src + i);
+        }
+      }
+      if constexpr (Cf::PFD == 1) issue(k2, rn, ksn, vsn);  // rn is rc here: refilled once consumed
+      // claims: resolve chunk c+3's attempt, attempt chunk c+4
+      if (claimer && helped) {
+        bool loc = false;
+        if (tried3) {
+          loc = ret3 == exp3;
+          cw = loc ? tag_word(E, c + 4) : ret3;
+        }
+        if (c + 3 < nch) dec[(c + 3) & 3] = loc ? 1 : 0;
+        tried3 = false;
+        if (c + 4 < nch && (tag_val(cw, E, 1) & ~CLAIM_FIN) == (uint32_t)(c + 4)) {
+          exp3 = cw;
+          ret3 = cas_dev(claimw, cw, tag_word(E, c + 5));
+          tried3 = true;
+        }
+      }
+      const bool more = end_step(0);
+      if (more) ++c;
+      return more;
+    };
+    for (;;) {
+      if constexpr (Cf::PFD == 2) {
+        if (!bstep(rb, ks_b, vs_b, ra, ks_a, vs_a)) break;
+        if (!bstep(ra, ks_a, vs_a, rb, ks_b, vs_b)) break;
+      } else {
+        if (!bstep(ra, ks_a, vs_a, ra, ks_a, vs_a)) break;
+      }
+    }
+
+    // KV tiles fetched: chunks [0, min(nch, c+3)) were loaded here or by a
+    // helper; with helpers, chunks claimed later by helpers were loaded by
+    // them, and chunks c+3, c+4 claimed here were never loaded.  Then close
+    // the stream for helpers.
+    if (claimer) {
+      int fetched = min(n, (c + 3) * C);
+      if (helped) {
+        bool own4 = false;
+        if (tried3) {
+          own4 = ret3 == exp3;
+          cw = own4 ? tag_word(E, c + 5) : ret3;
+        }
+        uint32_t cnt = 0;
+        for (int k = 0; k < (1 << 20); ++k) {
+          cnt = tag_val(cw, E, 1) & ~CLAIM_FIN;
+          const u64 r = cas_dev(claimw, cw, tag_word(E, CLAIM_FIN | cnt));
+          if (r == cw) break;
+          cw = r;
+        }
+        fetched = min(n, (int)cnt * C);
+        auto blocks = [&](int k) { return k < nch ? min(C, n - k * C) : 0; };
+        if (c + 3 < nch && (int)cnt > c + 3 && dec[(c + 3) & 3]) fetched -= blocks(c + 3);
+        if (own4) fetched -= blocks(c + 4);
+        if (err) st_dev32(p.sched_ctrl + 2, 1u);
+      }
+      if (p.blocks_fetched) p.blocks_fetched[stream] = fetched;
     }
   }
 }
@@ -1135,7 +1198,7 @@ __device__ void art_helper(const Params& p, int hid, uint32_t E, float* part, fl
   const int streams = p.batch * p.hkv;
   const int slot = lane < C ? lane : C - 1;
   int pref = hid % streams;
-  BlockRegs<Cf> regs[Cf::BPW];
+  BlockRegs<Cf> regs[1];
   for (int iter = 0;; ++iter) {
     // ---- wave 0 looks for a claimable chunk: 64 streams per round
     if (w == 0) {
@@ -1198,14 +1261,16 @@ __device__ void art_helper(const Params& p, int hid, uint32_t E, float* part, fl
     const int ob = orow[min(t0 + slot, n - 1)];
     const int pg = trow[ob];
     float ks = 1.f, vs = 1.f;
-    issue_chunk<Cf>(regs, p, kvh, L, ob, pg, nt, w, lane);
-    if constexpr (Cf::KV == KV_FP8) {
-      ks = p.k_scale[(size_t)pg * p.hkv + kvh];
-      vs = p.v_scale[(size_t)pg * p.hkv + kvh];
+    if (w < Cf::HWV) {
+      issue_chunk_part<Cf, 1>(regs, p, kvh, L, ob, pg, nt, w, lane);
+      if constexpr (Cf::KV == KV_FP8) {
+        ks = p.k_scale[(size_t)pg * p.hkv + kvh];
+        vs = p.v_scale[(size_t)pg * p.hkv + kvh];
+      }
+      uint4 qf[Cf::QF];
+      load_q<Cf>(p, s, kvh, lane, qf);
+      block_phase<Cf, 1>(regs, qf, ob, ks, vs, nt, L, p.qk_log2, w, lane, part, pbuf);
     }
-    uint4 qf[Cf::QF];
-    load_q<Cf>(p, s, kvh, lane, qf);
-    block_phase<Cf>(regs, qf, ob, ks, vs, nt, L, p.qk_log2, w, lane, part, pbuf);
     lds_barrier();
     u64* dst = reinterpret_cast<u64*>(p.sched_ring + ((size_t)st * p.ring + cc % p.ring) * p.slot_floats);
     const u64* src = reinterpret_cast<const u64*>(part);
@@ -1219,9 +1284,9 @@ __device__ void art_helper(const Params& p, int hid, uint32_t E, float* part, fl
 template <int KV, int D, int B, int GM>
 __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_sched_kernel(Params p) {
   using Cf = Cfg<KV, D, B, GM>;
-  __shared__ __attribute__((aligned(16))) float part[Cf::SLOT];
+  __shared__ __attribute__((aligned(16))) float part[2 * Cf::SLOT];
   __shared__ __attribute__((aligned(16))) float pbuf_all[Cf::NWA][Cf::PV4 ? GM * B : 4];
-  __shared__ int sh[4 + Cf::NWA];
+  __shared__ int sh[96];
   __shared__ uint32_t epoch_sh;
   if (threadIdx.x == 0) epoch_sh = epoch_of(ld_dev32(p.sched_ctrl));
   lds_barrier();
