@@ -1287,24 +1287,27 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_sched_kerne
   __shared__ __attribute__((aligned(16))) float part[2 * Cf::SLOT];
   __shared__ __attribute__((aligned(16))) float pbuf_all[Cf::NWA][Cf::PV4 ? GM * B : 4];
   __shared__ int sh[96];
-  __shared__ uint32_t epoch_sh;
-  if (threadIdx.x == 0) epoch_sh = epoch_of(ld_dev32(p.sched_ctrl));
-  lds_barrier();
-  const uint32_t E = epoch_sh;
   const int streams = p.batch * p.hkv;
+  // The epoch tags the scheduler words, which only calls with helpers use;
+  // it is constant during the launch (advanced by the last workgroup), so
+  // each role reads it where it needs it.
+  const bool helped = p.helpers > 0;
+  const uint32_t E = helped ? epoch_of(ld_dev32(p.sched_ctrl)) : 0u;
   if ((int)blockIdx.x < streams)
     art_scanner<Cf>(p, blockIdx.x, E, part, pbuf_all[threadIdx.x >> 6], sh);
   else
     art_helper<Cf>(p, blockIdx.x - streams, E, part, pbuf_all[threadIdx.x >> 6], sh);
-  // speculative loads may still be in flight; then count this workgroup out
-  // (the last one advances the epoch for the next call)
+  // speculative loads may still be in flight
   wait_all_memory();
-  lds_barrier();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(p.sched_ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev == gridDim.x - 1) {
-      st_dev32(p.sched_ctrl + 1, 0u);
-      st_dev32(p.sched_ctrl, E);
+  if (helped) {
+    // count this workgroup out; the last one advances the epoch
+    lds_barrier();
+    if (threadIdx.x == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(p.sched_ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == gridDim.x - 1) {
+        st_dev32(p.sched_ctrl + 1, 0u);
+        st_dev32(p.sched_ctrl, E);
+      }
     }
   }
 }

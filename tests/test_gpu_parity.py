@@ -271,22 +271,32 @@ def test_scheduler_variants_bit_identical(w, kw):
 
 
 def test_scheduler_epoch_advances_and_no_error():
+    """With helpers, every call advances the stored epoch by one and leaves the finished-workgroup counter at
+    0 and the error flag clear; without helpers the scheduler words are not touched."""
     import torch
 
     from kv_cache_run_amd import art
 
     case = synth.make_case(W.RAGGED, batch=2)
     dev = art.case_to_device(case)
-    dec = art.Decoder(dev["q"], dev["k_pages"], dev["block_table"])
-    outs = []
-    for i in range(4):
-        out, stop = dec(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"], dev["block_order"],
-                        dev["seq_lens"], case["eps_mag"], case["eps_dir"], case["patience"])
-        torch.cuda.synchronize()
-        ctrl = dec.workspace[:12].view(torch.int32).cpu().numpy()
-        assert ctrl[0] == i + 1, ctrl      # stored epoch
-        assert ctrl[1] == 0, ctrl          # finished-workgroup counter back to 0
-        assert ctrl[2] == 0, ctrl          # no bounded wait ran out
-        outs.append((out.cpu(), stop.cpu()))
-    for o, s in outs[1:]:
-        assert torch.equal(o, outs[0][0]) and torch.equal(s, outs[0][1])
+
+    def run(env, expect_epoch):
+        dec = _with_env(env, lambda: art.Decoder(dev["q"], dev["k_pages"], dev["block_table"]))
+        outs = []
+        for i in range(4):
+            out, stop = _with_env(env, lambda: dec(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"],
+                                                   dev["block_order"], dev["seq_lens"], case["eps_mag"],
+                                                   case["eps_dir"], case["patience"]))
+            torch.cuda.synchronize()
+            ctrl = dec.workspace[:12].view(torch.int32).cpu().numpy()
+            assert ctrl[0] == expect_epoch(i), ctrl   # stored epoch
+            assert ctrl[1] == 0, ctrl                 # finished-workgroup counter back to 0
+            assert ctrl[2] == 0, ctrl                 # no bounded wait ran out
+            outs.append((out.cpu(), stop.cpu()))
+        for o, s_ in outs[1:]:
+            assert torch.equal(o, outs[0][0]) and torch.equal(s_, outs[0][1])
+        return outs[0]
+
+    a = run(dict(ART_HELPERS="64"), lambda i: i + 1)
+    b = run(dict(ART_HELPERS="0"), lambda i: 0)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
