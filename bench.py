@@ -150,6 +150,8 @@ def main(argv=None) -> int:
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration under rocprofv3)")
     ap.add_argument("--modes", default="art,full")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the threshold sweep and the detector-overhead run")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -176,21 +178,21 @@ def main(argv=None) -> int:
     kv_tile = 2 * B * case["head_dim"] * {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}[case["kv_dtype"]]
     pool_bytes = case["k_pages"].nbytes + case["v_pages"].nbytes
 
-    # one reference call per mode to learn the work (stops, blocks read)
-    def one_call(mode, table, out, stop, fetched, dec, kp, vp, ks, vs):
-        em, ed = (case["eps_mag"], case["eps_dir"]) if mode == "art" else (0.0, 0.0)
-        dec(dev["q"], kp, vp, table, dev["block_order"], dev["seq_lens"], em, ed, case["patience"],
-            k_scale=ks, v_scale=vs, out=out, stop_block=stop, blocks_fetched=fetched)
-
-    results = {}
-    for mode in [m for m in args.modes.split(",") if m]:
+    # A "setting" is (thresholds, patience, flags).  One reference call learns
+    # the work (stops, tiles read); then K calls are captured into one HIP
+    # graph over rotating page-pool copies and replayed between two events.
+    def time_setting(em, ed, patience, flags, steps, warmup):
         out = torch.empty((case["batch"], case["num_q_heads"], case["head_dim"]), dtype=torch.float32,
                           device="cuda")
         stop = torch.empty((case["batch"], case["num_q_heads"]), dtype=torch.int32, device="cuda")
         fetched = torch.empty((case["batch"], case["num_kv_heads"]), dtype=torch.int32, device="cuda")
+
+        def one_call(table, dec, kp, vp, ks, vs):
+            dec(dev["q"], kp, vp, table, dev["block_order"], dev["seq_lens"], em, ed, patience, k_scale=ks,
+                v_scale=vs, out=out, stop_block=stop, blocks_fetched=fetched, flags=flags)
+
         dec = art.Decoder(dev["q"], dev["k_pages"], dev["block_table"])
-        one_call(mode, dev["block_table"], out, stop, fetched, dec, dev["k_pages"], dev["v_pages"],
-                 dev["k_scale"], dev["v_scale"])
+        one_call(dev["block_table"], dec, dev["k_pages"], dev["v_pages"], dev["k_scale"], dev["v_scale"])
         torch.cuda.synchronize()
         stop_h = stop.cpu().numpy()
         fetched_h = fetched.cpu().numpy()
@@ -198,6 +200,7 @@ def main(argv=None) -> int:
         # page-pool copies so that consecutive calls read cold memory
         R = int(min(64, max(2, math.ceil(512e6 / max(read_bytes, 1)) + 1),
                     max(2, (48 << 30) // max(pool_bytes, 1))))
+
         def rep(t):
             if t.dtype == torch.float8_e4m3fn:
                 return t.view(torch.uint8).repeat(R, 1, 1, 1).view(torch.float8_e4m3fn)
@@ -210,15 +213,13 @@ def main(argv=None) -> int:
         npages = case["num_pages"]
         tables = [dev["block_table"] + r * npages for r in range(R)]
         dec = art.Decoder(dev["q"], kp, dev["block_table"])
-        for i in range(args.warmup):
-            one_call(mode, tables[i % R], out, stop, fetched, dec, kp, vp, ks, vs)
+        for i in range(warmup):
+            one_call(tables[i % R], dec, kp, vp, ks, vs)
         torch.cuda.synchronize()
-        # The K timed calls are captured into one HIP graph so that host launch
-        # overhead does not gap the (few-µs) kernels; replays launch back to back.
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for i in range(args.steps):
-                one_call(mode, tables[(args.warmup + i) % R], out, stop, fetched, dec, kp, vp, ks, vs)
+            for i in range(steps):
+                one_call(tables[(warmup + i) % R], dec, kp, vp, ks, vs)
         graph.replay()  # first replay uploads the graph; untimed
         torch.cuda.synchronize()
         out_first = out.clone()
@@ -230,13 +231,14 @@ def main(argv=None) -> int:
         ev1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        ms = ev0.elapsed_time(ev1) / args.steps
+        ms = ev0.elapsed_time(ev1) / steps
         assert np.array_equal(stop.cpu().numpy(), stop_h), "stops changed across page copies / replays"
         assert torch.equal(out, out_first), "graph replays disagree"
-        del graph
+        del graph, kp, vp, ks, vs, tables, dec
+        torch.cuda.empty_cache()
         alg = algorithmic_bytes(case, stop_h)
         us = ms * 1e3
-        results[mode] = {
+        return {
             "us_per_step": us,
             "wall_s": wall,
             "page_copies": R,
@@ -247,8 +249,43 @@ def main(argv=None) -> int:
             "kv_fraction_read": float(fetched_h.sum()) / total_blocks,
             "kv_fraction_needed": alg["blocks"] / total_blocks,
         }
-        del kp, vp, ks, vs, tables, dec
-        torch.cuda.empty_cache()
+
+    em0, ed0, p0 = case["eps_mag"], case["eps_dir"], case["patience"]
+    results = {}
+    for mode in [m for m in args.modes.split(",") if m]:
+        if mode == "art":
+            results[mode] = time_setting(em0, ed0, p0, 0, args.steps, args.warmup)
+        elif mode == "full":
+            results[mode] = time_setting(0.0, 0.0, p0, art.ART_FLAG_FULL, args.steps, args.warmup)
+        else:
+            raise SystemExit(f"unknown mode {mode}")
+
+    extras = {}
+    if not args.no_extras and "art" in results and "full" in results:
+        # detector overhead: the terminating kernel with thresholds that can never pass (it folds every
+        # block and runs every test) against the full-attention kernel on the same work
+        keep = time_setting(0.0, 0.0, p0, art.ART_FLAG_KEEP_DETECTOR, max(5, args.steps // 2), 2)
+        extras["detector_overhead"] = {
+            "art_kernel_all_blocks_us": round(keep["us_per_step"], 3),
+            "full_kernel_us": round(results["full"]["us_per_step"], 3),
+            "ratio": round(keep["us_per_step"] / results["full"]["us_per_step"], 4),
+            "note": "ART path (detector + sequential scan) forced to fold all blocks vs the split full-attention "
+                    "path; the ratio includes the different parallel decomposition, not only the detector",
+        }
+        # step time against the KV fraction read: thresholds scaled by 1/4 .. 4 at fixed patience
+        pts = []
+        for f in (0.25, 0.5, 1.0, 2.0, 4.0):
+            r = results["art"] if f == 1.0 else time_setting(em0 * f, ed0 * f, p0, 0, max(5, args.steps // 2), 2)
+            pts.append({"eps_scale": f, "kv_fraction_read": round(r["kv_fraction_read"], 5),
+                        "kv_fraction_needed": round(r["kv_fraction_needed"], 5), "us_per_step": round(r["us_per_step"], 3)})
+        x = np.array([q["kv_fraction_read"] for q in pts])
+        y = np.array([q["us_per_step"] for q in pts])
+        slope, icpt = np.polyfit(x, y, 1) if np.ptp(x) > 0 else (0.0, float(y.mean()))
+        pred = slope * x + icpt
+        ss = float(((y - y.mean()) ** 2).sum())
+        r2 = 1.0 - float(((y - pred) ** 2).sum()) / ss if ss > 0 else 1.0
+        extras["scaling"] = {"points": pts, "slope_us_per_unit_fraction": round(float(slope), 3),
+                             "intercept_us": round(float(icpt), 3), "r2": round(r2, 4)}
 
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
@@ -263,7 +300,7 @@ def main(argv=None) -> int:
 
     head = results.get("art") or next(iter(results.values()))
     head_mode = "art" if "art" in results else next(iter(results))
-    kname = "art_chunk_kernel" if head_mode == "art" else "full_split_kernel"
+    kname = "art_sched_kernel" if head_mode == "art" else "full_split_kernel"
     traffic = read_traffic(kname, w.name)
     roofline = {
         "bound": "hbm",
@@ -303,6 +340,7 @@ def main(argv=None) -> int:
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),
     }
+    line.update(extras)
     print(json.dumps(line))
     return 0
 
