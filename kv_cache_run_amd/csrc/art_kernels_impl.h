@@ -95,9 +95,16 @@ struct Cfg {
   static constexpr int BPB = 1;                       // blocks per block wave per chunk
   static constexpr int HPS = (GM + NS - 1) / NS;      // scanner: query heads per scan wave
   static constexpr int HWV = C;                       // helper: waves computing blocks (one each)
-  // register ring depth of a block wave: two chunks in flight when a block's
-  // K+V tiles take at most 32 VGPRs per lane, else one
-  static constexpr int PFD = 2 * B * R / 64 <= 128 ? 2 : 1;
+  // register ring depth of a block wave (chunks held): two while the ring
+  // fits its VGPR budget (96 per lane, less for 8-head groups, fp8
+  // conversion and 32-token blocks, whose math needs more registers), else
+  // one.  (A third chunk in flight was measured: no faster on one CU, whose
+  // steps are bound by the VALU/MFMA work, and a longer start.)
+  static constexpr int TILE_VGPRS = 2 * B * R / 256;
+  static constexpr int RING_BUDGET = 96 - (GM > 4 ? 32 : 0) - (KV == KV_FP8 ? 32 : 0) - (B == 32 ? 32 : 0);
+  static constexpr int PFD = cmax(1, cmin(2, RING_BUDGET / TILE_VGPRS));
+  // the farthest chunk a block wave issues at step c is c + IA
+  static constexpr int IA = PFD == 3 ? 3 : 2;
   static constexpr int DPL = D / 64;                  // d per lane in the scan
   static constexpr int SH = 6 - ilog2(2 * C);         // stat reduction: lane >> SH = value index
   static constexpr int SLOT_A = C * GM * D;           // partials of one chunk: a[C][GM][D], m[C][GM], l[C][GM]
@@ -252,9 +259,12 @@ __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
-// Load one block: K in the QK A-operand layout, V in the PV A-operand layout.
-// V rows at or past nvalid are read from the last valid row instead, so that
-// every V value fed to the PV product is finite (their P is exactly 0).
+// Load one block: K in the QK A-operand layout, V in the PV operand layout.
+// Every row of the tile is read (a tile always holds B rows), so the loads
+// are a base address plus immediate offsets; when the block is the partial
+// last block of a sequence, the V values of rows at or past nvalid are then
+// zeroed, so that every V value fed to the PV product is finite (their P is
+// exactly 0; K of those rows only feeds masked scores).
 template <class Cf>
 __device__ __forceinline__ void load_block(BlockRegs<Cf>& r, const char* kt, const char* vt, int lane, int nvalid) {
   const int c = lane & 15;
@@ -268,39 +278,53 @@ __device__ __forceinline__ void load_block(BlockRegs<Cf>& r, const char* kt, con
     // load u covers token rows u*RPL .. u*RPL+RPL-1; lane: row u*RPL + lane/LPR,
     // bytes (lane % LPR) * BPL .. +BPL of it
     const int rg = lane / Cf::LPR;
-    const int cb = (lane % Cf::LPR) * Cf::BPL;
+    const char* src = vt + (size_t)rg * Cf::R + (lane % Cf::LPR) * Cf::BPL;
 #pragma unroll
     for (int u = 0; u < Cf::NLD; ++u) {
-      const int row = u * Cf::RPL + rg;
-      const char* src = vt + (size_t)min(row, nvalid - 1) * Cf::R + cb;
       if constexpr (Cf::VW == 1) {
-        r.v[u] = *reinterpret_cast<const uint32_t*>(src);
+        r.v[u] = *reinterpret_cast<const uint32_t*>(src + u * Cf::RPL * Cf::R);
       } else {
-        const uint2 x = *reinterpret_cast<const uint2*>(src);
+        const uint2 x = *reinterpret_cast<const uint2*>(src + u * Cf::RPL * Cf::R);
         r.v[2 * u] = x.x; r.v[2 * u + 1] = x.y;
       }
     }
+    if (nvalid < Cf::B) {
+#pragma unroll
+      for (int u = 0; u < Cf::NLD; ++u)
+#pragma unroll
+        for (int j = 0; j < Cf::VW; ++j)
+          if (u * Cf::RPL + rg >= nvalid) r.v[u * Cf::VW + j] = 0u;
+    }
   } else {
+    const char* src = vt + (size_t)(4 * q) * Cf::R + c * Cf::VBL;
 #pragma unroll
     for (int t = 0; t < Cf::T; ++t)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int row = 16 * t + 4 * q + rr;
-        const char* src = vt + (size_t)min(row, nvalid - 1) * Cf::R + c * Cf::VBL;
+        const char* row = src + (size_t)(16 * t + rr) * Cf::R;
         uint32_t* dst = &r.v[(t * 4 + rr) * Cf::VWD];
         if constexpr (Cf::VWD == 1) {
-          dst[0] = *reinterpret_cast<const uint32_t*>(src);
+          dst[0] = *reinterpret_cast<const uint32_t*>(row);
         } else if constexpr (Cf::VWD == 2) {
-          const uint2 x = *reinterpret_cast<const uint2*>(src);
+          const uint2 x = *reinterpret_cast<const uint2*>(row);
           dst[0] = x.x; dst[1] = x.y;
         } else {
 #pragma unroll
           for (int h = 0; h < Cf::VWD / 4; ++h) {
-            const uint4 x = *reinterpret_cast<const uint4*>(src + 16 * h);
+            const uint4 x = *reinterpret_cast<const uint4*>(row + 16 * h);
             dst[4 * h + 0] = x.x; dst[4 * h + 1] = x.y; dst[4 * h + 2] = x.z; dst[4 * h + 3] = x.w;
           }
         }
       }
+    if (nvalid < Cf::B) {
+#pragma unroll
+      for (int t = 0; t < Cf::T; ++t)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+          for (int j = 0; j < Cf::VWD; ++j)
+            if (16 * t + 4 * q + rr >= nvalid) r.v[(t * 4 + rr) * Cf::VWD + j] = 0u;
+    }
   }
 }
 
@@ -924,7 +948,7 @@ __device__ void art_scanner(const Params& p, int stream, uint32_t E, float* part
   const float* ringb = p.sched_ring + (size_t)stream * p.ring * p.slot_floats;
   const bool helped = p.helpers > 0;
   const bool claimer = w == NS && lane == 0;  // block wave 0, lane 0: the stream's claims
-  int* dec = sh + 16;                         // dec[k % 4]: 1 if chunk k is computed here (sh[0..15]: wave votes)
+  int* dec = sh + 16;                         // dec[k % 8]: 1 if chunk k is computed here (sh[0..15]: wave votes)
 
   if (n <= 0) {
     for (int i = threadIdx.x; i < g * Cf::D; i += NT) p.out[head0 * Cf::D + i] = 0.f;
@@ -949,10 +973,10 @@ __device__ void art_scanner(const Params& p, int stream, uint32_t E, float* part
 
   // Order and page entries: scan wave 0 keeps two lane-held windows of 64
   // visit positions, [W, W+64) and [W+64, W+128), and at step c writes chunk
-  // c+3's entries (lane = slot) into the LDS ring ent[(c+3) % 4]; the other
+  // c+4's entries (lane = slot) into the LDS ring ent[(c+4) % 8]; the other
   // waves read a chunk's entries from there.  Window 1 is re-read when the
   // windows slide (its pages one step after its order entries).
-  int* ent = sh + 32;  // [4][2][8]: order entry, page
+  int* ent = sh + 32;  // [8][2][8]: order entry, page
   int W = 0, ob_w0 = 0, ob_w1 = 0, pg_w0 = 0, pg_w1 = 0;
   bool pg_w1_due = false;
   auto publish_entries = [&](int k) {  // scan wave 0: chunk k (clamped) into ent[k % 4]
@@ -967,11 +991,11 @@ __device__ void art_scanner(const Params& p, int stream, uint32_t E, float* part
     const int idx = tc - W + slot;
     const int ob = __shfl(ob_w0, idx);
     const int pg = __shfl(pg_w0, idx);
-    if (lane < C) { ent[(k & 3) * 16 + lane] = ob; ent[(k & 3) * 16 + 8 + lane] = pg; }
+    if (lane < C) { ent[(k & 7) * 16 + lane] = ob; ent[(k & 7) * 16 + 8 + lane] = pg; }
   };
   auto entries = [&](int k, int& ob, int& pg) {  // lane-held entries of chunk k
-    ob = ent[(k & 3) * 16 + slot];
-    pg = ent[(k & 3) * 16 + 8 + slot];
+    ob = ent[(k & 7) * 16 + slot];
+    pg = ent[(k & 7) * 16 + 8 + slot];
   };
   if (w == 0) {
     ob_w0 = orow[min(lane, n - 1)];
@@ -981,19 +1005,22 @@ __device__ void art_scanner(const Params& p, int stream, uint32_t E, float* part
     publish_entries(0);
     publish_entries(1);
     publish_entries(2);
+    publish_entries(3);
   }
 
-  // claims (helpers only): chunk 0 is the scanner's; chunks 1 and 2 are
-  // claimed before the first step, chunk k >= 3 at step k-3 (attempted one
-  // step earlier); dec[k % 4] = 1 when chunk k is computed here
+  // claims (helpers only): chunk 0 is the scanner's; chunks 1 .. IA are
+  // claimed before the first step, chunk k > IA at step k-IA-1 (attempted
+  // one step earlier); dec[k % 8] = 1 when chunk k is computed here
+  constexpr int IA = Cf::IA;
   u64 cw = 0, exp3 = 0, ret3 = 0;
   bool tried3 = false;
   if (threadIdx.x == 0) {
-    dec[0] = 1; dec[1] = 1; dec[2] = 1; dec[3] = 1;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dec[k] = 1;
   }
   if (claimer && helped) {
     cw = ld_dev(claimw);
-    for (int k = 1; k <= 2 && k < nch; ++k) {
+    for (int k = 1; k <= IA && k < nch; ++k) {
       bool loc = false;
       if ((tag_val(cw, E, 1) & ~CLAIM_FIN) == (uint32_t)k) {
         const u64 r = cas_dev(claimw, cw, tag_word(E, k + 1));
@@ -1002,9 +1029,9 @@ __device__ void art_scanner(const Params& p, int stream, uint32_t E, float* part
       }
       dec[k] = loc ? 1 : 0;
     }
-    if (3 < nch && (tag_val(cw, E, 1) & ~CLAIM_FIN) == 3u) {
+    if (IA + 1 < nch && (tag_val(cw, E, 1) & ~CLAIM_FIN) == (uint32_t)(IA + 1)) {
       exp3 = cw;
-      ret3 = cas_dev(claimw, cw, tag_word(E, 4));
+      ret3 = cas_dev(claimw, cw, tag_word(E, IA + 2));
       tried3 = true;
     }
   }
@@ -1045,7 +1072,7 @@ __device__ void art_scanner(const Params& p, int stream, uint32_t E, float* part
       const unsigned long long sinkbits = __ballot(lane < nt && ob_c == 0);
       if (w == 0) {
         if (pg_w1_due) { pg_w1 = trow[ob_w1]; pg_w1_due = false; }
-        publish_entries(c + 3);
+        publish_entries(c + 4);
       }
       int a = 0;
 #pragma unroll
@@ -1073,10 +1100,12 @@ __device__ void art_scanner(const Params& p, int stream, uint32_t E, float* part
     }
   } else {
     // ================= block waves: chunk c+1 into buffer (c+1) % 2 =================
+    constexpr int PFD = Cf::PFD;
     uint4 qf[Cf::QF];
     load_q<Cf>(p, s, kvh, lane, qf);
-    BlockRegs<Cf> ra[BPB], rb[BPB];  // ring: chunk k in (k % 2 ? rb : ra); only ra when PFD == 1
-    float ks_a = 1.f, vs_a = 1.f, ks_b = 1.f, vs_b = 1.f;
+    // register ring: chunk k's tiles in slot k % PFD (one slot when PFD == 1)
+    BlockRegs<Cf> r0[BPB], r1[BPB], r2[BPB];
+    float ks0 = 1.f, vs0 = 1.f, ks1 = 1.f, vs1 = 1.f, ks2 = 1.f, vs2 = 1.f;
     // issue chunk k's loads for this block wave (k past the end re-reads the last chunk)
     auto issue = [&](int k, BlockRegs<Cf> (&rr)[BPB], float& ks, float& vs) {
       int ob, pg;
@@ -1088,33 +1117,35 @@ __device__ void art_scanner(const Params& p, int stream, uint32_t E, float* part
         vs = p.v_scale[(size_t)pg * p.hkv + kvh];
       }
     };
-    // prologue: chunk 0 into buffer 0, chunk 1 in flight
-    issue(0, ra, ks_a, vs_a);
-    if constexpr (Cf::PFD == 2) {
-      issue(dec[1] ? 1 : 0, rb, ks_b, vs_b);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    // the chunk to load at step c (issue distance IA); a chunk a helper took,
+    // or one past the end, re-reads chunk c+1 clamped into [0, nch) (cache
+    // hits; the loads stay unconditional so the waits stay exact)
+    auto target = [&](int k) { return (k < nch && dec[k & 7]) ? k : max(0, min(k - (IA - 1), nch - 1)); };
+    // prologue: chunk 0 into buffer 0, chunks 1 .. PFD-1 in flight
+    issue(0, r0, ks0, vs0);
+    if constexpr (PFD >= 2) issue(target(1), r1, ks1, vs1);
+    if constexpr (PFD >= 3) issue(target(2), r2, ks2, vs2);
+    __builtin_amdgcn_sched_barrier(0);
     {
       int ob0, pg0;
       entries(0, ob0, pg0);
-      block_phase<Cf, BPB>(ra, qf, ob0, ks_a, vs_a, min(C, n), L, p.qk_log2, bw, lane, part2, pbuf);
+      block_phase<Cf, BPB>(r0, qf, ob0, ks0, vs0, min(C, n), L, p.qk_log2, bw, lane, part2, pbuf);
     }
-    if constexpr (Cf::PFD == 1) issue(dec[1] ? 1 : 0, ra, ks_a, vs_a);
+    if constexpr (PFD == 1) issue(target(1), r0, ks0, vs0);
     lds_barrier();
 
-    // one step: rc holds chunk c+1's tiles, rn receives chunk c+2's
+    // one step: rc holds chunk c+1's tiles; rn receives chunk c+IA's
+    // (before the math when PFD == 2, after it otherwise)
     auto bstep = [&](BlockRegs<Cf> (&rc)[BPB], float& ksc, float& vsc, BlockRegs<Cf> (&rn)[BPB], float& ksn,
                      float& vsn) {
       const int t0 = c * C;
       float* nxt = part2 + ((c + 1) & 1) * Cf::SLOT;
-      const bool loc2 = dec[(c + 2) & 3] != 0;
-      const int k2 = (c + 2 < nch && loc2) ? c + 2 : c + 1;
-      if constexpr (Cf::PFD == 2) {
-        issue(k2, rn, ksn, vsn);
+      if constexpr (PFD == 2) {
+        issue(target(c + 2), rn, ksn, vsn);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (c + 1 < nch) {
-        if (dec[(c + 1) & 3]) {
+        if (dec[(c + 1) & 7]) {
           int ob1, pg1;
           entries(c + 1, ob1, pg1);
           block_phase<Cf, BPB>(rc, qf, ob1, ksc, vsc, min(C, n - t0 - C), L, p.qk_log2, bw, lane, nxt, pbuf);
@@ -1131,19 +1162,19 @@ __device__ void art_scanner(const Params& p, int stream, uint32_t E, float* part
           for (int i = threadIdx.x - 64 * NS; i < Cf::SLOT / 2; i += 64 * Cf::NBW) dst[i] = ld_dev(src + i);
         }
       }
-      if constexpr (Cf::PFD == 1) issue(k2, rn, ksn, vsn);  // rn is rc here: refilled once consumed
-      // claims: resolve chunk c+3's attempt, attempt chunk c+4
+      if constexpr (PFD != 2) issue(target(c + IA), rn, ksn, vsn);
+      // claims: resolve the attempt for chunk c+IA+1, attempt chunk c+IA+2
       if (claimer && helped) {
         bool loc = false;
         if (tried3) {
           loc = ret3 == exp3;
-          cw = loc ? tag_word(E, c + 4) : ret3;
+          cw = loc ? tag_word(E, c + IA + 2) : ret3;
         }
-        if (c + 3 < nch) dec[(c + 3) & 3] = loc ? 1 : 0;
+        if (c + IA + 1 < nch) dec[(c + IA + 1) & 7] = loc ? 1 : 0;
         tried3 = false;
-        if (c + 4 < nch && (tag_val(cw, E, 1) & ~CLAIM_FIN) == (uint32_t)(c + 4)) {
+        if (c + IA + 2 < nch && (tag_val(cw, E, 1) & ~CLAIM_FIN) == (uint32_t)(c + IA + 2)) {
           exp3 = cw;
-          ret3 = cas_dev(claimw, cw, tag_word(E, c + 5));
+          ret3 = cas_dev(claimw, cw, tag_word(E, c + IA + 3));
           tried3 = true;
         }
       }
@@ -1152,25 +1183,29 @@ __device__ void art_scanner(const Params& p, int stream, uint32_t E, float* part
       return more;
     };
     for (;;) {
-      if constexpr (Cf::PFD == 2) {
-        if (!bstep(rb, ks_b, vs_b, ra, ks_a, vs_a)) break;
-        if (!bstep(ra, ks_a, vs_a, rb, ks_b, vs_b)) break;
+      if constexpr (PFD == 3) {
+        if (!bstep(r1, ks1, vs1, r0, ks0, vs0)) break;  // c % 3 == 0: compute slot 1, issue into slot 0
+        if (!bstep(r2, ks2, vs2, r1, ks1, vs1)) break;
+        if (!bstep(r0, ks0, vs0, r2, ks2, vs2)) break;
+      } else if constexpr (PFD == 2) {
+        if (!bstep(r1, ks1, vs1, r0, ks0, vs0)) break;
+        if (!bstep(r0, ks0, vs0, r1, ks1, vs1)) break;
       } else {
-        if (!bstep(ra, ks_a, vs_a, ra, ks_a, vs_a)) break;
+        if (!bstep(r0, ks0, vs0, r0, ks0, vs0)) break;
       }
     }
 
-    // KV tiles fetched: chunks [0, min(nch, c+3)) were loaded here or by a
-    // helper; with helpers, chunks claimed later by helpers were loaded by
-    // them, and chunks c+3, c+4 claimed here were never loaded.  Then close
-    // the stream for helpers.
+    // KV tiles fetched: chunks [0, min(nch, c+IA+1)) were loaded here or by
+    // a helper; with helpers, chunks claimed later by helpers were loaded by
+    // them, and chunks c+IA+1, c+IA+2 claimed here were never loaded.  Then
+    // close the stream for helpers.
     if (claimer) {
-      int fetched = min(n, (c + 3) * C);
+      int fetched = min(n, (c + IA + 1) * C);
       if (helped) {
-        bool own4 = false;
+        bool own_last = false;
         if (tried3) {
-          own4 = ret3 == exp3;
-          cw = own4 ? tag_word(E, c + 5) : ret3;
+          own_last = ret3 == exp3;
+          cw = own_last ? tag_word(E, c + IA + 3) : ret3;
         }
         uint32_t cnt = 0;
         for (int k = 0; k < (1 << 20); ++k) {
@@ -1181,8 +1216,8 @@ __device__ void art_scanner(const Params& p, int stream, uint32_t E, float* part
         }
         fetched = min(n, (int)cnt * C);
         auto blocks = [&](int k) { return k < nch ? min(C, n - k * C) : 0; };
-        if (c + 3 < nch && (int)cnt > c + 3 && dec[(c + 3) & 3]) fetched -= blocks(c + 3);
-        if (own4) fetched -= blocks(c + 4);
+        if (c + IA + 1 < nch && (int)cnt > c + IA + 1 && dec[(c + IA + 1) & 7]) fetched -= blocks(c + IA + 1);
+        if (own_last) fetched -= blocks(c + IA + 2);
         if (err) st_dev32(p.sched_ctrl + 2, 1u);
       }
       if (p.blocks_fetched) p.blocks_fetched[stream] = fetched;
@@ -1286,7 +1321,7 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_sched_kerne
   using Cf = Cfg<KV, D, B, GM>;
   __shared__ __attribute__((aligned(16))) float part[2 * Cf::SLOT];
   __shared__ __attribute__((aligned(16))) float pbuf_all[Cf::NWA][Cf::PV4 ? GM * B : 4];
-  __shared__ int sh[96];
+  __shared__ int sh[192];
   const int streams = p.batch * p.hkv;
   // The epoch tags the scheduler words, which only calls with helpers use;
   // it is constant during the launch (advanced by the last workgroup), so
