@@ -86,11 +86,14 @@ size_t art_decode_workspace_bytes(const art_decode_desc* desc);
 /*
  * Put a workspace into its initial state (all bytes zero) on `stream`.
  * Must be called once on a new workspace before its first art_decode call.
- * The workspace holds the terminating kernel's scheduler words (tagged with
- * a per-call epoch that the kernel itself advances, so later calls need no
- * clearing and may be captured in a HIP graph) and the partial results that
- * helper workgroups hand to the per-stream scanners, or the full-attention
- * slices before their merge.
+ * The workspace holds the terminating kernel's scheduler state -- words
+ * tagged with a per-call epoch that the kernel itself advances, and per-stream
+ * counters that the kernel's last workgroup clears, so later calls need no
+ * clearing and may be captured in a HIP graph -- and the data handed between
+ * workgroups: per-chunk records of the look-back scheduler, the partial
+ * results helper workgroups hand to the per-stream scanners, or the
+ * full-attention slices before their merge.  Calls that share a workspace
+ * must not overlap.
  * Errors: ART_ERR_INVALID_ARG for NULL with bytes > 0 or a pointer that is
  * not 256-byte aligned, ART_ERR_HIP.
  */
@@ -123,6 +126,13 @@ art_status art_decode_workspace_init(void* workspace, size_t workspace_bytes, vo
  * blocks_fetched  optional [batch][Hkv] int32 (NULL to skip): KV blocks the
  *              kernels actually read for each (sequence, kv-head), speculative
  *              reads (chunks fetched ahead of the stop) included.
+ *
+ * The terminating kernel has two schedulers (environment ART_SCHED: "auto",
+ * the default, "scan" or "lb"): one scanner workgroup per stream that folds
+ * the stream's blocks in order, or persistent workgroups that take chunks of
+ * any stream and obtain the state entering a chunk from the records of the
+ * chunks before it.  Each is deterministic; their results differ only in
+ * floating-point rounding order (within the same tolerance of the method).
  * workspace    device scratch of at least art_decode_workspace_bytes(desc)
  *              bytes, initialized once with art_decode_workspace_init; may be
  *              NULL when that size is 0.  256-byte aligned.

@@ -58,20 +58,34 @@ art_status check_desc(const art_decode_desc* d) {
 }
 
 // Scheduler tuning knobs, read from the environment at every call (defaults
-// when unset): ART_RING slots per stream, ART_LOOKAHEAD initial helper
-// window, ART_HELPERS helper workgroups (default 0; -1: enough to reach
-// ART_TARGET_WGS workgroups in total).  The workspace size depends on ART_RING.
+// when unset).  ART_SCHED selects the terminating kernel: "scan" (one scanner
+// workgroup per stream, optional helpers), "lb" (the look-back scheduler) or
+// "auto" (default): the look-back scheduler when the streams are few (at
+// most half the CUs) and long (at least 256 chunks), where scanners would
+// leave most CUs idle for a long walk; scanners otherwise.
+// Look-back: ART_WINDOW chunks claimable past a stream's resolved frontier,
+// ART_WORKERS workgroups (0: one per resident slot), ART_ANCHOR chunks per
+// published inclusive state (results depend on it, not on the other knobs).  Scanners: ART_RING
+// slots per stream, ART_LOOKAHEAD initial helper window, ART_HELPERS helper
+// workgroups (default 0; -1: enough to reach ART_TARGET_WGS workgroups in
+// total).  ART_SPIN_LIMIT bounds every wait loop.  The workspace size depends
+// on ART_RING only.
 int env_int(const char* name, int def, int lo, int hi) {
   const char* v = getenv(name);
   int x = v ? atoi(v) : def;
   return x < lo ? lo : (x > hi ? hi : x);
 }
 struct Knobs {
-  int ring, lookahead, helpers, target;
+  int ring, lookahead, helpers, target, lb, window, workers, anchor;
 };
+enum { SCHED_SCAN = 0, SCHED_LB = 1, SCHED_AUTO = 2 };
 Knobs knobs() {
-  const Knobs k = {env_int("ART_RING", 8, 1, 64), env_int("ART_LOOKAHEAD", 3, 1, 64),
-                          env_int("ART_HELPERS", 0, -1, 1 << 16), env_int("ART_TARGET_WGS", 512, 1, 1 << 16)};
+  const char* sched = getenv("ART_SCHED");
+  const int mode = !sched || strcmp(sched, "auto") == 0 ? SCHED_AUTO : (strcmp(sched, "lb") == 0 ? SCHED_LB : SCHED_SCAN);
+  const Knobs k = {env_int("ART_RING", 8, 1, 64),          env_int("ART_LOOKAHEAD", 3, 1, 64),
+                   env_int("ART_HELPERS", 0, -1, 1 << 16), env_int("ART_TARGET_WGS", 512, 1, 1 << 16),
+                   mode,                                    env_int("ART_WINDOW", 32, 1, 32),
+                   env_int("ART_WORKERS", 0, 0, 1 << 20),   env_int("ART_ANCHOR", 8, 1, 32)};
   return k;
 }
 
@@ -95,7 +109,25 @@ art::WorkspacePlan plan_workspace(const art_decode_desc* d) {
   if (h > useful) h = useful;
   if (h < 0) h = 0;
   w.helpers = (int)h;
-  size_t off = 256;  // [0] stored epoch, [1] finished workgroups, [2] error flag
+  w.max_chunks = (int)max_chunks;
+  w.rec_floats = 2 * (d->head_dim + 4);
+  w.window = k.window;
+  w.anchor = k.anchor;
+  // Control words and counters never share memory with another mode's data:
+  // [0] stored epoch, [1] finished workgroups, [2] error flag; look-back
+  // counters and epoch-tagged words; scanner words; then one data region
+  // (helper ring, look-back records or full-mode partials).
+  size_t off = 256;
+  w.lb_fetch = off;
+  off += round256(streams * 4);
+  w.lb_claim = off;
+  off += round256(streams * 8);
+  w.lb_prog = off;
+  off += round256(streams * 8);
+  w.lb_heads = off;
+  off += round256(streams * 8);
+  w.lb_st = off;
+  off += round256(streams * (size_t)max_chunks * g * 8);
   w.claim = off;
   off += round256(streams * 8);
   w.done = off;
@@ -104,9 +136,12 @@ art::WorkspacePlan plan_workspace(const art_decode_desc* d) {
   off += round256(streams * (size_t)w.ring * 8);
   w.data = off;
   const size_t ring_bytes = streams * (size_t)w.ring * w.slot_floats * sizeof(float);
+  const size_t rec_bytes = streams * (size_t)max_chunks * g * w.rec_floats * sizeof(float);
   const art::SplitPlan sp = art::full_split_plan(d->batch, d->num_kv_heads, d->max_blocks_per_seq);
   const size_t part = sp.splits > 1 ? streams * sp.splits * gm * (size_t)(d->head_dim + 2) * sizeof(float) : 0;
-  off += round256(ring_bytes > part ? ring_bytes : part);
+  size_t data = ring_bytes > part ? ring_bytes : part;
+  if (rec_bytes > data) data = rec_bytes;
+  off += round256(data);
   w.total = off;
   return w;
 }
@@ -207,7 +242,30 @@ art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_
     p.slot_floats = wp.slot_floats;
     p.helpers = wp.helpers;
     p.lookahead = wp.lookahead;
-    p.spin_limit = 1 << 20;
+    p.spin_limit = env_int("ART_SPIN_LIMIT", 1 << 20, 64, 1 << 30);
+    p.lb_fetch = reinterpret_cast<uint32_t*>(ws + wp.lb_fetch);
+    p.lb_claim = reinterpret_cast<uint32_t*>(ws + wp.lb_claim);
+    p.lb_prog = reinterpret_cast<uint32_t*>(ws + wp.lb_prog);
+    p.lb_heads = reinterpret_cast<uint32_t*>(ws + wp.lb_heads);
+    p.lb_st = reinterpret_cast<unsigned long long*>(ws + wp.lb_st);
+    p.lb_rec = reinterpret_cast<float*>(ws + wp.data);
+    p.max_chunks = wp.max_chunks;
+    p.rec_floats = wp.rec_floats;
+    p.window = wp.window;
+    p.anchor = wp.anchor;
+    const Knobs k = knobs();
+    // the look-back records hold pass counts up to 4095; its claim sweep
+    // packs a stream index in 16 bits
+    const long streams = (long)desc->batch * desc->num_kv_heads;
+    bool lb = k.lb == SCHED_LB;
+    if (k.lb == SCHED_AUTO) {
+      int dev = 0, cus = 0;
+      if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+      lb = 2 * streams <= cus && wp.max_chunks >= 256;
+    }
+    p.lb = (lb && patience <= 4095 && streams <= 65535) ? 1 : 0;
+    p.workers = k.workers;
     e = v.kv == art::KV_F32 ? art::launch_art_f32(v, p, static_cast<hipStream_t>(stream))
         : v.kv == art::KV_BF16 ? art::launch_art_bf16(v, p, static_cast<hipStream_t>(stream))
                                : art::launch_art_fp8(v, p, static_cast<hipStream_t>(stream));

@@ -34,7 +34,7 @@ struct Params {
   float* ws_part;           // full mode with splits: [streams][splits][GM][D + 2]
   // ART scheduler (workspace): epoch-tagged control words and the ring of
   // partial-result slots helpers hand to scanners
-  uint32_t* sched_ctrl;                // [0] stored epoch, [1] finished workgroups, [2] error flag
+  uint32_t* sched_ctrl;                // [0] stored epoch, [1] finished workgroups, [2] error flag, [3] epoch of a failed call
   unsigned long long* sched_claim;     // [streams]
   unsigned long long* sched_done;      // [streams]
   unsigned long long* sched_ready;     // [streams][ring]
@@ -44,6 +44,21 @@ struct Params {
   int32_t helpers;                     // helper workgroups launched after the scanners
   int32_t lookahead;                   // helper window: chunk c is claimable while c < done + min(ring, lookahead + done)
   int32_t spin_limit;                  // bound of every wait loop
+  // look-back scheduler (art_lb_kernel): plain per-stream words (zero at the
+  // start of a call, reset by its last workgroup), an epoch-tagged status
+  // word and a record per (stream, chunk, head)
+  uint32_t* lb_claim;                  // [streams] chunks claimed | CLAIM_FIN
+  uint32_t* lb_prog;                   // [streams] resolved frontier (atomic max)
+  uint32_t* lb_heads;                  // [streams] bit mask of stopped heads
+  uint32_t* lb_fetch;                  // [streams] blocks loaded
+  unsigned long long* lb_st;           // [streams][max_chunks][g]
+  float* lb_rec;                       // [streams][max_chunks][g][rec_floats]
+  int32_t max_chunks;                  // ceil(max_blocks / chunk)
+  int32_t rec_floats;                  // 2 * (D + 4)
+  int32_t window;                      // chunks claimable past the resolved frontier (<= 32)
+  int32_t anchor;                      // every anchor-th chunk publishes its inclusive state (<= 32)
+  int32_t lb;                          // 1: launch art_lb_kernel, 0: scanners (+ helpers)
+  int32_t workers;                     // art_lb_kernel workgroups (0: one per resident slot)
   int32_t batch, hq, hkv, g;
   int32_t block_size;
   int32_t max_blocks;
@@ -73,8 +88,9 @@ SplitPlan full_split_plan(int batch, int hkv, int max_blocks);
 
 // Workspace layout (bytes from the workspace base, each region 256-B aligned).
 struct WorkspacePlan {
-  size_t claim, done, ready, data, total;
-  int ring, slot_floats, helpers, lookahead;
+  size_t lb_fetch, lb_claim, lb_prog, lb_heads, lb_st;  // look-back scheduler
+  size_t claim, done, ready, data, total;               // scanner + helpers; data: ring | records | full partials
+  int ring, slot_floats, helpers, lookahead, max_chunks, rec_floats, window, anchor;
 };
 
 // Launchers; return hipSuccess or the launch error.  One translation unit per

@@ -1348,6 +1348,672 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_sched_kerne
 }
 
 // ---------------------------------------------------------------------------
+// Terminating path, look-back scheduler: art_lb_kernel
+// ---------------------------------------------------------------------------
+//
+// Persistent workgroups ("workers") take items = (stream, chunk of C blocks)
+// from per-stream claim counters and carry each item through a three-step
+// pipeline, one item per step in each stage: the item's KV loads are issued
+// (block waves), its per-block partials computed into LDS (block waves), and
+// it is folded into the stream's ART state (scan waves, one query head per
+// wave).  Chunks of one stream can be on many workers at once; the state
+// entering chunk k comes from the records of earlier chunks (a decoupled
+// look-back over an associative combine):
+//   * (M, L, A): the online-softmax state is a monoid under
+//     (M1, L1, A1) + (M2, L2, A2) = (M, 2^(M1-M) L1 + 2^(M2-M) L2, same for A),
+//     M = max(M1, M2).  Every `anchor`-th chunk (k % anchor == anchor - 1)
+//     publishes its inclusive state, the other chunks their own aggregate;
+//     the state entering chunk k is the inclusive state of the anchor before
+//     it combined with the aggregates of the chunks in between, always in
+//     chunk order, so the arithmetic (and every result) is the same whatever
+//     the timing, the number of workers or the window.  The anchors form the
+//     only chain: one hand-off per `anchor` chunks.
+//   * The detector's inputs at the chunk's first position need only the
+//     output O = A / L entering it, so the statistics of all C positions (and
+//     their pass bits) follow from that state alone.
+//   * The pass count, the block-0-folded flag and whether the head still runs
+//     are replayed from the nearest resolved chunk over the pass bits of the
+//     chunks after it.
+// A head that fires writes its output and stop; when every head of a stream
+// has fired the stream's claim counter is closed, later chunks are no longer
+// claimed and chunks already in flight are dropped before their fold.
+//
+// Forward progress: an item only waits for records of earlier chunks of its
+// stream, which were claimed before it, and a worker's items are processed in
+// claim order; every wait therefore points to an item claimed earlier, and
+// the earliest unfinished item can always proceed -- whether or not every
+// worker is resident.
+//
+// Claims: a worker first tries the stream of its last item, else sweeps all
+// streams and takes one of those with the most unclaimed chunks (ties spread
+// over the workers by a hash).  Chunk k of a stream is claimable while
+// k < resolved + window, where resolved is one past the highest chunk whose
+// state is final for every head; that bounds the speculative reads past a
+// stop, and keeps the nearest resolved chunk of a chunk in flight within
+// about `window` chunks of it (the look-back waits otherwise).
+//
+// Record of (stream, chunk, head): a status word tag(E, payload) with
+//   bits 0-1   level: 1 aggregate, 2 pass bits (+ inclusive state for an
+//              anchor), 3 resolved
+//   bits 2-9   pass bits of the chunk's positions          (level >= 2)
+//   bits 10-17 positions holding block 0                   (level >= 2)
+//   bit 18     head still running after the chunk          (level 3)
+//   bit 19     block 0 folded by the end of the chunk      (level 3)
+//   bits 20-31 passes in a row at the chunk end, at most the patience (level 3)
+// and floats: aggregate [A(D), m, l] at 0 (chunks other than anchors),
+// inclusive [A(D), M, L] at D + 4 (anchors).
+// Data is stored with device-scope stores and the status after them
+// (s_waitcnt vmcnt(0) in between); readers load the status, then the data.
+
+constexpr uint32_t LB_AGG = 1u, LB_INCL = 2u, LB_FIN = 3u;
+constexpr uint32_t LB_RUNNING = 1u << 18, LB_SINKED = 1u << 19;
+constexpr uint32_t LB_BEFORE = LB_FIN | LB_RUNNING;  // the state before chunk 0
+constexpr int LB_ENT = 24;                          // ints per LDS item entry: s, k, n, L, ob[8], pg[8]
+constexpr int LB_BUBBLE = -1, LB_END = -2;
+
+template <class Cf>
+struct LbState {
+  float M, L;
+  float A[Cf::DPL];
+};
+
+template <class Cf>
+__device__ __forceinline__ void lb_load(const float* r, int lane, float& m, float& l, float (&a)[Cf::DPL]) {
+  if constexpr (Cf::DPL == 2) {
+    const u64 v = ld_dev(reinterpret_cast<const u64*>(r + 2 * lane));
+    a[0] = bitsf((uint32_t)v);
+    a[1] = bitsf((uint32_t)(v >> 32));
+  } else {
+    a[0] = bitsf(ld_dev32(reinterpret_cast<const uint32_t*>(r + lane)));
+  }
+  const u64 ml = ld_dev(reinterpret_cast<const u64*>(r + Cf::D));
+  m = bitsf((uint32_t)ml);
+  l = bitsf((uint32_t)(ml >> 32));
+}
+
+template <class Cf>
+__device__ __forceinline__ void lb_store(float* r, int lane, float m, float l, const float (&a)[Cf::DPL]) {
+  if constexpr (Cf::DPL == 2)
+    st_dev(reinterpret_cast<u64*>(r + 2 * lane), ((u64)fbits(a[1]) << 32) | fbits(a[0]));
+  else
+    st_dev32(reinterpret_cast<uint32_t*>(r + lane), fbits(a[0]));
+  if (lane == 0) st_dev(reinterpret_cast<u64*>(r + Cf::D), ((u64)fbits(l) << 32) | fbits(m));
+}
+
+// x <- x (+) (m, l, a)
+template <class Cf>
+__device__ __forceinline__ void lb_combine(LbState<Cf>& x, float m, float l, const float (&a)[Cf::DPL]) {
+  const float mn = fmaxf(x.M, m);
+  const bool empty = mn == NEG_INF;
+  const float fx = empty ? 0.f : __builtin_amdgcn_exp2f(x.M - mn);
+  const float fy = empty ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+  x.L = fmaf(fx, x.L, fy * l);
+#pragma unroll
+  for (int j = 0; j < Cf::DPL; ++j) x.A[j] = fmaf(fx, x.A[j], fy * a[j]);
+  x.M = mn;
+}
+
+// The chunk's own aggregate from its per-block partials (positions past the
+// chunk end are neutral: m = -inf, l = 0, a = 0; position 0 is a real block).
+template <class Cf>
+__device__ __forceinline__ void lb_aggregate(const ChunkIn<Cf>& in, float& m, float& l, float (&a)[Cf::DPL]) {
+  float mx = NEG_INF;
+#pragma unroll
+  for (int t = 0; t < Cf::C; ++t) mx = fmaxf(mx, readlanef(in.m, t));
+  l = 0.f;
+#pragma unroll
+  for (int j = 0; j < Cf::DPL; ++j) a[j] = 0.f;
+#pragma unroll
+  for (int t = 0; t < Cf::C; ++t) {
+    const float e = __builtin_amdgcn_exp2f(readlanef(in.m, t) - mx);
+    l = fmaf(e, readlanef(in.l, t), l);
+#pragma unroll
+    for (int j = 0; j < Cf::DPL; ++j) a[j] = fmaf(e, in.a[t][j], a[j]);
+  }
+  m = mx;
+}
+
+// Fold one chunk into the state entering it (x, with O_prev = Op and
+// Np = ‖Op‖²) and evaluate both statistics at every position of the chunk
+// (the same arithmetic as scan_head).  Returns the pass bits (bit t:
+// position t passed both tests); x becomes the inclusive state, Op the
+// output at the chunk's last position, oo[t] the output at position t.
+template <class Cf>
+__device__ __forceinline__ u64 lb_stats(LbState<Cf>& x, float (&Op)[Cf::DPL], float Np, const ChunkIn<Cf>& in,
+                                        int t0, int nt, const Params& p, int lane, float (&oo)[Cf::C][Cf::DPL]) {
+  constexpr int C = Cf::C, DPL = Cf::DPL, SH = Cf::SH;
+  const int slot = lane < C ? lane : C - 1;
+  float mx = in.m;
+  if constexpr (C > 1) mx = fmaxf(mx, row_shr<1>(mx, NEG_INF));
+  if constexpr (C > 2) mx = fmaxf(mx, row_shr<2>(mx, NEG_INF));
+  if constexpr (C > 4) mx = fmaxf(mx, row_shr<4>(mx, NEG_INF));
+  mx = fmaxf(mx, x.M);
+  const float mprev = row_shr<1>(mx, x.M);
+  const float al = mprev == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mprev - mx);
+  const float be = __builtin_amdgcn_exp2f(in.m - mx);
+  float fa = al, fb = be * in.l;
+  if constexpr (C > 1) { const float pa = row_shr<1>(fa, 1.f), pb = row_shr<1>(fb, 0.f); fb = fmaf(fa, pb, fb); fa *= pa; }
+  if constexpr (C > 2) { const float pa = row_shr<2>(fa, 1.f), pb = row_shr<2>(fb, 0.f); fb = fmaf(fa, pb, fb); fa *= pa; }
+  if constexpr (C > 4) { const float pa = row_shr<4>(fa, 1.f), pb = row_shr<4>(fb, 0.f); fb = fmaf(fa, pb, fb); fa *= pa; }
+  const float Lt = fmaf(fa, x.L, fb);
+  const float rl = __builtin_amdgcn_rcpf(Lt);
+
+  float st[2 * C];
+#pragma unroll
+  for (int t = 0; t < C; ++t) {
+    const float at = readlanef(al, t), bt = readlanef(be, t), rt = readlanef(rl, t);
+    float nn = 0.f, ee = 0.f;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) {
+      x.A[j] = fmaf(at, x.A[j], bt * in.a[t][j]);
+      const float o = x.A[j] * rt;
+      const float df = o - Op[j];
+      nn = fmaf(o, o, nn);
+      ee = fmaf(df, df, ee);
+      Op[j] = o;
+      oo[t][j] = o;
+    }
+    st[2 * t] = nn;
+    st[2 * t + 1] = ee;
+  }
+  const float v0 = xreduce<2 * C>(st, lane);
+  const float nn_t = __shfl(v0, (2 * slot) << SH);
+  const float ee_t = __shfl(v0, (2 * slot + 1) << SH);
+  float np_t = __shfl(v0, (2 * max(slot - 1, 0)) << SH);
+  if (lane == 0) np_t = Np;
+  bool ps = false;
+  if (lane < nt && t0 + lane >= 1) {
+    const float a = __builtin_amdgcn_sqrtf(nn_t);
+    const float bn = __builtin_amdgcn_sqrtf(np_t);
+    float dm, dd;
+    if (a == 0.f && bn == 0.f) {
+      dm = 0.f; dd = 0.f;
+    } else if (bn == 0.f) {
+      dm = __builtin_inff(); dd = 1.f;
+    } else {
+      const float df = a - bn;
+      dm = fabsf(df) * __builtin_amdgcn_rcpf(bn);
+      dd = (a == 0.f) ? 1.f : fmaxf(0.f, (ee_t - df * df) * __builtin_amdgcn_rcpf(2.f * a * bn));
+    }
+    ps = (dm < p.eps_mag) && (dd < p.eps_dir);
+  }
+  x.M = readlanef(mx, C - 1);
+  x.L = readlanef(Lt, C - 1);
+  return __ballot(ps);
+}
+
+// A wait that ran past its limit marks the call failed ([3] = this epoch,
+// [2] = 1); every other wait of the call then gives up at its next check.
+__device__ __forceinline__ void lb_fail(const Params& p, uint32_t E) {
+  st_dev32(p.sched_ctrl + 3, E);
+  st_dev32(p.sched_ctrl + 2, 1u);
+}
+__device__ __forceinline__ bool lb_give_up(const Params& p, uint32_t E, int spin) {
+  return spin > p.spin_limit || ((spin & 63) == 63 && ld_dev32(p.sched_ctrl + 3) == E);
+}
+
+// Status words of chunks k-1-lane (lanes < window); the state before chunk 0
+// for lanes that reach past it.
+__device__ __forceinline__ uint32_t lb_probe(const u64* st0, int g, int k, int window, uint32_t E, int lane) {
+  const int j = k - 1 - lane;
+  uint32_t v = LB_BEFORE;
+  if (lane < window && j >= 0) v = tag_val(ld_dev(st0 + (size_t)j * g), E, 0u);
+  if (lane >= window) v = 0u;
+  return v;
+}
+
+// One query head of one item: publish, look back, fold, detect, resolve.
+// Returns false if a wait ran past the spin limit (the head is then marked
+// stopped with stop = -1 and a NaN output).
+template <class Cf>
+__device__ bool lb_head(const Params& p, uint32_t E, int s, int k, int n, int h, const ChunkIn<Cf>& in,
+                        uint32_t sinkb, bool dead, int lane) {
+  constexpr int C = Cf::C, DPL = Cf::DPL;
+  const int g = p.g;
+  const int nt = min(C, n - k * C);
+  const int t0 = k * C;
+  const int nch = (n + C - 1) / C;
+  const int window = p.window;
+  const u64* st0 = p.lb_st + (size_t)s * p.max_chunks * g + h;  // chunk stride g
+  u64* stw = p.lb_st + ((size_t)s * p.max_chunks + k) * g + h;
+  const size_t rstride = (size_t)g * p.rec_floats;
+  const float* rec0 = p.lb_rec + ((size_t)s * p.max_chunks * g + h) * p.rec_floats;
+  float* rec = p.lb_rec + (((size_t)s * p.max_chunks + k) * g + h) * p.rec_floats;
+  const size_t head = (size_t)(s / p.hkv) * p.hq + (size_t)(s % p.hkv) * g + h;
+  const int incl = Cf::D + 4;
+  const int cap = min(p.patience, 4095);
+  if (dead) {
+    if (lane == 0) st_dev(stw, tag_word(E, LB_FIN | (sinkb << 10)));
+    return true;
+  }
+
+  // ---- state entering the chunk: the inclusive state of the anchor before
+  // it (every `anchor`-th chunk) combined with the aggregates after that, in
+  // chunk order -- a fixed order, so results do not depend on timing
+  const int r = k % p.anchor;
+  const bool is_anchor = r == p.anchor - 1;
+  LbState<Cf> x;
+  x.M = NEG_INF;
+  x.L = 0.f;
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) x.A[j] = 0.f;
+  bool ok = true;
+  if (!is_anchor && k < nch - 1) {
+    float m, l, a[DPL];
+    lb_aggregate<Cf>(in, m, l, a);
+    lb_store<Cf>(rec, lane, m, l, a);
+    wait_all_memory();
+    if (lane == 0) st_dev(stw, tag_word(E, LB_AGG));
+  }
+  if (k > 0) {
+    // lanes i < r: chunk k-1-i needs its aggregate; lane r: the anchor k-1-r
+    // (or the state before chunk 0) needs its inclusive state
+    for (int spin = 0;; ++spin) {
+      const uint32_t v = lb_probe(st0, g, k, r + 1, E, lane);
+      const bool ready = lane < r ? (v & 3u) >= LB_AGG : (lane == r ? (v & 3u) >= LB_INCL : true);
+      if (__ballot(!ready) == 0ull) break;
+      if (lb_give_up(p, E, spin)) { ok = false; break; }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (ok) {
+      const int jb = k - 1 - r;
+      if (jb >= 0) lb_load<Cf>(rec0 + (size_t)jb * rstride + incl, lane, x.M, x.L, x.A);
+      for (int i = r - 1; i >= 0; --i) {
+        float m, l, a[DPL];
+        lb_load<Cf>(rec0 + (size_t)(k - 1 - i) * rstride, lane, m, l, a);
+        lb_combine<Cf>(x, m, l, a);
+      }
+    }
+  }
+  float Op[DPL];
+  float np = 0.f;
+  {
+    const float rl = x.L > 0.f ? __builtin_amdgcn_rcpf(x.L) : 0.f;
+    float sq[1] = {0.f};
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) {
+      Op[j] = x.L > 0.f ? x.A[j] * rl : 0.f;
+      sq[0] = fmaf(Op[j], Op[j], sq[0]);
+    }
+    np = xreduce<1>(sq, lane);
+  }
+
+  // ---- statistics of every position; publish the inclusive state
+  float oo[C][DPL];
+  const u64 pass = lb_stats<Cf>(x, Op, np, in, t0, nt, p, lane, oo);
+  const uint32_t passb = (uint32_t)pass & 0xFFu;
+  if (ok) {
+    if (is_anchor) {
+      lb_store<Cf>(rec + incl, lane, x.M, x.L, x.A);
+      wait_all_memory();
+    }
+    if (lane == 0) st_dev(stw, tag_word(E, LB_INCL | (passb << 2) | (sinkb << 10)));
+  }
+
+  // ---- pass count, block-0 flag and running flag entering the chunk
+  int cnt = 0;
+  bool sink = false, alive = true;
+  if (ok && k > 0) {
+    int f = 0;
+    uint32_t v = 0;
+    for (int spin = 0;; ++spin) {
+      v = lb_probe(st0, g, k, window, E, lane);
+      const u64 fin = __ballot((v & 3u) == LB_FIN);
+      if (fin != 0ull) {
+        f = __builtin_ctzll(fin);
+        const u64 need = (1ull << f) - 1ull;
+        if ((__ballot((v & 3u) >= LB_INCL) & need) == need) break;
+      }
+      if (lb_give_up(p, E, spin)) { ok = false; break; }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (ok) {
+      const uint32_t wf = (uint32_t)readlane((int)v, f);
+      cnt = (int)(wf >> 20);
+      sink = (wf & LB_SINKED) != 0u;
+      alive = (wf & LB_RUNNING) != 0u;
+      for (int i = f - 1; i >= 0 && alive; --i) {
+        const uint32_t wi = (uint32_t)readlane((int)v, i);
+        const int ci = k - 1 - i;
+        const int nti = min(C, n - ci * C);
+        for (int t = 0; t < nti; ++t) {
+          cnt = ((wi >> (2 + t)) & 1u) ? min(cnt + 1, cap) : 0;
+          sink = sink || ((wi >> (10 + t)) & 1u);
+          if (cnt >= p.patience && sink) { alive = false; break; }
+        }
+      }
+    }
+  }
+
+  // ---- resolve this chunk
+  const int slot = lane < C ? lane : C - 1;
+  const u64 upto = (2ull << slot) - 1ull;
+  const u64 zeros = ~pass & upto;
+  const int cnt_t = zeros == 0ull ? min(cnt + slot + 1, cap) : slot - (63 - __builtin_clzll(zeros));
+  const bool sink_t = sink || ((u64)sinkb & upto) != 0ull;
+  const u64 fire = __ballot(ok && alive && lane < nt && cnt_t >= p.patience && sink_t);
+  float* out_row = p.out + head * Cf::D;
+  bool alive_out = ok && alive;
+  if (fire != 0ull) {
+    const int stop_t = __builtin_ctzll(fire);
+    float ov[DPL];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) ov[j] = oo[0][j];
+#pragma unroll
+    for (int t = 1; t < C; ++t)
+      if (stop_t == t)
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) ov[j] = oo[t][j];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) out_row[DPL * lane + j] = ov[j];
+    if (lane == 0) p.stop_block[head] = t0 + stop_t + 1;
+    alive_out = false;
+  } else if (alive_out && k == nch - 1) {
+    // never stopped: the output after all n blocks
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) out_row[DPL * lane + j] = Op[j];
+    if (lane == 0) p.stop_block[head] = n;
+  }
+  if (!ok) {
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) out_row[DPL * lane + j] = __builtin_nanf("");
+    if (lane == 0) {
+      p.stop_block[head] = -1;
+      lb_fail(p, E);
+    }
+  }
+  const int cnt_out = readlane(min(cnt_t, cap), nt - 1);
+  const bool sink_out = readlane(sink_t ? 1 : 0, nt - 1) != 0;
+  if (lane == 0) {
+    st_dev(stw, tag_word(E, LB_FIN | (passb << 2) | (sinkb << 10) | (alive_out ? LB_RUNNING : 0u) |
+                                (sink_out ? LB_SINKED : 0u) | ((uint32_t)cnt_out << 20)));
+    if (fire != 0ull || !ok) {
+      // mark the head stopped; close the stream when the whole group is
+      const uint32_t bit = 1u << h;
+      const uint32_t was = __hip_atomic_fetch_or(p.lb_heads + s, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((was | bit) == (1u << g) - 1u && was != (was | bit))
+        __hip_atomic_fetch_or(p.lb_claim + s, CLAIM_FIN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  return ok;
+}
+
+// Claim the next item into LDS entry e (whole claimer wave).  `cur` is the
+// stream of this worker's last claim, `ended` becomes true once no stream has
+// unclaimed chunks left.  A claim is an atomic add on the stream's counter,
+// attempted only while the counter is inside the window; concurrent claims
+// can pass the window or the chunk count by a few, which only makes the
+// later chunk wait for its look-back, or returns nothing.
+template <class Cf>
+__device__ void lb_claim(const Params& p, uint32_t E, int* e, char* qdst, int& cur, bool& ended, int lane) {
+  constexpr int C = Cf::C;
+  constexpr int QROWB = Cf::KV == KV_FP8 ? 2 * Cf::D : Cf::R;
+  const int S = p.batch * p.hkv;
+  int got_s = -1, got_k = 0;
+  (void)E;
+  if (!ended) {
+    auto nch_of = [&](int st) { return ((p.seq_lens[st / p.hkv] + Cf::B - 1) / Cf::B + C - 1) / C; };
+    auto take = [&](int st) {  // lane 0 adds, the wave gets the chunk index (or -1)
+      uint32_t k = 0;
+      if (lane == 0) k = __hip_atomic_fetch_add(p.lb_claim + st, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      k = (uint32_t)readlane((int)k, 0);
+      return ((k & CLAIM_FIN) || (int)k >= nch_of(st)) ? -1 : (int)k;
+    };
+    // the current stream first
+    if (cur >= 0) {
+      const uint32_t cv = ld_dev32(p.lb_claim + cur);
+      const uint32_t prog = ld_dev32(p.lb_prog + cur);
+      if (!(cv & CLAIM_FIN) && (int)cv < nch_of(cur) && cv < prog + (uint32_t)p.window) {
+        const int k = take(cur);
+        if (k >= 0) { got_s = cur; got_k = k; }
+      }
+    }
+    // else a claimable stream: most unclaimed chunks first (counted up to
+    // 16), ties spread over the workers
+    if (got_s < 0) {
+      uint32_t best = 0u;  // (min(remaining, 16) << 24) | (hash << 16) | stream, 0 = none
+      bool live_any = false;
+      const uint32_t hw = (blockIdx.x * 2654435761u) >> 24;
+      for (int base = 0; base < S; base += 64) {
+        const int st = base + lane;
+        uint32_t key = 0u;
+        if (st < S) {
+          const uint32_t cv = ld_dev32(p.lb_claim + st);
+          const uint32_t prog = ld_dev32(p.lb_prog + st);
+          const int nch = nch_of(st);
+          const bool live = !(cv & CLAIM_FIN) && (int)cv < nch;
+          live_any |= live;
+          if (live && cv < prog + (uint32_t)p.window)
+            key = ((uint32_t)min(nch - (int)cv, 16) << 24) | ((((uint32_t)st * 40503u) ^ hw) & 0xFFu) << 16 |
+                  (uint32_t)st;
+        }
+        uint32_t mk = key;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mk = max(mk, (uint32_t)__shfl_xor((int)mk, o));
+        best = max(best, mk);
+      }
+      live_any = __ballot(live_any) != 0ull;
+      if (best != 0u) {
+        const int st = (int)(best & 0xFFFFu);
+        const int k = take(st);
+        if (k >= 0) { got_s = st; got_k = k; }
+        cur = st;
+      } else if (!live_any) {
+        ended = true;
+      }
+    }
+  }
+  if (got_s < 0) {
+    if (lane == 0) e[0] = ended ? LB_END : LB_BUBBLE;
+    return;
+  }
+  cur = got_s;
+  // entries: visit order, pages, query rows of the group
+  const int sq = got_s / p.hkv;
+  const int kvh = got_s - sq * p.hkv;
+  const int L = p.seq_lens[sq];
+  const int n = (L + Cf::B - 1) / Cf::B;
+  const int32_t* orow = p.block_order + (size_t)sq * p.max_blocks;
+  const int32_t* trow = p.block_table + (size_t)sq * p.max_blocks;
+  const int ob = orow[min(got_k * C + min(lane, C - 1), n - 1)];
+  const char* qsrc = static_cast<const char*>(p.q) + ((size_t)sq * p.hq + (size_t)kvh * p.g) * QROWB;
+  const int qwords = p.g * QROWB / 16;
+  for (int i = lane; i < qwords; i += 64)
+    *reinterpret_cast<uint4*>(qdst + 16 * i) = *reinterpret_cast<const uint4*>(qsrc + 16 * i);
+  const int pg = trow[ob];
+  if (lane == 0) { e[0] = got_s; e[1] = got_k; e[2] = n; e[3] = L; }
+  if (lane < C) { e[4 + lane] = ob; e[4 + C + lane] = pg; }
+}
+
+// q fragments (as load_q) from the LDS copy of the group's query rows [GM][row bytes].
+template <class Cf>
+__device__ __forceinline__ void load_q_lds(const char* qs, int g, int lane, uint4 (&qf)[Cf::QF]) {
+  constexpr int QROWB = Cf::KV == KV_FP8 ? 2 * Cf::D : Cf::R;
+  const int c = lane & 15;
+#pragma unroll
+  for (int i = 0; i < Cf::QF; ++i) qf[i] = make_uint4(0, 0, 0, 0);
+  if (c >= g) return;
+  const char* row = qs + c * QROWB;
+  const int base = (lane >> 4) * 16;
+  if constexpr (Cf::KV == KV_FP8) {
+#pragma unroll
+    for (int i = 0; i < Cf::NKL; ++i)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        qf[2 * i + hf] = *reinterpret_cast<const uint4*>(row + 2 * (base + 64 * i + 8 * hf));
+  } else {
+#pragma unroll
+    for (int i = 0; i < Cf::NKL; ++i) qf[i] = *reinterpret_cast<const uint4*>(row + base + 64 * i);
+  }
+}
+
+template <int KV, int D, int B, int GM>
+__global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_lb_kernel(Params p) {
+  using Cf = Cfg<KV, D, B, GM>;
+  constexpr int C = Cf::C, NS = Cf::NS, HPS = Cf::HPS, PFD = Cf::PFD;
+  constexpr int QROWB = KV == KV_FP8 ? 2 * D : Cf::R;
+  constexpr int CLW = NS - 1;  // the scan wave that also claims
+  __shared__ __attribute__((aligned(16))) float part[2 * Cf::SLOT];
+  __shared__ __attribute__((aligned(16))) float pbuf_all[Cf::NWA][Cf::PV4 ? GM * B : 4];
+  __shared__ __attribute__((aligned(16))) char qring[4][GM * QROWB];
+  __shared__ int ent[4][LB_ENT];
+  __shared__ int last_wg;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int S = p.batch * p.hkv;
+  const uint32_t E = epoch_of(ld_dev32(p.sched_ctrl));
+  const int slot = lane < C ? lane : C - 1;
+
+  // streams without tokens: out = 0, stop = 0
+  for (int st = blockIdx.x; st < S; st += gridDim.x) {
+    const int sq = st / p.hkv;
+    if (p.seq_lens[sq] <= 0) {
+      const size_t head0 = (size_t)sq * p.hq + (size_t)(st - sq * p.hkv) * p.g;
+      for (int i = threadIdx.x; i < p.g * D; i += blockDim.x) p.out[head0 * D + i] = 0.f;
+      if ((int)threadIdx.x < p.g) p.stop_block[head0 + threadIdx.x] = 0;
+    }
+  }
+
+  int cur = (int)(blockIdx.x % (unsigned)S);
+  bool ended = false;
+  if (w == CLW) {
+    lb_claim<Cf>(p, E, ent[0], qring[0], cur, ended, lane);
+    lb_claim<Cf>(p, E, ent[1], qring[1], cur, ended, lane);
+  }
+  lds_barrier();
+
+  // Step j: the claimer takes item j+2, block waves issue item j+1's loads
+  // and compute item j into buffer j % 2, scan waves fold item j-1 from
+  // buffer (j-1) % 2.  One LDS barrier per step; LDS entry e % 4 and query
+  // copy e % 4 hold item e from its claim (step e-2) to its fold (step e+1).
+  if (w < NS) {
+    bool err = false;
+    int ps = -1, pk = 0;  // item folded in the previous step
+    for (int j = 0;; ++j) {
+      if (w == 0 && lane == 0 && ps >= 0)
+        __hip_atomic_fetch_max(p.lb_prog + ps, (uint32_t)pk + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ps = -1;
+      if (w == CLW) lb_claim<Cf>(p, E, ent[(j + 2) & 3], qring[(j + 2) & 3], cur, ended, lane);
+      if (j >= 1) {
+        const int* e = ent[(j - 1) & 3];
+        const int s = e[0];
+        if (s >= 0) {
+          const int k = e[1], n = e[2];
+          const int nt = min(C, n - k * C);
+          const int ob = e[4 + slot];
+          const uint32_t sinkb = (uint32_t)__ballot(lane < nt && ob == 0) & 0xFFu;
+          const uint32_t stopped = ld_dev32(p.lb_heads + s);
+          const float* buf = part + ((j - 1) & 1) * Cf::SLOT;
+#pragma unroll
+          for (int kk = 0; kk < HPS; ++kk) {
+            const int h = w + NS * kk;
+            if (h < p.g) {
+              ChunkIn<Cf> in;
+              gather_lds<Cf>(in, buf, h, lane);
+              if (!lb_head<Cf>(p, E, s, k, n, h, in, sinkb, ((stopped >> h) & 1u) != 0u, lane)) err = true;
+            }
+          }
+          ps = s;
+          pk = k;
+        }
+      }
+      lds_barrier();
+      if (ent[j & 3][0] == LB_END) break;
+    }
+    (void)err;
+  } else {
+    const int bw = w - NS;
+    float* pbuf = pbuf_all[w];
+    BlockRegs<Cf> r0[1], r1[1];
+    float ks0 = 1.f, vs0 = 1.f, ks1 = 1.f, vs1 = 1.f;
+    // issue item j's loads (a bubble or the end re-reads page 0's first tile,
+    // so the loads stay unconditional and the compiler's waits exact)
+    auto issue = [&](int j, BlockRegs<Cf> (&rr)[1], float& ks, float& vs) {
+      const int* e = ent[j & 3];
+      const int s = e[0];
+      if (s >= 0) {
+        const int k = e[1], n = e[2], L = e[3];
+        const int kvh = s % p.hkv;
+        const int ob = e[4 + slot], pg = e[4 + C + slot];
+        const int nt = min(C, n - k * C);
+        issue_chunk_part<Cf, 1>(rr, p, kvh, L, ob, pg, nt, bw, lane);
+        if constexpr (KV == KV_FP8) {
+          ks = p.k_scale[(size_t)pg * p.hkv + kvh];
+          vs = p.v_scale[(size_t)pg * p.hkv + kvh];
+        }
+        if (bw == 0 && lane == 0)
+          __hip_atomic_fetch_add(p.lb_fetch + s, (uint32_t)nt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        issue_chunk_part<Cf, 1>(rr, p, 0, Cf::B, 0, 0, 1, bw, lane);
+        if constexpr (KV == KV_FP8) {
+          ks = p.k_scale[0];
+          vs = p.v_scale[0];
+        }
+      }
+    };
+    auto compute = [&](int j, const BlockRegs<Cf> (&rr)[1], float ks, float vs) {
+      const int* e = ent[j & 3];
+      if (e[0] >= 0) {
+        const int k = e[1], n = e[2], L = e[3];
+        uint4 qf[Cf::QF];
+        load_q_lds<Cf>(qring[j & 3], p.g, lane, qf);
+        block_phase<Cf, 1>(rr, qf, e[4 + slot], ks, vs, min(C, n - k * C), L, p.qk_log2, bw, lane,
+                           part + (j & 1) * Cf::SLOT, pbuf);
+      }
+    };
+    auto bstep = [&](int j, BlockRegs<Cf> (&rc)[1], float& ksc, float& vsc, BlockRegs<Cf> (&rn)[1], float& ksn,
+                     float& vsn) {
+      if constexpr (PFD >= 2) {
+        issue(j + 1, rn, ksn, vsn);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(j, rc, ksc, vsc);
+      } else {
+        compute(j, rc, ksc, vsc);
+        issue(j + 1, rc, ksc, vsc);
+      }
+      lds_barrier();
+      return ent[j & 3][0] != LB_END;
+    };
+    issue(0, r0, ks0, vs0);
+    for (int j = 0;; j += 2) {
+      if constexpr (PFD >= 2) {
+        if (!bstep(j, r0, ks0, vs0, r1, ks1, vs1)) break;
+        if (!bstep(j + 1, r1, ks1, vs1, r0, ks0, vs0)) break;
+      } else {
+        if (!bstep(j, r0, ks0, vs0, r0, ks0, vs0)) break;
+        if (!bstep(j + 1, r0, ks0, vs0, r0, ks0, vs0)) break;
+      }
+    }
+  }
+  // loads issued ahead may still be in flight
+  wait_all_memory();
+  // count this workgroup out; the last one publishes the fetched counts,
+  // clears the per-stream words and advances the epoch
+  lds_barrier();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(p.sched_ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_wg = prev == gridDim.x - 1 ? 1 : 0;
+  }
+  lds_barrier();
+  if (last_wg) {
+    for (int st = threadIdx.x; st < S; st += blockDim.x) {
+      const uint32_t f = ld_dev32(p.lb_fetch + st);
+      if (p.blocks_fetched) p.blocks_fetched[st] = (int32_t)f;
+      st_dev32(p.lb_fetch + st, 0u);
+      st_dev32(p.lb_claim + st, 0u);
+      st_dev32(p.lb_prog + st, 0u);
+      st_dev32(p.lb_heads + st, 0u);
+    }
+    wait_all_memory();
+    lds_barrier();
+    if (threadIdx.x == 0) {
+      st_dev32(p.sched_ctrl + 1, 0u);
+      st_dev32(p.sched_ctrl, E);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Full-attention split kernel
 // ---------------------------------------------------------------------------
 template <class Cf>

@@ -1,13 +1,39 @@
-// Instantiations of art_sched_kernel for KV storage F32 (one translation unit per
+// Instantiations of art_sched_kernel and art_lb_kernel for KV storage F32 (one translation unit per
 // storage type and kernel so that the build runs in parallel).
 #include "art_kernels_impl.h"
 
 namespace art {
 namespace {
 
+// Workgroups of the look-back kernel: one per resident slot (occupancy x
+// CUs of the current device, computed once per device), unless given.
+template <class K>
+int resident_slots(K kernel, int threads) {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    cache[dev] = per_cu * cus;
+  }
+  return cache[dev];
+}
+
 template <int D, int B, int GM>
 hipError_t go(const Params& p, hipStream_t st) {
-  hipLaunchKernelGGL((kern::art_sched_kernel<KV_F32, D, B, GM>), dim3(p.batch * p.hkv + p.helpers), dim3(64 * kern::Cfg<KV_F32, D, B, GM>::NWA), 0, st, p);
+  constexpr int threads = 64 * kern::Cfg<KV_F32, D, B, GM>::NWA;
+  if (p.lb) {
+    auto kernel = kern::art_lb_kernel<KV_F32, D, B, GM>;
+    long wgs = p.workers > 0 ? p.workers : resident_slots(kernel, threads);
+    const long items = (long)p.batch * p.hkv * p.max_chunks;
+    if (wgs > items) wgs = items;
+    if (wgs < 1) wgs = 1;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(threads), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((kern::art_sched_kernel<KV_F32, D, B, GM>), dim3(p.batch * p.hkv + p.helpers), dim3(threads), 0, st, p);
+  }
   return hipGetLastError();
 }
 

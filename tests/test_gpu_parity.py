@@ -217,17 +217,27 @@ def test_full_size_sampled(w):
     check_full(case, sample=24)
 
 
-# ---- the workgroup scheduler ----------------------------------------------------------------------------
+# ---- the workgroup schedulers ---------------------------------------------------------------------------
 #
-# Partials are computed by the same code whichever workgroup (scanner or helper) takes a chunk, and the
-# scanner folds them in visit order, so results must be bit-identical across scheduling configurations.
+# Look-back scheduler (default): the state entering a chunk is always the anchor's inclusive state combined
+# with the aggregates after it in chunk order, so for a given anchor spacing the results are bit-identical
+# whatever the number of workers, the window or the timing.  Scanners: partials are computed by the same code
+# whichever workgroup (scanner or helper) takes a chunk and the scanner folds them in visit order, so results
+# are bit-identical across helper configurations.
 
-SCHED_VARIANTS = [
-    dict(ART_HELPERS="0"),                                    # scanners only
-    dict(ART_HELPERS="-1"),                                   # default helper count
-    dict(ART_HELPERS="2000", ART_RING="2", ART_LOOKAHEAD="2"),  # many helpers, tight ring
-    dict(ART_HELPERS="64", ART_RING="1", ART_LOOKAHEAD="1"),    # one slot per stream
-    dict(ART_HELPERS="300", ART_RING="16", ART_LOOKAHEAD="16"),  # deep speculation
+LB_VARIANTS = [
+    dict(ART_SCHED="lb"),                                     # defaults
+    dict(ART_SCHED="lb", ART_WORKERS="1"),                    # one worker: every item in claim order
+    dict(ART_SCHED="lb", ART_WINDOW="1"),                     # one chunk past the resolved frontier
+    dict(ART_SCHED="lb", ART_WINDOW="2", ART_WORKERS="3"),
+    dict(ART_SCHED="lb", ART_WINDOW="32", ART_WORKERS="5000"),  # more workgroups than resident slots
+]
+SCAN_VARIANTS = [
+    dict(ART_SCHED="scan", ART_HELPERS="0"),                  # scanners only
+    dict(ART_SCHED="scan", ART_HELPERS="-1"),                 # default helper count
+    dict(ART_SCHED="scan", ART_HELPERS="2000", ART_RING="2", ART_LOOKAHEAD="2"),  # many helpers, tight ring
+    dict(ART_SCHED="scan", ART_HELPERS="64", ART_RING="1", ART_LOOKAHEAD="1"),    # one slot per stream
+    dict(ART_SCHED="scan", ART_HELPERS="300", ART_RING="16", ART_LOOKAHEAD="16"),  # deep speculation
 ]
 
 
@@ -246,19 +256,21 @@ def _with_env(env, fn):
                 os.environ[k] = v
 
 
-@pytest.mark.parametrize("w,kw", [(W.LLAMA3_8B, dict(batch=3, context=8192 - 40)),
-                                  (W.RAGGED, dict(batch=3)),
-                                  (W.QWEN_FP8, dict(batch=2, context=16384 - 3))],
-                         ids=["llama", "ragged", "fp8"])
-def test_scheduler_variants_bit_identical(w, kw):
+SCHED_CASES = [(W.LLAMA3_8B, dict(batch=3, context=8192 - 40)), (W.RAGGED, dict(batch=3)),
+               (W.QWEN_FP8, dict(batch=2, context=16384 - 3)), (W.LONG, dict(batch=1, context=131072 - 17))]
+
+
+@pytest.mark.parametrize("variants", [LB_VARIANTS, SCAN_VARIANTS], ids=["lookback", "scanners"])
+@pytest.mark.parametrize("w,kw", SCHED_CASES, ids=["llama", "ragged", "fp8", "long"])
+def test_scheduler_variants_bit_identical(w, kw, variants):
     case = synth.make_case(w, **kw)
     em, ed, p = case["eps_mag"], case["eps_dir"], case["patience"]
     ref = None
-    for env in SCHED_VARIANTS:
+    for env in variants:
         print(f"[sched] {case['workload']} {env}", flush=True)
         out, stop, fetched = _with_env(env, lambda: _device_run(case, em, ed, p))
         if ref is None:
-            rep, ref_out, ref_stop, _ = check_art(case)
+            rep, ref_out, ref_stop, _ = _with_env(env, lambda: check_art(case))
             assert np.array_equal(ref_out, out) and np.array_equal(ref_stop, stop)
             ref = (out, stop)
         else:
@@ -270,9 +282,17 @@ def test_scheduler_variants_bit_identical(w, kw):
         assert np.all(fetched >= grp_max) and np.all(fetched <= n[:, None]), env
 
 
+@pytest.mark.parametrize("anchor", ["1", "3", "32"])
+def test_lookback_anchor_spacing(anchor):
+    """Other anchor spacings change the rounding order of the state entering a chunk, not the method."""
+    case = synth.make_case(W.LLAMA3_8B, batch=2, context=8192 - 40)
+    _with_env(dict(ART_SCHED="lb", ART_ANCHOR=anchor, ART_WINDOW="16"), lambda: check_art(case))
+
+
 def test_scheduler_epoch_advances_and_no_error():
-    """With helpers, every call advances the stored epoch by one and leaves the finished-workgroup counter at
-    0 and the error flag clear; without helpers the scheduler words are not touched."""
+    """The look-back scheduler and scanners with helpers advance the stored epoch by one per call and leave
+    the finished-workgroup counter at 0 and the error flag clear; scanners without helpers do not touch the
+    scheduler words.  Repeated calls give identical results."""
     import torch
 
     from kv_cache_run_amd import art
@@ -288,7 +308,7 @@ def test_scheduler_epoch_advances_and_no_error():
                                                    dev["block_order"], dev["seq_lens"], case["eps_mag"],
                                                    case["eps_dir"], case["patience"]))
             torch.cuda.synchronize()
-            ctrl = dec.workspace[:12].view(torch.int32).cpu().numpy()
+            ctrl = dec.workspace[:16].view(torch.int32).cpu().numpy()
             assert ctrl[0] == expect_epoch(i), ctrl   # stored epoch
             assert ctrl[1] == 0, ctrl                 # finished-workgroup counter back to 0
             assert ctrl[2] == 0, ctrl                 # no bounded wait ran out
@@ -297,6 +317,7 @@ def test_scheduler_epoch_advances_and_no_error():
             assert torch.equal(o, outs[0][0]) and torch.equal(s_, outs[0][1])
         return outs[0]
 
-    a = run(dict(ART_HELPERS="64"), lambda i: i + 1)
-    b = run(dict(ART_HELPERS="0"), lambda i: 0)
+    run(dict(ART_SCHED="lb"), lambda i: i + 1)
+    a = run(dict(ART_SCHED="scan", ART_HELPERS="64"), lambda i: i + 1)
+    b = run(dict(ART_SCHED="scan", ART_HELPERS="0"), lambda i: 0)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
