@@ -63,9 +63,9 @@ art_status check_desc(const art_decode_desc* d) {
 // "auto" (default): the look-back scheduler when the streams are few (at
 // most half the CUs) and long (at least 256 chunks), where scanners would
 // leave most CUs idle for a long walk; scanners otherwise.
-// Look-back: ART_WINDOW chunks claimable past a stream's resolved frontier,
-// ART_WORKERS workgroups (0: one per resident slot), ART_ANCHOR chunks per
-// published inclusive state (results depend on it, not on the other knobs).  Scanners: ART_RING
+// Look-back: ART_WINDOW chunks claimable past a stream's resolved frontier
+// (0: 1/16 of the longest stream's chunks, clamped to 8 .. 32), ART_WORKERS
+// workgroups (0: one per resident slot); results do not depend on either.  Scanners: ART_RING
 // slots per stream, ART_LOOKAHEAD initial helper window, ART_HELPERS helper
 // workgroups (default 0; -1: enough to reach ART_TARGET_WGS workgroups in
 // total).  ART_SPIN_LIMIT bounds every wait loop.  The workspace size depends
@@ -76,7 +76,7 @@ int env_int(const char* name, int def, int lo, int hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }
 struct Knobs {
-  int ring, lookahead, helpers, target, lb, window, workers, anchor;
+  int ring, lookahead, helpers, target, lb, window, workers;
 };
 enum { SCHED_SCAN = 0, SCHED_LB = 1, SCHED_AUTO = 2 };
 Knobs knobs() {
@@ -84,8 +84,8 @@ Knobs knobs() {
   const int mode = !sched || strcmp(sched, "auto") == 0 ? SCHED_AUTO : (strcmp(sched, "lb") == 0 ? SCHED_LB : SCHED_SCAN);
   const Knobs k = {env_int("ART_RING", 8, 1, 64),          env_int("ART_LOOKAHEAD", 3, 1, 64),
                    env_int("ART_HELPERS", 0, -1, 1 << 16), env_int("ART_TARGET_WGS", 512, 1, 1 << 16),
-                   mode,                                    env_int("ART_WINDOW", 32, 1, 32),
-                   env_int("ART_WORKERS", 0, 0, 1 << 20),   env_int("ART_ANCHOR", 8, 1, 32)};
+                   mode,                                    env_int("ART_WINDOW", 0, 0, 32),
+                   env_int("ART_WORKERS", 0, 0, 1 << 20)};
   return k;
 }
 
@@ -111,8 +111,8 @@ art::WorkspacePlan plan_workspace(const art_decode_desc* d) {
   w.helpers = (int)h;
   w.max_chunks = (int)max_chunks;
   w.rec_floats = 2 * (d->head_dim + 4);
-  w.window = k.window;
-  w.anchor = k.anchor;
+  // default window: 1/16 of the longest stream's chunks, 8 .. 32
+  w.window = k.window > 0 ? k.window : (int)(max_chunks / 16 < 8 ? 8 : (max_chunks / 16 > 32 ? 32 : max_chunks / 16));
   // Control words and counters never share memory with another mode's data:
   // [0] stored epoch, [1] finished workgroups, [2] error flag; look-back
   // counters and epoch-tagged words; scanner words; then one data region
@@ -252,9 +252,8 @@ art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_
     p.max_chunks = wp.max_chunks;
     p.rec_floats = wp.rec_floats;
     p.window = wp.window;
-    p.anchor = wp.anchor;
     const Knobs k = knobs();
-    // the look-back records hold pass counts up to 4095; its claim sweep
+    // the look-back records hold pass counts up to 2047; its claim sweep
     // packs a stream index in 16 bits
     const long streams = (long)desc->batch * desc->num_kv_heads;
     bool lb = k.lb == SCHED_LB;
@@ -264,7 +263,7 @@ art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_
         cus = 256;
       lb = 2 * streams <= cus && wp.max_chunks >= 256;
     }
-    p.lb = (lb && patience <= 4095 && streams <= 65535) ? 1 : 0;
+    p.lb = (lb && patience <= 2047 && streams <= 65535) ? 1 : 0;
     p.workers = k.workers;
     e = v.kv == art::KV_F32 ? art::launch_art_f32(v, p, static_cast<hipStream_t>(stream))
         : v.kv == art::KV_BF16 ? art::launch_art_bf16(v, p, static_cast<hipStream_t>(stream))

@@ -55,8 +55,7 @@ struct Params {
   float* lb_rec;                       // [streams][max_chunks][g][rec_floats]
   int32_t max_chunks;                  // ceil(max_blocks / chunk)
   int32_t rec_floats;                  // 2 * (D + 4)
-  int32_t window;                      // chunks claimable past the resolved frontier (<= 32)
-  int32_t anchor;                      // every anchor-th chunk publishes its inclusive state (<= 32)
+  int32_t window;                      // chunks claimable past the resolved frontier (1..32)
   int32_t lb;                          // 1: launch art_lb_kernel, 0: scanners (+ helpers)
   int32_t workers;                     // art_lb_kernel workgroups (0: one per resident slot)
   int32_t batch, hq, hkv, g;
@@ -90,7 +89,7 @@ SplitPlan full_split_plan(int batch, int hkv, int max_blocks);
 struct WorkspacePlan {
   size_t lb_fetch, lb_claim, lb_prog, lb_heads, lb_st;  // look-back scheduler
   size_t claim, done, ready, data, total;               // scanner + helpers; data: ring | records | full partials
-  int ring, slot_floats, helpers, lookahead, max_chunks, rec_floats, window, anchor;
+  int ring, slot_floats, helpers, lookahead, max_chunks, rec_floats, window;
 };
 
 // Launchers; return hipSuccess or the launch error.  One translation unit per

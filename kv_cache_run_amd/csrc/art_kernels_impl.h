@@ -1361,13 +1361,14 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_sched_kerne
 // look-back over an associative combine):
 //   * (M, L, A): the online-softmax state is a monoid under
 //     (M1, L1, A1) + (M2, L2, A2) = (M, 2^(M1-M) L1 + 2^(M2-M) L2, same for A),
-//     M = max(M1, M2).  Every `anchor`-th chunk (k % anchor == anchor - 1)
-//     publishes its inclusive state, the other chunks their own aggregate;
-//     the state entering chunk k is the inclusive state of the anchor before
-//     it combined with the aggregates of the chunks in between, always in
-//     chunk order, so the arithmetic (and every result) is the same whatever
-//     the timing, the number of workers or the window.  The anchors form the
-//     only chain: one hand-off per `anchor` chunks.
+//     M = max(M1, M2).  Each chunk publishes its own aggregate G_k (folded
+//     from its blocks) and its inclusive state I_k = X_k + G_k; the state
+//     entering chunk k is X_k = (((I_j + G_{j+1}) + G_{j+2}) + ... + G_{k-1})
+//     for the nearest chunk j whose inclusive state is out (X_0 = empty).
+//     Since every I_j is itself that left fold of G_0 .. G_j, the result has
+//     the same bits whichever j a chunk starts from: results do not depend on
+//     the timing, the number of workers or the window, and no chunk waits on
+//     a chain of other chunks' look-backs -- only on aggregates.
 //   * The detector's inputs at the chunk's first position need only the
 //     output O = A / L entering it, so the statistics of all C positions (and
 //     their pass bits) follow from that state alone.
@@ -1384,7 +1385,8 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_sched_kerne
 // the earliest unfinished item can always proceed -- whether or not every
 // worker is resident.
 //
-// Claims: a worker first tries the stream of its last item, else sweeps all
+// Claims: a worker stays on the stream of its last item while that stream
+// has unclaimed chunks (waiting while its window is full), else sweeps all
 // streams and takes one of those with the most unclaimed chunks (ties spread
 // over the workers by a hash).  Chunk k of a stream is claimable while
 // k < resolved + window, where resolved is one past the highest chunk whose
@@ -1393,21 +1395,24 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_sched_kerne
 // about `window` chunks of it (the look-back waits otherwise).
 //
 // Record of (stream, chunk, head): a status word tag(E, payload) with
-//   bits 0-1   level: 1 aggregate, 2 pass bits (+ inclusive state for an
-//              anchor), 3 resolved
-//   bits 2-9   pass bits of the chunk's positions          (level >= 2)
-//   bits 10-17 positions holding block 0                   (level >= 2)
-//   bit 18     head still running after the chunk          (level 3)
-//   bit 19     block 0 folded by the end of the chunk      (level 3)
-//   bits 20-31 passes in a row at the chunk end, at most the patience (level 3)
-// and floats: aggregate [A(D), m, l] at 0 (chunks other than anchors),
-// inclusive [A(D), M, L] at D + 4 (anchors).
+//   bits 0-2   level: 1 aggregate, 2 inclusive state, 3 pass bits, 4 resolved
+//              (a chunk can skip level 1 when its inclusive state follows at
+//              once; a dropped chunk goes straight to 4)
+//   bits 3-10  pass bits of the chunk's positions          (level >= 3)
+//   bits 11-18 positions holding block 0                   (level >= 3)
+//   bit 19     head still running after the chunk          (level 4)
+//   bit 20     block 0 folded by the end of the chunk      (level 4)
+//   bits 21-31 passes in a row at the chunk end, at most the patience (level 4)
+// and floats: aggregate [A(D), m, l] at 0, inclusive [A(D), M, L] at D + 4.
 // Data is stored with device-scope stores and the status after them
 // (s_waitcnt vmcnt(0) in between); readers load the status, then the data.
 
-constexpr uint32_t LB_AGG = 1u, LB_INCL = 2u, LB_FIN = 3u;
-constexpr uint32_t LB_RUNNING = 1u << 18, LB_SINKED = 1u << 19;
-constexpr uint32_t LB_BEFORE = LB_FIN | LB_RUNNING;  // the state before chunk 0
+constexpr uint32_t LB_AGG = 1u, LB_INCL = 2u, LB_PASS = 3u, LB_FIN = 4u;
+constexpr uint32_t LB_LEVEL = 7u;
+constexpr int LB_PASS_SH = 3, LB_SINK_SH = 11, LB_CNT_SH = 21;
+constexpr uint32_t LB_RUNNING = 1u << 19, LB_SINKED = 1u << 20;
+constexpr uint32_t LB_BEFORE = LB_FIN | LB_RUNNING;  // the state before chunk 0 (its inclusive state: empty)
+constexpr int LB_CNT_MAX = 2047;
 constexpr int LB_ENT = 24;                          // ints per LDS item entry: s, k, n, L, ob[8], pg[8]
 constexpr int LB_BUBBLE = -1, LB_END = -2;
 
@@ -1573,7 +1578,7 @@ __device__ bool lb_head(const Params& p, uint32_t E, int s, int k, int n, int h,
   const int nt = min(C, n - k * C);
   const int t0 = k * C;
   const int nch = (n + C - 1) / C;
-  const int window = p.window;
+  const int lbw = min(64, 2 * p.window);  // chunks a look-back examines
   const u64* st0 = p.lb_st + (size_t)s * p.max_chunks * g + h;  // chunk stride g
   u64* stw = p.lb_st + ((size_t)s * p.max_chunks + k) * g + h;
   const size_t rstride = (size_t)g * p.rec_floats;
@@ -1581,50 +1586,66 @@ __device__ bool lb_head(const Params& p, uint32_t E, int s, int k, int n, int h,
   float* rec = p.lb_rec + (((size_t)s * p.max_chunks + k) * g + h) * p.rec_floats;
   const size_t head = (size_t)(s / p.hkv) * p.hq + (size_t)(s % p.hkv) * g + h;
   const int incl = Cf::D + 4;
-  const int cap = min(p.patience, 4095);
+  const int cap = min(p.patience, LB_CNT_MAX);
+  const bool last = k == nch - 1;  // no chunk after it reads its records
   if (dead) {
-    if (lane == 0) st_dev(stw, tag_word(E, LB_FIN | (sinkb << 10)));
+    if (lane == 0) st_dev(stw, tag_word(E, LB_FIN | (sinkb << LB_SINK_SH)));
     return true;
   }
 
-  // ---- state entering the chunk: the inclusive state of the anchor before
-  // it (every `anchor`-th chunk) combined with the aggregates after that, in
-  // chunk order -- a fixed order, so results do not depend on timing
-  const int r = k % p.anchor;
-  const bool is_anchor = r == p.anchor - 1;
+  // ---- the chunk's own aggregate
+  float gm, gl, ga[DPL];
+  lb_aggregate<Cf>(in, gm, gl, ga);
+
+  // ---- state entering the chunk: nearest published inclusive state (lane f
+  // examines chunk k-1-f), then the aggregates after it in chunk order; the
+  // aggregate is published first unless that state can be had at once
   LbState<Cf> x;
   x.M = NEG_INF;
   x.L = 0.f;
 #pragma unroll
   for (int j = 0; j < DPL; ++j) x.A[j] = 0.f;
   bool ok = true;
-  if (!is_anchor && k < nch - 1) {
-    float m, l, a[DPL];
-    lb_aggregate<Cf>(in, m, l, a);
-    lb_store<Cf>(rec, lane, m, l, a);
-    wait_all_memory();
-    if (lane == 0) st_dev(stw, tag_word(E, LB_AGG));
-  }
+  int f = 0;
   if (k > 0) {
-    // lanes i < r: chunk k-1-i needs its aggregate; lane r: the anchor k-1-r
-    // (or the state before chunk 0) needs its inclusive state
+    bool published = last;
     for (int spin = 0;; ++spin) {
-      const uint32_t v = lb_probe(st0, g, k, r + 1, E, lane);
-      const bool ready = lane < r ? (v & 3u) >= LB_AGG : (lane == r ? (v & 3u) >= LB_INCL : true);
-      if (__ballot(!ready) == 0ull) break;
+      const uint32_t v = lb_probe(st0, g, k, lbw, E, lane);
+      const u64 inc = __ballot((v & LB_LEVEL) >= LB_INCL);
+      if (inc != 0ull) {
+        f = __builtin_ctzll(inc);
+        const u64 need = (1ull << f) - 1ull;
+        if ((__ballot((v & LB_LEVEL) >= LB_AGG) & need) == need) break;
+      }
+      if (!published) {
+        lb_store<Cf>(rec, lane, gm, gl, ga);
+        wait_all_memory();
+        if (lane == 0) st_dev(stw, tag_word(E, LB_AGG));
+        published = true;
+      }
       if (lb_give_up(p, E, spin)) { ok = false; break; }
       __builtin_amdgcn_s_sleep(1);
     }
     if (ok) {
-      const int jb = k - 1 - r;
+      const int jb = k - 1 - f;
       if (jb >= 0) lb_load<Cf>(rec0 + (size_t)jb * rstride + incl, lane, x.M, x.L, x.A);
-      for (int i = r - 1; i >= 0; --i) {
+      for (int i = f - 1; i >= 0; --i) {
         float m, l, a[DPL];
         lb_load<Cf>(rec0 + (size_t)(k - 1 - i) * rstride, lane, m, l, a);
         lb_combine<Cf>(x, m, l, a);
       }
     }
   }
+  // ---- publish the inclusive state X_k + G_k
+  if (ok && !last) {
+    LbState<Cf> xi = x;
+    lb_combine<Cf>(xi, gm, gl, ga);
+    lb_store<Cf>(rec + incl, lane, xi.M, xi.L, xi.A);
+    wait_all_memory();
+    if (lane == 0) st_dev(stw, tag_word(E, LB_INCL));
+  }
+
+  // ---- statistics of every position
   float Op[DPL];
   float np = 0.f;
   {
@@ -1637,39 +1658,32 @@ __device__ bool lb_head(const Params& p, uint32_t E, int s, int k, int n, int h,
     }
     np = xreduce<1>(sq, lane);
   }
-
-  // ---- statistics of every position; publish the inclusive state
   float oo[C][DPL];
   const u64 pass = lb_stats<Cf>(x, Op, np, in, t0, nt, p, lane, oo);
   const uint32_t passb = (uint32_t)pass & 0xFFu;
-  if (ok) {
-    if (is_anchor) {
-      lb_store<Cf>(rec + incl, lane, x.M, x.L, x.A);
-      wait_all_memory();
-    }
-    if (lane == 0) st_dev(stw, tag_word(E, LB_INCL | (passb << 2) | (sinkb << 10)));
-  }
+  const uint32_t bits = (passb << LB_PASS_SH) | (sinkb << LB_SINK_SH);
+  if (ok && lane == 0 && !last) st_dev(stw, tag_word(E, LB_PASS | bits));
 
-  // ---- pass count, block-0 flag and running flag entering the chunk
+  // ---- pass count, block-0 flag and running flag entering the chunk:
+  // replayed from the nearest resolved chunk over the pass bits after it
   int cnt = 0;
   bool sink = false, alive = true;
   if (ok && k > 0) {
-    int f = 0;
     uint32_t v = 0;
     for (int spin = 0;; ++spin) {
-      v = lb_probe(st0, g, k, window, E, lane);
-      const u64 fin = __ballot((v & 3u) == LB_FIN);
+      v = lb_probe(st0, g, k, lbw, E, lane);
+      const u64 fin = __ballot((v & LB_LEVEL) == LB_FIN);
       if (fin != 0ull) {
         f = __builtin_ctzll(fin);
         const u64 need = (1ull << f) - 1ull;
-        if ((__ballot((v & 3u) >= LB_INCL) & need) == need) break;
+        if ((__ballot((v & LB_LEVEL) >= LB_PASS) & need) == need) break;
       }
       if (lb_give_up(p, E, spin)) { ok = false; break; }
       __builtin_amdgcn_s_sleep(1);
     }
     if (ok) {
       const uint32_t wf = (uint32_t)readlane((int)v, f);
-      cnt = (int)(wf >> 20);
+      cnt = (int)(wf >> LB_CNT_SH);
       sink = (wf & LB_SINKED) != 0u;
       alive = (wf & LB_RUNNING) != 0u;
       for (int i = f - 1; i >= 0 && alive; --i) {
@@ -1677,8 +1691,8 @@ __device__ bool lb_head(const Params& p, uint32_t E, int s, int k, int n, int h,
         const int ci = k - 1 - i;
         const int nti = min(C, n - ci * C);
         for (int t = 0; t < nti; ++t) {
-          cnt = ((wi >> (2 + t)) & 1u) ? min(cnt + 1, cap) : 0;
-          sink = sink || ((wi >> (10 + t)) & 1u);
+          cnt = ((wi >> (LB_PASS_SH + t)) & 1u) ? min(cnt + 1, cap) : 0;
+          sink = sink || ((wi >> (LB_SINK_SH + t)) & 1u);
           if (cnt >= p.patience && sink) { alive = false; break; }
         }
       }
@@ -1708,7 +1722,7 @@ __device__ bool lb_head(const Params& p, uint32_t E, int s, int k, int n, int h,
     for (int j = 0; j < DPL; ++j) out_row[DPL * lane + j] = ov[j];
     if (lane == 0) p.stop_block[head] = t0 + stop_t + 1;
     alive_out = false;
-  } else if (alive_out && k == nch - 1) {
+  } else if (alive_out && last) {
     // never stopped: the output after all n blocks
 #pragma unroll
     for (int j = 0; j < DPL; ++j) out_row[DPL * lane + j] = Op[j];
@@ -1725,8 +1739,8 @@ __device__ bool lb_head(const Params& p, uint32_t E, int s, int k, int n, int h,
   const int cnt_out = readlane(min(cnt_t, cap), nt - 1);
   const bool sink_out = readlane(sink_t ? 1 : 0, nt - 1) != 0;
   if (lane == 0) {
-    st_dev(stw, tag_word(E, LB_FIN | (passb << 2) | (sinkb << 10) | (alive_out ? LB_RUNNING : 0u) |
-                                (sink_out ? LB_SINKED : 0u) | ((uint32_t)cnt_out << 20)));
+    st_dev(stw, tag_word(E, LB_FIN | bits | (alive_out ? LB_RUNNING : 0u) | (sink_out ? LB_SINKED : 0u) |
+                                ((uint32_t)cnt_out << LB_CNT_SH)));
     if (fire != 0ull || !ok) {
       // mark the head stopped; close the stream when the whole group is
       const uint32_t bit = 1u << h;
@@ -1759,18 +1773,22 @@ __device__ void lb_claim(const Params& p, uint32_t E, int* e, char* qdst, int& c
       k = (uint32_t)readlane((int)k, 0);
       return ((k & CLAIM_FIN) || (int)k >= nch_of(st)) ? -1 : (int)k;
     };
-    // the current stream first
+    // the current stream while it has unclaimed chunks (waiting while its
+    // window is full), so that a stream's chunks stay on a fixed set of
+    // workers and an item never queues behind another stream's
+    bool stay = false;
     if (cur >= 0) {
       const uint32_t cv = ld_dev32(p.lb_claim + cur);
       const uint32_t prog = ld_dev32(p.lb_prog + cur);
-      if (!(cv & CLAIM_FIN) && (int)cv < nch_of(cur) && cv < prog + (uint32_t)p.window) {
+      stay = !(cv & CLAIM_FIN) && (int)cv < nch_of(cur);
+      if (stay && cv < prog + (uint32_t)p.window) {
         const int k = take(cur);
         if (k >= 0) { got_s = cur; got_k = k; }
       }
     }
     // else a claimable stream: most unclaimed chunks first (counted up to
     // 16), ties spread over the workers
-    if (got_s < 0) {
+    if (got_s < 0 && !stay) {
       uint32_t best = 0u;  // (min(remaining, 16) << 24) | (hash << 16) | stream, 0 = none
       bool live_any = false;
       const uint32_t hw = (blockIdx.x * 2654435761u) >> 24;

@@ -219,9 +219,9 @@ def test_full_size_sampled(w):
 
 # ---- the workgroup schedulers ---------------------------------------------------------------------------
 #
-# Look-back scheduler (default): the state entering a chunk is always the anchor's inclusive state combined
-# with the aggregates after it in chunk order, so for a given anchor spacing the results are bit-identical
-# whatever the number of workers, the window or the timing.  Scanners: partials are computed by the same code
+# Look-back scheduler: the state entering a chunk is the left fold of the chunk aggregates before it,
+# whichever published inclusive state the look-back starts from, so the results are bit-identical whatever the
+# number of workers, the window or the timing.  Scanners: partials are computed by the same code
 # whichever workgroup (scanner or helper) takes a chunk and the scanner folds them in visit order, so results
 # are bit-identical across helper configurations.
 
@@ -280,13 +280,6 @@ def test_scheduler_variants_bit_identical(w, kw, variants):
         g = case["num_q_heads"] // case["num_kv_heads"]
         grp_max = stop.reshape(case["batch"], case["num_kv_heads"], g).max(axis=2)
         assert np.all(fetched >= grp_max) and np.all(fetched <= n[:, None]), env
-
-
-@pytest.mark.parametrize("anchor", ["1", "3", "32"])
-def test_lookback_anchor_spacing(anchor):
-    """Other anchor spacings change the rounding order of the state entering a chunk, not the method."""
-    case = synth.make_case(W.LLAMA3_8B, batch=2, context=8192 - 40)
-    _with_env(dict(ART_SCHED="lb", ART_ANCHOR=anchor, ART_WINDOW="16"), lambda: check_art(case))
 
 
 def test_scheduler_epoch_advances_and_no_error():
