@@ -300,7 +300,11 @@ def main(argv=None) -> int:
 
     head = results.get("art") or next(iter(results.values()))
     head_mode = "art" if "art" in results else next(iter(results))
-    kname = "art_sched_kernel" if head_mode == "art" else "full_split_kernel"
+    if head_mode == "art":
+        desc = art.make_desc(dev["q"], dev["k_pages"], dev["block_table"])
+        kname = art.KERNEL_NAMES[art.art_decode_kernel_choice(desc, case["eps_mag"], case["eps_dir"], case["patience"])]
+    else:
+        kname = "full_split_kernel"
     traffic = read_traffic(kname, w.name)
     roofline = {
         "bound": "hbm",

@@ -155,6 +155,17 @@ const char* art_status_string(art_status status);
 /* Library version as major*10000 + minor*100 + patch. */
 int32_t art_decode_version(void);
 
+/* Which kernel art_decode would run for these arguments (host only; the
+ * environment knob ART_SCHED and the current device's CU count are read as
+ * art_decode reads them):
+ *   ART_KERNEL_FULL      full attention (ART_FLAG_FULL, or a zero threshold
+ *                        without ART_FLAG_KEEP_DETECTOR),
+ *   ART_KERNEL_SCANNERS  one scanner workgroup per stream,
+ *   ART_KERNEL_LOOKBACK  the look-back scheduler,
+ * or minus the art_status art_decode would return for rejected arguments. */
+enum { ART_KERNEL_FULL = 0, ART_KERNEL_SCANNERS = 1, ART_KERNEL_LOOKBACK = 2 };
+int32_t art_decode_kernel_choice(const art_decode_desc* desc, float eps_mag, float eps_dir, int32_t patience);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,10 @@ ART_DTYPE_F32, ART_DTYPE_BF16, ART_DTYPE_FP8_E4M3FN = range(3)
 ART_FLAG_NONE, ART_FLAG_FULL, ART_FLAG_KEEP_DETECTOR = 0, 1, 2
 
 EXPORTED = ("art_decode_workspace_bytes", "art_decode_workspace_init", "art_decode", "art_status_string",
-            "art_decode_version")
+            "art_decode_version", "art_decode_kernel_choice")
+ART_KERNEL_FULL, ART_KERNEL_SCANNERS, ART_KERNEL_LOOKBACK = 0, 1, 2
+KERNEL_NAMES = {ART_KERNEL_FULL: "full_split_kernel", ART_KERNEL_SCANNERS: "art_sched_kernel",
+                ART_KERNEL_LOOKBACK: "art_lb_kernel"}
 
 
 class ArtDecodeDesc(ctypes.Structure):
@@ -70,6 +73,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.art_status_string.restype = ctypes.c_char_p
     lib.art_decode_version.argtypes = []
     lib.art_decode_version.restype = i32
+    lib.art_decode_kernel_choice.argtypes = [ctypes.POINTER(ArtDecodeDesc), f32, f32, i32]
+    lib.art_decode_kernel_choice.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -81,6 +86,14 @@ def art_status_string(status: int) -> str:
 
 def art_decode_version() -> int:
     return int(load_library().art_decode_version())
+
+
+def art_decode_kernel_choice(desc: ArtDecodeDesc, eps_mag: float, eps_dir: float, patience: int) -> int:
+    """ART_KERNEL_* that art_decode would run for these arguments (raises ArtError if it would reject them)."""
+    r = int(load_library().art_decode_kernel_choice(ctypes.byref(desc), float(eps_mag), float(eps_dir), int(patience)))
+    if r < 0:
+        _check(-r)
+    return r
 
 
 def _check(status: int) -> None:

@@ -146,6 +146,26 @@ art::WorkspacePlan plan_workspace(const art_decode_desc* d) {
   return w;
 }
 
+// Terminating kernel for a valid call: look-back scheduler or scanners.
+bool use_lookback(const art_decode_desc* d, const art::WorkspacePlan& wp, int32_t patience) {
+  const Knobs k = knobs();
+  // the look-back records hold pass counts up to 2047; its claim sweep
+  // packs a stream index in 16 bits
+  const long streams = (long)d->batch * d->num_kv_heads;
+  bool lb = k.lb == SCHED_LB;
+  if (k.lb == SCHED_AUTO) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+    lb = 2 * streams <= cus && wp.max_chunks >= 256;
+  }
+  return lb && patience <= 2047 && streams <= 65535;
+}
+
+bool full_mode(const art_decode_desc* d, float eps_mag, float eps_dir) {
+  return (d->flags & ART_FLAG_FULL) || ((eps_mag == 0.f || eps_dir == 0.f) && !(d->flags & ART_FLAG_KEEP_DETECTOR));
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,8 +207,7 @@ art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_
   }
   if (desc->batch == 0) return ART_OK;
 
-  const bool full = (desc->flags & ART_FLAG_FULL) ||
-                    ((eps_mag == 0.f || eps_dir == 0.f) && !(desc->flags & ART_FLAG_KEEP_DETECTOR));
+  const bool full = full_mode(desc, eps_mag, eps_dir);
   const int g = desc->num_q_heads / desc->num_kv_heads;
   art::Variant v;
   v.kv = desc->kv_dtype == ART_DTYPE_F32 ? art::KV_F32 : (fp8 ? art::KV_FP8 : art::KV_BF16);
@@ -252,19 +271,8 @@ art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_
     p.max_chunks = wp.max_chunks;
     p.rec_floats = wp.rec_floats;
     p.window = wp.window;
-    const Knobs k = knobs();
-    // the look-back records hold pass counts up to 2047; its claim sweep
-    // packs a stream index in 16 bits
-    const long streams = (long)desc->batch * desc->num_kv_heads;
-    bool lb = k.lb == SCHED_LB;
-    if (k.lb == SCHED_AUTO) {
-      int dev = 0, cus = 0;
-      if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
-      lb = 2 * streams <= cus && wp.max_chunks >= 256;
-    }
-    p.lb = (lb && patience <= 2047 && streams <= 65535) ? 1 : 0;
-    p.workers = k.workers;
+    p.lb = use_lookback(desc, wp, patience) ? 1 : 0;
+    p.workers = knobs().workers;
     e = v.kv == art::KV_F32 ? art::launch_art_f32(v, p, static_cast<hipStream_t>(stream))
         : v.kv == art::KV_BF16 ? art::launch_art_bf16(v, p, static_cast<hipStream_t>(stream))
                                : art::launch_art_fp8(v, p, static_cast<hipStream_t>(stream));
@@ -283,6 +291,14 @@ const char* art_status_string(art_status s) {
   return "ART: unknown status";
 }
 
-int32_t art_decode_version(void) { return 100; }
+int32_t art_decode_version(void) { return 200; }
+
+int32_t art_decode_kernel_choice(const art_decode_desc* desc, float eps_mag, float eps_dir, int32_t patience) {
+  const art_status ds = check_desc(desc);
+  if (ds != ART_OK) return -(int32_t)ds;
+  if (!(eps_mag >= 0.f) || !(eps_dir >= 0.f) || patience < 1) return -(int32_t)ART_ERR_INVALID_ARG;
+  if (full_mode(desc, eps_mag, eps_dir)) return ART_KERNEL_FULL;
+  return use_lookback(desc, plan_workspace(desc), patience) ? ART_KERNEL_LOOKBACK : ART_KERNEL_SCANNERS;
+}
 
 }  // extern "C"

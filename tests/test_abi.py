@@ -95,3 +95,23 @@ def test_workspace_size_query(lib):
     assert art.art_decode_workspace_bytes(_desc(batch=0)) == 0
     assert lib.art_decode_workspace_init(None, 0, None) == art.ART_OK
     assert lib.art_decode_workspace_init(None, 256, None) == art.ART_ERR_INVALID_ARG
+
+
+def test_kernel_choice_follows_the_knob_and_the_mode(lib, monkeypatch):
+    """Which kernel a call would run, without any device call: forced schedulers, full mode, rejected args."""
+    long_desc = _desc(batch=4, num_q_heads=64, num_kv_heads=8, block_size=32, max_blocks_per_seq=4096)
+    monkeypatch.setenv("ART_SCHED", "scan")
+    assert art.art_decode_kernel_choice(long_desc, 1e-3, 1e-4, 4) == art.ART_KERNEL_SCANNERS
+    monkeypatch.setenv("ART_SCHED", "lb")
+    assert art.art_decode_kernel_choice(_desc(), 1e-3, 1e-4, 4) == art.ART_KERNEL_LOOKBACK
+    # pass counts above 2047 do not fit the look-back records: scanners
+    assert art.art_decode_kernel_choice(_desc(), 1e-3, 1e-4, 2048) == art.ART_KERNEL_SCANNERS
+    # full attention: the flag, or a zero threshold without ART_FLAG_KEEP_DETECTOR
+    assert art.art_decode_kernel_choice(_desc(flags=art.ART_FLAG_FULL), 1e-3, 1e-4, 4) == art.ART_KERNEL_FULL
+    assert art.art_decode_kernel_choice(_desc(), 0.0, 1e-4, 4) == art.ART_KERNEL_FULL
+    assert art.art_decode_kernel_choice(_desc(flags=art.ART_FLAG_KEEP_DETECTOR), 0.0, 1e-4, 4) == art.ART_KERNEL_LOOKBACK
+    for bad in [dict(p=0), dict(em=-1.0), dict(ed=float("nan"))]:
+        with pytest.raises(art.ArtError):
+            art.art_decode_kernel_choice(_desc(), bad.get("em", 1e-3), bad.get("ed", 1e-4), bad.get("p", 4))
+    with pytest.raises(art.ArtError):
+        art.art_decode_kernel_choice(_desc(head_dim=96), 1e-3, 1e-4, 4)
