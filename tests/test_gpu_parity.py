@@ -314,3 +314,50 @@ def test_scheduler_epoch_advances_and_no_error():
     a = run(dict(ART_SCHED="scan", ART_HELPERS="64"), lambda i: i + 1)
     b = run(dict(ART_SCHED="scan", ART_HELPERS="0"), lambda i: 0)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ---- the look-back scheduler on every kernel variant and edge case ---------------------------------------
+#
+# ART_SCHED=auto sends only few, long streams to the look-back kernel; these run the shape corners and the
+# edge cases through it explicitly.
+
+@pytest.mark.parametrize("w", SHAPES, ids=[w.name for w in SHAPES])
+def test_lookback_shape_matrix(w):
+    case = synth.make_case(w, batch=2, context=2000 + 9)
+    print(f"[lb shape] {w.name}", flush=True)
+    _with_env(dict(ART_SCHED="lb"), lambda: check_art(case))
+
+
+def test_lookback_edge_cases():
+    env = dict(ART_SCHED="lb", ART_WINDOW="2")
+    base = synth.make_case(W.LLAMA3_8B, batch=5, context=700)
+    case = _with_lens(base, [0, 1, 15, 16, 17])
+    _with_env(env, lambda: check_art(case, patience=1, eps_mag=0.5, eps_dir=0.5))
+    _with_env(env, lambda: check_art(case))
+    out, stop, fetched = _with_env(env, lambda: _device_run(case, 1e-3, 1e-4, 4))
+    assert np.all(out[0] == 0.0) and np.all(stop[0] == 0) and np.all(fetched[0] == 0)
+
+    case = synth.make_case(W.LLAMA3_8B, batch=3, context=3000)
+    rng = np.random.default_rng(11)
+    n = int(_nblocks(case)[0])
+    order = case["block_order"].copy()
+    order[0, :n] = list(range(n - 1, -1, -1))  # block 0 last: nobody can stop early
+    order[1, :n] = rng.permutation(n)
+    order[2, :n] = [5, 4, 3, 2, 1, 0] + list(range(6, n))
+    case["block_order"] = order
+    rep, out, stop, fetched = _with_env(env, lambda: check_art(case, eps_mag=1e-2, eps_dir=1e-3, patience=2))
+    assert np.all(stop[0] == n)
+
+    case = synth.make_case(W.LLAMA3_8B, batch=2, context=4096)
+    rep, out, stop, fetched = _with_env(env, lambda: check_art(case, eps_mag=10.0, eps_dir=10.0, patience=1))
+    assert np.all(stop == 2)
+    _with_env(env, lambda: check_art(case, eps_mag=10.0, eps_dir=10.0, patience=5))
+    # patience above what the look-back records hold: the call runs the scanners, same contract
+    from kv_cache_run_amd import art
+
+    dev = art.case_to_device(case)
+    desc = art.make_desc(dev["q"], dev["k_pages"], dev["block_table"])
+    assert _with_env(env, lambda: art.art_decode_kernel_choice(desc, 1e-3, 1e-4, 3000)) == art.ART_KERNEL_SCANNERS
+    assert _with_env(env, lambda: art.art_decode_kernel_choice(desc, 1e-3, 1e-4, 30)) == art.ART_KERNEL_LOOKBACK
+    rep, out, stop, fetched = _with_env(env, lambda: check_art(case, eps_mag=10.0, eps_dir=10.0, patience=3000))
+    assert np.all(stop == _nblocks(case)[:, None])
