@@ -12,7 +12,11 @@ namespace art {
 
 SplitPlan full_split_plan(int batch, int hkv, int max_blocks) {
   const long streams = (long)batch * hkv;
-  const long target_wgs = 1024;  // about four workgroups per CU on 256 CUs
+  // about two workgroups per CU on 256 CUs (measured against 256 … 3072:
+  // fewer, longer slices avoid a tail of partly filled CUs and shrink the
+  // merge); ART_FULL_WGS overrides
+  const char* tw = getenv("ART_FULL_WGS");
+  const long target_wgs = tw && atol(tw) > 0 ? atol(tw) : 512;
   long splits = streams > 0 ? (target_wgs + streams - 1) / streams : 1;
   const long by_len = (max_blocks + 7) / 8;  // at least 8 blocks (2 per wave) per split
   if (splits > by_len) splits = by_len;
