@@ -127,12 +127,18 @@ art_status art_decode_workspace_init(void* workspace, size_t workspace_bytes, vo
  *              kernels actually read for each (sequence, kv-head), speculative
  *              reads (chunks fetched ahead of the stop) included.
  *
- * The terminating kernel has two schedulers (environment ART_SCHED: "auto",
- * the default, "scan" or "lb"): one scanner workgroup per stream that folds
- * the stream's blocks in order, or persistent workgroups that take chunks of
- * any stream and obtain the state entering a chunk from the records of the
- * chunks before it.  Each is deterministic; their results differ only in
- * floating-point rounding order (within the same tolerance of the method).
+ * The terminating kernel has three schedulers (environment ART_SCHED:
+ * "auto", the default, "scan", "lb" or "win"): one scanner workgroup per
+ * stream that folds the stream's blocks in order; persistent workgroups that
+ * take chunks of any stream and obtain the state entering a chunk from the
+ * records of the chunks before it (look-back); or windows of 2, 4, 8, ... 64
+ * chunks, two launches per window (partials, then fold).  Each is
+ * deterministic; the look-back and windowed schedulers give the same bits,
+ * the scanners differ from them only in floating-point rounding order
+ * (within the same tolerance of the method).  "auto" takes the windowed
+ * scheduler for few, long streams (at most half as many streams as CUs, at
+ * least 256 chunks of up to 8 blocks), the look-back scheduler for groups of
+ * more than 4 query heads, the scanners otherwise.
  * workspace    device scratch of at least art_decode_workspace_bytes(desc)
  *              bytes, initialized once with art_decode_workspace_init; may be
  *              NULL when that size is 0.  256-byte aligned.
@@ -162,8 +168,9 @@ int32_t art_decode_version(void);
  *                        without ART_FLAG_KEEP_DETECTOR),
  *   ART_KERNEL_SCANNERS  one scanner workgroup per stream,
  *   ART_KERNEL_LOOKBACK  the look-back scheduler,
+ *   ART_KERNEL_WINDOWED  the windowed scheduler,
  * or minus the art_status art_decode would return for rejected arguments. */
-enum { ART_KERNEL_FULL = 0, ART_KERNEL_SCANNERS = 1, ART_KERNEL_LOOKBACK = 2 };
+enum { ART_KERNEL_FULL = 0, ART_KERNEL_SCANNERS = 1, ART_KERNEL_LOOKBACK = 2, ART_KERNEL_WINDOWED = 3 };
 int32_t art_decode_kernel_choice(const art_decode_desc* desc, float eps_mag, float eps_dir, int32_t patience);
 
 #ifdef __cplusplus

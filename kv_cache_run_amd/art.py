@@ -22,9 +22,9 @@ ART_FLAG_NONE, ART_FLAG_FULL, ART_FLAG_KEEP_DETECTOR = 0, 1, 2
 
 EXPORTED = ("art_decode_workspace_bytes", "art_decode_workspace_init", "art_decode", "art_status_string",
             "art_decode_version", "art_decode_kernel_choice")
-ART_KERNEL_FULL, ART_KERNEL_SCANNERS, ART_KERNEL_LOOKBACK = 0, 1, 2
+ART_KERNEL_FULL, ART_KERNEL_SCANNERS, ART_KERNEL_LOOKBACK, ART_KERNEL_WINDOWED = 0, 1, 2, 3
 KERNEL_NAMES = {ART_KERNEL_FULL: "full_split_kernel", ART_KERNEL_SCANNERS: "art_sched_kernel",
-                ART_KERNEL_LOOKBACK: "art_lb_kernel"}
+                ART_KERNEL_LOOKBACK: "art_lb_kernel", ART_KERNEL_WINDOWED: "art_win_part_kernel"}
 
 
 class ArtDecodeDesc(ctypes.Structure):

@@ -63,10 +63,13 @@ art_status check_desc(const art_decode_desc* d) {
 
 // Scheduler tuning knobs, read from the environment at every call (defaults
 // when unset).  ART_SCHED selects the terminating kernel: "scan" (one scanner
-// workgroup per stream, optional helpers), "lb" (the look-back scheduler) or
-// "auto" (default): the look-back scheduler when the streams are few (at
-// most half the CUs) and long (at least 256 chunks), where scanners would
-// leave most CUs idle for a long walk; scanners otherwise.
+// workgroup per stream, optional helpers), "lb" (the look-back scheduler),
+// "win" (the windowed scheduler) or "auto" (default): windows when the
+// streams are few (at most half the CUs) and long (at least 256 chunks),
+// where scanners would leave most CUs idle for a long walk; the look-back
+// scheduler for groups of more than 4 query heads (a scanner has 4 scan
+// waves); scanners otherwise.  Windowed: ART_WIN_SPLIT fold workgroups per
+// (stream, head) (1 .. 4, default 1); results do not depend on it.
 // Look-back: ART_WINDOW chunks claimable past a stream's resolved frontier
 // (0: 1/16 of the longest stream's chunks, clamped to 8 .. 32), ART_WORKERS
 // workgroups (0: one per resident slot); results do not depend on either.  Scanners: ART_RING
@@ -80,16 +83,18 @@ int env_int(const char* name, int def, int lo, int hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }
 struct Knobs {
-  int ring, lookahead, helpers, target, lb, window, workers;
+  int ring, lookahead, helpers, target, lb, window, workers, win_split;
 };
-enum { SCHED_SCAN = 0, SCHED_LB = 1, SCHED_AUTO = 2 };
+enum { SCHED_SCAN = 0, SCHED_LB = 1, SCHED_AUTO = 2, SCHED_WIN = 3 };
 Knobs knobs() {
   const char* sched = getenv("ART_SCHED");
-  const int mode = !sched || strcmp(sched, "auto") == 0 ? SCHED_AUTO : (strcmp(sched, "lb") == 0 ? SCHED_LB : SCHED_SCAN);
+  const int mode = !sched || strcmp(sched, "auto") == 0
+                       ? SCHED_AUTO
+                       : (strcmp(sched, "lb") == 0 ? SCHED_LB : (strcmp(sched, "win") == 0 ? SCHED_WIN : SCHED_SCAN));
   const Knobs k = {env_int("ART_RING", 8, 1, 64),          env_int("ART_LOOKAHEAD", 3, 1, 64),
                    env_int("ART_HELPERS", 0, -1, 1 << 16), env_int("ART_TARGET_WGS", 512, 1, 1 << 16),
                    mode,                                    env_int("ART_WINDOW", 0, 0, 32),
-                   env_int("ART_WORKERS", 0, 0, 1 << 20)};
+                   env_int("ART_WORKERS", 0, 0, 1 << 20),       env_int("ART_WIN_SPLIT", 1, 1, art::art_win_split)};
   return k;
 }
 
@@ -132,6 +137,26 @@ art::WorkspacePlan plan_workspace(const art_decode_desc* d) {
   off += round256(streams * 8);
   w.lb_st = off;
   off += round256(streams * (size_t)max_chunks * g * 8);
+  w.win_dead = off;
+  off += round256(streams * 4);
+  w.win_dwin = off;
+  off += round256(streams * 4);
+  w.win_state = off;
+  off += round256(streams * (size_t)g * (d->head_dim + 8) * sizeof(float));
+  w.win_cnt = off;
+  off += round256(streams * (size_t)g * 4);
+  // windowed path: slots for the largest window, at most 64 chunks and about
+  // 256 MB over all streams
+  {
+    w.win_slot = (art::art_slot_floats(gm, d->head_dim) + gm * (d->head_dim + 4) + 63) / 64 * 64;
+    const size_t slot_bytes = (size_t)w.win_slot * sizeof(float);
+    long wm = (long)((256ull << 20) / (streams * slot_bytes));
+    if (wm > 64) wm = 64;
+    if (wm < 2) wm = 2;
+    w.win_max = (int)wm;
+  }
+  w.win_pass = off;
+  off += round256(streams * (size_t)g * w.win_max * 4);
   w.claim = off;
   off += round256(streams * 8);
   w.done = off;
@@ -145,25 +170,37 @@ art::WorkspacePlan plan_workspace(const art_decode_desc* d) {
   const size_t part = sp.splits > 1 ? streams * sp.splits * gm * (size_t)(d->head_dim + 2) * sizeof(float) : 0;
   size_t data = ring_bytes > part ? ring_bytes : part;
   if (rec_bytes > data) data = rec_bytes;
+  const size_t win_bytes = streams * (size_t)w.win_max * w.win_slot * sizeof(float);
+  if (win_bytes > data) data = win_bytes;
   off += round256(data);
   w.total = off;
   return w;
 }
 
-// Terminating kernel for a valid call: look-back scheduler or scanners.
-bool use_lookback(const art_decode_desc* d, const art::WorkspacePlan& wp, int32_t patience) {
+// Terminating kernel for a valid call.  The look-back records hold pass
+// counts up to 2047 and its claim sweep packs a stream index in 16 bits; the
+// windowed path carries the pass count as a float (exact to 2^24).  Either
+// falls back to the scanners outside those limits.
+enum Sched { SCHED_RUN_SCAN = 0, SCHED_RUN_LB = 1, SCHED_RUN_WIN = 2 };
+Sched terminating_kernel(const art_decode_desc* d, const art::WorkspacePlan& wp, int32_t patience) {
   const Knobs k = knobs();
-  // the look-back records hold pass counts up to 2047; its claim sweep
-  // packs a stream index in 16 bits
   const long streams = (long)d->batch * d->num_kv_heads;
-  bool lb = k.lb == SCHED_LB;
+  const int g = d->num_q_heads / d->num_kv_heads;
+  int want = k.lb == SCHED_LB ? SCHED_RUN_LB : (k.lb == SCHED_WIN ? SCHED_RUN_WIN : SCHED_RUN_SCAN);
   if (k.lb == SCHED_AUTO) {
+    // few, long streams: windows; large groups (more heads than a scanner
+    // has scan waves): look-back; else scanners
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
-    lb = 2 * streams <= cus && wp.max_chunks >= 256;
+    if (2 * streams <= cus && wp.max_chunks >= 256)
+      want = SCHED_RUN_WIN;
+    else if (g > 4 && wp.max_chunks >= 32)
+      want = SCHED_RUN_LB;
   }
-  return lb && patience <= 2047 && streams <= 65535;
+  if (want == SCHED_RUN_LB && (patience > 2047 || streams > 65535)) want = SCHED_RUN_SCAN;
+  if (want == SCHED_RUN_WIN && patience > (1 << 24)) want = SCHED_RUN_SCAN;
+  return static_cast<Sched>(want);
 }
 
 bool full_mode(const art_decode_desc* d, float eps_mag, float eps_dir) {
@@ -275,11 +312,46 @@ art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_
     p.max_chunks = wp.max_chunks;
     p.rec_floats = wp.rec_floats;
     p.window = wp.window;
-    p.lb = use_lookback(desc, wp, patience) ? 1 : 0;
+    const Sched sched = terminating_kernel(desc, wp, patience);
+    p.lb = sched == SCHED_RUN_LB ? 1 : 0;
     p.workers = knobs().workers;
-    e = v.kv == art::KV_F32 ? art::launch_art_f32(v, p, static_cast<hipStream_t>(stream))
-        : v.kv == art::KV_BF16 ? art::launch_art_bf16(v, p, static_cast<hipStream_t>(stream))
-                               : art::launch_art_fp8(v, p, static_cast<hipStream_t>(stream));
+    auto launch = [&](const art::Params& pp) {
+      return v.kv == art::KV_F32 ? art::launch_art_f32(v, pp, static_cast<hipStream_t>(stream))
+             : v.kv == art::KV_BF16 ? art::launch_art_bf16(v, pp, static_cast<hipStream_t>(stream))
+                                    : art::launch_art_fp8(v, pp, static_cast<hipStream_t>(stream));
+    };
+    if (sched == SCHED_RUN_WIN) {
+      // windows of 2, 4, 8, ... chunks (at most win_max), two launches each:
+      // the window's partials, then its fold
+      p.lb = 0;
+      p.win_max = wp.win_max;
+      p.win_slot = wp.win_slot;
+      p.win_slots = reinterpret_cast<float*>(ws + wp.data);
+      p.win_state = reinterpret_cast<float*>(ws + wp.win_state);
+      p.win_dead = reinterpret_cast<uint32_t*>(ws + wp.win_dead);
+      p.win_dwin = reinterpret_cast<uint32_t*>(ws + wp.win_dwin);
+      p.win_pass = reinterpret_cast<uint32_t*>(ws + wp.win_pass);
+      p.win_cnt = reinterpret_cast<uint32_t*>(ws + wp.win_cnt);
+      const int split = knobs().win_split;
+      e = hipSuccess;
+      for (int c0 = 0, size = 2, idx = 0; c0 < wp.max_chunks && e == hipSuccess; ++idx) {
+        const int nw = size < wp.max_chunks - c0 ? size : wp.max_chunks - c0;
+        p.win_c0 = c0;
+        p.win_n = nw;
+        p.win_idx = idx;
+        const int k = (nw + art::art_win_waves - 1) / art::art_win_waves;
+        p.win_k = k < split ? k : split;
+        p.win = 1;
+        e = launch(p);
+        if (e != hipSuccess) break;
+        p.win = 2;
+        e = launch(p);
+        c0 += nw;
+        size = 2 * size < wp.win_max ? 2 * size : wp.win_max;
+      }
+    } else {
+      e = launch(p);
+    }
   }
   return e == hipSuccess ? ART_OK : ART_ERR_HIP;
 }
@@ -302,7 +374,11 @@ int32_t art_decode_kernel_choice(const art_decode_desc* desc, float eps_mag, flo
   if (ds != ART_OK) return -(int32_t)ds;
   if (!(eps_mag >= 0.f) || !(eps_dir >= 0.f) || patience < 1) return -(int32_t)ART_ERR_INVALID_ARG;
   if (full_mode(desc, eps_mag, eps_dir)) return ART_KERNEL_FULL;
-  return use_lookback(desc, plan_workspace(desc), patience) ? ART_KERNEL_LOOKBACK : ART_KERNEL_SCANNERS;
+  switch (terminating_kernel(desc, plan_workspace(desc), patience)) {
+    case SCHED_RUN_LB: return ART_KERNEL_LOOKBACK;
+    case SCHED_RUN_WIN: return ART_KERNEL_WINDOWED;
+    default: return ART_KERNEL_SCANNERS;
+  }
 }
 
 }  // extern "C"

@@ -18,6 +18,11 @@ constexpr int art_slot_floats(int gm, int d) {
   return art_chunk_blocks(gm, d) * gm * d + 2 * art_chunk_blocks(gm, d) * gm;
 }
 
+// Windowed path: waves of a workgroup, and at most this many fold
+// workgroups per (stream, head).
+constexpr int art_win_waves = 16;
+constexpr int art_win_split = 4;
+
 // Everything a kernel needs, passed by value as the kernel argument.
 struct Params {
   const void* q;
@@ -58,6 +63,19 @@ struct Params {
   int32_t window;                      // chunks claimable past the resolved frontier (1..32)
   int32_t lb;                          // 1: launch art_lb_kernel, 0: scanners (+ helpers)
   int32_t workers;                     // art_lb_kernel workgroups (0: one per resident slot)
+  // windowed path (art_win_kernel): per window, a launch in the partials
+  // role, then one in the fold role
+  int32_t win;                         // 0: not windowed; 1: partials role; 2: fold role
+  int32_t win_c0, win_n, win_idx;      // the window's first chunk, chunk count and index
+  int32_t win_k;                       // fold role: workgroups per (stream, head)
+  int32_t win_max;                     // chunk slots per stream (largest window)
+  int32_t win_slot;                    // floats per slot: partials, then [GM][D + 4] chunk aggregates
+  float* win_slots;                    // [streams][win_max][win_slot]
+  float* win_state;                    // [streams][g][D + 8]: A, M, L, pass count, block-0 flag, running
+  uint32_t* win_dead;                  // [streams] bit mask of stopped heads
+  uint32_t* win_dwin;                  // [streams] 1 + index of the window in which the stream stopped (0: running)
+  uint32_t* win_pass;                  // [streams][g][win_max] pass bits | block-0 bits << 8, per chunk
+  uint32_t* win_cnt;                   // [streams][g] fold workgroups arrived (zero between launches)
   int32_t batch, hq, hkv, g;
   int32_t block_size;
   int32_t max_blocks;
@@ -88,8 +106,9 @@ SplitPlan full_split_plan(int batch, int hkv, int max_blocks);
 // Workspace layout (bytes from the workspace base, each region 256-B aligned).
 struct WorkspacePlan {
   size_t lb_fetch, lb_claim, lb_prog, lb_heads, lb_st;  // look-back scheduler
+  size_t win_dead, win_dwin, win_state, win_pass, win_cnt;  // windowed path (its slots are in data)
   size_t claim, done, ready, data, total;               // scanner + helpers; data: ring | records | full partials
-  int ring, slot_floats, helpers, lookahead, max_chunks, rec_floats, window;
+  int ring, slot_floats, helpers, lookahead, max_chunks, rec_floats, window, win_max, win_slot;
 };
 
 // Launchers; return hipSuccess or the launch error.  One translation unit per

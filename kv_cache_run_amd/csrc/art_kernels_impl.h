@@ -1458,6 +1458,19 @@ __device__ __forceinline__ void lb_combine(LbState<Cf>& x, float m, float l, con
   x.M = mn;
 }
 
+// O = A / L entering a chunk (0 before any block) and its squared norm.
+template <class Cf>
+__device__ __forceinline__ void lb_entering_output(const LbState<Cf>& x, int lane, float (&Op)[Cf::DPL], float& np) {
+  const float rl = x.L > 0.f ? __builtin_amdgcn_rcpf(x.L) : 0.f;
+  float sq[1] = {0.f};
+#pragma unroll
+  for (int j = 0; j < Cf::DPL; ++j) {
+    Op[j] = x.L > 0.f ? x.A[j] * rl : 0.f;
+    sq[0] = fmaf(Op[j], Op[j], sq[0]);
+  }
+  np = xreduce<1>(sq, lane);
+}
+
 // The chunk's own aggregate from its per-block partials (positions past the
 // chunk end are neutral: m = -inf, l = 0, a = 0; position 0 is a real block).
 template <class Cf>
@@ -2027,6 +2040,427 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_lb_kernel(P
     if (threadIdx.x == 0) {
       st_dev32(p.sched_ctrl + 1, 0u);
       st_dev32(p.sched_ctrl, E);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Terminating path, windowed: art_win_part_kernel + art_win_scan_kernel
+// ---------------------------------------------------------------------------
+//
+// A stream's chunks are processed window by window (windows of 2, 4, 8, ...
+// chunks, at most 64), two launches per window; launch boundaries are the
+// only waits between workgroups.
+//   * art_win_part_kernel: one workgroup per (stream, chunk), one wave per
+//     block, computes each chunk's per-block partials (m_b, l_b, a_b) for
+//     every head of the group and each head's chunk aggregate.  Streams whose
+//     heads have all stopped are skipped.
+//   * art_win_scan_kernel: K workgroups per (stream, query head) (K = 1 unless asked
+//     otherwise), in four phases: (1) each chunk's aggregate into LDS; (2) the
+//     state entering each chunk, in chunk order, from the state carried from
+//     the previous window; (3) the statistics of every position of the
+//     workgroup's own chunks (the detector at a chunk needs only the state
+//     entering it), whose pass bits are published; (4) in the last of the K
+//     workgroups to finish (an arrival counter; nothing waits), the
+//     patience/block-0 rule over the window's pass bits from the carried pass
+//     count.  A head that fires writes its output (folded again at its chunk)
+//     and its stop; a head that reaches the end of its stream writes the
+//     output after all n blocks.
+// Every combine runs in the order the look-back kernel uses, so results are
+// deterministic and the same bits as that kernel's.
+
+constexpr int WNW = art_win_waves;  // waves of art_win_scan_kernel
+
+// The chunk's partials of head h from its slot in global memory.
+template <class Cf>
+__device__ __forceinline__ void win_gather(ChunkIn<Cf>& in, const float* slotp, int h, int lane) {
+#pragma unroll
+  for (int t = 0; t < Cf::C; ++t) {
+    const float* src = slotp + ((size_t)t * Cf::GM + h) * Cf::D + Cf::DPL * lane;
+    if constexpr (Cf::DPL == 2) {
+      const f32x2 v = *reinterpret_cast<const f32x2*>(src);
+      in.a[t][0] = v.x; in.a[t][1] = v.y;
+    } else {
+      in.a[t][0] = src[0];
+    }
+  }
+  const int t = lane < Cf::C ? lane : 0;
+  in.m = lane < Cf::C ? slotp[Cf::SLOT_A + t * Cf::GM + h] : NEG_INF;
+  in.l = lane < Cf::C ? slotp[Cf::SLOT_A + Cf::C * Cf::GM + t * Cf::GM + h] : 0.f;
+}
+
+// Partials: workgroup `bid` takes one chunk of one stream of the window, one
+// wave per block.  Streams that have stopped are skipped.
+template <int KV, int D, int B, int GM>
+__global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::C)) void art_win_part_kernel(Params p) {
+  using Cf = Cfg<KV, D, B, GM>;
+  constexpr int C = Cf::C;
+  __shared__ __attribute__((aligned(16))) float pbuf_all[C][Cf::PV4 ? GM * B : 4];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int stream = blockIdx.x / p.win_n;
+  const int ci = blockIdx.x - stream * p.win_n;
+  const int c = p.win_c0 + ci;
+  const int s = stream / p.hkv;
+  const int kvh = stream - s * p.hkv;
+  if (p.win_idx == 0) {
+    // first window: clear the stop records (read from the next launch on)
+    if (ci == 0 && threadIdx.x == 0) {
+      p.win_dead[stream] = 0u;
+      p.win_dwin[stream] = 0u;
+    }
+  } else if (p.win_dwin[stream] != 0u) {
+    return;
+  }
+  const int L = p.seq_lens[s];
+  const int n = (L + B - 1) / B;
+  const int nch = (n + C - 1) / C;
+  if (c >= nch) return;
+  const int t0 = c * C;
+  const int nt = min(C, n - t0);
+  const int slot = lane < C ? lane : C - 1;
+  const int ob = p.block_order[(size_t)s * p.max_blocks + min(t0 + slot, n - 1)];
+  const int pg = p.block_table[(size_t)s * p.max_blocks + ob];
+  float ks = 1.f, vs = 1.f;
+  if constexpr (KV == KV_FP8) {
+    ks = p.k_scale[(size_t)pg * p.hkv + kvh];
+    vs = p.v_scale[(size_t)pg * p.hkv + kvh];
+  }
+  BlockRegs<Cf> regs[1];
+  issue_chunk_part<Cf, 1>(regs, p, kvh, L, ob, pg, nt, w, lane);
+  uint4 qf[Cf::QF];
+  load_q<Cf>(p, s, kvh, lane, qf);
+  float* dst = p.win_slots + ((size_t)stream * p.win_max + ci) * p.win_slot;
+  block_phase<Cf, 1>(regs, qf, ob, ks, vs, nt, L, p.qk_log2, w, lane, dst, pbuf_all[w]);
+  // each head's chunk aggregate [A(D), m, l] after the partials (the fold
+  // launch reads these first)
+  __syncthreads();
+  for (int h = w; h < p.g; h += C) {
+    ChunkIn<Cf> in;
+    win_gather<Cf>(in, dst, h, lane);
+    float m, l, a[Cf::DPL];
+    lb_aggregate<Cf>(in, m, l, a);
+    float* gq = dst + Cf::SLOT + h * (D + 4);
+#pragma unroll
+    for (int j = 0; j < Cf::DPL; ++j) gq[Cf::DPL * lane + j] = a[j];
+    if (lane == 0) { gq[D] = m; gq[D + 1] = l; }
+  }
+}
+
+// Fold: workgroup q of K of (stream, head) hs = blockIdx.x / K.
+template <int KV, int D, int B, int GM, int WMAXC>
+__global__ __launch_bounds__(64 * WNW) void art_win_scan_kernel(Params p) {
+  using Cf = Cfg<KV, D, B, GM>;
+  constexpr int C = Cf::C, DPL = Cf::DPL;
+  constexpr int XS = D + 4;  // floats per chunk entry: A[D], M, L
+  static_assert(WMAXC <= 64, "one lane per chunk of the window");
+  __shared__ __attribute__((aligned(16))) float xs[WMAXC * XS];
+  __shared__ uint32_t pas[WMAXC];  // one workgroup per head: its pass words stay here
+  __shared__ uint32_t arrived;
+  const int bid = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = p.g;
+  const int K = p.win_k;
+  const int hs = bid / K;  // (stream, head)
+  const int q = bid - hs * K;
+  const int stream = hs / g;
+  const int h = hs - stream * g;
+  const int s = stream / p.hkv;
+  const int kvh = stream - s * p.hkv;
+  const int L = p.seq_lens[s];
+  const int n = (L + B - 1) / B;
+  const int nch = (n + C - 1) / C;
+  const size_t head = (size_t)s * p.hq + (size_t)kvh * g + h;
+  float* st = p.win_state + (size_t)hs * (D + 8);
+  const bool first = p.win_c0 == 0;
+  float* out_row = p.out + head * D;
+  if (n == 0) {
+    if (first && q == 0) {
+      for (int i = threadIdx.x; i < D; i += 64 * WNW) out_row[i] = 0.f;
+      if (threadIdx.x == 0) {
+        p.stop_block[head] = 0;
+        if (h == 0 && p.blocks_fetched) p.blocks_fetched[stream] = 0;
+        atomicOr(p.win_dead + stream, 1u << h);
+      }
+    }
+    return;
+  }
+  // state entering the window (read by every workgroup of the head before
+  // any of them arrives below; only the last to arrive writes it)
+  int cnt = 0;
+  bool sink = false, alive = true;
+  LbState<Cf> x0;
+  x0.M = NEG_INF;
+  x0.L = 0.f;
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) x0.A[j] = 0.f;
+  if (!first) {
+    alive = st[D + 4] != 0.f;
+    if (!alive) return;
+    x0.M = st[D];
+    x0.L = st[D + 1];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) x0.A[j] = st[DPL * lane + j];
+    cnt = (int)st[D + 2];
+    sink = st[D + 3] != 0.f;
+  }
+  const int c0 = p.win_c0;
+  const int cend = min(nch, c0 + p.win_n);
+  if (c0 >= cend) return;
+  const int ncw = cend - c0;
+  const float* slots = p.win_slots + (size_t)stream * p.win_max * p.win_slot;
+  const int32_t* orow = p.block_order + (size_t)s * p.max_blocks;
+  uint32_t* pw = p.win_pass + (size_t)hs * p.win_max;
+
+  // (1) chunk aggregates, written by the partials launch, into LDS (a
+  // wave's loads go out together)
+  constexpr int U = (WMAXC + WNW - 1) / WNW;
+  {
+    float ga[U][DPL], gml[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ci = min(wv + WNW * u, ncw - 1);
+      const float* gq = slots + (size_t)ci * p.win_slot + Cf::SLOT + h * (D + 4);
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) ga[u][j] = gq[DPL * lane + j];
+      gml[u] = gq[D + (lane & 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ci = wv + WNW * u;
+      if (ci < ncw) {
+        float* e = xs + ci * XS;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) e[DPL * lane + j] = ga[u][j];
+        if (lane < 2) e[D + lane] = gml[u];
+      }
+    }
+  }
+  __syncthreads();
+  // (2) the state entering each chunk, in chunk order (every workgroup of
+  // the head, for all chunks of the window).  The running max is a prefix
+  // max over the chunks (lane k: chunk k) and each step's two scale factors
+  // follow from it, so the sequential part is one FMA per element and step
+  // -- the same operations as lb_combine, in the same order.
+  LbState<Cf> xw = x0;  // wave 0: the state after the window
+  if (wv == 0) {
+    const float mk = lane < ncw ? xs[lane * XS + D] : NEG_INF;
+    const float lk = lane < ncw ? xs[lane * XS + D + 1] : 0.f;
+    float mi = mk;  // max(m_0 .. m_lane)
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float v = __shfl_up(mi, o);
+      if (lane >= o) mi = fmaxf(mi, v);
+    }
+    const float mn = fmaxf(x0.M, mi);  // the running max after chunk `lane`
+    float me = __shfl_up(mn, 1);       // ... and before it
+    if (lane == 0) me = x0.M;
+    const bool empty = mn == NEG_INF;
+    const float fxv = empty ? 0.f : __builtin_amdgcn_exp2f(me - mn);
+    const float fyv = empty ? 0.f : __builtin_amdgcn_exp2f(mk - mn);
+    constexpr int PF = 4;  // entries read ahead of the chain
+    float na[PF][DPL];
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) na[u][j] = xs[min(u, ncw - 1) * XS + DPL * lane + j];
+    for (int cb = 0; cb < ncw; cb += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const int ci = cb + u;
+        if (ci < ncw) {
+          float* e = xs + ci * XS;
+          float a[DPL];
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) a[j] = na[u][j];
+          if (ci + PF < ncw) {  // read before the chain overwrites that entry
+#pragma unroll
+            for (int j = 0; j < DPL; ++j) na[u][j] = e[PF * XS + DPL * lane + j];
+          }
+          // cross-lane reads stay outside lane-divergent code
+          const float fx = readlanef(fxv, ci), fy = readlanef(fyv, ci);
+          const float l = readlanef(lk, ci), mc = readlanef(me, ci);
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) e[DPL * lane + j] = xw.A[j];
+          if (lane == 0) { e[D] = mc; e[D + 1] = xw.L; }
+          xw.L = fmaf(fx, xw.L, fy * l);
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) xw.A[j] = fmaf(fx, xw.A[j], fy * a[j]);
+        }
+      }
+    }
+    xw.M = readlanef(mn, ncw - 1);
+  }
+  __syncthreads();
+  // (3) pass bits of every position of this workgroup's chunks (wave w of
+  // workgroup q takes chunks (q + K u) WNW + w) and the positions holding
+  // block 0, published per chunk; the partials of a wave's next chunks are
+  // loaded while one is evaluated
+  ChunkIn<Cf> nx1, nx2;
+  {
+    const int c1 = q * WNW + wv, c2 = (q + K) * WNW + wv;
+    if (c1 < ncw) win_gather<Cf>(nx1, slots + (size_t)c1 * p.win_slot, h, lane);
+    if (c2 < ncw) win_gather<Cf>(nx2, slots + (size_t)c2 * p.win_slot, h, lane);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int ci = (q + K * u) * WNW + wv;
+    if (ci >= ncw) break;
+    const int c = c0 + ci;
+    const int t0 = c * C;
+    const int nt = min(C, n - t0);
+    const ChunkIn<Cf> in = nx1;
+    nx1 = nx2;
+    const int c3 = (q + K * (u + 2)) * WNW + wv;
+    if (c3 < ncw) win_gather<Cf>(nx2, slots + (size_t)c3 * p.win_slot, h, lane);
+    const float* e = xs + ci * XS;
+    LbState<Cf> x;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) x.A[j] = e[DPL * lane + j];
+    x.M = e[D];
+    x.L = e[D + 1];
+    float Op[DPL], np;
+    lb_entering_output<Cf>(x, lane, Op, np);
+    float oo[C][DPL];
+    const u64 pass = lb_stats<Cf>(x, Op, np, in, t0, nt, p, lane, oo);
+    const int ob = orow[min(t0 + (lane < C ? lane : C - 1), n - 1)];
+    const u64 sb = __ballot(lane < nt && ob == 0);
+    const uint32_t word = ((uint32_t)pass & 0xFFu) | (((uint32_t)sb & 0xFFu) << 8);
+    if (lane == 0) {
+      if (K == 1)
+        pas[ci] = word;
+      else
+        st_dev32(pw + ci, word);
+    }
+  }
+  if (K > 1) {
+    // the last workgroup of the head to get here applies the rule; nothing
+    // waits: the others leave
+    wait_all_memory();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      arrived = __hip_atomic_fetch_add(p.win_cnt + hs, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrived != (uint32_t)(K - 1)) return;
+  } else {
+    __syncthreads();
+  }
+  // (4) the patience/block-0 rule over the window: lane c holds chunk c.
+  // The passes in a row after chunk c follow R_c = a_c R_{c-1} + b_c (a_c = 1
+  // when every position of chunk c passed, b_c = its length then, else its
+  // trailing passes), composed lane-parallel; the block-0 flag is a prefix
+  // OR.  Each lane then evaluates its own chunk's positions from the state
+  // entering it; the first chunk that fires decides.
+  if (wv == 0) {
+    if (K > 1 && lane == 0) st_dev32(p.win_cnt + hs, 0u);  // zero again for the next launch
+    const int cap = min(p.patience, 1 << 24);  // the carried count is stored as a float
+    const bool lv = lane < ncw;
+    const uint32_t wd = !lv ? 0u : (K == 1 ? pas[lane] : ld_dev32(pw + lane));
+    const int ntl = lv ? min(C, n - (c0 + lane) * C) : 0;
+    const uint32_t full = (1u << ntl) - 1u;
+    const uint32_t pb = wd & full;
+    const uint32_t sb = (wd >> 8) & full;
+    const bool allp = lv && pb == full;
+    const uint32_t zeros = ~pb & full;
+    const int trail = zeros == 0u ? ntl : ntl - 1 - (31 - __builtin_clz(zeros));
+    // inclusive scan of (a, b): (a2, b2) after (a1, b1) = (a2 a1, a2 b1 + b2)
+    int a = (!lv || allp) ? 1 : 0;
+    int b = lv ? (allp ? ntl : trail) : 0;
+    int so = (lv && sb != 0u) ? 1 : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int pa = __shfl_up(a, o), pbv = __shfl_up(b, o), ps = __shfl_up(so, o);
+      if (lane >= o) {
+        b = a * pbv + b;
+        a = a * pa;
+        so = so | ps;
+      }
+    }
+    // state entering chunk `lane`: the exclusive values
+    int rin = __shfl_up(a * cnt + b, 1);  // R after chunk lane-1
+    int sin = __shfl_up(so, 1);
+    if (lane == 0) { rin = cnt; sin = 0; }
+    const bool sink_in = sink || sin != 0;
+    const int cnt_in = min(rin, cap);
+    // positions of this lane's chunk
+    int ft = -1;
+    {
+      int cc = cnt_in;
+      bool sk = sink_in;
+#pragma unroll
+      for (int t = 0; t < C; ++t) {
+        if (t < ntl && ft < 0) {
+          cc = ((pb >> t) & 1u) ? min(cc + 1, cap) : 0;
+          sk = sk || ((sb >> t) & 1u);
+          if (cc >= p.patience && sk) ft = t;
+        }
+      }
+    }
+    const u64 fires = __ballot(lv && ft >= 0);
+    int fire_ci = -1, fire_t = 0;
+    if (fires != 0ull) {
+      fire_ci = __builtin_ctzll(fires);
+      fire_t = readlane(ft, fire_ci);
+    } else {
+      // no stop in the window: carry the count and the flag to the next one
+      const int last = ncw - 1;
+      cnt = min(readlane(a * cnt + b, last), cap);
+      sink = sink || readlane(so, last) != 0;
+    }
+    const bool ends = cend == nch;
+    if (fire_ci >= 0 || ends) {
+      // the output at the stop (or after the last block), folded again
+      const int ci = fire_ci >= 0 ? fire_ci : ncw - 1;
+      const int c = c0 + ci;
+      const int t0 = c * C;
+      const int nt = min(C, n - t0);
+      ChunkIn<Cf> in;
+      win_gather<Cf>(in, slots + (size_t)ci * p.win_slot, h, lane);
+      const float* e = xs + ci * XS;
+      LbState<Cf> x;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) x.A[j] = e[DPL * lane + j];
+      x.M = e[D];
+      x.L = e[D + 1];
+      float Op[DPL], np;
+      lb_entering_output<Cf>(x, lane, Op, np);
+      float oo[C][DPL];
+      (void)lb_stats<Cf>(x, Op, np, in, t0, nt, p, lane, oo);
+      float ov[DPL];
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) ov[j] = Op[j];
+      if (fire_ci >= 0) {
+#pragma unroll
+        for (int t = 0; t < C; ++t)
+          if (fire_t == t)
+#pragma unroll
+            for (int j = 0; j < DPL; ++j) ov[j] = oo[t][j];
+      }
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) out_row[DPL * lane + j] = ov[j];
+      if (lane == 0) p.stop_block[head] = fire_ci >= 0 ? t0 + fire_t + 1 : n;
+      alive = false;
+    }
+    // the state carried to the next window
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) st[DPL * lane + j] = xw.A[j];
+    if (lane == 0) {
+      st[D] = xw.M;
+      st[D + 1] = xw.L;
+      st[D + 2] = (float)cnt;
+      st[D + 3] = sink ? 1.f : 0.f;
+      st[D + 4] = alive ? 1.f : 0.f;
+      if (!alive) {
+        // the head completing the mask records the window in which the
+        // stream stopped and the blocks it loaded (through this window)
+        const uint32_t bit = 1u << h;
+        const uint32_t was = atomicOr(p.win_dead + stream, bit);
+        if ((was | bit) == (1u << g) - 1u && was != (was | bit)) {
+          p.win_dwin[stream] = (uint32_t)p.win_idx + 1u;
+          if (p.blocks_fetched) p.blocks_fetched[stream] = min(n, cend * C);
+        }
+      }
     }
   }
 }

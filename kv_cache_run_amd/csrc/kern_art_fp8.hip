@@ -1,4 +1,4 @@
-// Instantiations of art_sched_kernel and art_lb_kernel for KV storage FP8 (one translation unit per
+// Instantiations of the terminating kernels (scanners, look-back, windowed) for KV storage FP8 (one translation unit per
 // storage type and kernel so that the build runs in parallel).
 #include "art_kernels_impl.h"
 
@@ -24,7 +24,15 @@ int resident_slots(K kernel, int threads) {
 template <int D, int B, int GM>
 hipError_t go(const Params& p, hipStream_t st) {
   constexpr int threads = 64 * kern::Cfg<KV_FP8, D, B, GM>::NWA;
-  if (p.lb) {
+  if (p.win == 1) {
+    // windowed, partials: one workgroup per (stream, chunk of the window)
+    hipLaunchKernelGGL((kern::art_win_part_kernel<KV_FP8, D, B, GM>), dim3(p.batch * p.hkv * p.win_n),
+                       dim3(64 * kern::Cfg<KV_FP8, D, B, GM>::C), 0, st, p);
+  } else if (p.win == 2) {
+    // windowed, fold: win_k workgroups per (stream, query head)
+    hipLaunchKernelGGL((kern::art_win_scan_kernel<KV_FP8, D, B, GM, 64>), dim3(p.batch * p.hkv * p.g * p.win_k),
+                       dim3(64 * kern::WNW), 0, st, p);
+  } else if (p.lb) {
     auto kernel = kern::art_lb_kernel<KV_FP8, D, B, GM>;
     long wgs = p.workers > 0 ? p.workers : resident_slots(kernel, threads);
     const long items = (long)p.batch * p.hkv * p.max_chunks;

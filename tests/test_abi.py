@@ -100,8 +100,20 @@ def test_workspace_size_query(lib):
 def test_kernel_choice_follows_the_knob_and_the_mode(lib, monkeypatch):
     """Which kernel a call would run, without any device call: forced schedulers, full mode, rejected args."""
     long_desc = _desc(batch=4, num_q_heads=64, num_kv_heads=8, block_size=32, max_blocks_per_seq=4096)
+    qwen_desc = _desc(batch=64, num_q_heads=28, num_kv_heads=4, max_blocks_per_seq=1024,
+                      kv_dtype=art.ART_DTYPE_FP8_E4M3FN)
+    # auto (no device here: 256 CUs assumed): few long streams -> windows, groups above 4 heads -> look-back
+    monkeypatch.delenv("ART_SCHED", raising=False)
+    assert art.art_decode_kernel_choice(long_desc, 5e-4, 5e-5, 6) == art.ART_KERNEL_WINDOWED
+    assert art.art_decode_kernel_choice(qwen_desc, 1e-3, 1e-4, 4) == art.ART_KERNEL_LOOKBACK
+    assert art.art_decode_kernel_choice(_desc(), 1e-3, 1e-4, 4) == art.ART_KERNEL_SCANNERS
+    assert art.art_decode_kernel_choice(_desc(max_blocks_per_seq=8192), 1e-3, 1e-4, 4) == art.ART_KERNEL_WINDOWED
     monkeypatch.setenv("ART_SCHED", "scan")
     assert art.art_decode_kernel_choice(long_desc, 1e-3, 1e-4, 4) == art.ART_KERNEL_SCANNERS
+    monkeypatch.setenv("ART_SCHED", "win")
+    assert art.art_decode_kernel_choice(_desc(), 1e-3, 1e-4, 4) == art.ART_KERNEL_WINDOWED
+    # the windowed path carries the pass count as a float: beyond 2^24, scanners
+    assert art.art_decode_kernel_choice(_desc(), 1e-3, 1e-4, (1 << 24) + 1) == art.ART_KERNEL_SCANNERS
     monkeypatch.setenv("ART_SCHED", "lb")
     assert art.art_decode_kernel_choice(_desc(), 1e-3, 1e-4, 4) == art.ART_KERNEL_LOOKBACK
     # pass counts above 2047 do not fit the look-back records: scanners

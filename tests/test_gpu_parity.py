@@ -241,6 +241,13 @@ SCAN_VARIANTS = [
 ]
 
 
+WIN_VARIANTS = [
+    dict(ART_SCHED="win"),                                    # one fold workgroup per (stream, head)
+    dict(ART_SCHED="win", ART_WIN_SPLIT="2"),
+    dict(ART_SCHED="win", ART_WIN_SPLIT="4"),                 # a 64-chunk window over four workgroups
+]
+
+
 def _with_env(env, fn):
     import os
 
@@ -260,7 +267,7 @@ SCHED_CASES = [(W.LLAMA3_8B, dict(batch=3, context=8192 - 40)), (W.RAGGED, dict(
                (W.QWEN_FP8, dict(batch=2, context=16384 - 3)), (W.LONG, dict(batch=1, context=131072 - 17))]
 
 
-@pytest.mark.parametrize("variants", [LB_VARIANTS, SCAN_VARIANTS], ids=["lookback", "scanners"])
+@pytest.mark.parametrize("variants", [LB_VARIANTS, SCAN_VARIANTS, WIN_VARIANTS], ids=["lookback", "scanners", "windowed"])
 @pytest.mark.parametrize("w,kw", SCHED_CASES, ids=["llama", "ragged", "fp8", "long"])
 def test_scheduler_variants_bit_identical(w, kw, variants):
     case = synth.make_case(w, **kw)
@@ -280,6 +287,18 @@ def test_scheduler_variants_bit_identical(w, kw, variants):
         g = case["num_q_heads"] // case["num_kv_heads"]
         grp_max = stop.reshape(case["batch"], case["num_kv_heads"], g).max(axis=2)
         assert np.all(fetched >= grp_max) and np.all(fetched <= n[:, None]), env
+
+
+@pytest.mark.parametrize("w,kw", SCHED_CASES, ids=["llama", "ragged", "fp8", "long"])
+def test_windowed_and_lookback_give_the_same_bits(w, kw):
+    """Both fold the same chunk aggregates left to right and evaluate every position from the state entering
+    its chunk with the same arithmetic, so outputs and stops agree bit for bit."""
+    case = synth.make_case(w, **kw)
+    em, ed, p = case["eps_mag"], case["eps_dir"], case["patience"]
+    print(f"[win=lb] {case['workload']}", flush=True)
+    a = _with_env(dict(ART_SCHED="lb"), lambda: _device_run(case, em, ed, p))
+    b = _with_env(dict(ART_SCHED="win"), lambda: _device_run(case, em, ed, p))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
 def test_scheduler_epoch_advances_and_no_error():
@@ -310,7 +329,9 @@ def test_scheduler_epoch_advances_and_no_error():
             assert torch.equal(o, outs[0][0]) and torch.equal(s_, outs[0][1])
         return outs[0]
 
-    run(dict(ART_SCHED="lb"), lambda i: i + 1)
+    lb = run(dict(ART_SCHED="lb"), lambda i: i + 1)
+    wn = run(dict(ART_SCHED="win"), lambda i: 0)   # the windowed path uses no epoch-tagged words
+    assert torch.equal(lb[0], wn[0]) and torch.equal(lb[1], wn[1])
     a = run(dict(ART_SCHED="scan", ART_HELPERS="64"), lambda i: i + 1)
     b = run(dict(ART_SCHED="scan", ART_HELPERS="0"), lambda i: 0)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
@@ -321,15 +342,17 @@ def test_scheduler_epoch_advances_and_no_error():
 # ART_SCHED=auto sends only few, long streams to the look-back kernel; these run the shape corners and the
 # edge cases through it explicitly.
 
+@pytest.mark.parametrize("sched", ["lb", "win"])
 @pytest.mark.parametrize("w", SHAPES, ids=[w.name for w in SHAPES])
-def test_lookback_shape_matrix(w):
+def test_lookback_and_windowed_shape_matrix(w, sched):
     case = synth.make_case(w, batch=2, context=2000 + 9)
-    print(f"[lb shape] {w.name}", flush=True)
-    _with_env(dict(ART_SCHED="lb"), lambda: check_art(case))
+    print(f"[{sched} shape] {w.name}", flush=True)
+    _with_env(dict(ART_SCHED=sched), lambda: check_art(case))
 
 
-def test_lookback_edge_cases():
-    env = dict(ART_SCHED="lb", ART_WINDOW="2")
+@pytest.mark.parametrize("env", [dict(ART_SCHED="lb", ART_WINDOW="2"), dict(ART_SCHED="win", ART_WIN_SPLIT="2")],
+                         ids=["lookback", "windowed"])
+def test_lookback_and_windowed_edge_cases(env):
     base = synth.make_case(W.LLAMA3_8B, batch=5, context=700)
     case = _with_lens(base, [0, 1, 15, 16, 17])
     _with_env(env, lambda: check_art(case, patience=1, eps_mag=0.5, eps_dir=0.5))
@@ -352,12 +375,16 @@ def test_lookback_edge_cases():
     rep, out, stop, fetched = _with_env(env, lambda: check_art(case, eps_mag=10.0, eps_dir=10.0, patience=1))
     assert np.all(stop == 2)
     _with_env(env, lambda: check_art(case, eps_mag=10.0, eps_dir=10.0, patience=5))
-    # patience above what the look-back records hold: the call runs the scanners, same contract
+    # a patience no head can reach: every head runs to its end
+    rep, out, stop, fetched = _with_env(env, lambda: check_art(case, eps_mag=10.0, eps_dir=10.0, patience=3000))
+    assert np.all(stop == _nblocks(case)[:, None])
     from kv_cache_run_amd import art
 
     dev = art.case_to_device(case)
     desc = art.make_desc(dev["q"], dev["k_pages"], dev["block_table"])
-    assert _with_env(env, lambda: art.art_decode_kernel_choice(desc, 1e-3, 1e-4, 3000)) == art.ART_KERNEL_SCANNERS
-    assert _with_env(env, lambda: art.art_decode_kernel_choice(desc, 1e-3, 1e-4, 30)) == art.ART_KERNEL_LOOKBACK
-    rep, out, stop, fetched = _with_env(env, lambda: check_art(case, eps_mag=10.0, eps_dir=10.0, patience=3000))
-    assert np.all(stop == _nblocks(case)[:, None])
+    if env["ART_SCHED"] == "lb":
+        # patience above what the look-back records hold: that call ran the scanners, same contract
+        assert _with_env(env, lambda: art.art_decode_kernel_choice(desc, 1e-3, 1e-4, 3000)) == art.ART_KERNEL_SCANNERS
+        assert _with_env(env, lambda: art.art_decode_kernel_choice(desc, 1e-3, 1e-4, 30)) == art.ART_KERNEL_LOOKBACK
+    else:
+        assert _with_env(env, lambda: art.art_decode_kernel_choice(desc, 1e-3, 1e-4, 3000)) == art.ART_KERNEL_WINDOWED
