@@ -140,6 +140,126 @@ def read_traffic(kernel: str, workload: str) -> dict | None:
         return None
 
 
+# A "setting" is (thresholds, patience, flags).  One reference call learns
+# the work (stops, tiles read); then K calls are captured into one HIP
+# graph over rotating page-pool copies and replayed between two events.
+def time_setting(case, dev, em, ed, patience, flags, steps, warmup, outputs=False):
+    import torch
+
+    from kv_cache_run_amd import art
+
+    stream = torch.cuda.current_stream()
+    B = case["block_size"]
+    n = (case["seq_lens"].astype(np.int64) + B - 1) // B
+    total_blocks = int(n.sum()) * case["num_kv_heads"]
+    kv_tile = 2 * B * case["head_dim"] * {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}[case["kv_dtype"]]
+    pool_bytes = case["k_pages"].nbytes + case["v_pages"].nbytes
+    out = torch.empty((case["batch"], case["num_q_heads"], case["head_dim"]), dtype=torch.float32,
+                      device="cuda")
+    stop = torch.empty((case["batch"], case["num_q_heads"]), dtype=torch.int32, device="cuda")
+    fetched = torch.empty((case["batch"], case["num_kv_heads"]), dtype=torch.int32, device="cuda")
+
+    def one_call(table, dec, kp, vp, ks, vs):
+        dec(dev["q"], kp, vp, table, dev["block_order"], dev["seq_lens"], em, ed, patience, k_scale=ks,
+            v_scale=vs, out=out, stop_block=stop, blocks_fetched=fetched, flags=flags)
+
+    dec = art.Decoder(dev["q"], dev["k_pages"], dev["block_table"])
+    one_call(dev["block_table"], dec, dev["k_pages"], dev["v_pages"], dev["k_scale"], dev["v_scale"])
+    torch.cuda.synchronize()
+    stop_h = stop.cpu().numpy()
+    fetched_h = fetched.cpu().numpy()
+    out_h = out.cpu().numpy() if outputs else None
+    read_bytes = int(fetched_h.sum()) * kv_tile
+    # page-pool copies so that consecutive calls read cold memory
+    R = int(min(64, max(2, math.ceil(512e6 / max(read_bytes, 1)) + 1),
+                max(2, (48 << 30) // max(pool_bytes, 1))))
+
+    def rep(t):
+        if t.dtype == torch.float8_e4m3fn:
+            return t.view(torch.uint8).repeat(R, 1, 1, 1).view(torch.float8_e4m3fn)
+        return t.repeat(R, 1, 1, 1)
+
+    kp = rep(dev["k_pages"])
+    vp = rep(dev["v_pages"])
+    ks = None if dev["k_scale"] is None else dev["k_scale"].repeat(R, 1)
+    vs = None if dev["v_scale"] is None else dev["v_scale"].repeat(R, 1)
+    npages = case["num_pages"]
+    tables = [dev["block_table"] + r * npages for r in range(R)]
+    dec = art.Decoder(dev["q"], kp, dev["block_table"])
+    for i in range(warmup):
+        one_call(tables[i % R], dec, kp, vp, ks, vs)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            one_call(tables[(warmup + i) % R], dec, kp, vp, ks, vs)
+    graph.replay()  # first replay uploads the graph; untimed
+    torch.cuda.synchronize()
+    out_first = out.clone()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / steps
+    assert np.array_equal(stop.cpu().numpy(), stop_h), "stops changed across page copies / replays"
+    assert torch.equal(out, out_first), "graph replays disagree"
+    del graph, kp, vp, ks, vs, tables, dec
+    torch.cuda.empty_cache()
+    alg = algorithmic_bytes(case, stop_h)
+    us = ms * 1e3
+    res = {
+        "us_per_step": us,
+        "wall_s": wall,
+        "page_copies": R,
+        "alg_bytes": alg["total"],
+        "read_bytes": read_bytes,
+        "achieved_GBps": alg["total"] / (us * 1e-6) / 1e9,
+        "read_GBps": read_bytes / (us * 1e-6) / 1e9,
+        "kv_fraction_read": float(fetched_h.sum()) / total_blocks,
+        "kv_fraction_needed": alg["blocks"] / total_blocks,
+    }
+    if outputs:
+        res["out"], res["stop"] = out_h, stop_h
+    return res
+
+
+def ablation(steps: int, warmup: int) -> dict:
+    """Detector ablation: per workload and variant, the step time, the KV fractions and the error of the
+    output at the stop against full attention on the same inputs (both from the device).  A switched-off
+    test is a threshold of +inf."""
+    from kv_cache_run_amd import art, synth, workloads
+
+    res = {}
+    for w in workloads.ABLATION:
+        case = synth.make_case(w)
+        dev = art.case_to_device(case)
+        em, ed, p = case["eps_mag"], case["eps_dir"], case["patience"]
+        full = time_setting(case, dev, 0.0, 0.0, p, art.ART_FLAG_FULL, steps, warmup, outputs=True)
+        ref = full["out"].astype(np.float64)
+        nrm = np.linalg.norm(ref, axis=-1)
+        n = (case["seq_lens"].astype(np.int64) + case["block_size"] - 1) // case["block_size"]
+        rows = {"full": {"us_per_step": round(full["us_per_step"], 3)}}
+        for name, (e1, e2, pp) in {"both": (em, ed, p), "scale_only": (em, math.inf, p),
+                                   "direction_only": (math.inf, ed, p), "patience_1": (em, ed, 1)}.items():
+            r = time_setting(case, dev, e1, e2, pp, 0, steps, warmup, outputs=True)
+            err = np.linalg.norm(r["out"].astype(np.float64) - ref, axis=-1) / np.maximum(nrm, 1e-30)
+            rows[name] = {
+                "us_per_step": round(r["us_per_step"], 3),
+                "kv_fraction_read": round(r["kv_fraction_read"], 5),
+                "stop_fraction_mean": round(float((r["stop"] / n[:, None]).mean()), 5),
+                "rel_err_vs_full_mean": float(f"{err.mean():.4g}"),
+                "rel_err_vs_full_p99": float(f"{np.percentile(err, 99):.4g}"),
+                "rel_err_vs_full_max": float(f"{err.max():.4g}"),
+            }
+        res[w.name] = rows
+        del dev
+    return res
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +272,9 @@ def main(argv=None) -> int:
     ap.add_argument("--modes", default="art,full")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the threshold sweep and the detector-overhead run")
+    ap.add_argument("--ablation", action="store_true",
+                    help="also run the detector ablation (both tests, scale only, direction only, patience 1) on "
+                         "the Llama-3-8B shape with Gaussian, heavy-tailed and value-heavy K/V")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -171,92 +294,15 @@ def main(argv=None) -> int:
     torch.cuda.set_device(0)
     case = synth.make_case(w)
     dev = art.case_to_device(case)
-    stream = torch.cuda.current_stream()
     B = case["block_size"]
-    n = (case["seq_lens"].astype(np.int64) + B - 1) // B
-    total_blocks = int(n.sum()) * case["num_kv_heads"]
-    kv_tile = 2 * B * case["head_dim"] * {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}[case["kv_dtype"]]
-    pool_bytes = case["k_pages"].nbytes + case["v_pages"].nbytes
-
-    # A "setting" is (thresholds, patience, flags).  One reference call learns
-    # the work (stops, tiles read); then K calls are captured into one HIP
-    # graph over rotating page-pool copies and replayed between two events.
-    def time_setting(em, ed, patience, flags, steps, warmup):
-        out = torch.empty((case["batch"], case["num_q_heads"], case["head_dim"]), dtype=torch.float32,
-                          device="cuda")
-        stop = torch.empty((case["batch"], case["num_q_heads"]), dtype=torch.int32, device="cuda")
-        fetched = torch.empty((case["batch"], case["num_kv_heads"]), dtype=torch.int32, device="cuda")
-
-        def one_call(table, dec, kp, vp, ks, vs):
-            dec(dev["q"], kp, vp, table, dev["block_order"], dev["seq_lens"], em, ed, patience, k_scale=ks,
-                v_scale=vs, out=out, stop_block=stop, blocks_fetched=fetched, flags=flags)
-
-        dec = art.Decoder(dev["q"], dev["k_pages"], dev["block_table"])
-        one_call(dev["block_table"], dec, dev["k_pages"], dev["v_pages"], dev["k_scale"], dev["v_scale"])
-        torch.cuda.synchronize()
-        stop_h = stop.cpu().numpy()
-        fetched_h = fetched.cpu().numpy()
-        read_bytes = int(fetched_h.sum()) * kv_tile
-        # page-pool copies so that consecutive calls read cold memory
-        R = int(min(64, max(2, math.ceil(512e6 / max(read_bytes, 1)) + 1),
-                    max(2, (48 << 30) // max(pool_bytes, 1))))
-
-        def rep(t):
-            if t.dtype == torch.float8_e4m3fn:
-                return t.view(torch.uint8).repeat(R, 1, 1, 1).view(torch.float8_e4m3fn)
-            return t.repeat(R, 1, 1, 1)
-
-        kp = rep(dev["k_pages"])
-        vp = rep(dev["v_pages"])
-        ks = None if dev["k_scale"] is None else dev["k_scale"].repeat(R, 1)
-        vs = None if dev["v_scale"] is None else dev["v_scale"].repeat(R, 1)
-        npages = case["num_pages"]
-        tables = [dev["block_table"] + r * npages for r in range(R)]
-        dec = art.Decoder(dev["q"], kp, dev["block_table"])
-        for i in range(warmup):
-            one_call(tables[i % R], dec, kp, vp, ks, vs)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(steps):
-                one_call(tables[(warmup + i) % R], dec, kp, vp, ks, vs)
-        graph.replay()  # first replay uploads the graph; untimed
-        torch.cuda.synchronize()
-        out_first = out.clone()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        ev0.record(stream)
-        graph.replay()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        ms = ev0.elapsed_time(ev1) / steps
-        assert np.array_equal(stop.cpu().numpy(), stop_h), "stops changed across page copies / replays"
-        assert torch.equal(out, out_first), "graph replays disagree"
-        del graph, kp, vp, ks, vs, tables, dec
-        torch.cuda.empty_cache()
-        alg = algorithmic_bytes(case, stop_h)
-        us = ms * 1e3
-        return {
-            "us_per_step": us,
-            "wall_s": wall,
-            "page_copies": R,
-            "alg_bytes": alg["total"],
-            "read_bytes": read_bytes,
-            "achieved_GBps": alg["total"] / (us * 1e-6) / 1e9,
-            "read_GBps": read_bytes / (us * 1e-6) / 1e9,
-            "kv_fraction_read": float(fetched_h.sum()) / total_blocks,
-            "kv_fraction_needed": alg["blocks"] / total_blocks,
-        }
 
     em0, ed0, p0 = case["eps_mag"], case["eps_dir"], case["patience"]
     results = {}
     for mode in [m for m in args.modes.split(",") if m]:
         if mode == "art":
-            results[mode] = time_setting(em0, ed0, p0, 0, args.steps, args.warmup)
+            results[mode] = time_setting(case, dev, em0, ed0, p0, 0, args.steps, args.warmup)
         elif mode == "full":
-            results[mode] = time_setting(0.0, 0.0, p0, art.ART_FLAG_FULL, args.steps, args.warmup)
+            results[mode] = time_setting(case, dev, 0.0, 0.0, p0, art.ART_FLAG_FULL, args.steps, args.warmup)
         else:
             raise SystemExit(f"unknown mode {mode}")
 
@@ -264,7 +310,7 @@ def main(argv=None) -> int:
     if not args.no_extras and "art" in results and "full" in results:
         # detector overhead: the terminating kernel with thresholds that can never pass (it folds every
         # block and runs every test) against the full-attention kernel on the same work
-        keep = time_setting(0.0, 0.0, p0, art.ART_FLAG_KEEP_DETECTOR, max(5, args.steps // 2), 2)
+        keep = time_setting(case, dev, 0.0, 0.0, p0, art.ART_FLAG_KEEP_DETECTOR, max(5, args.steps // 2), 2)
         extras["detector_overhead"] = {
             "art_kernel_all_blocks_us": round(keep["us_per_step"], 3),
             "full_kernel_us": round(results["full"]["us_per_step"], 3),
@@ -275,7 +321,7 @@ def main(argv=None) -> int:
         # step time against the KV fraction read: thresholds scaled by 1/4 .. 4 at fixed patience
         pts = []
         for f in (0.25, 0.5, 1.0, 2.0, 4.0):
-            r = results["art"] if f == 1.0 else time_setting(em0 * f, ed0 * f, p0, 0, max(5, args.steps // 2), 2)
+            r = results["art"] if f == 1.0 else time_setting(case, dev, em0 * f, ed0 * f, p0, 0, max(5, args.steps // 2), 2)
             pts.append({"eps_scale": f, "kv_fraction_read": round(r["kv_fraction_read"], 5),
                         "kv_fraction_needed": round(r["kv_fraction_needed"], 5), "us_per_step": round(r["us_per_step"], 3)})
         x = np.array([q["kv_fraction_read"] for q in pts])
@@ -286,6 +332,9 @@ def main(argv=None) -> int:
         r2 = 1.0 - float(((y - pred) ** 2).sum()) / ss if ss > 0 else 1.0
         extras["scaling"] = {"points": pts, "slope_us_per_unit_fraction": round(float(slope), 3),
                              "intercept_us": round(float(icpt), 3), "r2": round(r2, 4)}
+
+    if args.ablation:
+        extras["ablation"] = ablation(max(5, args.steps // 2), 2)
 
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)

@@ -11,15 +11,22 @@ Recipe (fixed draw order from ``numpy.random.Generator(PCG64(seed))``):
    uniformly from [lo, hi] (inclusive).
 2. ``q`` ~ N(0, 1) of shape [batch, Hq, D], rounded to the q storage type.
 3. For each stream (sequence s, kv-head k), in that order:
-   a. K, V ~ N(0, 1) of shape [L_s, D] (float32 draws);
+   a. K, V ~ N(0, 1) of shape [L_s, D] (float32 draws), or Student-t with 3
+      degrees of freedom divided by sqrt(3) (unit variance, heavy tails) for
+      ``kv_dist = "student_t3"``;
    b. the heavy-key positions: ``round(f * L_s)`` distinct positions for
       ("frac", f); for ("frac_range", lo, hi) first f ~ U(lo, hi) per stream;
       for ("spans", c, w) c non-overlapping spans of w tokens with uniformly
-      drawn starts (redrawn on overlap);
+      drawn starts (redrawn on overlap); for ("recent", f, w) ``round(f * L_s)``
+      distinct positions among the newest ``ceil(w * L_s)`` tokens;
    c. alpha ~ U(2, 4) per heavy position; K at that position becomes
       ``8 * alpha * qbar / |qbar|`` where qbar is the sum of the stored q
       vectors of the kv-head's query group;
-   d. K and V are rounded to the KV storage type (bfloat16: round to nearest
+   d. only for workloads that ask for them, after c: value-heavy positions,
+      ``round(f * L_s)`` distinct positions drawn uniformly from the oldest
+      quarter [B, L_s / 4) (block 0 excluded), whose V rows are multiplied by
+      ``gain``;
+   e. K and V are rounded to the KV storage type (bfloat16: round to nearest
       even; fp8 E4M3FN: per (page, kv-head) tile scale = amax / 448, or 1 for
       an all-zero tile, code = nearest-even E4M3FN of value / scale clamped
       to +-448).
@@ -72,6 +79,11 @@ def _heavy_positions(rng: np.random.Generator, heavy: tuple, L: int) -> np.ndarr
         f = rng.uniform(heavy[1], heavy[2])
         cnt = int(round(f * L))
         return np.sort(rng.choice(L, size=min(cnt, L), replace=False))
+    if kind == "recent":
+        # round(f * L) distinct positions among the newest ceil(w * L) tokens
+        span = min(L, max(1, int(np.ceil(heavy[2] * L))))
+        cnt = min(int(round(heavy[1] * L)), span)
+        return np.sort(L - span + rng.choice(span, size=cnt, replace=False))
     if kind == "spans":
         count, width = int(heavy[1]), int(heavy[2])
         starts = []
@@ -152,14 +164,21 @@ def make_case(w: Workload, *, seed: Optional[int] = None, batch: Optional[int] =
         raise ValueError(w.kv_dtype)
 
     planted = {}
+    planted_value = {}
     # 3. per stream K/V, heavy keys, storage rounding, paging
     for s in range(batch):
         L = int(seq_lens[s])
         n = int(nblk[s])
         pages = block_table[s, :n].astype(np.int64)
         for k in range(Hkv):
-            K = rng.standard_normal((L, D), dtype=np.float32)
-            V = rng.standard_normal((L, D), dtype=np.float32)
+            if w.kv_dist == "normal":
+                K = rng.standard_normal((L, D), dtype=np.float32)
+                V = rng.standard_normal((L, D), dtype=np.float32)
+            elif w.kv_dist == "student_t3":
+                K = (rng.standard_t(3.0, size=(L, D)) / np.sqrt(3.0)).astype(np.float32)
+                V = (rng.standard_t(3.0, size=(L, D)) / np.sqrt(3.0)).astype(np.float32)
+            else:
+                raise ValueError(w.kv_dist)
             pos = _heavy_positions(rng, w.heavy, L)
             alpha = rng.uniform(2.0, 4.0, size=len(pos))
             qbar = q_vals[s, k * g:(k + 1) * g].sum(axis=0)
@@ -167,6 +186,13 @@ def make_case(w: Workload, *, seed: Optional[int] = None, batch: Optional[int] =
             if len(pos):
                 K[pos] = (8.0 * alpha[:, None] * (qbar / nq)[None, :]).astype(np.float32)
             planted[(s, k)] = (pos, alpha)
+            if w.value_heavy:
+                f, gain = w.value_heavy
+                lo, hi = min(B, L), max(min(B, L), L // 4)
+                cnt = min(int(round(f * L)), hi - lo)
+                vpos = np.sort(rng.choice(np.arange(lo, hi), size=cnt, replace=False)) if cnt > 0 else np.zeros(0, np.int64)
+                V[vpos] *= np.float32(gain)
+                planted_value[(s, k)] = vpos
             pad = n * B - L
             Kp = np.concatenate([K, np.zeros((pad, D), np.float32)]).reshape(n, B, D)
             Vp = np.concatenate([V, np.zeros((pad, D), np.float32)]).reshape(n, B, D)
@@ -202,7 +228,7 @@ def make_case(w: Workload, *, seed: Optional[int] = None, batch: Optional[int] =
         "batch": batch, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": B,
         "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype, "max_blocks": max_blocks, "num_pages": num_pages,
         "eps_mag": w.eps_mag, "eps_dir": w.eps_dir, "patience": w.patience,
-        "planted": planted,
+        "planted": planted, "planted_value": planted_value,
     }
 
 

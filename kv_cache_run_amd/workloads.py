@@ -32,6 +32,8 @@ class Workload:
     seed: int
     order: str = "sink_then_newest"        # block 0 first, then newest to oldest
     tail_fill: bool = True                 # poison rows past seq_len in the last page
+    kv_dist: str = "normal"                # K/V entries: "normal" N(0, 1) | "student_t3" (3 degrees of freedom)
+    value_heavy: tuple = ()                # () | (f, gain): round(f * L) positions in the oldest quarter, V *= gain
 
     @property
     def group(self) -> int:
@@ -67,4 +69,16 @@ QWEN_FP8 = Workload(
     eps_mag=1e-3, eps_dir=1e-4, patience=4, seed=5)
 
 ALL = (TINY, LLAMA3_8B, RAGGED, LONG, QWEN_FP8)
-BY_NAME = {w.name: w for w in ALL}
+
+# Inputs for the ablation of the detector (scale-only, direction-only,
+# patience 1), all on the Llama-3-8B shape: heavy-tailed K/V; a few
+# value-heavy tokens (ordinary keys, values 32x larger) among the oldest,
+# which the default order visits last -- a head can look converged before it
+# has seen what matters; and, as the control, heavy keys only among the
+# newest 5% of tokens, which the default order visits first.
+HEAVY_TAIL = LLAMA3_8B.scaled(name="heavytail-t3-gqa4-bf16-b8-ctx8192-blk16", kv_dist="student_t3", seed=6)
+VALUE_HEAVY = LLAMA3_8B.scaled(name="valueheavy-gqa4-bf16-b8-ctx8192-blk16", value_heavy=(0.002, 32.0), seed=7)
+RECENT = LLAMA3_8B.scaled(name="recent-gqa4-bf16-b8-ctx8192-blk16", heavy=("recent", 0.01, 0.05), seed=8)
+ABLATION = (LLAMA3_8B, HEAVY_TAIL, VALUE_HEAVY, RECENT)
+
+BY_NAME = {w.name: w for w in ALL + ABLATION}

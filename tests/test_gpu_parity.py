@@ -7,6 +7,8 @@ same tolerance.  Reduced sizes compare every head; full sizes compare sampled
 heads plus properties that hold at any size.
 """
 
+import math
+
 import numpy as np
 import pytest
 
@@ -388,3 +390,24 @@ def test_lookback_and_windowed_edge_cases(env):
         assert _with_env(env, lambda: art.art_decode_kernel_choice(desc, 1e-3, 1e-4, 30)) == art.ART_KERNEL_LOOKBACK
     else:
         assert _with_env(env, lambda: art.art_decode_kernel_choice(desc, 1e-3, 1e-4, 3000)) == art.ART_KERNEL_WINDOWED
+
+
+# ---- detector ablation: one test switched off (threshold +inf) or patience 1 -----------------------------
+
+ABLATION_VARIANTS = {"scale_only": (None, math.inf, None), "direction_only": (math.inf, None, None),
+                     "patience_1": (None, None, 1), "both_off": (math.inf, math.inf, None)}
+
+
+@pytest.mark.parametrize("variant", list(ABLATION_VARIANTS), ids=list(ABLATION_VARIANTS))
+@pytest.mark.parametrize("w", [W.HEAVY_TAIL, W.VALUE_HEAVY, W.RECENT], ids=["heavytail", "valueheavy", "recent"])
+def test_ablation_variants_parity(w, variant):
+    case = synth.make_case(w, batch=2, context=4096 - 5)
+    em, ed, p = ABLATION_VARIANTS[variant]
+    check_art(case, eps_mag=em, eps_dir=ed, patience=p)
+
+
+@pytest.mark.parametrize("sched", ["lb", "win"])
+def test_ablation_through_lookback_and_windowed(sched):
+    case = synth.make_case(W.VALUE_HEAVY, batch=2, context=4096 - 5)
+    _with_env(dict(ART_SCHED=sched), lambda: check_art(case, eps_dir=math.inf))
+    _with_env(dict(ART_SCHED=sched), lambda: check_art(case, eps_mag=math.inf, patience=1))

@@ -69,3 +69,41 @@ def test_fp8_tiles_use_amax_over_448_scales():
     # each tile's largest code is +-448 (the amax maps to the top of the range)
     assert np.all(mags.reshape(codes.shape[0], codes.shape[1], -1).max(-1) == 448.0)
     assert np.all(c["k_scale"] > 0) and c["k_scale"].dtype == np.float32
+
+
+def test_value_heavy_rows_sit_in_the_oldest_quarter_with_the_gain():
+    """The value-heavy recipe scales V at round(f L) positions in [B, L/4) by the gain.  Its positions are drawn
+    after the first stream's K/V, so that stream matches the same seed without the recipe except at them."""
+    w = W.VALUE_HEAVY
+    c = synth.make_case(w, batch=2, context=4096)
+    plain = synth.make_case(w.scaled(value_heavy=()), batch=2, context=4096)
+    B = w.block_size
+    f, gain = w.value_heavy
+    for (s, k), vpos in c["planted_value"].items():
+        assert len(vpos) == round(f * 4096) and len(np.unique(vpos)) == len(vpos)
+        assert vpos.min() >= B and vpos.max() < 4096 // 4
+    vpos = c["planted_value"][(0, 0)]
+    tab = c["block_table"][0]
+    assert np.array_equal(c["k_pages"][tab, 0], plain["k_pages"][tab, 0])
+    got = oracle.decode_bf16(c["v_pages"][tab, 0]).reshape(-1, w.head_dim)
+    ref = oracle.decode_bf16(plain["v_pages"][tab, 0]).reshape(-1, w.head_dim)
+    rest = np.setdiff1d(np.arange(4096), vpos)
+    assert np.array_equal(got[rest], ref[rest])
+    # bf16(gain * x) == gain * bf16(x) for a power-of-two gain
+    assert np.array_equal(got[vpos], gain * ref[vpos])
+
+
+def test_student_t_draws_have_heavier_tails_than_normal():
+    """kv_dist="student_t3": unit variance, kurtosis far above the normal's 3."""
+    c = synth.make_case(W.HEAVY_TAIL, batch=1, context=8192)
+    v = oracle.decode_bf16(c["v_pages"][c["block_table"][0, :512], 0]).ravel()
+    assert abs(v.var() - 1.0) < 0.25
+    kurt = np.mean((v - v.mean()) ** 4) / v.var() ** 2
+    assert kurt > 6.0
+
+
+def test_recent_recipe_plants_only_among_the_newest_tokens():
+    c = synth.make_case(W.RECENT, batch=2, context=4096)
+    for (s, k), (pos, alpha) in c["planted"].items():
+        assert len(pos) == round(0.01 * 4096) and len(np.unique(pos)) == len(pos)
+        assert pos.min() >= 4096 - int(np.ceil(0.05 * 4096))
