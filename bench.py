@@ -143,7 +143,7 @@ def read_traffic(kernel: str, workload: str) -> dict | None:
 # A "setting" is (thresholds, patience, flags).  One reference call learns
 # the work (stops, tiles read); then K calls are captured into one HIP
 # graph over rotating page-pool copies and replayed between two events.
-def time_setting(case, dev, em, ed, patience, flags, steps, warmup, outputs=False):
+def time_setting(case, dev, em, ed, patience, flags, steps, warmup, outputs=False, visit_lens=None):
     import torch
 
     from kv_cache_run_amd import art
@@ -161,7 +161,7 @@ def time_setting(case, dev, em, ed, patience, flags, steps, warmup, outputs=Fals
 
     def one_call(table, dec, kp, vp, ks, vs):
         dec(dev["q"], kp, vp, table, dev["block_order"], dev["seq_lens"], em, ed, patience, k_scale=ks,
-            v_scale=vs, out=out, stop_block=stop, blocks_fetched=fetched, flags=flags)
+            v_scale=vs, out=out, stop_block=stop, blocks_fetched=fetched, flags=flags, visit_lens=visit_lens)
 
     dec = art.Decoder(dev["q"], dev["k_pages"], dev["block_table"])
     one_call(dev["block_table"], dec, dev["k_pages"], dev["v_pages"], dev["k_scale"], dev["v_scale"])
@@ -227,6 +227,33 @@ def time_setting(case, dev, em, ed, patience, flags, steps, warmup, outputs=Fals
     return res
 
 
+def pruned(case: dict, dev: dict, steps: int, warmup: int) -> dict:
+    """ART over a pruned cache (the default order visits block 0, then newest to oldest, so its first 1 + w
+    entries are block 0 plus a recent window of w blocks) against full attention over the same blocks."""
+    import torch
+
+    from kv_cache_run_amd import art
+
+    B = case["block_size"]
+    n = (case["seq_lens"].astype(np.int64) + B - 1) // B
+    res = {}
+    for frac in (4, 16):
+        vl_h = np.minimum(n, 1 + np.maximum(1, n // frac)).astype(np.int32)
+        vl = torch.from_numpy(vl_h).cuda()
+        a = time_setting(case, dev, case["eps_mag"], case["eps_dir"], case["patience"], 0, steps, warmup,
+                         visit_lens=vl)
+        f = time_setting(case, dev, 0.0, 0.0, case["patience"], art.ART_FLAG_FULL, steps, warmup, visit_lens=vl)
+        tot = int(n.sum()) * case["num_kv_heads"]
+        res[f"sink_plus_newest_1_{frac}"] = {
+            "visited_fraction": round(float(vl_h.sum()) * case["num_kv_heads"] / tot, 5),
+            "art_us_per_step": round(a["us_per_step"], 3),
+            "art_kv_fraction_read": round(a["kv_fraction_read"], 5),
+            "full_over_subset_us_per_step": round(f["us_per_step"], 3),
+            "full_over_subset_kv_fraction_read": round(f["kv_fraction_read"], 5),
+        }
+    return res
+
+
 def ablation(steps: int, warmup: int) -> dict:
     """Detector ablation: per workload and variant, the step time, the KV fractions and the error of the
     output at the stop against full attention on the same inputs (both from the device).  A switched-off
@@ -272,6 +299,9 @@ def main(argv=None) -> int:
     ap.add_argument("--modes", default="art,full")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the threshold sweep and the detector-overhead run")
+    ap.add_argument("--pruned", action="store_true",
+                    help="also run ART over a pruned cache (block 0 plus the newest quarter / sixteenth of the "
+                         "blocks, through art_decode_visits) against full attention over the same blocks")
     ap.add_argument("--ablation", action="store_true",
                     help="also run the detector ablation (both tests, scale only, direction only, patience 1) on "
                          "the Llama-3-8B shape with Gaussian, heavy-tailed and value-heavy K/V")
@@ -335,6 +365,8 @@ def main(argv=None) -> int:
 
     if args.ablation:
         extras["ablation"] = ablation(max(5, args.steps // 2), 2)
+    if args.pruned:
+        extras["pruned"] = pruned(case, dev, max(5, args.steps // 2), 2)
 
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)

@@ -155,6 +155,32 @@ art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_
                       int32_t patience, float* out, int32_t* stop_block, int32_t* blocks_fetched,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * ART over a pruned cache: art_decode with every sequence visiting only the
+ * first visit_lens[s] entries of its block_order row -- a caller-chosen
+ * subset of its blocks, e.g. block 0 plus a recent window, or a selected set
+ * (the ART explainer, Technical Summary 2.4, layers ART over cache-pruning
+ * methods through the traversal order; section 4 evaluates it combined with
+ * them).  The detector, the patience rule and the block-0 condition run over
+ * the visited blocks only, so a head whose subset lacks block 0 never stops
+ * early.
+ *
+ * visit_lens   [batch] int32 device array, or NULL (= art_decode: n_s each).
+ *              Entry s is clamped to [0, n_s]; the first visit_lens[s]
+ *              entries of block_order row s must be distinct logical blocks
+ *              in [0, n_s) (they need not be a permutation of all of them).
+ * stop_block   then counts visited blocks: 0 .. visit_lens[s] (visit_lens[s]
+ *              when the head never stopped; 0 for an empty subset, with out 0).
+ * Full attention (ART_FLAG_FULL or a zero threshold) attends over the
+ * visited blocks.  Every other argument, error and the workspace are as for
+ * art_decode, which equals art_decode_visits with visit_lens = NULL.
+ */
+art_status art_decode_visits(const art_decode_desc* desc, const void* q, const void* k_pages, const void* v_pages,
+                             const float* k_scale, const float* v_scale, const int32_t* block_table,
+                             const int32_t* block_order, const int32_t* seq_lens, const int32_t* visit_lens,
+                             float eps_mag, float eps_dir, int32_t patience, float* out, int32_t* stop_block,
+                             int32_t* blocks_fetched, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code (host memory, never NULL). */
 const char* art_status_string(art_status status);
 

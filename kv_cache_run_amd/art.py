@@ -20,8 +20,8 @@ ART_OK, ART_ERR_INVALID_ARG, ART_ERR_UNSUPPORTED, ART_ERR_WORKSPACE, ART_ERR_HIP
 ART_DTYPE_F32, ART_DTYPE_BF16, ART_DTYPE_FP8_E4M3FN = range(3)
 ART_FLAG_NONE, ART_FLAG_FULL, ART_FLAG_KEEP_DETECTOR = 0, 1, 2
 
-EXPORTED = ("art_decode_workspace_bytes", "art_decode_workspace_init", "art_decode", "art_status_string",
-            "art_decode_version", "art_decode_kernel_choice")
+EXPORTED = ("art_decode_workspace_bytes", "art_decode_workspace_init", "art_decode", "art_decode_visits",
+            "art_status_string", "art_decode_version", "art_decode_kernel_choice")
 ART_KERNEL_FULL, ART_KERNEL_SCANNERS, ART_KERNEL_LOOKBACK, ART_KERNEL_WINDOWED = 0, 1, 2, 3
 KERNEL_NAMES = {ART_KERNEL_FULL: "full_split_kernel", ART_KERNEL_SCANNERS: "art_sched_kernel",
                 ART_KERNEL_LOOKBACK: "art_lb_kernel", ART_KERNEL_WINDOWED: "art_win_part_kernel"}
@@ -69,6 +69,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.art_decode.argtypes = [ctypes.POINTER(ArtDecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, f32, f32, i32, vp,
                                vp, vp, vp, sz, vp]
     lib.art_decode.restype = ctypes.c_int
+    lib.art_decode_visits.argtypes = [ctypes.POINTER(ArtDecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, f32,
+                                      i32, vp, vp, vp, vp, sz, vp]
+    lib.art_decode_visits.restype = ctypes.c_int
     lib.art_status_string.argtypes = [ctypes.c_int]
     lib.art_status_string.restype = ctypes.c_char_p
     lib.art_decode_version.argtypes = []
@@ -146,18 +149,27 @@ def art_decode_workspace_init(workspace, stream=None) -> None:
 
 def art_decode(q, k_pages, v_pages, block_table, block_order, seq_lens, eps_mag: float, eps_dir: float,
                patience: int, out, stop_block, *, k_scale=None, v_scale=None, blocks_fetched=None, workspace=None,
-               flags: int = 0, stream=None) -> None:
-    """Enqueue one ART decode step (see include/art_decode.h); tensors must be contiguous on the device."""
+               flags: int = 0, stream=None, visit_lens=None) -> None:
+    """Enqueue one ART decode step (see include/art_decode.h); tensors must be contiguous on the device.
+    ``visit_lens`` (int32 [batch]) visits only the first visit_lens[s] order entries: art_decode_visits."""
     for t in (q, k_pages, v_pages, block_table, block_order, seq_lens, out, stop_block, k_scale, v_scale,
-              blocks_fetched, workspace):
+              blocks_fetched, workspace, visit_lens):
         if t is not None and not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
     desc = make_desc(q, k_pages, block_table, flags)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load_library().art_decode(ctypes.byref(desc), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
+    lib = load_library()
+    if visit_lens is None:
+        st = lib.art_decode(ctypes.byref(desc), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale), _ptr(v_scale),
+                            _ptr(block_table), _ptr(block_order), _ptr(seq_lens), float(eps_mag), float(eps_dir),
+                            int(patience), _ptr(out), _ptr(stop_block), _ptr(blocks_fetched), _ptr(workspace), nbytes,
+                            _stream(stream))
+    else:
+        st = lib.art_decode_visits(ctypes.byref(desc), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
                                    _ptr(v_scale), _ptr(block_table), _ptr(block_order), _ptr(seq_lens),
-                                   float(eps_mag), float(eps_dir), int(patience), _ptr(out), _ptr(stop_block),
-                                   _ptr(blocks_fetched), _ptr(workspace), nbytes, _stream(stream))
+                                   _ptr(visit_lens), float(eps_mag), float(eps_dir), int(patience), _ptr(out),
+                                   _ptr(stop_block), _ptr(blocks_fetched), _ptr(workspace), nbytes,
+                                   _stream(stream))
     _check(st)
 
 
@@ -175,7 +187,8 @@ class Decoder:
             art_decode_workspace_init(self.workspace)
 
     def __call__(self, q, k_pages, v_pages, block_table, block_order, seq_lens, eps_mag, eps_dir, patience, *,
-                 k_scale=None, v_scale=None, out=None, stop_block=None, blocks_fetched=None, flags=0, stream=None):
+                 k_scale=None, v_scale=None, out=None, stop_block=None, blocks_fetched=None, flags=0, stream=None,
+                 visit_lens=None):
         import torch
 
         batch, hq, d = q.shape
@@ -185,7 +198,7 @@ class Decoder:
             stop_block = torch.empty((batch, hq), dtype=torch.int32, device=q.device)
         art_decode(q, k_pages, v_pages, block_table, block_order, seq_lens, eps_mag, eps_dir, patience, out,
                    stop_block, k_scale=k_scale, v_scale=v_scale, blocks_fetched=blocks_fetched,
-                   workspace=self.workspace, flags=flags, stream=stream)
+                   workspace=self.workspace, flags=flags, stream=stream, visit_lens=visit_lens)
         return out, stop_block
 
 

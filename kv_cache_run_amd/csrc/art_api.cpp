@@ -229,6 +229,16 @@ art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_
                       const int32_t* block_order, const int32_t* seq_lens, float eps_mag, float eps_dir,
                       int32_t patience, float* out, int32_t* stop_block, int32_t* blocks_fetched,
                       void* workspace, size_t workspace_bytes, void* stream) {
+  return art_decode_visits(desc, q, k_pages, v_pages, k_scale, v_scale, block_table, block_order, seq_lens, nullptr,
+                           eps_mag, eps_dir, patience, out, stop_block, blocks_fetched, workspace, workspace_bytes,
+                           stream);
+}
+
+art_status art_decode_visits(const art_decode_desc* desc, const void* q, const void* k_pages, const void* v_pages,
+                             const float* k_scale, const float* v_scale, const int32_t* block_table,
+                             const int32_t* block_order, const int32_t* seq_lens, const int32_t* visit_lens,
+                             float eps_mag, float eps_dir, int32_t patience, float* out, int32_t* stop_block,
+                             int32_t* blocks_fetched, void* workspace, size_t workspace_bytes, void* stream) {
   const art_status ds = check_desc(desc);
   if (ds != ART_OK) return ds;
   if (!(eps_mag >= 0.f) || !(eps_dir >= 0.f) || patience < 1) return ART_ERR_INVALID_ARG;
@@ -239,7 +249,7 @@ art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_
   if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16) ||
       !aligned(block_table, 4) || !aligned(block_order, 4) || !aligned(seq_lens, 4) || !aligned(stop_block, 4) ||
       (blocks_fetched && !aligned(blocks_fetched, 4)) || (k_scale && !aligned(k_scale, 4)) ||
-      (v_scale && !aligned(v_scale, 4)))
+      (v_scale && !aligned(v_scale, 4)) || (visit_lens && !aligned(visit_lens, 4)))
     return ART_ERR_INVALID_ARG;
   const art::WorkspacePlan wp = plan_workspace(desc);
   if (wp.total > 0) {
@@ -265,6 +275,7 @@ art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_
   p.v_scale = v_scale;
   p.block_table = block_table;
   p.block_order = block_order;
+  p.visit_lens = visit_lens;
   p.seq_lens = seq_lens;
   p.out = out;
   p.stop_block = stop_block;

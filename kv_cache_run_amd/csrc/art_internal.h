@@ -33,6 +33,7 @@ struct Params {
   const int32_t* block_table;
   const int32_t* block_order;
   const int32_t* seq_lens;
+  const int32_t* visit_lens;  // [batch] visited leading entries of block_order (null: all n_s)
   float* out;
   int32_t* stop_block;
   int32_t* blocks_fetched;  // may be null

@@ -603,6 +603,18 @@ __device__ __forceinline__ void pv_store(float* dst, int lane, const f32x4 (&acc
 __device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
 __device__ __forceinline__ float readlanef(float v, int l) { return bitsf(__builtin_amdgcn_readlane(fbits(v), l)); }
 
+// Visit positions of sequence s: n_s = ceil(L / B), or the caller's visit
+// count (a pruned cache: only the first visit_lens[s] entries of the order
+// are visited) clamped to [0, n_s].
+__device__ __forceinline__ int visit_count_b(const Params& p, int s, int L, int B) {
+  const int n = (L + B - 1) / B;
+  return p.visit_lens ? min(max(p.visit_lens[s], 0), n) : n;
+}
+template <int B>
+__device__ __forceinline__ int visit_count(const Params& p, int s, int L) {
+  return visit_count_b(p, s, L, B);
+}
+
 // ---------------------------------------------------------------------------
 // Terminating path: one launch = per-stream scanners + helper workgroups
 // ---------------------------------------------------------------------------
@@ -939,7 +951,7 @@ __device__ void art_scanner(const Params& p, int stream, uint32_t E, float* part
   const int kvh = stream - s * p.hkv;
   const int g = p.g;
   const int L = p.seq_lens[s];
-  const int n = (L + Cf::B - 1) / Cf::B;
+  const int n = visit_count<Cf::B>(p, s, L);
   const int nch = (n + C - 1) / C;
   const size_t head0 = (size_t)s * p.hq + (size_t)kvh * g;
   u64* claimw = p.sched_claim + stream;
@@ -1248,7 +1260,7 @@ __device__ void art_helper(const Params& p, int hid, uint32_t E, float* part, fl
         if (valid) {
           cwv = ld_dev(p.sched_claim + st);
           dwv = ld_dev(p.sched_done + st);
-          const int nb = (p.seq_lens[st / p.hkv] + Cf::B - 1) / Cf::B;
+          const int nb = visit_count<Cf::B>(p, st / p.hkv, p.seq_lens[st / p.hkv]);
           nchv = (nb + C - 1) / C;
         }
         const uint32_t cv = tag_val(cwv, E, 1);
@@ -1288,7 +1300,7 @@ __device__ void art_helper(const Params& p, int hid, uint32_t E, float* part, fl
     const int s = st / p.hkv;
     const int kvh = st - s * p.hkv;
     const int L = p.seq_lens[s];
-    const int n = (L + Cf::B - 1) / Cf::B;
+    const int n = visit_count<Cf::B>(p, s, L);
     const int t0 = cc * C;
     const int nt = min(C, n - t0);
     const int32_t* trow = p.block_table + (size_t)s * p.max_blocks;
@@ -1779,7 +1791,7 @@ __device__ void lb_claim(const Params& p, uint32_t E, int* e, char* qdst, int& c
   int got_s = -1, got_k = 0;
   (void)E;
   if (!ended) {
-    auto nch_of = [&](int st) { return ((p.seq_lens[st / p.hkv] + Cf::B - 1) / Cf::B + C - 1) / C; };
+    auto nch_of = [&](int st) { return (visit_count<Cf::B>(p, st / p.hkv, p.seq_lens[st / p.hkv]) + C - 1) / C; };
     auto take = [&](int st) {  // lane 0 adds, the wave gets the chunk index (or -1)
       uint32_t k = 0;
       if (lane == 0) k = __hip_atomic_fetch_add(p.lb_claim + st, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1843,7 +1855,7 @@ __device__ void lb_claim(const Params& p, uint32_t E, int* e, char* qdst, int& c
   const int sq = got_s / p.hkv;
   const int kvh = got_s - sq * p.hkv;
   const int L = p.seq_lens[sq];
-  const int n = (L + Cf::B - 1) / Cf::B;
+  const int n = visit_count<Cf::B>(p, sq, L);
   const int32_t* orow = p.block_order + (size_t)sq * p.max_blocks;
   const int32_t* trow = p.block_table + (size_t)sq * p.max_blocks;
   const int ob = orow[min(got_k * C + min(lane, C - 1), n - 1)];
@@ -1898,7 +1910,7 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_lb_kernel(P
   // streams without tokens: out = 0, stop = 0
   for (int st = blockIdx.x; st < S; st += gridDim.x) {
     const int sq = st / p.hkv;
-    if (p.seq_lens[sq] <= 0) {
+    if (visit_count<Cf::B>(p, sq, p.seq_lens[sq]) <= 0) {
       const size_t head0 = (size_t)sq * p.hq + (size_t)(st - sq * p.hkv) * p.g;
       for (int i = threadIdx.x; i < p.g * D; i += blockDim.x) p.out[head0 * D + i] = 0.f;
       if ((int)threadIdx.x < p.g) p.stop_block[head0 + threadIdx.x] = 0;
@@ -2113,7 +2125,7 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::C)) void art_win_part_kern
     return;
   }
   const int L = p.seq_lens[s];
-  const int n = (L + B - 1) / B;
+  const int n = visit_count<B>(p, s, L);
   const int nch = (n + C - 1) / C;
   if (c >= nch) return;
   const int t0 = c * C;
@@ -2169,7 +2181,7 @@ __global__ __launch_bounds__(64 * WNW) void art_win_scan_kernel(Params p) {
   const int s = stream / p.hkv;
   const int kvh = stream - s * p.hkv;
   const int L = p.seq_lens[s];
-  const int n = (L + B - 1) / B;
+  const int n = visit_count<B>(p, s, L);
   const int nch = (n + C - 1) / C;
   const size_t head = (size_t)s * p.hq + (size_t)kvh * g + h;
   float* st = p.win_state + (size_t)hs * (D + 8);
@@ -2512,11 +2524,13 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
   const int kvh = stream - s * p.hkv;
   const int g = p.g;
   const int L = p.seq_lens[s];
-  const int n = (L + B - 1) / B;
+  const int n = visit_count<B>(p, s, L);
   const size_t head0 = (size_t)s * p.hq + (size_t)kvh * g;
   const int b0 = split * p.split_blocks;
   const int b1 = min(n, b0 + p.split_blocks);
-  // this wave folds blocks b0 + w + NW * k, k < cnt (cnt <= 64 by the split plan)
+  // this wave folds the blocks at positions b0 + w + NW * k, k < cnt (cnt <= 64
+  // by the split plan): logical blocks in order, or, for a pruned cache, the
+  // visited blocks block_order[s][t] (the order does not change the result)
   const int cnt = b0 + w < b1 ? (b1 - b0 - w + NW - 1) / NW : 0;
 
   uint4 qf[Cf::QF];
@@ -2527,11 +2541,14 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
   const char* vbase = static_cast<const char*>(p.v_pages);
   const int32_t* trow = p.block_table + (size_t)s * p.max_blocks;
 
-  // lane k holds the page (and fp8 scales) of the wave's k-th block
-  int tab = 0;
+  // lane k holds the logical block, the page (and fp8 scales) of the wave's
+  // k-th block
+  int tab = 0, blk = 0;
   float ks_t = 1.f, vs_t = 1.f;
   if (cnt > 0) {
-    tab = trow[b0 + w + NW * min(lane, cnt - 1)];
+    const int t = b0 + w + NW * min(lane, cnt - 1);
+    blk = p.visit_lens ? p.block_order[(size_t)s * p.max_blocks + t] : t;
+    tab = trow[blk];
     if constexpr (KV == KV_FP8) {
       ks_t = p.k_scale[(size_t)tab * p.hkv + kvh];
       vs_t = p.v_scale[(size_t)tab * p.hkv + kvh];
@@ -2543,7 +2560,7 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
   pv_zero<Cf>(acc);
   float* pbuf = pbuf_all[w];
 
-  auto nvalid_of = [&](int k) { return min(B, L - (b0 + w + NW * k) * B); };
+  auto nvalid_of = [&](int k) { return min(B, L - readlane(blk, k) * B); };
   auto tile_of = [&](int k) { return ((size_t)readlane(tab, k) * p.hkv + kvh) * tile; };
   auto fold = [&](const BlockRegs<Cf>& r, int k) {
     float ks = 1.f, vs = 1.f;
@@ -2634,7 +2651,7 @@ __global__ __launch_bounds__(64) void full_merge_kernel(Params p) {
   const int h = blockIdx.x - stream * g;
   const int s = stream / p.hkv;
   const int kvh = stream - s * p.hkv;
-  const int n = (p.seq_lens[s] + p.block_size - 1) / p.block_size;
+  const int n = visit_count_b(p, s, p.seq_lens[s], p.block_size);
   const size_t head = (size_t)s * p.hq + (size_t)kvh * g + h;
   const size_t sstride = (size_t)GM * (D + 2);
   const float* src = p.ws_part + ((size_t)stream * p.splits * GM + h) * (D + 2);

@@ -233,9 +233,12 @@ def make_case(w: Workload, *, seed: Optional[int] = None, batch: Optional[int] =
 
 
 def oracle_kwargs(case: dict) -> dict:
-    """Keyword arguments shared by the oracle entry points."""
-    return dict(block_size=case["block_size"], num_kv_heads=case["num_kv_heads"], q_dtype=case["q_dtype"],
-                kv_dtype=case["kv_dtype"], k_scale=case["k_scale"], v_scale=case["v_scale"])
+    """Keyword arguments shared by the oracle entry points (``visit_lens`` when the case prunes its cache)."""
+    kw = dict(block_size=case["block_size"], num_kv_heads=case["num_kv_heads"], q_dtype=case["q_dtype"],
+              kv_dtype=case["kv_dtype"], k_scale=case["k_scale"], v_scale=case["v_scale"])
+    if case.get("visit_lens") is not None:
+        kw["visit_lens"] = case["visit_lens"]
+    return kw
 
 
 def oracle_arrays(case: dict) -> tuple:

@@ -280,11 +280,26 @@ def _check_order(order_row: np.ndarray, n: int) -> np.ndarray:
     return o
 
 
+def _visited(order_row: np.ndarray, n: int, visit_lens, s: int) -> np.ndarray:
+    """Visit order of sequence s: the whole permutation, or -- a pruned cache -- the first visit_lens[s]
+    entries (clamped to [0, n]), which must be distinct blocks of [0, n)."""
+    if visit_lens is None:
+        return _check_order(order_row, n)
+    m = min(max(int(visit_lens[s]), 0), n)
+    o = np.asarray(order_row[:m], dtype=np.int64)
+    if len(np.unique(o)) != m or (m and (o.min() < 0 or o.max() >= n)):
+        raise ValueError("visited block_order entries must be distinct blocks of range(n)")
+    return o
+
+
 def art_reference(q, k_pages, v_pages, block_table, block_order, seq_lens, *, block_size: int,
                   num_kv_heads: int, q_dtype: str, kv_dtype: str, eps_mag: float, eps_dir: float,
                   patience: int, k_scale=None, v_scale=None,
-                  pairs: Optional[Iterable[Tuple[int, int]]] = None) -> dict:
+                  pairs: Optional[Iterable[Tuple[int, int]]] = None, visit_lens=None) -> dict:
     """ART decode for every (sequence, q-head) or for the listed ``pairs``.
+
+    ``visit_lens`` (a pruned cache): sequence s visits only the first visit_lens[s] entries of its order
+    row; the rule runs over those blocks alone and ``stop`` counts them.
 
     Returns ``{"out": float64 [batch, Hq, D] (NaN where not computed),
     "stop": int64 [batch, Hq] (-1 where not computed), "heads": {(s, h): art_head result}}``.
@@ -307,7 +322,7 @@ def art_reference(q, k_pages, v_pages, block_table, block_order, seq_lens, *, bl
     for (s, kvh), heads in sorted(by_stream.items()):
         L = int(seq_lens[s])
         n = _nblocks(L, B)
-        order = _check_order(block_order[s], n)
+        order = _visited(block_order[s], n, visit_lens, s)
         st = _Stream(k_pages, v_pages, k_scale, v_scale, kv_dtype, block_table[s], L, B, kvh)
         for h in heads:
             r = art_head(Q[s, h], st, order, eps_mag, eps_dir, patience)
@@ -320,15 +335,15 @@ def art_reference(q, k_pages, v_pages, block_table, block_order, seq_lens, *, bl
 def head_stats_trajectory(q, k_pages, v_pages, block_table, block_order, seq_lens, *, s: int, h: int,
                           block_size: int, num_kv_heads: int, q_dtype: str, kv_dtype: str,
                           eps_mag: float, eps_dir: float, patience: int, k_scale=None, v_scale=None,
-                          keep_outputs: Iterable[int] = ()) -> dict:
-    """Run one head over all n blocks, recording the statistics at every position."""
+                          keep_outputs: Iterable[int] = (), visit_lens=None) -> dict:
+    """Run one head over all its visited blocks, recording the statistics at every position."""
     Q = _decoder(q_dtype)(q)
     Hq = Q.shape[1]
     g = Hq // int(num_kv_heads)
     B = int(block_size)
     L = int(seq_lens[s])
     n = _nblocks(L, B)
-    order = _check_order(block_order[s], n)
+    order = _visited(block_order[s], n, visit_lens, s)
     st = _Stream(k_pages, v_pages, k_scale, v_scale, kv_dtype, block_table[s], L, B, h // g)
     return art_head(Q[s, h], st, order, eps_mag, eps_dir, patience, run_to_end=True,
                     keep_outputs=keep_outputs)
@@ -336,7 +351,7 @@ def head_stats_trajectory(q, k_pages, v_pages, block_table, block_order, seq_len
 
 def prefix_output(q, k_pages, v_pages, block_table, block_order, seq_lens, *, s: int, h: int, nfold: int,
                   block_size: int, num_kv_heads: int, q_dtype: str, kv_dtype: str, k_scale=None,
-                  v_scale=None) -> np.ndarray:
+                  v_scale=None, visit_lens=None) -> np.ndarray:
     """Attention output of (s, h) over the first ``nfold`` blocks of the visit order.
 
     Computed from the definition (one softmax over all tokens of those
@@ -348,7 +363,7 @@ def prefix_output(q, k_pages, v_pages, block_table, block_order, seq_lens, *, s:
     B = int(block_size)
     L = int(seq_lens[s])
     n = _nblocks(L, B)
-    order = _check_order(block_order[s], n)
+    order = _visited(block_order[s], n, visit_lens, s)
     if nfold == 0:
         return np.zeros(D)
     st = _Stream(k_pages, v_pages, k_scale, v_scale, kv_dtype, block_table[s], L, B, h // g)
@@ -362,12 +377,14 @@ def prefix_output(q, k_pages, v_pages, block_table, block_order, seq_lens, *, s:
 
 def full_attention(q, k_pages, v_pages, block_table, seq_lens, *, block_size: int, num_kv_heads: int,
                    q_dtype: str, kv_dtype: str, k_scale=None, v_scale=None,
-                   pairs: Optional[Iterable[Tuple[int, int]]] = None) -> np.ndarray:
+                   pairs: Optional[Iterable[Tuple[int, int]]] = None, block_order=None,
+                   visit_lens=None) -> np.ndarray:
     """Textbook softmax attention of each decode query over all its valid tokens.
 
     out[s, h] = sum_j softmax_j(K_j . q / sqrt(D)) V_j over logical positions
     j < seq_len[s], with K, V gathered through the block table.  The result
-    the streaming method reaches when it never stops.
+    the streaming method reaches when it never stops.  With ``visit_lens``
+    (and ``block_order``) only the tokens of the visited blocks count.
     """
     Q = _decoder(q_dtype)(q)
     batch, Hq, D = Q.shape
@@ -382,8 +399,9 @@ def full_attention(q, k_pages, v_pages, block_table, seq_lens, *, block_size: in
         key = (s, h // g)
         if key not in cache:
             st = _Stream(k_pages, v_pages, k_scale, v_scale, kv_dtype, block_table[s], L, B, h // g)
-            if n:
-                Ks, Vs = zip(*[st.block(b) for b in range(n)])
+            blocks = range(n) if visit_lens is None else _visited(block_order[s], n, visit_lens, s)
+            if len(blocks):
+                Ks, Vs = zip(*[st.block(int(b)) for b in blocks])
                 cache = {key: (np.concatenate(Ks), np.concatenate(Vs))}
             else:
                 cache = {key: (np.zeros((0, D)), np.zeros((0, D)))}

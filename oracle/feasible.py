@@ -90,7 +90,8 @@ def compare_with_oracle(dev_out: np.ndarray, dev_stop: np.ndarray, inputs: dict,
     """
     kw = dict(block_size=inputs["block_size"], num_kv_heads=inputs["num_kv_heads"],
               q_dtype=inputs["q_dtype"], kv_dtype=inputs["kv_dtype"],
-              k_scale=inputs.get("k_scale"), v_scale=inputs.get("v_scale"))
+              k_scale=inputs.get("k_scale"), v_scale=inputs.get("v_scale"),
+              visit_lens=inputs.get("visit_lens"))
     arrs = (inputs["q"], inputs["k_pages"], inputs["v_pages"], inputs["block_table"],
             inputs["block_order"], inputs["seq_lens"])
     if pairs is None:

@@ -127,3 +127,11 @@ def test_kernel_choice_follows_the_knob_and_the_mode(lib, monkeypatch):
             art.art_decode_kernel_choice(_desc(), bad.get("em", 1e-3), bad.get("ed", 1e-4), bad.get("p", 4))
     with pytest.raises(art.ArtError):
         art.art_decode_kernel_choice(_desc(head_dim=96), 1e-3, 1e-4, 4)
+
+
+def test_visits_entry_point_validates_like_art_decode(lib):
+    """art_decode_visits: NULL visit_lens is art_decode; a misaligned visit_lens is rejected before any work."""
+    args = lambda vl: (ctypes.byref(_desc()), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, vl, 1e-3, 1e-4, 4,
+                       FAKE, FAKE, None, FAKE, 16, None)
+    assert lib.art_decode_visits(*args(None)) == art.ART_ERR_WORKSPACE      # same checks, same order
+    assert lib.art_decode_visits(*args(FAKE + 2)) == art.ART_ERR_INVALID_ARG  # 4-byte alignment

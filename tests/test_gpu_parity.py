@@ -28,11 +28,12 @@ def _device_run(case, eps_mag, eps_dir, patience, flags=0, reps=1):
     dev = art.case_to_device(case)
     dec = art.Decoder(dev["q"], dev["k_pages"], dev["block_table"])
     fetched = torch.full((case["batch"], case["num_kv_heads"]), -7, dtype=torch.int32, device="cuda")
+    vl = None if case.get("visit_lens") is None else torch.from_numpy(case["visit_lens"].astype(np.int32)).cuda()
     outs = []
     for _ in range(reps):
         out, stop = dec(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"], dev["block_order"],
                         dev["seq_lens"], eps_mag, eps_dir, patience, k_scale=dev["k_scale"], v_scale=dev["v_scale"],
-                        blocks_fetched=fetched, flags=flags)
+                        blocks_fetched=fetched, flags=flags, visit_lens=vl)
         torch.cuda.synchronize()
         outs.append((out.cpu().numpy().astype(np.float64), stop.cpu().numpy(), fetched.cpu().numpy()))
     return outs if reps > 1 else outs[0]
@@ -48,7 +49,11 @@ def _pairs(case, sample=None, seed=0):
 
 
 def _nblocks(case):
-    return (case["seq_lens"].astype(np.int64) + case["block_size"] - 1) // case["block_size"]
+    """Visit positions per sequence: n_s, or the case's visit counts (a pruned cache) clamped to n_s."""
+    n = (case["seq_lens"].astype(np.int64) + case["block_size"] - 1) // case["block_size"]
+    if case.get("visit_lens") is not None:
+        n = np.clip(case["visit_lens"].astype(np.int64), 0, n)
+    return n
 
 
 def check_art(case, eps_mag=None, eps_dir=None, patience=None, sample=None, flags=0):
@@ -78,7 +83,7 @@ def check_full(case, sample=None, flags=0):
     out, stop, fetched = _device_run(case, 0.0, 0.0, 1, flags=flags)
     pairs = _pairs(case, sample)
     ref = oracle.full_attention(case["q"], case["k_pages"], case["v_pages"], case["block_table"], case["seq_lens"],
-                                pairs=pairs, **synth.oracle_kwargs(case))
+                                pairs=pairs, block_order=case["block_order"], **synth.oracle_kwargs(case))
     worst = 0.0
     for s, h in pairs:
         worst = max(worst, oracle.feasible.max_rel_err(out[s, h], ref[s, h]))
@@ -411,3 +416,50 @@ def test_ablation_through_lookback_and_windowed(sched):
     case = synth.make_case(W.VALUE_HEAVY, batch=2, context=4096 - 5)
     _with_env(dict(ART_SCHED=sched), lambda: check_art(case, eps_dir=math.inf))
     _with_env(dict(ART_SCHED=sched), lambda: check_art(case, eps_mag=math.inf, patience=1))
+
+
+# ---- ART over a pruned cache: only the first visit_lens[s] entries of the order are visited ------------
+
+def _pruned_case():
+    """Block 0 plus a recent window (the default order's first entries), a random subset in random order with
+    block 0 inside, one without block 0, an empty subset, a single block and the whole sequence."""
+    case = synth.make_case(W.LLAMA3_8B, batch=6, context=3000 - 7)
+    rng = np.random.default_rng(21)
+    n = int(_nblocks(case)[0])
+    order = case["block_order"].copy()
+    vl = np.zeros(6, np.int32)
+    vl[0] = 1 + 24                                       # sink + 24 newest blocks
+    perm = rng.permutation(n)
+    order[1, :n] = perm
+    vl[1] = int(np.where(perm == 0)[0][0]) + 40          # random subset that holds block 0
+    order[2, :n] = list(range(n - 1, -1, -1))            # block 0 last ...
+    vl[2] = n // 2                                       # ... and not visited: no early stop
+    vl[3] = 0
+    vl[4] = 1
+    vl[5] = n
+    case["block_order"] = order
+    case["visit_lens"] = vl
+    return case
+
+
+@pytest.mark.parametrize("sched", ["scan", "lb", "win"])
+def test_pruned_cache_parity(sched):
+    case = _pruned_case()
+    print(f"[pruned] {sched}", flush=True)
+    rep, out, stop, fetched = _with_env(dict(ART_SCHED=sched), lambda: check_art(case))
+    n = _nblocks(case)
+    assert np.all(stop[2] == n[2])          # no block 0 among the visited blocks
+    assert np.all(stop[3] == 0) and np.all(out[3] == 0.0) and np.all(fetched[3] == 0)
+    _with_env(dict(ART_SCHED=sched), lambda: check_art(case, eps_mag=0.5, eps_dir=0.5, patience=1))
+
+
+def test_pruned_cache_full_attention():
+    case = _pruned_case()
+    check_full(case)
+    ref_case = dict(case)
+    ref_case["visit_lens"] = None
+    a = _device_run(case, 0.0, 0.0, 1)
+    b = _device_run(ref_case, 0.0, 0.0, 1)
+    # the whole sequence visited (row 5) is the plain call, summed in visit order instead of logical order
+    assert np.array_equal(a[1][5], b[1][5])
+    assert oracle.feasible.max_rel_err(a[0][5], b[0][5]) <= 1e-5
