@@ -227,6 +227,34 @@ def time_setting(case, dev, em, ed, patience, flags, steps, warmup, outputs=Fals
     return res
 
 
+def probe(case: dict, dev: dict, steps: int, warmup: int) -> dict:
+    """Probe-vector detector over the leading P coordinates of the output: step time, the detector's cost
+    (every block folded with the detector kept, against the full-attention path) and how far the stops move
+    from the whole-vector detector's."""
+    from kv_cache_run_amd import art
+
+    em, ed, p = case["eps_mag"], case["eps_dir"], case["patience"]
+    B = case["block_size"]
+    n = (case["seq_lens"].astype(np.int64) + B - 1) // B
+    D = case["head_dim"]
+    ref = time_setting(case, dev, em, ed, p, 0, steps, warmup, outputs=True)
+    res = {}
+    for P in (8, 16, 32, 64, D):
+        fl = art.art_flag_probe(P) if P < D else 0
+        r = ref if P == D else time_setting(case, dev, em, ed, p, fl, steps, warmup, outputs=True)
+        keep = time_setting(case, dev, 0.0, 0.0, p, art.ART_FLAG_KEEP_DETECTOR | fl, steps, warmup)
+        moved = r["stop"] != ref["stop"]
+        res[f"P{P}"] = {
+            "us_per_step": round(r["us_per_step"], 3),
+            "kv_fraction_read": round(r["kv_fraction_read"], 5),
+            "all_blocks_with_detector_us": round(keep["us_per_step"], 3),
+            "heads_with_other_stop": round(float(moved.mean()), 5),
+            "stop_shift_mean_blocks": round(float((r["stop"] - ref["stop"]).mean()), 4),
+            "stop_shift_mean_abs_over_n": round(float((np.abs(r["stop"] - ref["stop"]) / n[:, None]).mean()), 6),
+        }
+    return res
+
+
 def pruned(case: dict, dev: dict, steps: int, warmup: int) -> dict:
     """ART over a pruned cache (the default order visits block 0, then newest to oldest, so its first 1 + w
     entries are block 0 plus a recent window of w blocks) against full attention over the same blocks."""
@@ -302,6 +330,9 @@ def main(argv=None) -> int:
     ap.add_argument("--pruned", action="store_true",
                     help="also run ART over a pruned cache (block 0 plus the newest quarter / sixteenth of the "
                          "blocks, through art_decode_visits) against full attention over the same blocks")
+    ap.add_argument("--probe", action="store_true",
+                    help="also run the probe-vector detector (statistics over the leading P output coordinates) "
+                         "for several P: step time, detector cost and stop drift against all D coordinates")
     ap.add_argument("--ablation", action="store_true",
                     help="also run the detector ablation (both tests, scale only, direction only, patience 1) on "
                          "the Llama-3-8B shape with Gaussian, heavy-tailed and value-heavy K/V")
@@ -367,6 +398,8 @@ def main(argv=None) -> int:
         extras["ablation"] = ablation(max(5, args.steps // 2), 2)
     if args.pruned:
         extras["pruned"] = pruned(case, dev, max(5, args.steps // 2), 2)
+    if args.probe:
+        extras["probe"] = probe(case, dev, max(5, args.steps // 2), 2)
 
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)

@@ -63,6 +63,16 @@ enum {
   ART_FLAG_KEEP_DETECTOR = 2u
 };
 
+/* Probe-vector detector: bits 8..15 of flags hold P / 8, where the two
+ * statistics are computed over the leading P coordinates of the output only
+ * (O[0 .. P-1] of O_t and O_{t-1}; the explainer's Technical Summary 2.2
+ * mentions monitoring a subset of coordinates).  0 = all D coordinates.  P
+ * must not exceed D (else ART_ERR_INVALID_ARG).  The output written at the
+ * stop is still the whole D-vector. */
+#define ART_FLAG_PROBE_SHIFT 8
+#define ART_FLAG_PROBE_MASK (0xFFu << ART_FLAG_PROBE_SHIFT)
+#define ART_FLAG_PROBE(P) (((uint32_t)(P) / 8u) << ART_FLAG_PROBE_SHIFT)
+
 /* Shapes and storage types of one call (host memory). */
 typedef struct {
   int32_t batch;               /* number of sequences, >= 0                    */

@@ -19,6 +19,14 @@ LIB_PATH = os.path.join(HERE, "libart_decode.so")
 ART_OK, ART_ERR_INVALID_ARG, ART_ERR_UNSUPPORTED, ART_ERR_WORKSPACE, ART_ERR_HIP = range(5)
 ART_DTYPE_F32, ART_DTYPE_BF16, ART_DTYPE_FP8_E4M3FN = range(3)
 ART_FLAG_NONE, ART_FLAG_FULL, ART_FLAG_KEEP_DETECTOR = 0, 1, 2
+ART_FLAG_PROBE_SHIFT = 8
+
+
+def art_flag_probe(p: int) -> int:
+    """Flag bits of a probe-vector detector over the leading ``p`` output coordinates (p a multiple of 8)."""
+    if p % 8 or not 0 <= p <= 2040:
+        raise ValueError("probe size must be a multiple of 8")
+    return (p // 8) << ART_FLAG_PROBE_SHIFT
 
 EXPORTED = ("art_decode_workspace_bytes", "art_decode_workspace_init", "art_decode", "art_decode_visits",
             "art_status_string", "art_decode_version", "art_decode_kernel_choice")

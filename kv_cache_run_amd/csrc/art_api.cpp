@@ -43,10 +43,11 @@ art_status check_desc(const art_decode_desc* d) {
       d->num_pages < 1)
     return ART_ERR_INVALID_ARG;
   if (d->num_q_heads % d->num_kv_heads != 0) return ART_ERR_INVALID_ARG;
-  if (d->flags & ~(uint32_t)(ART_FLAG_FULL | ART_FLAG_KEEP_DETECTOR)) return ART_ERR_INVALID_ARG;
+  if (d->flags & ~(uint32_t)(ART_FLAG_FULL | ART_FLAG_KEEP_DETECTOR | ART_FLAG_PROBE_MASK)) return ART_ERR_INVALID_ARG;
   const int g = d->num_q_heads / d->num_kv_heads;
   if (g > 16) return ART_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return ART_ERR_UNSUPPORTED;
+  if (((d->flags & ART_FLAG_PROBE_MASK) >> ART_FLAG_PROBE_SHIFT) * 8 > (uint32_t)d->head_dim) return ART_ERR_INVALID_ARG;
   if (d->block_size != 16 && d->block_size != 32) return ART_ERR_UNSUPPORTED;
   const bool ok_types = (d->q_dtype == ART_DTYPE_F32 && d->kv_dtype == ART_DTYPE_F32) ||
                         (d->q_dtype == ART_DTYPE_BF16 && d->kv_dtype == ART_DTYPE_BF16) ||
@@ -276,6 +277,10 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
   p.block_table = block_table;
   p.block_order = block_order;
   p.visit_lens = visit_lens;
+  {
+    const int probe8 = (int)((desc->flags & ART_FLAG_PROBE_MASK) >> ART_FLAG_PROBE_SHIFT);
+    p.probe = probe8 ? 8 * probe8 : desc->head_dim;
+  }
   p.seq_lens = seq_lens;
   p.out = out;
   p.stop_block = stop_block;

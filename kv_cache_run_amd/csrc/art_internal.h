@@ -84,6 +84,7 @@ struct Params {
   int32_t split_blocks;     // full mode: blocks per split
   float eps_mag, eps_dir;
   int32_t patience;
+  int32_t probe;            // the detector's statistics use coordinates [0, probe) of O (D: all)
   float qk_log2;            // log2(e) / sqrt(D)
 };
 

@@ -857,8 +857,10 @@ __device__ __forceinline__ bool scan_head(HeadCarry<Cf>& hc, const ChunkIn<Cf>& 
       hc.A[j] = fmaf(at, hc.A[j], bt * in.a[t][j]);
       const float o = hc.A[j] * rt;
       const float df = o - hc.Op[j];
-      nn = fmaf(o, o, nn);
-      ee = fmaf(df, df, ee);
+      const float op = DPL * lane + j < p.probe ? o : 0.f;  // coordinates outside the probe do not count
+      const float dp = DPL * lane + j < p.probe ? df : 0.f;
+      nn = fmaf(op, op, nn);
+      ee = fmaf(dp, dp, ee);
       hc.Op[j] = o;
       oo[t][j] = o;
     }
@@ -1470,15 +1472,18 @@ __device__ __forceinline__ void lb_combine(LbState<Cf>& x, float m, float l, con
   x.M = mn;
 }
 
-// O = A / L entering a chunk (0 before any block) and its squared norm.
+// O = A / L entering a chunk (0 before any block) and the squared norm of
+// its coordinates [0, probe).
 template <class Cf>
-__device__ __forceinline__ void lb_entering_output(const LbState<Cf>& x, int lane, float (&Op)[Cf::DPL], float& np) {
+__device__ __forceinline__ void lb_entering_output(const LbState<Cf>& x, int lane, int probe, float (&Op)[Cf::DPL],
+                                                   float& np) {
   const float rl = x.L > 0.f ? __builtin_amdgcn_rcpf(x.L) : 0.f;
   float sq[1] = {0.f};
 #pragma unroll
   for (int j = 0; j < Cf::DPL; ++j) {
     Op[j] = x.L > 0.f ? x.A[j] * rl : 0.f;
-    sq[0] = fmaf(Op[j], Op[j], sq[0]);
+    const float op = Cf::DPL * lane + j < probe ? Op[j] : 0.f;
+    sq[0] = fmaf(op, op, sq[0]);
   }
   np = xreduce<1>(sq, lane);
 }
@@ -1538,8 +1543,10 @@ __device__ __forceinline__ u64 lb_stats(LbState<Cf>& x, float (&Op)[Cf::DPL], fl
       x.A[j] = fmaf(at, x.A[j], bt * in.a[t][j]);
       const float o = x.A[j] * rt;
       const float df = o - Op[j];
-      nn = fmaf(o, o, nn);
-      ee = fmaf(df, df, ee);
+      const float op = DPL * lane + j < p.probe ? o : 0.f;  // coordinates outside the probe do not count
+      const float dp = DPL * lane + j < p.probe ? df : 0.f;
+      nn = fmaf(op, op, nn);
+      ee = fmaf(dp, dp, ee);
       Op[j] = o;
       oo[t][j] = o;
     }
@@ -1673,16 +1680,7 @@ __device__ bool lb_head(const Params& p, uint32_t E, int s, int k, int n, int h,
   // ---- statistics of every position
   float Op[DPL];
   float np = 0.f;
-  {
-    const float rl = x.L > 0.f ? __builtin_amdgcn_rcpf(x.L) : 0.f;
-    float sq[1] = {0.f};
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) {
-      Op[j] = x.L > 0.f ? x.A[j] * rl : 0.f;
-      sq[0] = fmaf(Op[j], Op[j], sq[0]);
-    }
-    np = xreduce<1>(sq, lane);
-  }
+  lb_entering_output<Cf>(x, lane, p.probe, Op, np);
   float oo[C][DPL];
   const u64 pass = lb_stats<Cf>(x, Op, np, in, t0, nt, p, lane, oo);
   const uint32_t passb = (uint32_t)pass & 0xFFu;
@@ -2333,7 +2331,7 @@ __global__ __launch_bounds__(64 * WNW) void art_win_scan_kernel(Params p) {
     x.M = e[D];
     x.L = e[D + 1];
     float Op[DPL], np;
-    lb_entering_output<Cf>(x, lane, Op, np);
+    lb_entering_output<Cf>(x, lane, p.probe, Op, np);
     float oo[C][DPL];
     const u64 pass = lb_stats<Cf>(x, Op, np, in, t0, nt, p, lane, oo);
     const int ob = orow[min(t0 + (lane < C ? lane : C - 1), n - 1)];
@@ -2436,7 +2434,7 @@ __global__ __launch_bounds__(64 * WNW) void art_win_scan_kernel(Params p) {
       x.M = e[D];
       x.L = e[D + 1];
       float Op[DPL], np;
-      lb_entering_output<Cf>(x, lane, Op, np);
+      lb_entering_output<Cf>(x, lane, p.probe, Op, np);
       float oo[C][DPL];
       (void)lb_stats<Cf>(x, Op, np, in, t0, nt, p, lane, oo);
       float ov[DPL];

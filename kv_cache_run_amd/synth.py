@@ -241,6 +241,11 @@ def oracle_kwargs(case: dict) -> dict:
     return kw
 
 
+def oracle_detector_kwargs(case: dict) -> dict:
+    """The probe coordinates for the oracle's detector when the case asks for a probe vector."""
+    return {} if case.get("probe_coords") is None else {"probe": case["probe_coords"]}
+
+
 def oracle_arrays(case: dict) -> tuple:
     return (case["q"], case["k_pages"], case["v_pages"], case["block_table"], case["block_order"],
             case["seq_lens"])

@@ -193,7 +193,7 @@ class _Stream:
 
 def art_head(qv: np.ndarray, stream: _Stream, order: Sequence[int], eps_mag: float,
              eps_dir: float, patience: int, *, run_to_end: bool = False,
-             keep_outputs: Iterable[int] = ()) -> dict:
+             keep_outputs: Iterable[int] = (), probe=None) -> dict:
     """Stream the blocks of one (sequence, q-head) in visit order.
 
     Each block is folded into an online-softmax state (running max m, running
@@ -202,7 +202,11 @@ def art_head(qv: np.ndarray, stream: _Stream, order: Sequence[int], eps_mag: flo
     stop.  With ``run_to_end`` the fold continues past the stop so that the
     statistics of every position are recorded (the stop is still the first
     firing).  ``keep_outputs`` lists fold counts whose O is returned.
+    ``probe`` (coordinate indices, None = all): the statistics compare only
+    those coordinates of O_t and O_{t-1} (a probe vector, Technical Summary
+    2.2); the output returned is still the whole vector.
     """
+    pidx = None if probe is None else np.asarray(probe, dtype=np.int64)
     D = qv.shape[0]
     n = len(order)
     scale = 1.0 / math.sqrt(D)
@@ -233,7 +237,7 @@ def art_head(qv: np.ndarray, stream: _Stream, order: Sequence[int], eps_mag: flo
         o = acc / l
         sink = sink or (b == 0)
         if t >= 1:
-            dm, dd = direction_magnitude(o, o_prev)
+            dm, dd = direction_magnitude(o, o_prev) if pidx is None else direction_magnitude(o[pidx], o_prev[pidx])
             d_mag_tr.append(dm)
             d_dir_tr.append(dd)
             ok = (dm < eps_mag) and (dd < eps_dir)
@@ -295,7 +299,7 @@ def _visited(order_row: np.ndarray, n: int, visit_lens, s: int) -> np.ndarray:
 def art_reference(q, k_pages, v_pages, block_table, block_order, seq_lens, *, block_size: int,
                   num_kv_heads: int, q_dtype: str, kv_dtype: str, eps_mag: float, eps_dir: float,
                   patience: int, k_scale=None, v_scale=None,
-                  pairs: Optional[Iterable[Tuple[int, int]]] = None, visit_lens=None) -> dict:
+                  pairs: Optional[Iterable[Tuple[int, int]]] = None, visit_lens=None, probe=None) -> dict:
     """ART decode for every (sequence, q-head) or for the listed ``pairs``.
 
     ``visit_lens`` (a pruned cache): sequence s visits only the first visit_lens[s] entries of its order
@@ -325,7 +329,7 @@ def art_reference(q, k_pages, v_pages, block_table, block_order, seq_lens, *, bl
         order = _visited(block_order[s], n, visit_lens, s)
         st = _Stream(k_pages, v_pages, k_scale, v_scale, kv_dtype, block_table[s], L, B, kvh)
         for h in heads:
-            r = art_head(Q[s, h], st, order, eps_mag, eps_dir, patience)
+            r = art_head(Q[s, h], st, order, eps_mag, eps_dir, patience, probe=probe)
             out[s, h] = r["out"]
             stop[s, h] = r["stop"]
             res[(s, h)] = r
@@ -335,7 +339,7 @@ def art_reference(q, k_pages, v_pages, block_table, block_order, seq_lens, *, bl
 def head_stats_trajectory(q, k_pages, v_pages, block_table, block_order, seq_lens, *, s: int, h: int,
                           block_size: int, num_kv_heads: int, q_dtype: str, kv_dtype: str,
                           eps_mag: float, eps_dir: float, patience: int, k_scale=None, v_scale=None,
-                          keep_outputs: Iterable[int] = (), visit_lens=None) -> dict:
+                          keep_outputs: Iterable[int] = (), visit_lens=None, probe=None) -> dict:
     """Run one head over all its visited blocks, recording the statistics at every position."""
     Q = _decoder(q_dtype)(q)
     Hq = Q.shape[1]
@@ -346,7 +350,7 @@ def head_stats_trajectory(q, k_pages, v_pages, block_table, block_order, seq_len
     order = _visited(block_order[s], n, visit_lens, s)
     st = _Stream(k_pages, v_pages, k_scale, v_scale, kv_dtype, block_table[s], L, B, h // g)
     return art_head(Q[s, h], st, order, eps_mag, eps_dir, patience, run_to_end=True,
-                    keep_outputs=keep_outputs)
+                    keep_outputs=keep_outputs, probe=probe)
 
 
 def prefix_output(q, k_pages, v_pages, block_table, block_order, seq_lens, *, s: int, h: int, nfold: int,

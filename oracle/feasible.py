@@ -108,7 +108,7 @@ def compare_with_oracle(dev_out: np.ndarray, dev_stop: np.ndarray, inputs: dict,
             ref = oracle_res["out"][s, h]
         else:
             tr = head_stats_trajectory(*arrs, s=s, h=h, eps_mag=eps_mag, eps_dir=eps_dir,
-                                       patience=patience, **kw)
+                                       patience=patience, probe=inputs.get("probe_coords"), **kw)
             st = classify_tests(tr["d_mag"], tr["d_dir"], eps_mag, eps_dir, band)
             if feasible_stop(st, tr["sinks"], patience, sg, tr["n"]):
                 n_excused += 1

@@ -135,3 +135,13 @@ def test_visits_entry_point_validates_like_art_decode(lib):
                        FAKE, FAKE, None, FAKE, 16, None)
     assert lib.art_decode_visits(*args(None)) == art.ART_ERR_WORKSPACE      # same checks, same order
     assert lib.art_decode_visits(*args(FAKE + 2)) == art.ART_ERR_INVALID_ARG  # 4-byte alignment
+
+
+def test_probe_flag_is_validated(lib):
+    """Probe sizes up to D are accepted (the call then fails only on the fake workspace); beyond D, rejected."""
+    ok = _desc(flags=art.art_flag_probe(64))
+    assert art.art_decode_workspace_bytes(ok) > 0
+    assert art.art_decode_workspace_bytes(_desc(flags=art.art_flag_probe(128))) > 0
+    assert art.art_decode_workspace_bytes(_desc(flags=art.art_flag_probe(136))) == 0   # P > D
+    assert _call(lib, _desc(flags=art.art_flag_probe(136))) == art.ART_ERR_INVALID_ARG
+    assert _call(lib, _desc(flags=art.art_flag_probe(8)), wsb=16) == art.ART_ERR_WORKSPACE

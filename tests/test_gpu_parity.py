@@ -29,6 +29,8 @@ def _device_run(case, eps_mag, eps_dir, patience, flags=0, reps=1):
     dec = art.Decoder(dev["q"], dev["k_pages"], dev["block_table"])
     fetched = torch.full((case["batch"], case["num_kv_heads"]), -7, dtype=torch.int32, device="cuda")
     vl = None if case.get("visit_lens") is None else torch.from_numpy(case["visit_lens"].astype(np.int32)).cuda()
+    if case.get("probe"):
+        flags |= art.art_flag_probe(case["probe"])
     outs = []
     for _ in range(reps):
         out, stop = dec(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"], dev["block_order"],
@@ -64,7 +66,7 @@ def check_art(case, eps_mag=None, eps_dir=None, patience=None, sample=None, flag
     out, stop, fetched = _device_run(case, em, ed, p, flags=flags)
     pairs = _pairs(case, sample)
     ref = oracle.art_reference(*synth.oracle_arrays(case), eps_mag=em, eps_dir=ed, patience=p,
-                               pairs=pairs, **synth.oracle_kwargs(case))
+                               pairs=pairs, **synth.oracle_kwargs(case), **synth.oracle_detector_kwargs(case))
     rep = oracle.compare_with_oracle(out, stop, case, ref, eps_mag=em, eps_dir=ed, patience=p, pairs=pairs)
     assert rep["bad"] == [], rep
     assert rep["max_rel_err"] <= TOL, rep
@@ -463,3 +465,24 @@ def test_pruned_cache_full_attention():
     # the whole sequence visited (row 5) is the plain call, summed in visit order instead of logical order
     assert np.array_equal(a[1][5], b[1][5])
     assert oracle.feasible.max_rel_err(a[0][5], b[0][5]) <= 1e-5
+
+
+# ---- probe-vector detector: the statistics over the leading P output coordinates -------------------------
+
+@pytest.mark.parametrize("sched", ["scan", "lb", "win"])
+@pytest.mark.parametrize("w,P", [(W.LLAMA3_8B, 8), (W.LLAMA3_8B, 32), (W.LLAMA3_8B, 64), (W.TINY, 16)],
+                         ids=["llama-P8", "llama-P32", "llama-P64", "tiny-P16"])
+def test_probe_vector_parity(w, P, sched):
+    case = synth.make_case(w, batch=min(w.batch, 3), context=3000 - 11)
+    case["probe"] = P
+    case["probe_coords"] = np.arange(P)
+    print(f"[probe] {w.name} P={P} {sched}", flush=True)
+    _with_env(dict(ART_SCHED=sched), lambda: check_art(case))
+
+
+def test_probe_of_every_coordinate_is_the_plain_detector():
+    case = synth.make_case(W.LLAMA3_8B, batch=2, context=2000)
+    a = _device_run(case, case["eps_mag"], case["eps_dir"], case["patience"])
+    case["probe"] = case["head_dim"]
+    b = _device_run(case, case["eps_mag"], case["eps_dir"], case["patience"])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
