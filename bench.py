@@ -20,6 +20,7 @@ algorithmic and on actually-read bytes, and the CPU oracle timed on the host.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -227,6 +228,58 @@ def time_setting(case, dev, em, ed, patience, flags, steps, warmup, outputs=Fals
     return res
 
 
+def importance(steps: int, warmup: int) -> dict:
+    """Recency-first (the default order) against importance-first (block 0, then blocks by the largest
+    q . mean-key score): ART step time, KV read, the output's error against full attention on the same
+    inputs (all on the device), and the order pre-pass's own time (the key summary is cache-write work:
+    timed apart)."""
+    import torch
+
+    from kv_cache_run_amd import art, synth, workloads
+
+    res = {}
+    for w in (workloads.LLAMA3_8B, workloads.RECENT, workloads.LONG):
+        case = synth.make_case(w)
+        dev = art.case_to_device(case)
+        em, ed, p = case["eps_mag"], case["eps_dir"], case["patience"]
+        full = time_setting(case, dev, 0.0, 0.0, p, art.ART_FLAG_FULL, steps, warmup, outputs=True)
+        ref = full["out"].astype(np.float64)
+        nrm = np.maximum(np.linalg.norm(ref, axis=-1), 1e-30)
+
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record()
+        sm = art.block_key_summary(dev["q"], dev["k_pages"], dev["block_table"], dev["seq_lens"],
+                                   k_scale=dev["k_scale"])
+        ev[1].record()
+        desc = art.make_desc(dev["q"], dev["k_pages"], dev["block_table"])
+        ows = torch.empty(max(1, art.load_library().art_importance_order_workspace_bytes(ctypes.byref(desc))),
+                          dtype=torch.uint8, device="cuda")
+        order = art.importance_order(dev["q"], dev["k_pages"], sm, dev["block_table"], dev["seq_lens"], workspace=ows)
+        torch.cuda.synchronize()
+        reps = 20
+        ev[2].record()
+        for _ in range(reps):
+            art.importance_order(dev["q"], dev["k_pages"], sm, dev["block_table"], dev["seq_lens"], block_order=order,
+                                 workspace=ows)
+        ev[3].record()
+        torch.cuda.synchronize()
+        rows = {"summary_us": round(ev[0].elapsed_time(ev[1]) * 1e3, 2),
+                "order_prepass_us": round(ev[2].elapsed_time(ev[3]) * 1e3 / reps, 2),
+                "full_us_per_step": round(full["us_per_step"], 3)}
+        for name, d in (("recency_first", dev), ("importance_first", dict(dev, block_order=order))):
+            r = time_setting(case, d, em, ed, p, 0, steps, warmup, outputs=True)
+            err = np.linalg.norm(r["out"].astype(np.float64) - ref, axis=-1) / nrm
+            rows[name] = {"us_per_step": round(r["us_per_step"], 3),
+                          "kv_fraction_read": round(r["kv_fraction_read"], 5),
+                          "kv_fraction_needed": round(r["kv_fraction_needed"], 5),
+                          "rel_err_vs_full_mean": float(f"{err.mean():.4g}"),
+                          "rel_err_vs_full_p99": float(f"{np.percentile(err, 99):.4g}")}
+        res[w.name] = rows
+        del dev, sm, order
+        torch.cuda.empty_cache()
+    return res
+
+
 def probe(case: dict, dev: dict, steps: int, warmup: int) -> dict:
     """Probe-vector detector over the leading P coordinates of the output: step time, the detector's cost
     (every block folded with the detector kept, against the full-attention path) and how far the stops move
@@ -333,6 +386,9 @@ def main(argv=None) -> int:
     ap.add_argument("--probe", action="store_true",
                     help="also run the probe-vector detector (statistics over the leading P output coordinates) "
                          "for several P: step time, detector cost and stop drift against all D coordinates")
+    ap.add_argument("--importance", action="store_true",
+                    help="also compare the importance-first order (key-summary pre-pass) with recency-first on the "
+                         "Llama-3-8B shape and the recency control: step time, KV read, error against full attention")
     ap.add_argument("--ablation", action="store_true",
                     help="also run the detector ablation (both tests, scale only, direction only, patience 1) on "
                          "the Llama-3-8B shape with Gaussian, heavy-tailed and value-heavy K/V")
@@ -400,6 +456,8 @@ def main(argv=None) -> int:
         extras["pruned"] = pruned(case, dev, max(5, args.steps // 2), 2)
     if args.probe:
         extras["probe"] = probe(case, dev, max(5, args.steps // 2), 2)
+    if args.importance:
+        extras["importance"] = importance(max(5, args.steps // 2), 2)
 
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)

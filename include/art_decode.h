@@ -191,6 +191,40 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
                              float eps_mag, float eps_dir, int32_t patience, float* out, int32_t* stop_block,
                              int32_t* blocks_fetched, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Importance-first traversal (the ART explainer, Technical Summary 2.4,
+ * names it beside recency-first as an order ART can take): a pre-pass that
+ * writes block_order from a cheap per-block summary of the keys, after which
+ * art_decode runs unchanged.
+ *
+ * art_block_key_summary: summary[page][kv-head][d] (float32, device,
+ * [num_pages][Hkv][D]) = the mean of the block's valid key rows (fp8: times
+ * the tile's k_scale), for every page that some (s, b < n_s) references;
+ * other pages are not written.  A cache would store this when it writes a
+ * block.  Arguments as for art_decode.
+ *
+ * art_importance_order: block_order[s] (device, [batch][max_blocks_per_seq],
+ * written for positions < n_s only) = block 0 first, then the other blocks
+ * by descending score(s, b) = max over query heads h of
+ * q_h . summary[page(s, b)][kv-head(h)] / sqrt(D) (float32 dot products),
+ * ties to the higher (newer) block.  Needs max_blocks_per_seq <= 4096 (else
+ * ART_ERR_UNSUPPORTED) and a device workspace of
+ * art_importance_order_workspace_bytes(desc) bytes (the scores between the
+ * pre-pass's two launches; 256-byte aligned; no initialisation needed; calls
+ * that share one must not overlap).
+ *
+ * Both enqueue on `stream` and never synchronize.  Errors: ART_ERR_INVALID_ARG
+ * (NULL or misaligned pointers: 16 bytes for q, k_pages and summary, 4 for
+ * the rest; fp8 without k_scale), ART_ERR_WORKSPACE, the descriptor's errors,
+ * ART_ERR_HIP.
+ */
+art_status art_block_key_summary(const art_decode_desc* desc, const void* k_pages, const float* k_scale,
+                                 const int32_t* block_table, const int32_t* seq_lens, float* summary, void* stream);
+size_t art_importance_order_workspace_bytes(const art_decode_desc* desc);
+art_status art_importance_order(const art_decode_desc* desc, const void* q, const float* summary,
+                                const int32_t* block_table, const int32_t* seq_lens, int32_t* block_order,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code (host memory, never NULL). */
 const char* art_status_string(art_status status);
 

@@ -29,7 +29,8 @@ def art_flag_probe(p: int) -> int:
     return (p // 8) << ART_FLAG_PROBE_SHIFT
 
 EXPORTED = ("art_decode_workspace_bytes", "art_decode_workspace_init", "art_decode", "art_decode_visits",
-            "art_status_string", "art_decode_version", "art_decode_kernel_choice")
+            "art_status_string", "art_decode_version", "art_decode_kernel_choice", "art_block_key_summary",
+            "art_importance_order_workspace_bytes", "art_importance_order")
 ART_KERNEL_FULL, ART_KERNEL_SCANNERS, ART_KERNEL_LOOKBACK, ART_KERNEL_WINDOWED = 0, 1, 2, 3
 KERNEL_NAMES = {ART_KERNEL_FULL: "full_split_kernel", ART_KERNEL_SCANNERS: "art_sched_kernel",
                 ART_KERNEL_LOOKBACK: "art_lb_kernel", ART_KERNEL_WINDOWED: "art_win_part_kernel"}
@@ -80,6 +81,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.art_decode_visits.argtypes = [ctypes.POINTER(ArtDecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, f32,
                                       i32, vp, vp, vp, vp, sz, vp]
     lib.art_decode_visits.restype = ctypes.c_int
+    lib.art_block_key_summary.argtypes = [ctypes.POINTER(ArtDecodeDesc), vp, vp, vp, vp, vp, vp]
+    lib.art_block_key_summary.restype = ctypes.c_int
+    lib.art_importance_order_workspace_bytes.argtypes = [ctypes.POINTER(ArtDecodeDesc)]
+    lib.art_importance_order_workspace_bytes.restype = sz
+    lib.art_importance_order.argtypes = [ctypes.POINTER(ArtDecodeDesc), vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.art_importance_order.restype = ctypes.c_int
     lib.art_status_string.argtypes = [ctypes.c_int]
     lib.art_status_string.restype = ctypes.c_char_p
     lib.art_decode_version.argtypes = []
@@ -179,6 +186,37 @@ def art_decode(q, k_pages, v_pages, block_table, block_order, seq_lens, eps_mag:
                                    _ptr(stop_block), _ptr(blocks_fetched), _ptr(workspace), nbytes,
                                    _stream(stream))
     _check(st)
+
+
+def block_key_summary(q, k_pages, block_table, seq_lens, *, k_scale=None, summary=None, stream=None):
+    """Enqueue art_block_key_summary; returns the float32 [num_pages, Hkv, D] summary tensor."""
+    import torch
+
+    desc = make_desc(q, k_pages, block_table)
+    if summary is None:
+        summary = torch.empty((k_pages.shape[0], k_pages.shape[1], k_pages.shape[3]), dtype=torch.float32,
+                              device=k_pages.device)
+    _check(load_library().art_block_key_summary(ctypes.byref(desc), _ptr(k_pages), _ptr(k_scale), _ptr(block_table),
+                                                _ptr(seq_lens), _ptr(summary), _stream(stream)))
+    return summary
+
+
+def importance_order(q, k_pages, summary, block_table, seq_lens, *, block_order=None, workspace=None, stream=None):
+    """Enqueue art_importance_order; returns the int32 [batch, max_blocks] order tensor (valid below n_s).
+    ``workspace``: a uint8 device tensor of art_importance_order_workspace_bytes bytes (allocated if None)."""
+    import torch
+
+    lib = load_library()
+    desc = make_desc(q, k_pages, block_table)
+    if block_order is None:
+        block_order = torch.full(tuple(block_table.shape), -1, dtype=torch.int32, device=block_table.device)
+    need = lib.art_importance_order_workspace_bytes(ctypes.byref(desc))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=block_table.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.art_importance_order(ctypes.byref(desc), _ptr(q), _ptr(summary), _ptr(block_table), _ptr(seq_lens),
+                                    _ptr(block_order), _ptr(workspace), nbytes, _stream(stream)))
+    return block_order
 
 
 class Decoder:

@@ -372,6 +372,51 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
   return e == hipSuccess ? ART_OK : ART_ERR_HIP;
 }
 
+art_status art_block_key_summary(const art_decode_desc* desc, const void* k_pages, const float* k_scale,
+                                 const int32_t* block_table, const int32_t* seq_lens, float* summary, void* stream) {
+  const art_status ds = check_desc(desc);
+  if (ds != ART_OK) return ds;
+  const bool fp8 = desc->kv_dtype == ART_DTYPE_FP8_E4M3FN;
+  if (!k_pages || !block_table || !seq_lens || !summary || fp8 != (k_scale != nullptr)) return ART_ERR_INVALID_ARG;
+  if (!aligned(k_pages, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(summary, 16) ||
+      (k_scale && !aligned(k_scale, 4)))
+    return ART_ERR_INVALID_ARG;
+  if (desc->batch == 0) return ART_OK;
+  const int kv = desc->kv_dtype == ART_DTYPE_F32 ? art::KV_F32 : (fp8 ? art::KV_FP8 : art::KV_BF16);
+  const hipError_t e = art::launch_order_summary(k_pages, k_scale, block_table, seq_lens, summary, desc->batch,
+                                                 desc->max_blocks_per_seq, desc->num_kv_heads, desc->head_dim,
+                                                 desc->block_size, kv, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ART_OK : ART_ERR_HIP;
+}
+
+size_t art_importance_order_workspace_bytes(const art_decode_desc* desc) {
+  if (check_desc(desc) != ART_OK || desc->batch == 0) return 0;
+  return round256((size_t)desc->batch * desc->max_blocks_per_seq * sizeof(float));
+}
+
+art_status art_importance_order(const art_decode_desc* desc, const void* q, const float* summary,
+                                const int32_t* block_table, const int32_t* seq_lens, int32_t* block_order,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  const art_status ds = check_desc(desc);
+  if (ds != ART_OK) return ds;
+  if (!q || !summary || !block_table || !seq_lens || !block_order) return ART_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(summary, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4) ||
+      !aligned(block_order, 4))
+    return ART_ERR_INVALID_ARG;
+  if (desc->max_blocks_per_seq > art::order_max_blocks()) return ART_ERR_UNSUPPORTED;
+  const size_t need = art_importance_order_workspace_bytes(desc);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return ART_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return ART_ERR_INVALID_ARG;
+  }
+  if (desc->batch == 0) return ART_OK;
+  const int qd = desc->q_dtype == ART_DTYPE_F32 ? art::KV_F32 : art::KV_BF16;
+  const hipError_t e = art::launch_order(q, summary, block_table, seq_lens, block_order, static_cast<float*>(workspace),
+                                         desc->batch, desc->max_blocks_per_seq, desc->num_q_heads, desc->num_kv_heads,
+                                         desc->head_dim, desc->block_size, qd, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ART_OK : ART_ERR_HIP;
+}
+
 const char* art_status_string(art_status s) {
   switch (s) {
     case ART_OK: return "ART_OK";

@@ -122,4 +122,13 @@ hipError_t launch_full_f32(const Variant& v, const Params& p, hipStream_t stream
 hipError_t launch_full_bf16(const Variant& v, const Params& p, hipStream_t stream);
 hipError_t launch_full_fp8(const Variant& v, const Params& p, hipStream_t stream);
 
+// Importance-first order pre-pass (kern_order.hip).
+int order_max_blocks();
+hipError_t launch_order_summary(const void* k_pages, const float* k_scale, const int32_t* block_table,
+                                const int32_t* seq_lens, float* summary, int batch, int max_blocks, int hkv, int d,
+                                int bs, int kv_dtype, hipStream_t st);
+hipError_t launch_order(const void* q, const float* summary, const int32_t* block_table, const int32_t* seq_lens,
+                        int32_t* block_order, float* scores, int batch, int max_blocks, int hq, int hkv, int d, int bs,
+                        int q_dtype, hipStream_t st);
+
 }  // namespace art

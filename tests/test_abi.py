@@ -145,3 +145,18 @@ def test_probe_flag_is_validated(lib):
     assert art.art_decode_workspace_bytes(_desc(flags=art.art_flag_probe(136))) == 0   # P > D
     assert _call(lib, _desc(flags=art.art_flag_probe(136))) == art.ART_ERR_INVALID_ARG
     assert _call(lib, _desc(flags=art.art_flag_probe(8)), wsb=16) == art.ART_ERR_WORKSPACE
+
+
+def test_importance_order_entry_points_validate(lib):
+    """Workspace size query and the checks art_importance_order makes before any work."""
+    d = _desc()
+    need = lib.art_importance_order_workspace_bytes(ctypes.byref(d))
+    assert need >= 2 * 64 * 4 and need % 256 == 0
+    call = lambda desc, ws, wsb: lib.art_importance_order(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, FAKE, ws, wsb,
+                                                          None)
+    assert call(d, FAKE, 16) == art.ART_ERR_WORKSPACE
+    assert call(d, FAKE + 64, need) == art.ART_ERR_INVALID_ARG                    # 256-byte alignment
+    assert call(_desc(max_blocks_per_seq=4097), FAKE, 1 << 30) == art.ART_ERR_UNSUPPORTED
+    assert lib.art_importance_order(ctypes.byref(d), FAKE, FAKE + 4, FAKE, FAKE, FAKE, FAKE, need,
+                                    None) == art.ART_ERR_INVALID_ARG             # summary: 16-byte alignment
+    assert lib.art_block_key_summary(ctypes.byref(d), FAKE, None, FAKE, FAKE, None, None) == art.ART_ERR_INVALID_ARG

@@ -486,3 +486,61 @@ def test_probe_of_every_coordinate_is_the_plain_detector():
     case["probe"] = case["head_dim"]
     b = _device_run(case, case["eps_mag"], case["eps_dir"], case["patience"])
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---- importance-first order: key summaries and the order pre-pass, then ART on that order ---------------
+
+def _device_order(case):
+    import torch
+
+    from kv_cache_run_amd import art
+
+    dev = art.case_to_device(case)
+    sm = art.block_key_summary(dev["q"], dev["k_pages"], dev["block_table"], dev["seq_lens"], k_scale=dev["k_scale"])
+    order = art.importance_order(dev["q"], dev["k_pages"], sm, dev["block_table"], dev["seq_lens"])
+    torch.cuda.synchronize()
+    return sm.cpu().numpy().astype(np.float64), order.cpu().numpy()
+
+
+def _oracle_scores(case, summary):
+    return oracle.block_scores(case["q"], summary, case["block_table"], case["seq_lens"],
+                               block_size=case["block_size"], num_kv_heads=case["num_kv_heads"],
+                               q_dtype=case["q_dtype"])
+
+
+@pytest.mark.parametrize("w", [W.TINY, W.LLAMA3_8B, W.QWEN_FP8, W.RAGGED], ids=["f32", "bf16", "fp8", "ragged"])
+def test_importance_order_parity(w):
+    case = synth.make_case(w, batch=min(w.batch, 3), context=(700, 3000) if isinstance(w.context, tuple) else 2500 - 3)
+    print(f"[order] {w.name}", flush=True)
+    sm, order = _device_order(case)
+    ref_sm = oracle.block_key_summary(case["k_pages"], case["block_table"], case["seq_lens"],
+                                      block_size=case["block_size"], num_kv_heads=case["num_kv_heads"],
+                                      kv_dtype=case["kv_dtype"], k_scale=case["k_scale"])
+    used = np.unique(np.concatenate([case["block_table"][s, :n] for s, n in enumerate(_nblocks(case))]))
+    assert np.allclose(sm[used], ref_sm[used], rtol=1e-5, atol=1e-6)
+    sc = _oracle_scores(case, ref_sm)
+    ref = oracle.importance_order(sc, case["seq_lens"], block_size=case["block_size"])
+    for s, n in enumerate(_nblocks(case)):
+        o = order[s, :n]
+        assert o[0] == 0 and np.array_equal(np.sort(o), np.arange(n))
+        # the same descending score sequence; the blocks may swap only where scores agree to float32 rounding
+        a, b = sc[s, o[1:]], sc[s, ref[s, 1:n]]
+        tol = 1e-5 * max(1.0, float(np.abs(sc[s, :n]).max()))
+        assert np.all(np.abs(a - b) <= tol)
+        assert np.all(np.diff(a) <= tol)
+
+
+def test_importance_order_with_equal_scores_is_recency_first():
+    case = synth.make_case(W.LLAMA3_8B, batch=2, context=1500)
+    case["k_pages"] = np.zeros_like(case["k_pages"])   # every summary 0: every score ties
+    sm, order = _device_order(case)
+    for s, n in enumerate(_nblocks(case)):
+        assert list(order[s, :n]) == [0] + list(range(n - 1, 0, -1))
+
+
+@pytest.mark.parametrize("sched", ["scan", "lb", "win"])
+def test_art_on_the_importance_order(sched):
+    case = synth.make_case(W.LLAMA3_8B, batch=3, context=3000 - 5)
+    _, order = _device_order(case)
+    case["block_order"] = order.astype(np.int32)
+    _with_env(dict(ART_SCHED=sched), lambda: check_art(case))
