@@ -447,7 +447,7 @@ def main(argv=None) -> int:
         pred = slope * x + icpt
         ss = float(((y - y.mean()) ** 2).sum())
         r2 = 1.0 - float(((y - pred) ** 2).sum()) / ss if ss > 0 else 1.0
-        extras["scaling"] = {"points": pts, "slope_us_per_unit_fraction": round(float(slope), 3),
+        extras["threshold_sweep"] = {"points": pts, "slope_us_per_unit_fraction": round(float(slope), 3),
                              "intercept_us": round(float(icpt), 3), "r2": round(r2, 4)}
 
     if args.ablation:
