@@ -70,7 +70,10 @@ art_status check_desc(const art_decode_desc* d) {
 // where scanners would leave most CUs idle for a long walk; the look-back
 // scheduler for groups of more than 4 query heads (a scanner has 4 scan
 // waves); scanners otherwise.  Windowed: ART_WIN_SPLIT fold workgroups per
-// (stream, head) (1 .. 4, default 1); results do not depend on it.
+// (stream, head) (1 .. 4, default 1), ART_WIN_FIRST chunks in the first
+// window (0, the default: 1/8 of the longest stream's chunks, 2 .. 64) and
+// ART_WIN_GROWTH the factor from one window to the next (default 2, windows
+// at most 64 chunks); results depend on none of them.
 // Look-back: ART_WINDOW chunks claimable past a stream's resolved frontier
 // (0: 1/16 of the longest stream's chunks, clamped to 8 .. 32), ART_WORKERS
 // workgroups (0: one per resident slot); results do not depend on either.  Scanners: ART_RING
@@ -84,7 +87,7 @@ int env_int(const char* name, int def, int lo, int hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }
 struct Knobs {
-  int ring, lookahead, helpers, target, lb, window, workers, win_split;
+  int ring, lookahead, helpers, target, lb, window, workers, win_split, win_first, win_growth;
 };
 enum { SCHED_SCAN = 0, SCHED_LB = 1, SCHED_AUTO = 2, SCHED_WIN = 3 };
 Knobs knobs() {
@@ -95,7 +98,8 @@ Knobs knobs() {
   const Knobs k = {env_int("ART_RING", 8, 1, 64),          env_int("ART_LOOKAHEAD", 3, 1, 64),
                    env_int("ART_HELPERS", 0, -1, 1 << 16), env_int("ART_TARGET_WGS", 512, 1, 1 << 16),
                    mode,                                    env_int("ART_WINDOW", 0, 0, 32),
-                   env_int("ART_WORKERS", 0, 0, 1 << 20),       env_int("ART_WIN_SPLIT", 1, 1, art::art_win_split)};
+                   env_int("ART_WORKERS", 0, 0, 1 << 20),       env_int("ART_WIN_SPLIT", 1, 1, art::art_win_split),
+                   env_int("ART_WIN_FIRST", 0, 0, 64),          env_int("ART_WIN_GROWTH", 2, 2, 8)};
   return k;
 }
 
@@ -348,9 +352,15 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
       p.win_dwin = reinterpret_cast<uint32_t*>(ws + wp.win_dwin);
       p.win_pass = reinterpret_cast<uint32_t*>(ws + wp.win_pass);
       p.win_cnt = reinterpret_cast<uint32_t*>(ws + wp.win_cnt);
-      const int split = knobs().win_split;
+      const Knobs kn = knobs();
+      const int split = kn.win_split;
       e = hipSuccess;
-      for (int c0 = 0, size = 2, idx = 0; c0 < wp.max_chunks && e == hipSuccess; ++idx) {
+      // first window: ART_WIN_FIRST, else 1/8 of the longest stream's chunks
+      // (2 .. win_max): the windowed path serves long streams, whose fixed
+      // cost per window outweighs reading a few chunks past early stops
+      int first = kn.win_first > 0 ? kn.win_first : wp.max_chunks / 8;
+      first = first < 2 ? 2 : (first > wp.win_max ? wp.win_max : first);
+      for (int c0 = 0, size = first, idx = 0; c0 < wp.max_chunks && e == hipSuccess; ++idx) {
         const int nw = size < wp.max_chunks - c0 ? size : wp.max_chunks - c0;
         p.win_c0 = c0;
         p.win_n = nw;
@@ -363,7 +373,7 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
         p.win = 2;
         e = launch(p);
         c0 += nw;
-        size = 2 * size < wp.win_max ? 2 * size : wp.win_max;
+        size = kn.win_growth * size < wp.win_max ? kn.win_growth * size : wp.win_max;
       }
     } else {
       e = launch(p);

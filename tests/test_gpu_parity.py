@@ -254,6 +254,9 @@ WIN_VARIANTS = [
     dict(ART_SCHED="win"),                                    # one fold workgroup per (stream, head)
     dict(ART_SCHED="win", ART_WIN_SPLIT="2"),
     dict(ART_SCHED="win", ART_WIN_SPLIT="4"),                 # a 64-chunk window over four workgroups
+    dict(ART_SCHED="win", ART_WIN_FIRST="2", ART_WIN_GROWTH="2"),   # windows 2, 4, 8, ...
+    dict(ART_SCHED="win", ART_WIN_FIRST="64", ART_WIN_SPLIT="3"),   # every window 64 chunks
+    dict(ART_SCHED="win", ART_WIN_FIRST="3", ART_WIN_GROWTH="5"),   # windows 3, 15, 64, ...
 ]
 
 
