@@ -141,8 +141,9 @@ art_status art_decode_workspace_init(void* workspace, size_t workspace_bytes, vo
  * "auto", the default, "scan", "lb" or "win"): one scanner workgroup per
  * stream that folds the stream's blocks in order; persistent workgroups that
  * take chunks of any stream and obtain the state entering a chunk from the
- * records of the chunks before it (look-back); or windows of 2, 4, 8, ... 64
- * chunks, two launches per window (partials, then fold).  Each is
+ * records of the chunks before it (look-back); or growing windows of chunks
+ * (the first 1/8 of the longest stream, doubling, at most 64), two launches
+ * per window (partials, then fold).  Each is
  * deterministic; the look-back and windowed schedulers give the same bits,
  * the scanners differ from them only in floating-point rounding order
  * (within the same tolerance of the method).  "auto" takes the windowed

@@ -341,8 +341,8 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
                                     : art::launch_art_fp8(v, pp, static_cast<hipStream_t>(stream));
     };
     if (sched == SCHED_RUN_WIN) {
-      // windows of 2, 4, 8, ... chunks (at most win_max), two launches each:
-      // the window's partials, then its fold
+      // growing windows of chunks (at most win_max), two launches each: the
+      // window's partials, then its fold
       p.lb = 0;
       p.win_max = wp.win_max;
       p.win_slot = wp.win_slot;

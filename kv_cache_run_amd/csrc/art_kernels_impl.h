@@ -2058,9 +2058,9 @@ __global__ __launch_bounds__((64 * Cfg<KV, D, B, GM>::NWA)) void art_lb_kernel(P
 // Terminating path, windowed: art_win_part_kernel + art_win_scan_kernel
 // ---------------------------------------------------------------------------
 //
-// A stream's chunks are processed window by window (windows of 2, 4, 8, ...
-// chunks, at most 64), two launches per window; launch boundaries are the
-// only waits between workgroups.
+// A stream's chunks are processed window by window (growing windows of at
+// most 64 chunks; the host picks their sizes), two launches per window;
+// launch boundaries are the only waits between workgroups.
 //   * art_win_part_kernel: one workgroup per (stream, chunk), one wave per
 //     block, computes each chunk's per-block partials (m_b, l_b, a_b) for
 //     every head of the group and each head's chunk aggregate.  Streams whose
