@@ -238,7 +238,7 @@ def importance(steps: int, warmup: int) -> dict:
     from kv_cache_run_amd import art, synth, workloads
 
     res = {}
-    for w in (workloads.LLAMA3_8B, workloads.RECENT, workloads.LONG):
+    for w in (workloads.LLAMA3_8B, workloads.RECENT, workloads.LONG, workloads.QWEN_FP8):
         case = synth.make_case(w)
         dev = art.case_to_device(case)
         em, ed, p = case["eps_mag"], case["eps_dir"], case["patience"]
