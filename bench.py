@@ -428,12 +428,16 @@ def main(argv=None) -> int:
         # detector overhead: the terminating kernel with thresholds that can never pass (it folds every
         # block and runs every test) against the full-attention kernel on the same work
         keep = time_setting(case, dev, 0.0, 0.0, p0, art.ART_FLAG_KEEP_DETECTOR, max(5, args.steps // 2), 2)
+        nostats = time_setting(case, dev, 0.0, 0.0, p0, art.ART_FLAG_SKIP_STATS, max(5, args.steps // 2), 2)
         extras["detector_overhead"] = {
             "art_kernel_all_blocks_us": round(keep["us_per_step"], 3),
+            "art_kernel_all_blocks_without_statistics_us": round(nostats["us_per_step"], 3),
+            "detector_cost_fraction": round(keep["us_per_step"] / nostats["us_per_step"] - 1.0, 4),
             "full_kernel_us": round(results["full"]["us_per_step"], 3),
-            "ratio": round(keep["us_per_step"] / results["full"]["us_per_step"], 4),
-            "note": "ART path (detector + sequential scan) forced to fold all blocks vs the split full-attention "
-                    "path; the ratio includes the different parallel decomposition, not only the detector",
+            "ratio_to_full": round(keep["us_per_step"] / results["full"]["us_per_step"], 4),
+            "note": "the terminating kernel folding every block with and without computing the statistics "
+                    "(detector_cost_fraction), and against the split full-attention path (ratio_to_full: mostly "
+                    "the per-stream sequential decomposition)",
         }
         # step time against the KV fraction read: thresholds scaled by 1/4 .. 4 at fixed patience
         pts = []

@@ -60,7 +60,14 @@ enum {
   ART_FLAG_FULL = 1u,
   /* Run the terminating kernel (statistics and patience counters) even when
    * the thresholds make a stop impossible; used to measure detector cost. */
-  ART_FLAG_KEEP_DETECTOR = 2u
+  ART_FLAG_KEEP_DETECTOR = 2u,
+  /* Measurement only: run the terminating kernel over every block with no
+   * test able to pass (both thresholds taken as 0, like KEEP_DETECTOR with
+   * zero thresholds) and the scanners not computing the statistics at all.
+   * The result is full attention; against ART_FLAG_KEEP_DETECTOR with zero
+   * thresholds it isolates what the detector costs (the ART explainer,
+   * section 4, reports about 1.3 %). */
+  ART_FLAG_SKIP_STATS = 4u
 };
 
 /* Probe-vector detector: bits 8..15 of flags hold P / 8, where the two

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libart_decode.so")
 
 ART_OK, ART_ERR_INVALID_ARG, ART_ERR_UNSUPPORTED, ART_ERR_WORKSPACE, ART_ERR_HIP = range(5)
 ART_DTYPE_F32, ART_DTYPE_BF16, ART_DTYPE_FP8_E4M3FN = range(3)
-ART_FLAG_NONE, ART_FLAG_FULL, ART_FLAG_KEEP_DETECTOR = 0, 1, 2
+ART_FLAG_NONE, ART_FLAG_FULL, ART_FLAG_KEEP_DETECTOR, ART_FLAG_SKIP_STATS = 0, 1, 2, 4
 ART_FLAG_PROBE_SHIFT = 8
 
 

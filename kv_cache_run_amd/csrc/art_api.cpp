@@ -43,7 +43,8 @@ art_status check_desc(const art_decode_desc* d) {
       d->num_pages < 1)
     return ART_ERR_INVALID_ARG;
   if (d->num_q_heads % d->num_kv_heads != 0) return ART_ERR_INVALID_ARG;
-  if (d->flags & ~(uint32_t)(ART_FLAG_FULL | ART_FLAG_KEEP_DETECTOR | ART_FLAG_PROBE_MASK)) return ART_ERR_INVALID_ARG;
+  if (d->flags & ~(uint32_t)(ART_FLAG_FULL | ART_FLAG_KEEP_DETECTOR | ART_FLAG_SKIP_STATS | ART_FLAG_PROBE_MASK))
+    return ART_ERR_INVALID_ARG;
   const int g = d->num_q_heads / d->num_kv_heads;
   if (g > 16) return ART_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return ART_ERR_UNSUPPORTED;
@@ -209,7 +210,8 @@ Sched terminating_kernel(const art_decode_desc* d, const art::WorkspacePlan& wp,
 }
 
 bool full_mode(const art_decode_desc* d, float eps_mag, float eps_dir) {
-  return (d->flags & ART_FLAG_FULL) || ((eps_mag == 0.f || eps_dir == 0.f) && !(d->flags & ART_FLAG_KEEP_DETECTOR));
+  return (d->flags & ART_FLAG_FULL) ||
+         ((eps_mag == 0.f || eps_dir == 0.f) && !(d->flags & (ART_FLAG_KEEP_DETECTOR | ART_FLAG_SKIP_STATS)));
 }
 
 }  // namespace
@@ -284,6 +286,12 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
   {
     const int probe8 = (int)((desc->flags & ART_FLAG_PROBE_MASK) >> ART_FLAG_PROBE_SHIFT);
     p.probe = probe8 ? 8 * probe8 : desc->head_dim;
+  }
+  if (desc->flags & ART_FLAG_SKIP_STATS) {
+    // no test may pass in any kernel; the scanners also skip computing them
+    eps_mag = 0.f;
+    eps_dir = 0.f;
+    p.skip_stats = 1;
   }
   p.seq_lens = seq_lens;
   p.out = out;

@@ -85,6 +85,7 @@ struct Params {
   float eps_mag, eps_dir;
   int32_t patience;
   int32_t probe;            // the detector's statistics use coordinates [0, probe) of O (D: all)
+  int32_t skip_stats;       // 1: scanners skip the statistics (thresholds are then 0: no test passes)
   float qk_log2;            // log2(e) / sqrt(D)
 };
 

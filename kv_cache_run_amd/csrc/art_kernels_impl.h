@@ -867,14 +867,16 @@ __device__ __forceinline__ bool scan_head(HeadCarry<Cf>& hc, const ChunkIn<Cf>& 
     st[2 * t] = nn;
     st[2 * t + 1] = ee;
   }
+  float nn_t = 0.f;
+  bool ps = false;
+  if (!p.skip_stats) {  // uniform: off only to measure what the statistics cost
   const float v0 = xreduce<2 * C>(st, lane);
   // lane (2t) << SH holds ‖O_t‖², lane (2t+1) << SH holds ‖O_t - O_{t-1}‖²;
   // gather them so that lane t < C evaluates position t.
-  const float nn_t = __shfl(v0, (2 * slot) << SH);
+  nn_t = __shfl(v0, (2 * slot) << SH);
   const float ee_t = __shfl(v0, (2 * slot + 1) << SH);
   float np_t = __shfl(v0, (2 * max(slot - 1, 0)) << SH);
   if (lane == 0) np_t = hc.Np;
-  bool ps = false;
   if (lane < nt && t0 + lane >= 1) {
     const float a = __builtin_amdgcn_sqrtf(nn_t);
     const float bn = __builtin_amdgcn_sqrtf(np_t);
@@ -890,6 +892,7 @@ __device__ __forceinline__ bool scan_head(HeadCarry<Cf>& hc, const ChunkIn<Cf>& 
       dd = (a == 0.f) ? 1.f : fmaxf(0.f, (ee_t - df * df) * __builtin_amdgcn_rcpf(2.f * a * bn));
     }
     ps = (dm < p.eps_mag) && (dd < p.eps_dir);
+  }
   }
   // patience rule for every position at once: lane t counts the passes in a
   // row that end at t (carrying the count from earlier chunks when every test

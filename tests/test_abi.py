@@ -122,6 +122,11 @@ def test_kernel_choice_follows_the_knob_and_the_mode(lib, monkeypatch):
     assert art.art_decode_kernel_choice(_desc(flags=art.ART_FLAG_FULL), 1e-3, 1e-4, 4) == art.ART_KERNEL_FULL
     assert art.art_decode_kernel_choice(_desc(), 0.0, 1e-4, 4) == art.ART_KERNEL_FULL
     assert art.art_decode_kernel_choice(_desc(flags=art.ART_FLAG_KEEP_DETECTOR), 0.0, 1e-4, 4) == art.ART_KERNEL_LOOKBACK
+    # the measurement flag runs the terminating kernel too, whatever the thresholds
+    assert art.art_decode_kernel_choice(_desc(flags=art.ART_FLAG_SKIP_STATS), 0.0, 0.0, 4) == art.ART_KERNEL_LOOKBACK
+    assert art.art_decode_kernel_choice(_desc(flags=art.ART_FLAG_SKIP_STATS), 1e-3, 1e-4, 4) == art.ART_KERNEL_LOOKBACK
+    with pytest.raises(art.ArtError):   # an unknown flag bit
+        art.art_decode_kernel_choice(_desc(flags=8), 1e-3, 1e-4, 4)
     for bad in [dict(p=0), dict(em=-1.0), dict(ed=float("nan"))]:
         with pytest.raises(art.ArtError):
             art.art_decode_kernel_choice(_desc(), bad.get("em", 1e-3), bad.get("ed", 1e-4), bad.get("p", 4))

@@ -547,3 +547,18 @@ def test_art_on_the_importance_order(sched):
     _, order = _device_order(case)
     case["block_order"] = order.astype(np.int32)
     _with_env(dict(ART_SCHED=sched), lambda: check_art(case))
+
+
+def test_skip_statistics_flag_gives_full_attention_in_every_scheduler():
+    """ART_FLAG_SKIP_STATS (a measurement flag) folds every block with no test passing: the result is the
+    terminating kernel's full attention, whatever the thresholds, through every scheduler."""
+    from kv_cache_run_amd import art
+
+    case = synth.make_case(W.LLAMA3_8B, batch=2, context=1500)
+    ref = _device_run(case, 0.0, 0.0, 4, flags=art.ART_FLAG_KEEP_DETECTOR)
+    n = _nblocks(case)
+    for sched in ("scan", "lb", "win"):
+        out, stop, fetched = _with_env(dict(ART_SCHED=sched),
+                                       lambda: _device_run(case, 1e-3, 1e-4, 4, flags=art.ART_FLAG_SKIP_STATS))
+        assert np.all(stop == n[:, None]), sched
+        assert oracle.feasible.max_rel_err(out, ref[0]) <= 1e-5, sched
