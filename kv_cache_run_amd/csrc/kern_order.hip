@@ -5,8 +5,8 @@
 //
 //   * order_summary_kernel: the mean of each block's valid keys per kv-head
 //     (what a cache would store at write time): one workgroup per
-//     (sequence, logical block), threads over (kv-head, coordinate), rows
-//     read coalesced.
+//     (sequence, logical block), a thread per (kv-head, eight coordinates),
+//     16-byte row loads.
 //   * order_score_kernel: score(s, b) = max over query heads h of
 //     q_h . summary(page(s, b), kv-head of h) / sqrt(D); 16 blocks per
 //     workgroup, q staged in LDS transposed, one lane per query head forming
@@ -32,6 +32,34 @@ __device__ __forceinline__ float load_elem(const void* base, size_t idx, int dty
   return __builtin_amdgcn_cvt_f32_fp8((int) static_cast<const uint8_t*>(base)[idx], 0);  // OCP E4M3FN
 }
 
+// Eight consecutive elements of a row (16-byte aligned for bf16, 8 for fp8,
+// two 16-byte loads for f32) as floats.
+__device__ __forceinline__ void load8(const void* base, size_t idx, int dtype, float (&v)[8]) {
+  if (dtype == KV_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    const float4 a = p[0], c = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+  } else if (dtype == KV_BF16) {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + idx);
+    const uint32_t u[2] = {w.x, w.y};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {  // OCP E4M3FN; the byte selector must be a literal
+      v[4 * i + 0] = __builtin_amdgcn_cvt_f32_fp8((int)u[i], 0);
+      v[4 * i + 1] = __builtin_amdgcn_cvt_f32_fp8((int)u[i], 1);
+      v[4 * i + 2] = __builtin_amdgcn_cvt_f32_fp8((int)u[i], 2);
+      v[4 * i + 3] = __builtin_amdgcn_cvt_f32_fp8((int)u[i], 3);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void order_summary_kernel(const void* k_pages, const float* k_scale,
                                                             const int32_t* block_table, const int32_t* seq_lens,
                                                             float* summary, int max_blocks, int hkv, int d, int bs,
@@ -44,13 +72,22 @@ __global__ __launch_bounds__(256) void order_summary_kernel(const void* k_pages,
   const int page = block_table[(size_t)s * max_blocks + b];
   const int rows = min(bs, L - b * bs);
   const float inv = 1.f / (float)rows;
-  for (int e = threadIdx.x; e < hkv * d; e += blockDim.x) {
-    const int kvh = e / d, c = e - kvh * d;
+  // a thread sums eight consecutive coordinates of one kv-head over the rows
+  const int d8 = d / 8;
+  for (int e = threadIdx.x; e < hkv * d8; e += blockDim.x) {
+    const int kvh = e / d8, c = (e - kvh * d8) * 8;
     const size_t tile = ((size_t)page * hkv + kvh) * bs * d;
-    float acc = 0.f;
-    for (int r = 0; r < rows; ++r) acc += load_elem(k_pages, tile + (size_t)r * d + c, kv_dtype);
-    if (kv_dtype == KV_FP8) acc *= k_scale[(size_t)page * hkv + kvh];
-    summary[((size_t)page * hkv + kvh) * d + c] = acc * inv;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < rows; ++r) {
+      float v[8];
+      load8(k_pages, tile + (size_t)r * d + c, kv_dtype, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    const float f = inv * (kv_dtype == KV_FP8 ? k_scale[(size_t)page * hkv + kvh] : 1.f);
+    float4* dst = reinterpret_cast<float4*>(summary + ((size_t)page * hkv + kvh) * d + c);
+    dst[0] = make_float4(acc[0] * f, acc[1] * f, acc[2] * f, acc[3] * f);
+    dst[1] = make_float4(acc[4] * f, acc[5] * f, acc[6] * f, acc[7] * f);
   }
 }
 
