@@ -562,3 +562,26 @@ def test_skip_statistics_flag_gives_full_attention_in_every_scheduler():
                                        lambda: _device_run(case, 1e-3, 1e-4, 4, flags=art.ART_FLAG_SKIP_STATS))
         assert np.all(stop == n[:, None]), sched
         assert oracle.feasible.max_rel_err(out, ref[0]) <= 1e-5, sched
+
+
+def test_importance_order_on_degenerate_lengths():
+    """Empty, one-token, one-block, block-boundary and longer sequences: the pre-pass writes a valid order
+    (block 0 first) of exactly n_s entries, with the oracle's score sequence; ART then runs on it."""
+    base = synth.make_case(W.LLAMA3_8B, batch=6, context=1000)
+    case = _with_lens(base, [0, 1, 16, 17, 250, 1000])
+    sm, order = _device_order(case)
+    ref_sm = oracle.block_key_summary(case["k_pages"], case["block_table"], case["seq_lens"],
+                                      block_size=case["block_size"], num_kv_heads=case["num_kv_heads"],
+                                      kv_dtype=case["kv_dtype"], k_scale=case["k_scale"])
+    sc = _oracle_scores(case, ref_sm)
+    ref = oracle.importance_order(sc, case["seq_lens"], block_size=case["block_size"])
+    for s, n in enumerate(_nblocks(case)):
+        assert np.all(order[s, n:] == -1)          # positions past n_s untouched
+        if n == 0:
+            continue
+        o = order[s, :n]
+        assert o[0] == 0 and np.array_equal(np.sort(o), np.arange(n))
+        tol = 1e-5 * max(1.0, float(np.abs(sc[s, :n]).max()))
+        assert np.all(np.abs(sc[s, o[1:]] - sc[s, ref[s, 1:n]]) <= tol)
+    case["block_order"] = order.astype(np.int32)
+    check_art(case)
