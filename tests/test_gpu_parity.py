@@ -585,3 +585,51 @@ def test_importance_order_on_degenerate_lengths():
         assert np.all(np.abs(sc[s, o[1:]] - sc[s, ref[s, 1:n]]) <= tol)
     case["block_order"] = order.astype(np.int32)
     check_art(case)
+
+
+# ---- seeded random configurations: features combined across the supported matrix ----------------------
+
+def _random_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    D = int(rng.choice([64, 128]))
+    B = int(rng.choice([16, 32]))
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 3, 4, 7, 8, 16]))
+    kv = str(rng.choice(["f32", "bf16", "fp8_e4m3fn"]))
+    q = "f32" if kv == "f32" else "bf16"
+    batch = int(rng.integers(1, 4))
+    w = W.LLAMA3_8B.scaled(name=f"random-{seed}", batch=batch, num_q_heads=hkv * g, num_kv_heads=hkv, head_dim=D,
+                           block_size=B, q_dtype=q, kv_dtype=kv, context=(1, 40 * B),
+                           heavy=("frac", float(rng.uniform(0.0, 0.08))), seed=2000 + seed)
+    case = synth.make_case(w)
+    lens = case["seq_lens"].copy()
+    lens[0] = int(rng.choice([0, 1, B, B + 1, lens[0]]))   # a degenerate first sequence now and then
+    case = _with_lens(case, lens)
+    n = _nblocks(case)
+    order = case["block_order"].copy()
+    for s in range(batch):
+        kind = int(rng.integers(0, 3))
+        if n[s] > 1 and kind == 1:      # random order
+            order[s, :n[s]] = rng.permutation(n[s])
+        elif n[s] > 1 and kind == 2:    # block 0 last
+            order[s, :n[s]] = list(range(n[s] - 1, -1, -1))
+    case["block_order"] = order
+    if rng.random() < 0.3:
+        case["visit_lens"] = np.array([int(rng.integers(0, m + 1)) for m in n], dtype=np.int32)
+    if rng.random() < 0.3:
+        P = int(rng.choice([8, 16, D // 2]))
+        case["probe"], case["probe_coords"] = P, np.arange(P)
+    em = float(10 ** rng.uniform(-4, -1))
+    ed = float(10 ** rng.uniform(-5, -2))
+    p = int(rng.integers(1, 7))
+    sched = str(rng.choice(["scan", "lb", "win", "auto"]))
+    return case, em, ed, p, sched
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_configurations(seed):
+    case, em, ed, p, sched = _random_case(seed)
+    print(f"[random {seed}] D={case['head_dim']} B={case['block_size']} Hq={case['num_q_heads']} "
+          f"Hkv={case['num_kv_heads']} {case['kv_dtype']} lens={list(case['seq_lens'])} sched={sched} "
+          f"visits={case.get('visit_lens')} probe={case.get('probe')} eps=({em:.2e},{ed:.2e}) p={p}", flush=True)
+    _with_env(dict(ART_SCHED=sched), lambda: check_art(case, eps_mag=em, eps_dir=ed, patience=p))
