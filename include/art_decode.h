@@ -56,7 +56,8 @@ enum {
   ART_FLAG_NONE = 0,
   /* Full attention: every block is folded, stop_block = n.  Selected
    * automatically when eps_mag == 0 or eps_dir == 0 (a strict "<" test can
-   * then never pass), unless ART_FLAG_KEEP_DETECTOR is set. */
+   * then never pass), unless ART_FLAG_KEEP_DETECTOR or ART_FLAG_SKIP_STATS
+   * is set. */
   ART_FLAG_FULL = 1u,
   /* Run the terminating kernel (statistics and patience counters) even when
    * the thresholds make a stop impossible; used to measure detector cost. */
