@@ -71,7 +71,8 @@ art_status check_desc(const art_decode_desc* d) {
 // where scanners would leave most CUs idle for a long walk; the look-back
 // scheduler for groups of more than 4 query heads (a scanner has 4 scan
 // waves); scanners otherwise.  Windowed: ART_WIN_SPLIT fold workgroups per
-// (stream, head) (1 .. 4, default 1), ART_WIN_FIRST chunks in the first
+// (stream, head) (1 .. 4; 0, the default: 2 when there are few heads, else
+// 1), ART_WIN_FIRST chunks in the first
 // window (0, the default: 1/8 of the longest stream's chunks, 2 .. 64) and
 // ART_WIN_GROWTH the factor from one window to the next (default 2, windows
 // at most 64 chunks); results depend on none of them.
@@ -99,7 +100,7 @@ Knobs knobs() {
   const Knobs k = {env_int("ART_RING", 8, 1, 64),          env_int("ART_LOOKAHEAD", 3, 1, 64),
                    env_int("ART_HELPERS", 0, -1, 1 << 16), env_int("ART_TARGET_WGS", 512, 1, 1 << 16),
                    mode,                                    env_int("ART_WINDOW", 0, 0, 32),
-                   env_int("ART_WORKERS", 0, 0, 1 << 20),       env_int("ART_WIN_SPLIT", 1, 1, art::art_win_split),
+                   env_int("ART_WORKERS", 0, 0, 1 << 20),       env_int("ART_WIN_SPLIT", 0, 0, art::art_win_split),
                    env_int("ART_WIN_FIRST", 0, 0, 64),          env_int("ART_WIN_GROWTH", 2, 2, 8)};
   return k;
 }
@@ -361,7 +362,19 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
       p.win_pass = reinterpret_cast<uint32_t*>(ws + wp.win_pass);
       p.win_cnt = reinterpret_cast<uint32_t*>(ws + wp.win_cnt);
       const Knobs kn = knobs();
-      const int split = kn.win_split;
+      // fold workgroups per (stream, head): ART_WIN_SPLIT, else 2 while the
+      // doubled fold grid still fits two workgroups per CU (few heads: the
+      // split shortens each window's fold), 1 otherwise (many heads: the
+      // chip is full and the split only repeats the prefix work)
+      int split = kn.win_split;
+      if (split == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+          cus = 256;
+        const long folds = (long)desc->batch * desc->num_q_heads;
+        split = 2 * folds <= 2L * cus ? 2 : 1;
+      }
       e = hipSuccess;
       // first window: ART_WIN_FIRST, else 1/8 of the longest stream's chunks
       // (2 .. win_max): the windowed path serves long streams, whose fixed

@@ -251,7 +251,8 @@ SCAN_VARIANTS = [
 
 
 WIN_VARIANTS = [
-    dict(ART_SCHED="win"),                                    # one fold workgroup per (stream, head)
+    dict(ART_SCHED="win"),                                    # default: two fold workgroups when heads are few
+    dict(ART_SCHED="win", ART_WIN_SPLIT="1"),                 # one fold workgroup per (stream, head)
     dict(ART_SCHED="win", ART_WIN_SPLIT="2"),
     dict(ART_SCHED="win", ART_WIN_SPLIT="4"),                 # a 64-chunk window over four workgroups
     dict(ART_SCHED="win", ART_WIN_FIRST="2", ART_WIN_GROWTH="2"),   # windows 2, 4, 8, ...
