@@ -398,8 +398,9 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md for how the "
-              "decode would shard across GPUs); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the decode has no multi-GPU path (sequences and kv-heads "
+              "are independent, so a batch would split across GPUs with no communication); run with --gpus 1",
+              file=sys.stderr)
         return 2
 
     import torch

@@ -20,7 +20,7 @@ Large Language Model Decoding" (gist.science explainer of the paper):
   block 0 (the attention sink) must be folded before any stop; positional
   encoding and the mask are applied before accumulation.
 
-Readings where the page is silent or loose (each is listed in the design doc):
+Readings where the page is silent or loose:
 
 * the monitored vector is the whole normalized partial output
   ``O_t = acc_t / l_t`` (not a few probe coordinates);

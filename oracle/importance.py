@@ -1,7 +1,7 @@
 """Importance-first visit order, plain float64 (TEST INFRASTRUCTURE ONLY; see art_oracle.py's header).
 
 The ART explainer (Technical Summary 2.4) names "importance-first" beside "recency-first" as a traversal
-order ART can run over; it does not define the importance.  The reading taken here (R28):
+order ART can run over; it does not define the importance.  The reading taken here:
 
 * a block's key summary per kv-head is the mean of its valid key rows (what a cache could store when it
   writes the block);
