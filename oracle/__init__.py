@@ -25,3 +25,4 @@ from .art_oracle import (  # noqa: F401
 from .bruteforce import prefix_attention_bruteforce  # noqa: F401
 from .feasible import classify_tests, feasible_stop, compare_with_oracle  # noqa: F401
 from .importance import block_key_summary, block_scores, importance_order  # noqa: F401
+from .inputs_check import check_inputs  # noqa: F401
