@@ -25,7 +25,8 @@
  *    before anything is enqueued, and returned synchronously.
  *  - Content errors (a block_order row that is not a permutation of
  *    [0, n_s), a block_table entry outside [0, num_pages), seq_lens[s] >
- *    max_blocks_per_seq * block_size) are undefined behaviour.
+ *    max_blocks_per_seq * block_size) are undefined behaviour in the decode;
+ *    art_check_inputs finds them.
  *  - Two calls that share a workspace must not overlap in time.
  */
 #ifndef ART_DECODE_H
@@ -233,6 +234,36 @@ size_t art_importance_order_workspace_bytes(const art_decode_desc* desc);
 art_status art_importance_order(const art_decode_desc* desc, const void* q, const float* summary,
                                 const int32_t* block_table, const int32_t* seq_lens, int32_t* block_order,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Input-contract check: finds, on the device, the content errors the decode
+ * takes as absent (its inputs walk a sequence's blocks in a traversal order
+ * through a paged cache: the ART explainer, Technical Summary 2.4).  Meant
+ * for debugging and for callers that take tables from elsewhere; the decode
+ * itself never checks.  For each sequence s in turn:
+ *   code 1  seq_lens[s] < 0 or > max_blocks_per_seq * block_size
+ *           (position 0, value = seq_lens[s]);
+ * and with n_s = ceil(seq_lens[s] / block_size) and v_s = n_s, or
+ * visit_lens[s] clamped to [0, n_s] when visit_lens is not NULL (as for
+ * art_decode_visits), at each visit position t < v_s, b = block_order[s][t]:
+ *   code 2  b outside [0, n_s)                              (value = b),
+ *   code 3  b also at another visit position t' < v_s       (value = b),
+ *   code 4  block_table[s][b] outside [0, desc->num_pages)  (value = page).
+ * result (device int32[4], 8-byte aligned, caller-owned; also used as
+ * scratch while the check runs) receives {code, s, t, value} of the first
+ * violation in (s, t, code) order, or {0, 0, 0, 0}.  Only cells of
+ * block_order and block_table at visited positions and their blocks are
+ * read (all within [batch][max_blocks_per_seq]), so any contents are safe.
+ * Enqueued on `stream` (three small launches, no synchronization; calls
+ * that share `result` must not overlap).  Needs max_blocks_per_seq <= 2^18
+ * (else ART_ERR_UNSUPPORTED).  Errors: ART_ERR_INVALID_ARG (NULL or
+ * misaligned pointers: 8 bytes for result, 4 for the rest), the
+ * descriptor's errors, ART_ERR_HIP.
+ */
+enum { ART_CHECK_OK = 0, ART_CHECK_SEQ_LEN = 1, ART_CHECK_ORDER_RANGE = 2, ART_CHECK_ORDER_REPEAT = 3,
+       ART_CHECK_PAGE_RANGE = 4 };
+art_status art_check_inputs(const art_decode_desc* desc, const int32_t* block_table, const int32_t* block_order,
+                            const int32_t* seq_lens, const int32_t* visit_lens, int32_t* result, void* stream);
 
 /* Static, human-readable name of a status code (host memory, never NULL). */
 const char* art_status_string(art_status status);

@@ -30,8 +30,13 @@ def art_flag_probe(p: int) -> int:
 
 EXPORTED = ("art_decode_workspace_bytes", "art_decode_workspace_init", "art_decode", "art_decode_visits",
             "art_status_string", "art_decode_version", "art_decode_kernel_choice", "art_block_key_summary",
-            "art_importance_order_workspace_bytes", "art_importance_order")
+            "art_importance_order_workspace_bytes", "art_importance_order", "art_check_inputs")
 ART_KERNEL_FULL, ART_KERNEL_SCANNERS, ART_KERNEL_LOOKBACK, ART_KERNEL_WINDOWED = 0, 1, 2, 3
+ART_CHECK_OK, ART_CHECK_SEQ_LEN, ART_CHECK_ORDER_RANGE, ART_CHECK_ORDER_REPEAT, ART_CHECK_PAGE_RANGE = 0, 1, 2, 3, 4
+CHECK_NAMES = {ART_CHECK_SEQ_LEN: "sequence length outside [0, max_blocks * block_size]",
+               ART_CHECK_ORDER_RANGE: "order entry outside [0, n_s)",
+               ART_CHECK_ORDER_REPEAT: "order entry repeated among the visited positions",
+               ART_CHECK_PAGE_RANGE: "page outside [0, num_pages)"}
 KERNEL_NAMES = {ART_KERNEL_FULL: "full_split_kernel", ART_KERNEL_SCANNERS: "art_sched_kernel",
                 ART_KERNEL_LOOKBACK: "art_lb_kernel", ART_KERNEL_WINDOWED: "art_win_part_kernel"}
 
@@ -87,6 +92,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.art_importance_order_workspace_bytes.restype = sz
     lib.art_importance_order.argtypes = [ctypes.POINTER(ArtDecodeDesc), vp, vp, vp, vp, vp, vp, sz, vp]
     lib.art_importance_order.restype = ctypes.c_int
+    lib.art_check_inputs.argtypes = [ctypes.POINTER(ArtDecodeDesc), vp, vp, vp, vp, vp, vp]
+    lib.art_check_inputs.restype = ctypes.c_int
     lib.art_status_string.argtypes = [ctypes.c_int]
     lib.art_status_string.restype = ctypes.c_char_p
     lib.art_decode_version.argtypes = []
@@ -219,12 +226,36 @@ def importance_order(q, k_pages, summary, block_table, seq_lens, *, block_order=
     return block_order
 
 
-class Decoder:
-    """Holds a device workspace for one descriptor shape and calls :func:`art_decode`."""
+def check_inputs(q, k_pages, block_table, block_order, seq_lens, *, visit_lens=None, result=None, stream=None):
+    """Enqueue art_check_inputs; returns the int32 [4] device tensor (code, sequence, position, value)."""
+    import torch
 
-    def __init__(self, q, k_pages, block_table, device=None):
+    desc = make_desc(q, k_pages, block_table)
+    if result is None:
+        result = torch.empty(4, dtype=torch.int32, device=block_table.device)
+    _check(load_library().art_check_inputs(ctypes.byref(desc), _ptr(block_table), _ptr(block_order), _ptr(seq_lens),
+                                           _ptr(visit_lens), _ptr(result), _stream(stream)))
+    return result
+
+
+def validate_inputs(q, k_pages, block_table, block_order, seq_lens, *, visit_lens=None, stream=None) -> None:
+    """Run the input-contract check and wait for it; raises ValueError naming the first violation."""
+    r = check_inputs(q, k_pages, block_table, block_order, seq_lens, visit_lens=visit_lens, stream=stream)
+    code, s, t, val = (int(x) for x in r.cpu())
+    if code != ART_CHECK_OK:
+        raise ValueError(f"decode inputs: {CHECK_NAMES[code]} (sequence {s}, visit position {t}, value {val})")
+
+
+class Decoder:
+    """Holds a device workspace for one descriptor shape and calls :func:`art_decode`.
+
+    With ``check_inputs`` (default: environment ART_CHECK_INPUTS=1) every call first runs the input-contract
+    check and waits for it (a debugging aid: it synchronizes the stream)."""
+
+    def __init__(self, q, k_pages, block_table, device=None, check_inputs=None):
         import torch
 
+        self.check = os.environ.get("ART_CHECK_INPUTS") == "1" if check_inputs is None else bool(check_inputs)
         self.desc = make_desc(q, k_pages, block_table)
         nbytes = art_decode_workspace_bytes(self.desc)
         self.workspace = None
@@ -238,6 +269,8 @@ class Decoder:
         import torch
 
         batch, hq, d = q.shape
+        if self.check:
+            validate_inputs(q, k_pages, block_table, block_order, seq_lens, visit_lens=visit_lens, stream=stream)
         if out is None:
             out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
         if stop_block is None:

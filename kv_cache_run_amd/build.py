@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libart_decode.so")
 
 SOURCES = ["kern_art_bf16.hip", "kern_art_fp8.hip", "kern_art_f32.hip", "kern_full_bf16.hip",
-           "kern_full_fp8.hip", "kern_full_f32.hip", "kern_order.hip", "art_api.cpp"]
+           "kern_full_fp8.hip", "kern_full_f32.hip", "kern_order.hip", "kern_check.hip", "art_api.cpp"]
 
 # Packed-FP32 VALU forms are disabled for every HIP translation unit: the
 # compiler would otherwise pack float2 arithmetic into them on its own.

@@ -448,6 +448,21 @@ art_status art_importance_order(const art_decode_desc* desc, const void* q, cons
   return e == hipSuccess ? ART_OK : ART_ERR_HIP;
 }
 
+art_status art_check_inputs(const art_decode_desc* desc, const int32_t* block_table, const int32_t* block_order,
+                            const int32_t* seq_lens, const int32_t* visit_lens, int32_t* result, void* stream) {
+  const art_status ds = check_desc(desc);
+  if (ds != ART_OK) return ds;
+  if (!block_table || !block_order || !seq_lens || !result) return ART_ERR_INVALID_ARG;
+  if (!aligned(block_table, 4) || !aligned(block_order, 4) || !aligned(seq_lens, 4) || !aligned(result, 8) ||
+      (visit_lens && !aligned(visit_lens, 4)))
+    return ART_ERR_INVALID_ARG;
+  if (desc->max_blocks_per_seq > art::check_max_blocks()) return ART_ERR_UNSUPPORTED;
+  const hipError_t e =
+      art::launch_check(block_table, block_order, seq_lens, visit_lens, result, desc->batch, desc->max_blocks_per_seq,
+                        desc->block_size, desc->num_pages, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ART_OK : ART_ERR_HIP;
+}
+
 const char* art_status_string(art_status s) {
   switch (s) {
     case ART_OK: return "ART_OK";

@@ -123,6 +123,12 @@ hipError_t launch_full_f32(const Variant& v, const Params& p, hipStream_t stream
 hipError_t launch_full_bf16(const Variant& v, const Params& p, hipStream_t stream);
 hipError_t launch_full_fp8(const Variant& v, const Params& p, hipStream_t stream);
 
+// Input-contract check (kern_check.hip).
+int check_max_blocks();
+hipError_t launch_check(const int32_t* block_table, const int32_t* block_order, const int32_t* seq_lens,
+                        const int32_t* visit_lens, int32_t* result, int batch, int max_blocks, int bs, int num_pages,
+                        hipStream_t stream);
+
 // Importance-first order pre-pass (kern_order.hip).
 int order_max_blocks();
 hipError_t launch_order_summary(const void* k_pages, const float* k_scale, const int32_t* block_table,

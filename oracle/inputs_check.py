@@ -16,6 +16,7 @@ The first violation in (sequence, visit position) order is reported, and at one 
 
 from __future__ import annotations
 
+from collections import Counter
 from typing import Tuple
 
 import numpy as np
@@ -38,10 +39,11 @@ def check_inputs(block_table, block_order, seq_lens, *, num_pages: int, block_si
         n = -(-L // block_size)
         v = n if visit_lens is None else min(max(int(visit_lens[s]), 0), n)
         row = [int(x) for x in block_order[s, :v]]
+        times = Counter(row)  # how often each entry occurs among the visited positions
         for t, b in enumerate(row):
             if not 0 <= b < n:
                 return ORDER_RANGE, s, t, b
-            if row.count(b) > 1:
+            if times[b] > 1:
                 return ORDER_REPEAT, s, t, b
             pg = int(block_table[s, b])
             if not 0 <= pg < num_pages:

@@ -165,3 +165,16 @@ def test_importance_order_entry_points_validate(lib):
     assert lib.art_importance_order(ctypes.byref(d), FAKE, FAKE + 4, FAKE, FAKE, FAKE, FAKE, need,
                                     None) == art.ART_ERR_INVALID_ARG             # summary: 16-byte alignment
     assert lib.art_block_key_summary(ctypes.byref(d), FAKE, None, FAKE, FAKE, None, None) == art.ART_ERR_INVALID_ARG
+
+
+def test_check_inputs_entry_point_validates(lib):
+    """art_check_inputs rejects NULL and misaligned pointers, a bad descriptor and too-long rows before any work."""
+    d = _desc()
+    call = lambda desc, bt, bo, sl, vl, res: lib.art_check_inputs(ctypes.byref(desc), bt, bo, sl, vl, res, None)
+    assert call(d, None, FAKE, FAKE, None, FAKE) == art.ART_ERR_INVALID_ARG
+    assert call(d, FAKE, FAKE, FAKE, None, None) == art.ART_ERR_INVALID_ARG
+    assert call(d, FAKE, FAKE, FAKE, None, FAKE + 4) == art.ART_ERR_INVALID_ARG   # result: 8-byte alignment
+    assert call(d, FAKE + 2, FAKE, FAKE, None, FAKE) == art.ART_ERR_INVALID_ARG   # tables: 4-byte alignment
+    assert call(d, FAKE, FAKE, FAKE, FAKE + 1, FAKE) == art.ART_ERR_INVALID_ARG
+    assert call(_desc(max_blocks_per_seq=(1 << 18) + 1), FAKE, FAKE, FAKE, None, FAKE) == art.ART_ERR_UNSUPPORTED
+    assert call(_desc(num_kv_heads=3), FAKE, FAKE, FAKE, None, FAKE) != art.ART_OK

@@ -8,6 +8,7 @@ heads plus properties that hold at any size.
 """
 
 import math
+import zlib
 
 import numpy as np
 import pytest
@@ -634,3 +635,121 @@ def test_random_configurations(seed):
           f"Hkv={case['num_kv_heads']} {case['kv_dtype']} lens={list(case['seq_lens'])} sched={sched} "
           f"visits={case.get('visit_lens')} probe={case.get('probe')} eps=({em:.2e},{ed:.2e}) p={p}", flush=True)
     _with_env(dict(ART_SCHED=sched), lambda: check_art(case, eps_mag=em, eps_dir=ed, patience=p))
+
+
+# ---- the input-contract check (art_check_inputs) -------------------------------------------------------
+
+_TORCH_DT = {"bf16": "bfloat16", "fp8_e4m3fn": "float8_e4m3fn", "f32": "float32"}
+
+
+def _check_dev(case, bt, bo, sl, vl=None, num_pages=None):
+    """art_check_inputs on device copies of the integer tables (q and the pages enter only through their
+    shapes and dtypes, so they are meta tensors)."""
+    import torch
+
+    from kv_cache_run_amd import art
+
+    pages = case["k_pages"].shape[0] if num_pages is None else num_pages
+    q = torch.empty(case["q"].shape, dtype=getattr(torch, _TORCH_DT[case["q_dtype"]]), device="meta")
+    kp = torch.empty((pages,) + tuple(case["k_pages"].shape[1:]), dtype=getattr(torch, _TORCH_DT[case["kv_dtype"]]),
+                     device="meta")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    r = art.check_inputs(q, kp, t(bt), t(bo), t(sl), visit_lens=None if vl is None else t(vl))
+    torch.cuda.synchronize()
+    return tuple(int(x) for x in r.cpu())
+
+
+def _corrupt(case, rng):
+    """1-3 planted violations of random kinds at random places (and sometimes a visit count per sequence)."""
+    bt, bo, sl = case["block_table"].copy(), case["block_order"].copy(), case["seq_lens"].copy()
+    batch, mb = bo.shape
+    B = case["block_size"]
+    pages = case["k_pages"].shape[0]
+    n = -(-sl.astype(np.int64) // B)
+    for _ in range(int(rng.integers(1, 4))):
+        s = int(rng.integers(0, batch))
+        kind = int(rng.integers(0, 6))
+        if kind == 0:
+            sl[s] = int(rng.choice([-1, -int(rng.integers(2, 1 << 20)), mb * B + 1, mb * B + int(rng.integers(2, 999))]))
+        elif n[s] >= 2:
+            t, u = (int(x) for x in rng.choice(n[s], size=2, replace=False))
+            if kind == 1:
+                bo[s, u] = int(rng.choice([-1, n[s], n[s] + int(rng.integers(0, 99)), -(1 << 30)]))
+            elif kind == 2:
+                bo[s, u] = bo[s, t]
+            elif kind == 3:
+                b = bo[s, u]
+                if 0 <= b < n[s]:
+                    bt[s, b] = int(rng.choice([pages, pages + int(rng.integers(0, 99)), -1]))
+            elif kind == 4:
+                bo[s, u], bo[s, t] = bo[s, t], bo[s, u]  # still valid
+            else:
+                bt[s, mb - 1] = -5  # a cell no visit reaches when n_s < max_blocks
+    vl = None
+    if rng.random() < 0.3:
+        vl = np.array([int(rng.integers(-2, m + 3)) for m in n], dtype=np.int32)
+    return bt, bo, sl, vl
+
+
+@pytest.mark.parametrize("w,kw", REDUCED, ids=[f"{w.name}-{kw}" for w, kw in REDUCED])
+def test_check_inputs_matches_the_oracle(w, kw):
+    case = synth.make_case(w, **kw)
+    pages = case["k_pages"].shape[0]
+    args = (case["block_table"], case["block_order"], case["seq_lens"])
+    print(f"[check] {case['workload']}", flush=True)
+    assert _check_dev(case, *args) == (0, 0, 0, 0)
+    rng = np.random.default_rng(zlib.crc32(case["workload"].encode()))
+    codes = set()
+    for trial in range(24):
+        bt, bo, sl, vl = _corrupt(case, rng)
+        want = oracle.check_inputs(bt, bo, sl, num_pages=pages, block_size=case["block_size"], visit_lens=vl)
+        got = _check_dev(case, bt, bo, sl, vl)
+        assert got == want, (trial, got, want)
+        codes.add(want[0])
+    assert len(codes) >= 3, codes
+
+
+def test_check_inputs_at_the_longest_rows():
+    """Rows of 2^18 blocks (the largest the check takes), one at full capacity: valid, then a repeat and a bad
+    page near the end of the row, and an entry out of range in the second sequence."""
+    base = synth.make_case(W.TINY, batch=2, context=64)
+    mb, B = 1 << 18, base["block_size"]
+    rng = np.random.default_rng(3)
+    pages = 1 << 20
+    bt = rng.integers(0, pages, size=(2, mb)).astype(np.int32)
+    bo = np.full((2, mb), -1, dtype=np.int32)
+    bo[0] = np.concatenate([[0], rng.permutation(np.arange(1, mb))])
+    n1 = 100000
+    bo[1, :n1] = rng.permutation(n1)
+    sl = np.array([mb * B, n1 * B - 3], dtype=np.int32)
+    case = dict(base, block_size=B)
+    assert _check_dev(case, bt, bo, sl, num_pages=pages) == (0, 0, 0, 0)
+    bo2 = bo.copy()
+    bo2[0, 262000] = bo2[0, 200000]
+    bt2 = bt.copy()
+    bt2[0, bo[0, 150000]] = pages
+    bo2[1, 5] = n1
+    for a in ((bt, bo2, sl), (bt2, bo, sl), (bt2, bo2, sl), (bt, bo2, sl[::-1].copy())):
+        want = oracle.check_inputs(*a, num_pages=pages, block_size=B)
+        assert _check_dev(case, *a, num_pages=pages) == want, want
+    assert oracle.check_inputs(bt, bo2, sl, num_pages=pages, block_size=B) == (3, 0, 200000, int(bo[0, 200000]))
+
+
+def test_decoder_checks_inputs_when_asked():
+    import torch
+
+    from kv_cache_run_amd import art
+
+    case = synth.make_case(W.TINY)
+    dev = art.case_to_device(case)
+    dec = art.Decoder(dev["q"], dev["k_pages"], dev["block_table"], check_inputs=True)
+    out, stop = dec(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"], dev["block_order"], dev["seq_lens"],
+                    case["eps_mag"], case["eps_dir"], case["patience"])
+    torch.cuda.synchronize()
+    ref = _device_run(case, case["eps_mag"], case["eps_dir"], case["patience"])
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), ref[0]) and np.array_equal(stop.cpu().numpy(), ref[1])
+    bad = dev["block_order"].clone()
+    bad[0, 3] = bad[0, 1]
+    with pytest.raises(ValueError, match="repeated"):
+        dec(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"], bad, dev["seq_lens"], case["eps_mag"],
+            case["eps_dir"], case["patience"])
