@@ -63,7 +63,7 @@ constexpr float NEG_INF = -__builtin_inff();
 constexpr int NW = 4;        // waves per workgroup, full-attention kernel
 constexpr int WG = 64 * NW;  // threads per workgroup, full-attention kernel
 #ifndef FULL_PREFETCH
-#define FULL_PREFETCH 3  // blocks in the full kernel's register ring
+#define FULL_PREFETCH 2  // blocks in the full kernel's register ring
 #endif
 
 template <int KV> struct ElemSize;
@@ -2519,8 +2519,16 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int split = blockIdx.x % p.splits;
-  const int stream = blockIdx.x / p.splits;
+  // Workgroup i takes slice i / streams of stream i % streams (streams =
+  // (sequence, kv-head), kv-head fastest).  Workgroups are dealt to the 8
+  // XCDs round-robin: slice-major keeps each XCD's share of a ragged batch
+  // equal (stream-major with 8 slices per stream would give XCD k every
+  // slice k, and late slices of short sequences are empty), puts the
+  // slices that always hold blocks first, and lets adjacent workgroups read
+  // the adjacent kv-head tiles of the same pages together.
+  const int streams = p.batch * p.hkv;
+  const int split = blockIdx.x / streams;
+  const int stream = blockIdx.x - split * streams;
   const int s = stream / p.hkv;
   const int kvh = stream - s * p.hkv;
   const int g = p.g;
