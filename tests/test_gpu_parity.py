@@ -753,3 +753,48 @@ def test_decoder_checks_inputs_when_asked():
     with pytest.raises(ValueError, match="repeated"):
         dec(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"], bad, dev["seq_lens"], case["eps_mag"],
             case["eps_dir"], case["patience"])
+
+
+@pytest.mark.parametrize("w", [W.LLAMA3_8B, W.QWEN_FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("sched", ["scan", "lb", "win", "full"])
+def test_pages_past_4_gib(sched, w):
+    """Page addressing is 64-bit: the same pages (and fp8 scales) placed past 4 GiB of K and of V (a pool
+    of ≈4.3 GiB each) give the same bits as at low page ids, for each ART scheduler and for full attention."""
+    import torch
+
+    from kv_cache_run_amd import art
+
+    case = synth.make_case(w, batch=2, context=3000)
+    dev = art.case_to_device(case)
+    k, v = dev["k_pages"], dev["v_pages"]
+    page_bytes = k[0].numel() * k.element_size()
+    base = (4 << 30) // page_bytes + 1000
+    kb = torch.empty((base + k.shape[0],) + tuple(k.shape[1:]), dtype=k.dtype, device=k.device)
+    vb = torch.empty_like(kb)
+    kb[base:] = k
+    vb[base:] = v
+    scales = {}
+    if dev["k_scale"] is not None:
+        for name in ("k_scale", "v_scale"):
+            sc = torch.ones((base + k.shape[0], k.shape[1]), dtype=torch.float32, device=k.device)
+            sc[base:] = dev[name]
+            scales[name] = sc
+    bt = dev["block_table"] + base
+    assert (int(bt.min()) * page_bytes) >= (4 << 30)
+    em, ed, p = (0.0, 0.0, 1) if sched == "full" else (case["eps_mag"], case["eps_dir"], case["patience"])
+    env = {} if sched == "full" else dict(ART_SCHED=sched)
+    print(f"[4gib] {sched} pool {kb.shape[0]} pages ({kb.numel() * kb.element_size() >> 20} MiB each for K and V)",
+          flush=True)
+
+    def run(kp, vp, table, ks, vs):
+        dec = art.Decoder(dev["q"], kp, table)
+        out, stop = dec(dev["q"], kp, vp, table, dev["block_order"], dev["seq_lens"], em, ed, p, k_scale=ks,
+                        v_scale=vs)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), stop.cpu().numpy()
+
+    lo = _with_env(env, lambda: run(k, v, dev["block_table"], dev["k_scale"], dev["v_scale"]))
+    hi = _with_env(env, lambda: run(kb, vb, bt, scales.get("k_scale"), scales.get("v_scale")))
+    assert np.array_equal(lo[0], hi[0]) and np.array_equal(lo[1], hi[1])
+    del kb, vb
+    torch.cuda.empty_cache()
