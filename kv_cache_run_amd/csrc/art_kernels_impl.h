@@ -259,13 +259,47 @@ __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
+// One KV load of 16, 8 or 4 bytes; NT: non-temporal (streamed past the
+// caches, for data read exactly once).
+template <bool NT>
+__device__ __forceinline__ uint4 ld_kv16(const char* a) {
+  if constexpr (NT) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a));
+    return make_uint4(x.x, x.y, x.z, x.w);
+  } else {
+    return *reinterpret_cast<const uint4*>(a);
+  }
+}
+template <bool NT>
+__device__ __forceinline__ uint2 ld_kv8(const char* a) {
+  if constexpr (NT) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a));
+    return make_uint2(x.x, x.y);
+  } else {
+    return *reinterpret_cast<const uint2*>(a);
+  }
+}
+template <bool NT>
+__device__ __forceinline__ uint32_t ld_kv4(const char* a) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a));
+  else
+    return *reinterpret_cast<const uint32_t*>(a);
+}
+
 // Load one block: K in the QK A-operand layout, V in the PV operand layout.
 // Every row of the tile is read (a tile always holds B rows), so the loads
 // are a base address plus immediate offsets; when the block is the partial
 // last block of a sequence, the V values of rows at or past nvalid are then
 // zeroed, so that every V value fed to the PV product is finite (their P is
 // exactly 0; K of those rows only feeds masked scores).
-template <class Cf>
+// NT: non-temporal loads.  The full-attention kernel reads every tile once
+// and streams them (measured: 0.82 instead of 0.73 of HBM peak on 8 KiB
+// tiles); the terminating kernels keep the default, since their clamped
+// re-reads of a chunk past a stream's end are meant to hit in the cache.
+template <class Cf, bool NT = false>
 __device__ __forceinline__ void load_block(BlockRegs<Cf>& r, const char* kt, const char* vt, int lane, int nvalid) {
   const int c = lane & 15;
   const int q = lane >> 4;
@@ -273,7 +307,7 @@ __device__ __forceinline__ void load_block(BlockRegs<Cf>& r, const char* kt, con
   for (int t = 0; t < Cf::T; ++t)
 #pragma unroll
     for (int i = 0; i < Cf::NKL; ++i)
-      r.k[t][i] = *reinterpret_cast<const uint4*>(kt + (size_t)(16 * t + c) * Cf::R + q * 16 + 64 * i);
+      r.k[t][i] = ld_kv16<NT>(kt + (size_t)(16 * t + c) * Cf::R + q * 16 + 64 * i);
   if constexpr (Cf::PV4) {
     // load u covers token rows u*RPL .. u*RPL+RPL-1; lane: row u*RPL + lane/LPR,
     // bytes (lane % LPR) * BPL .. +BPL of it
@@ -282,9 +316,9 @@ __device__ __forceinline__ void load_block(BlockRegs<Cf>& r, const char* kt, con
 #pragma unroll
     for (int u = 0; u < Cf::NLD; ++u) {
       if constexpr (Cf::VW == 1) {
-        r.v[u] = *reinterpret_cast<const uint32_t*>(src + u * Cf::RPL * Cf::R);
+        r.v[u] = ld_kv4<NT>(src + u * Cf::RPL * Cf::R);
       } else {
-        const uint2 x = *reinterpret_cast<const uint2*>(src + u * Cf::RPL * Cf::R);
+        const uint2 x = ld_kv8<NT>(src + u * Cf::RPL * Cf::R);
         r.v[2 * u] = x.x; r.v[2 * u + 1] = x.y;
       }
     }
@@ -304,14 +338,14 @@ __device__ __forceinline__ void load_block(BlockRegs<Cf>& r, const char* kt, con
         const char* row = src + (size_t)(16 * t + rr) * Cf::R;
         uint32_t* dst = &r.v[(t * 4 + rr) * Cf::VWD];
         if constexpr (Cf::VWD == 1) {
-          dst[0] = *reinterpret_cast<const uint32_t*>(row);
+          dst[0] = ld_kv4<NT>(row);
         } else if constexpr (Cf::VWD == 2) {
-          const uint2 x = *reinterpret_cast<const uint2*>(row);
+          const uint2 x = ld_kv8<NT>(row);
           dst[0] = x.x; dst[1] = x.y;
         } else {
 #pragma unroll
           for (int h = 0; h < Cf::VWD / 4; ++h) {
-            const uint4 x = *reinterpret_cast<const uint4*>(row + 16 * h);
+            const uint4 x = ld_kv16<NT>(row + 16 * h);
             dst[4 * h + 0] = x.x; dst[4 * h + 1] = x.y; dst[4 * h + 2] = x.z; dst[4 * h + 3] = x.w;
           }
         }
@@ -2588,14 +2622,14 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
     for (int j = 0; j < PF - 1; ++j) {
       const int kk = min(j, cnt - 1);
       const size_t o = tile_of(kk);
-      load_block<Cf>(ring[j], kbase + o, vbase + o, lane, nvalid_of(kk));
+      load_block<Cf, true>(ring[j], kbase + o, vbase + o, lane, nvalid_of(kk));
     }
     for (int k = 0; k < cnt; k += PF) {
 #pragma unroll
       for (int j = 0; j < PF; ++j) {
         const int kk = min(k + j + PF - 1, cnt - 1);
         const size_t o = tile_of(kk);
-        load_block<Cf>(ring[(j + PF - 1) % PF], kbase + o, vbase + o, lane, nvalid_of(kk));
+        load_block<Cf, true>(ring[(j + PF - 1) % PF], kbase + o, vbase + o, lane, nvalid_of(kk));
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
         if (k + j < cnt) fold(ring[j], k + j);
       }
