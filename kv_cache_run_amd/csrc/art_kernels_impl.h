@@ -2203,6 +2203,7 @@ __global__ __launch_bounds__(64 * WNW) void art_win_scan_kernel(Params p) {
   static_assert(WMAXC <= 64, "one lane per chunk of the window");
   __shared__ __attribute__((aligned(16))) float xs[WMAXC * XS];
   __shared__ uint32_t pas[WMAXC];  // one workgroup per head: its pass words stay here
+  __shared__ float4 fsc[64];        // phase 2: per-chunk scalars of the chain
   __shared__ uint32_t arrived;
   const int bid = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -2306,12 +2307,20 @@ __global__ __launch_bounds__(64 * WNW) void art_win_scan_kernel(Params p) {
     const bool empty = mn == NEG_INF;
     const float fxv = empty ? 0.f : __builtin_amdgcn_exp2f(me - mn);
     const float fyv = empty ? 0.f : __builtin_amdgcn_exp2f(mk - mn);
+    // each step's scalars (scale factors, the chunk's sum, the running max
+    // entering it), one lane per chunk, into LDS: the chain reads them back
+    // as broadcasts, prefetched with the aggregates, instead of a cross-lane
+    // read per scalar and step (same values, so the same bits)
+    fsc[lane] = make_float4(fxv, fyv, lk, me);
     constexpr int PF = 4;  // entries read ahead of the chain
     float na[PF][DPL];
+    float4 nf[PF];
 #pragma unroll
-    for (int u = 0; u < PF; ++u)
+    for (int u = 0; u < PF; ++u) {
 #pragma unroll
       for (int j = 0; j < DPL; ++j) na[u][j] = xs[min(u, ncw - 1) * XS + DPL * lane + j];
+      nf[u] = fsc[min(u, ncw - 1)];
+    }
     for (int cb = 0; cb < ncw; cb += PF) {
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
@@ -2321,19 +2330,18 @@ __global__ __launch_bounds__(64 * WNW) void art_win_scan_kernel(Params p) {
           float a[DPL];
 #pragma unroll
           for (int j = 0; j < DPL; ++j) a[j] = na[u][j];
+          const float4 f = nf[u];  // fx, fy, l, running max entering the chunk
           if (ci + PF < ncw) {  // read before the chain overwrites that entry
 #pragma unroll
             for (int j = 0; j < DPL; ++j) na[u][j] = e[PF * XS + DPL * lane + j];
+            nf[u] = fsc[ci + PF];
           }
-          // cross-lane reads stay outside lane-divergent code
-          const float fx = readlanef(fxv, ci), fy = readlanef(fyv, ci);
-          const float l = readlanef(lk, ci), mc = readlanef(me, ci);
 #pragma unroll
           for (int j = 0; j < DPL; ++j) e[DPL * lane + j] = xw.A[j];
-          if (lane == 0) { e[D] = mc; e[D + 1] = xw.L; }
-          xw.L = fmaf(fx, xw.L, fy * l);
+          if (lane == 0) { e[D] = f.w; e[D + 1] = xw.L; }
+          xw.L = fmaf(f.x, xw.L, f.y * f.z);
 #pragma unroll
-          for (int j = 0; j < DPL; ++j) xw.A[j] = fmaf(fx, xw.A[j], fy * a[j]);
+          for (int j = 0; j < DPL; ++j) xw.A[j] = fmaf(f.x, xw.A[j], f.y * a[j]);
         }
       }
     }
