@@ -34,13 +34,19 @@ __device__ __forceinline__ float load_elem(const void* base, size_t idx, int dty
 
 // Eight consecutive elements of a row (16-byte aligned for bf16, 8 for fp8,
 // two 16-byte loads for f32) as floats.
+// Every key is read once: the loads are non-temporal (streamed past the caches).
+typedef unsigned int ou32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int ou32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void load8(const void* base, size_t idx, int dtype, float (&v)[8]) {
   if (dtype == KV_F32) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
-    const float4 a = p[0], c = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+    const ou32x4* p = reinterpret_cast<const ou32x4*>(static_cast<const float*>(base) + idx);
+    const ou32x4 a = __builtin_nontemporal_load(p), c = __builtin_nontemporal_load(p + 1);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z);
+    v[3] = __uint_as_float(a.w); v[4] = __uint_as_float(c.x); v[5] = __uint_as_float(c.y);
+    v[6] = __uint_as_float(c.z); v[7] = __uint_as_float(c.w);
   } else if (dtype == KV_BF16) {
-    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    const ou32x4 w =
+        __builtin_nontemporal_load(reinterpret_cast<const ou32x4*>(static_cast<const uint16_t*>(base) + idx));
     const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -48,7 +54,8 @@ __device__ __forceinline__ void load8(const void* base, size_t idx, int dtype, f
       v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
     }
   } else {
-    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + idx);
+    const ou32x2 w =
+        __builtin_nontemporal_load(reinterpret_cast<const ou32x2*>(static_cast<const uint8_t*>(base) + idx));
     const uint32_t u[2] = {w.x, w.y};
 #pragma unroll
     for (int i = 0; i < 2; ++i) {  // OCP E4M3FN; the byte selector must be a literal
