@@ -73,3 +73,31 @@ def test_summary_is_the_mean_of_valid_rows():
     pg = f8["block_table"][0, 1]
     want = oracle.decode_e4m3fn(f8["k_pages"][pg, 2]).mean(0) * f8["k_scale"][pg, 2]
     assert np.allclose(s8[pg, 2], want, rtol=1e-12)
+
+
+def test_score_is_max_over_heads_with_contiguous_groups():
+    """Hand-worked scores for two kv-heads of two query heads each (reading: max over the query heads,
+    kv-head h // g, scale 1/sqrt(D)).  Each alternative reading gives another order:
+
+    * mean or sum over the heads puts block 2 (every head scores 2) before block 1 (one head scores 3);
+    * kv-head h % g (interleaved groups) sends head 1 to kv-head 1, where block 3 scores 5 for it.
+    """
+    D = 2
+    q = np.array([[[1.0, 0.0], [0.0, 1.0], [-1.0, 0.0], [0.0, -1.0]]], np.float32)  # [1, Hq=4, D]
+    summ = np.zeros((4, 2, D))                                                        # [page, Hkv, D]
+    summ[1, 0] = [3.0, 0.0]                      # block 1: head 0 scores 3, the other heads 0
+    summ[2, 0] = [2.0, 2.0]                      # block 2: heads 0, 1 score 2 ...
+    summ[2, 1] = [-2.0, -2.0]                    # ... and heads 2, 3 score 2
+    summ[3, 1] = [0.0, 5.0]                      # block 3: head 2 scores 0, head 3 scores -5
+    table = np.array([[0, 1, 2, 3]], np.int32)   # logical block b on page b
+    lens = np.array([4], np.int32)
+    sc = oracle.block_scores(q, summ, table, lens, block_size=1, num_kv_heads=2, q_dtype="f32")
+    r2 = np.sqrt(2.0)
+    assert np.allclose(sc[0, 1:], [3.0 / r2, 2.0 / r2, 0.0], rtol=0, atol=1e-15)
+    o = oracle.importance_order(sc, lens, block_size=1)
+    assert list(o[0]) == [0, 1, 2, 3]
+    # the alternatives, written out by hand, would order the blocks otherwise
+    mean_scores = {1: 0.75, 2: 2.0, 3: -1.25}
+    assert sorted(mean_scores, key=lambda b: -mean_scores[b]) == [2, 1, 3]
+    interleaved = {1: 3.0, 2: 2.0, 3: 5.0}       # max over heads with kv-head h % g
+    assert sorted(interleaved, key=lambda b: -interleaved[b]) == [3, 1, 2]

@@ -72,7 +72,13 @@ def test_stop_monotone_in_thresholds_and_patience():
         if prev is not None:
             assert np.all(st >= prev)
         prev = st
-    assert len(np.unique(st)) > 1 or True
+    # the sweeps are not vacuous: some heads stop before their last block, and
+    # the thresholds move at least one stop
+    n = (case["seq_lens"] + case["block_size"] - 1) // case["block_size"]
+    loose = _run(case, 1e-1, 1e-3, 2)["stop"]
+    tight = _run(case, 1e-5, 1e-3, 2)["stop"]
+    assert np.any(loose < n[:, None])
+    assert np.any(loose < tight)
 
 
 def test_page_placement_never_matters():
@@ -92,9 +98,18 @@ def test_full_mode_is_visit_order_invariant():
     b, _ = _heavy_case(3, order=orders)
     ra, rb = _run(a, 0.0, 0.0, 1), _run(b, 0.0, 0.0, 1)
     assert np.allclose(ra["out"], rb["out"], rtol=1e-12, atol=1e-14)
-    # ART mode generally does depend on the order (it decides along it)
-    sa, sb = _run(a, 2e-2, 2e-3, 2), _run(b, 2e-2, 2e-3, 2)
-    assert sa["stop"].shape == sb["stop"].shape
+    # ART mode decides along the order, so its stops may move with it; under
+    # any order its output is full attention over exactly the blocks it folded
+    for case in (a, b):
+        r = _run(case, 2e-2, 2e-3, 2)
+        for s in range(2):
+            for h in range(4):
+                lens = np.zeros(2, np.int32)
+                lens[s] = r["stop"][s, h]
+                want = oracle.full_attention(case["q"], case["k_pages"], case["v_pages"], case["block_table"],
+                                             case["seq_lens"], block_order=case["block_order"], visit_lens=lens,
+                                             pairs=[(s, h)], **okw(case))
+                assert np.allclose(r["out"][s, h], want[s, h], rtol=1e-12, atol=1e-14)
 
 
 def test_value_scaling_and_orthogonal_map_keep_stops():
