@@ -1,8 +1,10 @@
 """Benchmark: ART paged decode attention on one MI355X.
 
 One step = one ``art_decode`` call over the whole batch (one decode step of
-one attention layer) on the Llama-3-8B-shaped workload (batch 8, 32 q heads /
-8 kv heads, D=128, bf16 K/V, context 8192, KV block 16).  Prints one JSON line.
+one attention layer).  The headline is the ragged long-batch decode (batch 32,
+32 q heads / 8 kv heads, D=128, bf16 K/V, context U(4096, 32768) per
+sequence, KV block 16): the largest of the workloads, 2.27 GB of KV.  Prints
+one JSON line.
 
 Timing: inputs are resident in HBM before the timed region.  To keep the
 256 MB MALL and the L2s cold without a flush kernel inside the timed region,
@@ -10,11 +12,14 @@ the page pool holds R copies of the cache and consecutive calls use block
 tables that point into different copies (R chosen so that R-1 calls read more
 than 512 MB).  The K timed calls are captured into one HIP graph (so host
 launch overhead cannot gap the few-µs kernels) and replayed back to back on
-the current stream between two HIP events; µs/step = elapsed / K.
+the current stream between two HIP events; µs/step = elapsed / K.  The same K
+calls launched eagerly from Python (ctypes, no graph) are timed as well.
 
 Also reported: full-attention mode, the fraction of KV blocks the kernel read
-(its own counter), the oracle's floor for that fraction, achieved bandwidth on
-algorithmic and on actually-read bytes, and the CPU oracle timed on the host.
+(its own counter), the floor for that fraction from the kernel's own stops,
+achieved bandwidth on algorithmic and on actually-read bytes, every other
+workload in both modes, threshold sweeps (step time against the KV fraction
+read), and the CPU oracle timed on the host.
 """
 
 from __future__ import annotations
@@ -68,11 +73,18 @@ def algorithmic_bytes(case: dict, stop: np.ndarray) -> dict:
     return {"total": kv + meta + q + outb, "kv": kv, "blocks": int(F.sum()), "tile": tile}
 
 
+_CPU_CASE = None  # the case the oracle workers read (inherited through fork, never pickled)
+
+
 def _oracle_worker(args):
-    (case, pairs, mode) = args
+    """Run the oracle on one stream (sequence, kv-head): all its query heads; returns the wall seconds."""
+    (s, kvh, mode) = args
+    case = _CPU_CASE
     import oracle
     from kv_cache_run_amd import synth
 
+    g = case["num_q_heads"] // case["num_kv_heads"]
+    pairs = [(s, kvh * g + j) for j in range(g)]
     t = time.perf_counter()
     if mode == "art":
         oracle.art_reference(*synth.oracle_arrays(case), eps_mag=case["eps_mag"], eps_dir=case["eps_dir"],
@@ -83,30 +95,27 @@ def _oracle_worker(args):
     return time.perf_counter() - t
 
 
-def cpu_baseline(case: dict, mode: str, max_seconds: float = 12.0) -> dict:
-    """Time the float64 oracle as it stands on the host cores, on whole sequences.
+def cpu_baseline(case: dict, max_seconds: float = 10.0) -> dict:
+    """Time the float64 oracle as it stands on the host, in ART and in full-attention mode.
 
-    Sequences are handed to one worker process per core (single-threaded
-    BLAS each).  A bounded prefix of the batch is timed and scaled to one step.
+    Work items are streams (sequence, kv-head) with all their query heads: the oracle decodes a stream's
+    blocks once for its heads.  Per mode, a seeded random order of the streams is run (a) on one core, item
+    by item until the batch is done or ``max_seconds`` have passed, and (b) on a pool of one single-threaded
+    worker process per core, at most 16 (the host share of one GPU on the box), over as many items as the
+    one-core rate says fit in ``max_seconds`` of wall time.  A partial sample is scaled to the whole batch
+    by the fraction of streams it covered.  Must run before the GPU is initialised (the pool forks).
     """
     import multiprocessing as mp
 
-    os.environ["OMP_NUM_THREADS"] = "1"
-    os.environ["OPENBLAS_NUM_THREADS"] = "1"
-    os.environ["MKL_NUM_THREADS"] = "1"
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
-    hq = case["num_q_heads"]
-    # probe one sequence on one core to size the sample
-    t1 = _oracle_worker((case, [(0, h) for h in range(hq)], mode))
-    per_seq = max(t1, 1e-6)
-    nseq = int(min(case["batch"], max(1, math.floor(max_seconds * cores / per_seq))))
-    ctx = mp.get_context("fork")
-    jobs = [(case, [(s, h) for h in range(hq)], mode) for s in range(nseq)]
-    t = time.perf_counter()
-    with ctx.Pool(min(cores, nseq)) as pool:
-        pool.map(_oracle_worker, jobs)
-    wall = time.perf_counter() - t
-    us_step = wall * 1e6 * case["batch"] / nseq
+    global _CPU_CASE
+    _CPU_CASE = case
+    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[k] = "1"
+    host_cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, host_cores))
+    items = [(s, k) for s in range(case["batch"]) for k in range(case["num_kv_heads"])]
+    rng = np.random.default_rng(0)
+    items = [items[i] for i in rng.permutation(len(items))]
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -116,10 +125,30 @@ def cpu_baseline(case: dict, mode: str, max_seconds: float = 12.0) -> dict:
                     break
     except OSError:
         pass
-    return {"value": us_step, "unit": "us/step", "cores": min(cores, nseq), "kind": "oracle",
-            "sample": f"{mode} mode, {nseq} of {case['batch']} sequences (all {hq} heads each), "
-                      f"scaled to the whole batch; float64 NumPy oracle; host CPU: {model}",
-            "wall_s": wall}
+    res = {"host_cores": host_cores, "cpu_model": model}
+    ctx = mp.get_context("fork")
+    for mode in ("art", "full"):
+        t0 = time.perf_counter()
+        done1 = 0
+        for s, k in items:
+            _oracle_worker((s, k, mode))
+            done1 += 1
+            if time.perf_counter() - t0 > max_seconds:
+                break
+        wall1 = time.perf_counter() - t0
+        us1 = wall1 * 1e6 * len(items) / done1
+        per_item = wall1 / done1
+        nwant = int(min(len(items), max(workers, math.floor(max_seconds * workers / max(per_item, 1e-9)))))
+        jobs = [(s, k, mode) for s, k in items[:nwant]]
+        t0 = time.perf_counter()
+        with ctx.Pool(workers) as pool:
+            pool.map(_oracle_worker, jobs, chunksize=1)
+        walln = time.perf_counter() - t0
+        res[mode] = {"us_per_step": walln * 1e6 * len(items) / nwant, "cores": workers,
+                     "streams_timed": nwant, "wall_s": walln,
+                     "one_core_us_per_step": us1, "one_core_streams_timed": done1, "one_core_wall_s": wall1}
+    res["streams"] = len(items)
+    return res
 
 
 def read_traffic(kernel: str, workload: str) -> dict | None:
@@ -208,12 +237,21 @@ def time_setting(case, dev, em, ed, patience, flags, steps, warmup, outputs=Fals
     ms = ev0.elapsed_time(ev1) / steps
     assert np.array_equal(stop.cpu().numpy(), stop_h), "stops changed across page copies / replays"
     assert torch.equal(out, out_first), "graph replays disagree"
+    # the same calls launched eagerly from Python (ctypes per call, no graph)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(steps):
+        one_call(tables[(warmup + i) % R], dec, kp, vp, ks, vs)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_eager = ev0.elapsed_time(ev1) / steps
     del graph, kp, vp, ks, vs, tables, dec
     torch.cuda.empty_cache()
     alg = algorithmic_bytes(case, stop_h)
     us = ms * 1e3
     res = {
         "us_per_step": us,
+        "us_per_step_eager": ms_eager * 1e3,
         "wall_s": wall,
         "page_copies": R,
         "alg_bytes": alg["total"],
@@ -371,18 +409,52 @@ def ablation(steps: int, warmup: int) -> dict:
     return res
 
 
+def sweep(case, dev, res_art, steps) -> dict:
+    """Step time against the KV fraction read: thresholds scaled by 1/4 .. 4 at fixed patience, with a
+    least-squares line through the points."""
+    em0, ed0, p0 = case["eps_mag"], case["eps_dir"], case["patience"]
+    pts = []
+    for f in (0.25, 0.5, 1.0, 2.0, 4.0):
+        r = res_art if f == 1.0 else time_setting(case, dev, em0 * f, ed0 * f, p0, 0, steps, 2)
+        pts.append({"eps_scale": f, "kv_fraction_read": round(r["kv_fraction_read"], 5),
+                    "kv_fraction_needed": round(r["kv_fraction_needed"], 5), "us_per_step": round(r["us_per_step"], 3)})
+    x = np.array([q["kv_fraction_read"] for q in pts])
+    y = np.array([q["us_per_step"] for q in pts])
+    slope, icpt = np.polyfit(x, y, 1) if np.ptp(x) > 0 else (0.0, float(y.mean()))
+    pred = slope * x + icpt
+    ss = float(((y - y.mean()) ** 2).sum())
+    r2 = 1.0 - float(((y - pred) ** 2).sum()) / ss if ss > 0 else 1.0
+    return {"points": pts, "slope_us_per_unit_fraction": round(float(slope), 3), "intercept_us": round(float(icpt), 3),
+            "r2": round(r2, 4)}
+
+
+def summary_row(r: dict) -> dict:
+    keys = ("us_per_step", "us_per_step_eager", "alg_bytes", "read_bytes", "achieved_GBps", "read_GBps",
+            "kv_fraction_read", "kv_fraction_needed")
+    row = {k: (round(r[k], 5) if isinstance(r[k], float) else r[k]) for k in keys}
+    row["alg_frac_of_peak"] = round(r["achieved_GBps"] / PEAK_GBPS, 4)
+    row["read_frac_of_peak"] = round(r["read_GBps"] / PEAK_GBPS, 4)
+    return row
+
+
+def kernel_name(art_mod, dev, case) -> str:
+    desc = art_mod.make_desc(dev["q"], dev["k_pages"], dev["block_table"])
+    return art_mod.KERNEL_NAMES[art_mod.art_decode_kernel_choice(desc, case["eps_mag"], case["eps_dir"],
+                                                                 case["patience"])]
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=None, help="workload name (default: the Llama-3-8B-shaped decode)")
+    ap.add_argument("--workload", default=None, help="workload name (default: the ragged long-batch decode)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration under rocprofv3)")
     ap.add_argument("--modes", default="art,full")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the threshold sweep and the detector-overhead run")
+                    help="skip the other workloads, the threshold sweeps and the detector-overhead run")
     ap.add_argument("--pruned", action="store_true",
                     help="also run ART over a pruned cache (block 0 plus the newest quarter / sixteenth of the "
                          "blocks, through art_decode_visits) against full attention over the same blocks")
@@ -403,19 +475,27 @@ def main(argv=None) -> int:
               file=sys.stderr)
         return 2
 
+    from kv_cache_run_amd import synth, workloads
+
+    w = workloads.BY_NAME[args.workload] if args.workload else workloads.RAGGED
+    case = synth.make_case(w)
+    # the CPU oracle first: its worker pool forks, which must happen before the GPU is initialised
+    cpu = None
+    if not args.no_cpu and "art" in args.modes.split(","):
+        cpu = cpu_baseline(case)
+
     import torch
 
-    from kv_cache_run_amd import art, synth, workloads
+    from kv_cache_run_amd import art
 
     if not os.path.exists(art.LIB_PATH):
         from kv_cache_run_amd import build as _b
 
         _b.build()
-    w = workloads.BY_NAME[args.workload] if args.workload else workloads.LLAMA3_8B
     torch.cuda.set_device(0)
-    case = synth.make_case(w)
     dev = art.case_to_device(case)
     B = case["block_size"]
+    steps_x = max(5, args.steps // 2)
 
     em0, ed0, p0 = case["eps_mag"], case["eps_dir"], case["patience"]
     results = {}
@@ -426,13 +506,16 @@ def main(argv=None) -> int:
             results[mode] = time_setting(case, dev, 0.0, 0.0, p0, art.ART_FLAG_FULL, args.steps, args.warmup)
         else:
             raise SystemExit(f"unknown mode {mode}")
+    head_mode = "art" if "art" in results else next(iter(results))
+    kname = kernel_name(art, dev, case) if head_mode == "art" else "full_split_kernel"
 
     extras = {}
     if not args.no_extras and "art" in results and "full" in results:
         # detector overhead: the terminating kernel with thresholds that can never pass (it folds every
-        # block and runs every test) against the full-attention kernel on the same work
-        keep = time_setting(case, dev, 0.0, 0.0, p0, art.ART_FLAG_KEEP_DETECTOR, max(5, args.steps // 2), 2)
-        nostats = time_setting(case, dev, 0.0, 0.0, p0, art.ART_FLAG_SKIP_STATS, max(5, args.steps // 2), 2)
+        # block and runs every test) against the same kernel without the statistics, and against the
+        # full-attention kernel on the same work
+        keep = time_setting(case, dev, 0.0, 0.0, p0, art.ART_FLAG_KEEP_DETECTOR, steps_x, 2)
+        nostats = time_setting(case, dev, 0.0, 0.0, p0, art.ART_FLAG_SKIP_STATS, steps_x, 2)
         extras["detector_overhead"] = {
             "art_kernel_all_blocks_us": round(keep["us_per_step"], 3),
             "art_kernel_all_blocks_without_statistics_us": round(nostats["us_per_step"], 3),
@@ -440,32 +523,40 @@ def main(argv=None) -> int:
             "full_kernel_us": round(results["full"]["us_per_step"], 3),
             "ratio_to_full": round(keep["us_per_step"] / results["full"]["us_per_step"], 4),
             "note": "the terminating kernel folding every block with and without computing the statistics "
-                    "(detector_cost_fraction), and against the split full-attention path (ratio_to_full: mostly "
-                    "the per-stream sequential decomposition)",
+                    "(detector_cost_fraction), and against the split full-attention path (ratio_to_full)",
         }
-        # step time against the KV fraction read: thresholds scaled by 1/4 .. 4 at fixed patience
-        pts = []
-        for f in (0.25, 0.5, 1.0, 2.0, 4.0):
-            r = results["art"] if f == 1.0 else time_setting(case, dev, em0 * f, ed0 * f, p0, 0, max(5, args.steps // 2), 2)
-            pts.append({"eps_scale": f, "kv_fraction_read": round(r["kv_fraction_read"], 5),
-                        "kv_fraction_needed": round(r["kv_fraction_needed"], 5), "us_per_step": round(r["us_per_step"], 3)})
-        x = np.array([q["kv_fraction_read"] for q in pts])
-        y = np.array([q["us_per_step"] for q in pts])
-        slope, icpt = np.polyfit(x, y, 1) if np.ptp(x) > 0 else (0.0, float(y.mean()))
-        pred = slope * x + icpt
-        ss = float(((y - y.mean()) ** 2).sum())
-        r2 = 1.0 - float(((y - pred) ** 2).sum()) / ss if ss > 0 else 1.0
-        extras["threshold_sweep"] = {"points": pts, "slope_us_per_unit_fraction": round(float(slope), 3),
-                             "intercept_us": round(float(icpt), 3), "r2": round(r2, 4)}
+        extras["threshold_sweep"] = {w.name: sweep(case, dev, results["art"], steps_x)}
+        # every other workload, both modes; sweeps on the Llama-3-8B and 128k shapes too
+        per = {w.name: {"kernel": kname, "art": summary_row(results["art"]), "full": summary_row(results["full"])}}
+        del dev
+        torch.cuda.empty_cache()
+        for w2 in workloads.ALL:
+            if w2.name == w.name:
+                continue
+            c2 = synth.make_case(w2)
+            d2 = art.case_to_device(c2)
+            ra = time_setting(c2, d2, c2["eps_mag"], c2["eps_dir"], c2["patience"], 0, steps_x, 2)
+            rf = time_setting(c2, d2, 0.0, 0.0, c2["patience"], art.ART_FLAG_FULL, steps_x, 2)
+            per[w2.name] = {"kernel": kernel_name(art, d2, c2), "art": summary_row(ra), "full": summary_row(rf),
+                            "art_over_full": round(ra["us_per_step"] / rf["us_per_step"], 4)}
+            if w2 in (workloads.LLAMA3_8B, workloads.LONG):
+                extras["threshold_sweep"][w2.name] = sweep(c2, d2, ra, steps_x)
+            del c2, d2
+            torch.cuda.empty_cache()
+        per[w.name]["art_over_full"] = round(results["art"]["us_per_step"] / results["full"]["us_per_step"], 4)
+        extras["workloads"] = per
+        dev = None
 
+    if args.ablation or args.pruned or args.probe:
+        dev = dev or art.case_to_device(case)
     if args.ablation:
-        extras["ablation"] = ablation(max(5, args.steps // 2), 2)
+        extras["ablation"] = ablation(steps_x, 2)
     if args.pruned:
-        extras["pruned"] = pruned(case, dev, max(5, args.steps // 2), 2)
+        extras["pruned"] = pruned(case, dev, steps_x, 2)
     if args.probe:
-        extras["probe"] = probe(case, dev, max(5, args.steps // 2), 2)
+        extras["probe"] = probe(case, dev, steps_x, 2)
     if args.importance:
-        extras["importance"] = importance(max(5, args.steps // 2), 2)
+        extras["importance"] = importance(steps_x, 2)
 
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
@@ -474,17 +565,7 @@ def main(argv=None) -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    cpu = None
-    if not args.no_cpu and "art" in results:
-        cpu = cpu_baseline(case, "art")
-
-    head = results.get("art") or next(iter(results.values()))
-    head_mode = "art" if "art" in results else next(iter(results))
-    if head_mode == "art":
-        desc = art.make_desc(dev["q"], dev["k_pages"], dev["block_table"])
-        kname = art.KERNEL_NAMES[art.art_decode_kernel_choice(desc, case["eps_mag"], case["eps_dir"], case["patience"])]
-    else:
-        kname = "full_split_kernel"
+    head = results[head_mode]
     traffic = read_traffic(kname, w.name)
     roofline = {
         "bound": "hbm",
@@ -495,7 +576,24 @@ def main(argv=None) -> int:
         "frac": round(head["achieved_GBps"] / PEAK_GBPS, 4),
         "traffic": None if traffic is None else traffic["bytes_per_launch"],
         "alg_bytes_per_launch": head["alg_bytes"],
+        "read_GBps": round(head["read_GBps"], 1),
+        "read_frac": round(head["read_GBps"] / PEAK_GBPS, 4),
     }
+    cpu_line = None
+    if cpu is not None:
+        cpu_line = {"value": round(cpu["art"]["us_per_step"], 1), "unit": "us/step", "cores": cpu["art"]["cores"],
+                    "kind": "oracle",
+                    "sample": f"float64 NumPy oracle, ART mode, {cpu['art']['streams_timed']} of {cpu['streams']} "
+                              f"streams (sequence, kv-head) with all their query heads on a pool of "
+                              f"{cpu['art']['cores']} single-threaded processes (host: {cpu['host_cores']} cores, "
+                              f"{cpu['cpu_model']}; at most 16 workers, the host share of one GPU), scaled to the "
+                              f"whole batch",
+                    "full_mode_us_per_step": round(cpu["full"]["us_per_step"], 1),
+                    "one_core": {"art_us_per_step": round(cpu["art"]["one_core_us_per_step"], 1),
+                                 "full_us_per_step": round(cpu["full"]["one_core_us_per_step"], 1),
+                                 "art_streams_timed": cpu["art"]["one_core_streams_timed"],
+                                 "full_streams_timed": cpu["full"]["one_core_streams_timed"]},
+                    "detail": cpu}
     line = {
         "metric": METRIC,
         "value": round(head["us_per_step"], 3),
@@ -511,8 +609,9 @@ def main(argv=None) -> int:
         "data": "synthetic (seeded Gaussian q/K/V with planted heavy keys; no dataset or weights)",
         "config": {"workload": w.name, "mode": head_mode, "batch": case["batch"], "q_heads": case["num_q_heads"],
                    "kv_heads": case["num_kv_heads"], "head_dim": case["head_dim"],
-                   "context": int(case["seq_lens"].max()), "block_size": B, "eps_mag": case["eps_mag"],
-                   "eps_dir": case["eps_dir"], "patience": case["patience"]},
+                   "context": [int(case["seq_lens"].min()), int(case["seq_lens"].max())], "block_size": B,
+                   "kv_bytes": int(case["k_pages"].nbytes + case["v_pages"].nbytes),
+                   "eps_mag": case["eps_mag"], "eps_dir": case["eps_dir"], "patience": case["patience"]},
         "achieved_GBps": round(head["achieved_GBps"], 1),
         "hbm_frac": round(head["achieved_GBps"] / PEAK_GBPS, 4),
         "read_GBps": round(head["read_GBps"], 1),
@@ -521,7 +620,7 @@ def main(argv=None) -> int:
         "modes": {m: {k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}
                   for m, r in results.items()},
         "roofline": roofline,
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu_line,
         "kernel_source_hash": kernel_source_hash(),
     }
     line.update(extras)

@@ -272,16 +272,26 @@ const char* art_status_string(art_status status);
 int32_t art_decode_version(void);
 
 /* Which kernel art_decode would run for these arguments (host only; the
- * environment knob ART_SCHED and the current device's CU count are read as
- * art_decode reads them):
+ * environment knob ART_SCHED and the current device's CU count are taken as
+ * art_decode takes them):
  *   ART_KERNEL_FULL      full attention (ART_FLAG_FULL, or a zero threshold
  *                        without ART_FLAG_KEEP_DETECTOR),
- *   ART_KERNEL_SCANNERS  one scanner workgroup per stream,
+ *   ART_KERNEL_SCANNERS  one scanner workgroup per stream, lock-step chunks,
  *   ART_KERNEL_LOOKBACK  the look-back scheduler,
  *   ART_KERNEL_WINDOWED  the windowed scheduler,
+ *   ART_KERNEL_STREAM    the stream kernel (one workgroup per stream,
+ *                        producer and detector waves sharing an LDS ring),
  * or minus the art_status art_decode would return for rejected arguments. */
-enum { ART_KERNEL_FULL = 0, ART_KERNEL_SCANNERS = 1, ART_KERNEL_LOOKBACK = 2, ART_KERNEL_WINDOWED = 3 };
+enum { ART_KERNEL_FULL = 0, ART_KERNEL_SCANNERS = 1, ART_KERNEL_LOOKBACK = 2, ART_KERNEL_WINDOWED = 3,
+       ART_KERNEL_STREAM = 4 };
 int32_t art_decode_kernel_choice(const art_decode_desc* desc, float eps_mag, float eps_dir, int32_t patience);
+
+/* Re-read the tuning environment variables (ART_SCHED and the scheduler
+ * knobs listed with art_decode).  The library reads them once, at the first
+ * call that needs them; a process that changes them afterwards calls this
+ * for the change to take effect.  Host only; not thread-safe against
+ * concurrent art_decode calls. */
+void art_decode_reload_environment(void);
 
 #ifdef __cplusplus
 }

@@ -30,15 +30,17 @@ def art_flag_probe(p: int) -> int:
 
 EXPORTED = ("art_decode_workspace_bytes", "art_decode_workspace_init", "art_decode", "art_decode_visits",
             "art_status_string", "art_decode_version", "art_decode_kernel_choice", "art_block_key_summary",
-            "art_importance_order_workspace_bytes", "art_importance_order", "art_check_inputs")
-ART_KERNEL_FULL, ART_KERNEL_SCANNERS, ART_KERNEL_LOOKBACK, ART_KERNEL_WINDOWED = 0, 1, 2, 3
+            "art_importance_order_workspace_bytes", "art_importance_order", "art_check_inputs",
+            "art_decode_reload_environment")
+ART_KERNEL_FULL, ART_KERNEL_SCANNERS, ART_KERNEL_LOOKBACK, ART_KERNEL_WINDOWED, ART_KERNEL_STREAM = 0, 1, 2, 3, 4
 ART_CHECK_OK, ART_CHECK_SEQ_LEN, ART_CHECK_ORDER_RANGE, ART_CHECK_ORDER_REPEAT, ART_CHECK_PAGE_RANGE = 0, 1, 2, 3, 4
 CHECK_NAMES = {ART_CHECK_SEQ_LEN: "sequence length outside [0, max_blocks * block_size]",
                ART_CHECK_ORDER_RANGE: "order entry outside [0, n_s)",
                ART_CHECK_ORDER_REPEAT: "order entry repeated among the visited positions",
                ART_CHECK_PAGE_RANGE: "page outside [0, num_pages)"}
 KERNEL_NAMES = {ART_KERNEL_FULL: "full_split_kernel", ART_KERNEL_SCANNERS: "art_sched_kernel",
-                ART_KERNEL_LOOKBACK: "art_lb_kernel", ART_KERNEL_WINDOWED: "art_win_part_kernel"}
+                ART_KERNEL_LOOKBACK: "art_lb_kernel", ART_KERNEL_WINDOWED: "art_win_part_kernel",
+                ART_KERNEL_STREAM: "art_stream_kernel"}
 
 
 class ArtDecodeDesc(ctypes.Structure):
@@ -100,6 +102,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.art_decode_version.restype = i32
     lib.art_decode_kernel_choice.argtypes = [ctypes.POINTER(ArtDecodeDesc), f32, f32, i32]
     lib.art_decode_kernel_choice.restype = i32
+    lib.art_decode_reload_environment.argtypes = []
+    lib.art_decode_reload_environment.restype = None
     if path is None:
         _lib = lib
     return lib
@@ -111,6 +115,11 @@ def art_status_string(status: int) -> str:
 
 def art_decode_version() -> int:
     return int(load_library().art_decode_version())
+
+
+def reload_environment() -> None:
+    """Make the library re-read its tuning environment variables (it reads them once otherwise)."""
+    load_library().art_decode_reload_environment()
 
 
 def art_decode_kernel_choice(desc: ArtDecodeDesc, eps_mag: float, eps_dir: float, patience: int) -> int:

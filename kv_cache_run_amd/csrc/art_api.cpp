@@ -10,13 +10,12 @@
 
 namespace art {
 
-SplitPlan full_split_plan(int batch, int hkv, int max_blocks) {
+SplitPlan full_split_plan(int batch, int hkv, int max_blocks, int target) {
   const long streams = (long)batch * hkv;
   // about two workgroups per CU on 256 CUs (measured against 256 … 3072:
   // fewer, longer slices avoid a tail of partly filled CUs and shrink the
   // merge); ART_FULL_WGS overrides
-  const char* tw = getenv("ART_FULL_WGS");
-  const long target_wgs = tw && atol(tw) > 0 ? atol(tw) : 512;
+  const long target_wgs = target;
   long splits = streams > 0 ? (target_wgs + streams - 1) / streams : 1;
   const long by_len = (max_blocks + 7) / 8;  // at least 8 blocks (2 per wave) per split
   if (splits > by_len) splits = by_len;
@@ -63,23 +62,30 @@ art_status check_desc(const art_decode_desc* d) {
   return ART_OK;
 }
 
-// Scheduler tuning knobs, read from the environment at every call (defaults
-// when unset).  ART_SCHED selects the terminating kernel: "scan" (one scanner
-// workgroup per stream, optional helpers), "lb" (the look-back scheduler),
+// Scheduler tuning knobs, read from the environment once (at the first call
+// that needs them, and again whenever art_decode_reload_environment is
+// called; defaults when unset).  ART_SCHED selects the terminating kernel:
+// "stream" (one workgroup per stream: producer waves and detector waves
+// sharing an LDS ring), "scan" (one scanner workgroup per stream that folds
+// chunks in lock step, optional helpers), "lb" (the look-back scheduler),
 // "win" (the windowed scheduler) or "auto" (default): windows when the
 // streams are few (at most half the CUs) and long (at least 256 chunks),
-// where scanners would leave most CUs idle for a long walk; the look-back
-// scheduler for groups of more than 4 query heads (a scanner has 4 scan
-// waves); scanners otherwise.  Windowed: ART_WIN_SPLIT fold workgroups per
-// (stream, head) (1 .. 4; 0, the default: 2 when there are few heads, else
-// 1), ART_WIN_FIRST chunks in the first
+// where one workgroup per stream would leave most CUs idle for a long walk;
+// the stream kernel for groups of up to 4 query heads (one detector wave per
+// head); the look-back scheduler for larger groups with long streams (at
+// least 32 chunks); the stream kernel for groups of 5 to 8 heads otherwise,
+// scanners for larger groups.
+// Stream kernel: ART_LA0 and ART_LA_SHIFT set its lookahead, la0 +
+// (frontier >> la_shift) blocks (defaults 16 and 1).  Windowed:
+// ART_WIN_SPLIT fold workgroups per (stream, head) (1 .. 4; 0, the default:
+// 2 when there are few heads, else 1), ART_WIN_FIRST chunks in the first
 // window (0, the default: 1/8 of the longest stream's chunks, 2 .. 64) and
 // ART_WIN_GROWTH the factor from one window to the next (default 2, windows
-// at most 64 chunks); results depend on none of them.
-// Look-back: ART_WINDOW chunks claimable past a stream's resolved frontier
-// (0: 1/16 of the longest stream's chunks, clamped to 8 .. 32), ART_WORKERS
-// workgroups (0: one per resident slot); results do not depend on either.  Scanners: ART_RING
-// slots per stream, ART_LOOKAHEAD initial helper window, ART_HELPERS helper
+// at most 64 chunks); results depend on none of them.  Look-back: ART_WINDOW
+// chunks claimable past a stream's resolved frontier (0: 1/16 of the longest
+// stream's chunks, clamped to 8 .. 32), ART_WORKERS workgroups (0: one per
+// resident slot); results do not depend on either.  Scanners: ART_RING slots
+// per stream, ART_LOOKAHEAD initial helper window, ART_HELPERS helper
 // workgroups (default 0; -1: enough to reach ART_TARGET_WGS workgroups in
 // total).  ART_SPIN_LIMIT bounds every wait loop.  The workspace size depends
 // on ART_RING only.
@@ -90,19 +96,46 @@ int env_int(const char* name, int def, int lo, int hi) {
 }
 struct Knobs {
   int ring, lookahead, helpers, target, lb, window, workers, win_split, win_first, win_growth;
+  int la0, la_shift, spin_limit, full_wgs;
 };
-enum { SCHED_SCAN = 0, SCHED_LB = 1, SCHED_AUTO = 2, SCHED_WIN = 3 };
-Knobs knobs() {
+enum { SCHED_SCAN = 0, SCHED_LB = 1, SCHED_AUTO = 2, SCHED_WIN = 3, SCHED_STREAM = 4 };
+Knobs read_knobs() {
   const char* sched = getenv("ART_SCHED");
-  const int mode = !sched || strcmp(sched, "auto") == 0
-                       ? SCHED_AUTO
-                       : (strcmp(sched, "lb") == 0 ? SCHED_LB : (strcmp(sched, "win") == 0 ? SCHED_WIN : SCHED_SCAN));
+  int mode = SCHED_SCAN;
+  if (!sched || strcmp(sched, "auto") == 0) mode = SCHED_AUTO;
+  else if (strcmp(sched, "lb") == 0) mode = SCHED_LB;
+  else if (strcmp(sched, "win") == 0) mode = SCHED_WIN;
+  else if (strcmp(sched, "stream") == 0) mode = SCHED_STREAM;
   const Knobs k = {env_int("ART_RING", 8, 1, 64),          env_int("ART_LOOKAHEAD", 3, 1, 64),
                    env_int("ART_HELPERS", 0, -1, 1 << 16), env_int("ART_TARGET_WGS", 512, 1, 1 << 16),
                    mode,                                    env_int("ART_WINDOW", 0, 0, 32),
                    env_int("ART_WORKERS", 0, 0, 1 << 20),       env_int("ART_WIN_SPLIT", 0, 0, art::art_win_split),
-                   env_int("ART_WIN_FIRST", 0, 0, 64),          env_int("ART_WIN_GROWTH", 2, 2, 8)};
+                   env_int("ART_WIN_FIRST", 0, 0, 64),          env_int("ART_WIN_GROWTH", 2, 2, 8),
+                   env_int("ART_LA0", 16, 1, 1 << 20),          env_int("ART_LA_SHIFT", 1, 0, 30),
+                   env_int("ART_SPIN_LIMIT", 1 << 20, 64, 1 << 30), env_int("ART_FULL_WGS", 512, 1, 1 << 20)};
   return k;
+}
+// The knobs in effect; guarded by a flag so that the environment is read once.
+Knobs g_knobs;
+bool g_knobs_read = false;
+const Knobs& knobs() {
+  if (!g_knobs_read) {
+    g_knobs = read_knobs();
+    g_knobs_read = true;
+  }
+  return g_knobs;
+}
+// CUs of a device, queried once per device.
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
 }
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
@@ -111,7 +144,7 @@ art::WorkspacePlan plan_workspace(const art_decode_desc* d) {
   art::WorkspacePlan w;
   memset(&w, 0, sizeof(w));
   if (d->batch == 0) return w;
-  const Knobs k = knobs();
+  const Knobs& k = knobs();
   const int g = d->num_q_heads / d->num_kv_heads;
   const int gm = art::group_capacity(g);
   const size_t streams = (size_t)d->batch * d->num_kv_heads;
@@ -173,7 +206,7 @@ art::WorkspacePlan plan_workspace(const art_decode_desc* d) {
   w.data = off;
   const size_t ring_bytes = streams * (size_t)w.ring * w.slot_floats * sizeof(float);
   const size_t rec_bytes = streams * (size_t)max_chunks * g * w.rec_floats * sizeof(float);
-  const art::SplitPlan sp = art::full_split_plan(d->batch, d->num_kv_heads, d->max_blocks_per_seq);
+  const art::SplitPlan sp = art::full_split_plan(d->batch, d->num_kv_heads, d->max_blocks_per_seq, knobs().full_wgs);
   const size_t part = sp.splits > 1 ? streams * sp.splits * gm * (size_t)(d->head_dim + 2) * sizeof(float) : 0;
   size_t data = ring_bytes > part ? ring_bytes : part;
   if (rec_bytes > data) data = rec_bytes;
@@ -188,23 +221,28 @@ art::WorkspacePlan plan_workspace(const art_decode_desc* d) {
 // counts up to 2047 and its claim sweep packs a stream index in 16 bits; the
 // windowed path carries the pass count as a float (exact to 2^24).  Either
 // falls back to the scanners outside those limits.
-enum Sched { SCHED_RUN_SCAN = 0, SCHED_RUN_LB = 1, SCHED_RUN_WIN = 2 };
+enum Sched { SCHED_RUN_SCAN = 0, SCHED_RUN_LB = 1, SCHED_RUN_WIN = 2, SCHED_RUN_STREAM = 3 };
 Sched terminating_kernel(const art_decode_desc* d, const art::WorkspacePlan& wp, int32_t patience) {
-  const Knobs k = knobs();
+  const Knobs& k = knobs();
   const long streams = (long)d->batch * d->num_kv_heads;
   const int g = d->num_q_heads / d->num_kv_heads;
-  int want = k.lb == SCHED_LB ? SCHED_RUN_LB : (k.lb == SCHED_WIN ? SCHED_RUN_WIN : SCHED_RUN_SCAN);
+  int want = k.lb == SCHED_LB ? SCHED_RUN_LB
+             : k.lb == SCHED_WIN ? SCHED_RUN_WIN
+             : k.lb == SCHED_STREAM ? SCHED_RUN_STREAM
+                                    : SCHED_RUN_SCAN;
   if (k.lb == SCHED_AUTO) {
-    // few, long streams: windows; large groups (more heads than a scanner
-    // has scan waves): look-back; else scanners
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      cus = 256;
-    if (2 * streams <= cus && wp.max_chunks >= 256)
+    // few, long streams: windows; groups of up to 8 heads: the stream
+    // kernel; larger groups: look-back for long streams, else scanners
+    if (2 * streams <= cu_count() && wp.max_chunks >= 256)
       want = SCHED_RUN_WIN;
-    else if (g > 4 && wp.max_chunks >= 32)
+    else if (g <= 4)
+      want = SCHED_RUN_STREAM;
+    else if (wp.max_chunks >= 32)
       want = SCHED_RUN_LB;
+    else if (g <= 8)
+      want = SCHED_RUN_STREAM;
   }
+  if (want == SCHED_RUN_STREAM && g > 8) want = SCHED_RUN_SCAN;
   if (want == SCHED_RUN_LB && (patience > 2047 || streams > 65535)) want = SCHED_RUN_SCAN;
   if (want == SCHED_RUN_WIN && patience > (1 << 24)) want = SCHED_RUN_SCAN;
   return static_cast<Sched>(want);
@@ -311,7 +349,7 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
 
   hipError_t e;
   if (full) {
-    const art::SplitPlan sp = art::full_split_plan(desc->batch, desc->num_kv_heads, desc->max_blocks_per_seq);
+    const art::SplitPlan sp = art::full_split_plan(desc->batch, desc->num_kv_heads, desc->max_blocks_per_seq, knobs().full_wgs);
     p.splits = sp.splits;
     p.split_blocks = sp.split_blocks;
     if (sp.splits > 1) p.ws_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + wp.data);
@@ -331,7 +369,7 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
     p.slot_floats = wp.slot_floats;
     p.helpers = wp.helpers;
     p.lookahead = wp.lookahead;
-    p.spin_limit = env_int("ART_SPIN_LIMIT", 1 << 20, 64, 1 << 30);
+    p.spin_limit = knobs().spin_limit;
     p.lb_fetch = reinterpret_cast<uint32_t*>(ws + wp.lb_fetch);
     p.lb_claim = reinterpret_cast<uint32_t*>(ws + wp.lb_claim);
     p.lb_prog = reinterpret_cast<uint32_t*>(ws + wp.lb_prog);
@@ -343,6 +381,9 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
     p.window = wp.window;
     const Sched sched = terminating_kernel(desc, wp, patience);
     p.lb = sched == SCHED_RUN_LB ? 1 : 0;
+    p.stream2 = sched == SCHED_RUN_STREAM ? 1 : 0;
+    p.la0 = knobs().la0;
+    p.la_shift = knobs().la_shift;
     p.workers = knobs().workers;
     auto launch = [&](const art::Params& pp) {
       return v.kv == art::KV_F32 ? art::launch_art_f32(v, pp, static_cast<hipStream_t>(stream))
@@ -361,19 +402,15 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
       p.win_dwin = reinterpret_cast<uint32_t*>(ws + wp.win_dwin);
       p.win_pass = reinterpret_cast<uint32_t*>(ws + wp.win_pass);
       p.win_cnt = reinterpret_cast<uint32_t*>(ws + wp.win_cnt);
-      const Knobs kn = knobs();
+      const Knobs& kn = knobs();
       // fold workgroups per (stream, head): ART_WIN_SPLIT, else 2 while the
       // doubled fold grid still fits two workgroups per CU (few heads: the
       // split shortens each window's fold), 1 otherwise (many heads: the
       // chip is full and the split only repeats the prefix work)
       int split = kn.win_split;
       if (split == 0) {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-          cus = 256;
         const long folds = (long)desc->batch * desc->num_q_heads;
-        split = 2 * folds <= 2L * cus ? 2 : 1;
+        split = 2 * folds <= 2L * cu_count() ? 2 : 1;
       }
       e = hipSuccess;
       // first window: ART_WIN_FIRST, else 1/8 of the longest stream's chunks
@@ -474,7 +511,12 @@ const char* art_status_string(art_status s) {
   return "ART: unknown status";
 }
 
-int32_t art_decode_version(void) { return 200; }
+int32_t art_decode_version(void) { return 300; }
+
+void art_decode_reload_environment(void) {
+  g_knobs = read_knobs();
+  g_knobs_read = true;
+}
 
 int32_t art_decode_kernel_choice(const art_decode_desc* desc, float eps_mag, float eps_dir, int32_t patience) {
   const art_status ds = check_desc(desc);
@@ -484,6 +526,7 @@ int32_t art_decode_kernel_choice(const art_decode_desc* desc, float eps_mag, flo
   switch (terminating_kernel(desc, plan_workspace(desc), patience)) {
     case SCHED_RUN_LB: return ART_KERNEL_LOOKBACK;
     case SCHED_RUN_WIN: return ART_KERNEL_WINDOWED;
+    case SCHED_RUN_STREAM: return ART_KERNEL_STREAM;
     default: return ART_KERNEL_SCANNERS;
   }
 }

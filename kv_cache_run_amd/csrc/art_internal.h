@@ -63,6 +63,8 @@ struct Params {
   int32_t rec_floats;                  // 2 * (D + 4)
   int32_t window;                      // chunks claimable past the resolved frontier (1..32)
   int32_t lb;                          // 1: launch art_lb_kernel, 0: scanners (+ helpers)
+  int32_t stream2;                     // 1: launch art_stream_kernel (one workgroup per stream)
+  int32_t la0, la_shift;               // stream kernel: lookahead la0 + (frontier >> la_shift) blocks
   int32_t workers;                     // art_lb_kernel workgroups (0: one per resident slot)
   // windowed path (art_win_kernel): per window, a launch in the partials
   // role, then one in the fold role
@@ -104,7 +106,7 @@ struct SplitPlan {
   int splits;
   int split_blocks;
 };
-SplitPlan full_split_plan(int batch, int hkv, int max_blocks);
+SplitPlan full_split_plan(int batch, int hkv, int max_blocks, int target_wgs);
 
 // Workspace layout (bytes from the workspace base, each region 256-B aligned).
 struct WorkspacePlan {

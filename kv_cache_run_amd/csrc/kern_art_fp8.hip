@@ -1,6 +1,7 @@
 // Instantiations of the terminating kernels (scanners, look-back, windowed) for KV storage FP8 (one translation unit per
 // storage type and kernel so that the build runs in parallel).
 #include "art_kernels_impl.h"
+#include "art_stream.h"
 
 namespace art {
 namespace {
@@ -24,6 +25,14 @@ int resident_slots(K kernel, int threads) {
 template <int D, int B, int GM>
 hipError_t go(const Params& p, hipStream_t st) {
   constexpr int threads = 64 * kern::Cfg<KV_FP8, D, B, GM>::NWA;
+  if (p.stream2) {
+    if constexpr (GM <= 8) {
+      hipLaunchKernelGGL((kern::art_stream_kernel<KV_FP8, D, B, GM>), dim3(p.batch * p.hkv),
+                         dim3(64 * kern::StreamCfg<KV_FP8, D, B, GM>::NW2), 0, st, p);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   if (p.win == 1) {
     // windowed, partials: one workgroup per (stream, chunk of the window)
     hipLaunchKernelGGL((kern::art_win_part_kernel<KV_FP8, D, B, GM>), dim3(p.batch * p.hkv * p.win_n),

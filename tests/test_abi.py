@@ -97,25 +97,57 @@ def test_workspace_size_query(lib):
     assert lib.art_decode_workspace_init(None, 256, None) == art.ART_ERR_INVALID_ARG
 
 
-def test_kernel_choice_follows_the_knob_and_the_mode(lib, monkeypatch):
+@pytest.fixture()
+def env(monkeypatch):
+    """Set or clear tuning variables; the library reads them again after each change and once more at the end."""
+    class Env:
+        def set(self, k, v):
+            monkeypatch.setenv(k, v)
+            art.reload_environment()
+
+        def unset(self, k):
+            monkeypatch.delenv(k, raising=False)
+            art.reload_environment()
+    yield Env()
+    monkeypatch.undo()
+    art.reload_environment()
+
+
+def test_kernel_choice_follows_the_knob_and_the_mode(lib, env):
     """Which kernel a call would run, without any device call: forced schedulers, full mode, rejected args."""
     long_desc = _desc(batch=4, num_q_heads=64, num_kv_heads=8, block_size=32, max_blocks_per_seq=4096)
     qwen_desc = _desc(batch=64, num_q_heads=28, num_kv_heads=4, max_blocks_per_seq=1024,
                       kv_dtype=art.ART_DTYPE_FP8_E4M3FN)
-    # auto (no device here: 256 CUs assumed): few long streams -> windows, groups above 4 heads -> look-back
-    monkeypatch.delenv("ART_SCHED", raising=False)
+    # auto (no device here: 256 CUs assumed): few long streams -> windows, groups of up to 4 heads -> the
+    # stream kernel, larger groups -> look-back for long streams, else the stream kernel (up to 8 heads) or
+    # scanners
+    env.unset("ART_SCHED")
     assert art.art_decode_kernel_choice(long_desc, 5e-4, 5e-5, 6) == art.ART_KERNEL_WINDOWED
     assert art.art_decode_kernel_choice(qwen_desc, 1e-3, 1e-4, 4) == art.ART_KERNEL_LOOKBACK
-    assert art.art_decode_kernel_choice(_desc(), 1e-3, 1e-4, 4) == art.ART_KERNEL_SCANNERS
+    assert art.art_decode_kernel_choice(_desc(num_q_heads=56, max_blocks_per_seq=64), 1e-3, 1e-4, 4) == \
+        art.ART_KERNEL_STREAM
+    assert art.art_decode_kernel_choice(_desc(), 1e-3, 1e-4, 4) == art.ART_KERNEL_STREAM
+    assert art.art_decode_kernel_choice(_desc(num_q_heads=128, max_blocks_per_seq=256), 1e-3, 1e-4, 4) == \
+        art.ART_KERNEL_LOOKBACK
+    assert art.art_decode_kernel_choice(_desc(num_q_heads=128, max_blocks_per_seq=16), 1e-3, 1e-4, 4) == \
+        art.ART_KERNEL_SCANNERS
     assert art.art_decode_kernel_choice(_desc(max_blocks_per_seq=8192), 1e-3, 1e-4, 4) == art.ART_KERNEL_WINDOWED
-    monkeypatch.setenv("ART_SCHED", "scan")
+    env.set("ART_SCHED", "stream")
+    assert art.art_decode_kernel_choice(long_desc, 1e-3, 1e-4, 4) == art.ART_KERNEL_STREAM
+    # groups of more than 8 heads: the stream kernel takes none, scanners instead
+    assert art.art_decode_kernel_choice(_desc(num_q_heads=128), 1e-3, 1e-4, 4) == art.ART_KERNEL_SCANNERS
+    env.set("ART_SCHED", "scan")
     assert art.art_decode_kernel_choice(long_desc, 1e-3, 1e-4, 4) == art.ART_KERNEL_SCANNERS
-    monkeypatch.setenv("ART_SCHED", "win")
+    env.set("ART_SCHED", "win")
     assert art.art_decode_kernel_choice(_desc(), 1e-3, 1e-4, 4) == art.ART_KERNEL_WINDOWED
     # the windowed path carries the pass count as a float: beyond 2^24, scanners
     assert art.art_decode_kernel_choice(_desc(), 1e-3, 1e-4, (1 << 24) + 1) == art.ART_KERNEL_SCANNERS
-    monkeypatch.setenv("ART_SCHED", "lb")
+    env.set("ART_SCHED", "lb")
     assert art.art_decode_kernel_choice(_desc(), 1e-3, 1e-4, 4) == art.ART_KERNEL_LOOKBACK
+    # the environment is read once: a change without the reload call has no effect
+    os.environ["ART_SCHED"] = "scan"
+    assert art.art_decode_kernel_choice(_desc(), 1e-3, 1e-4, 4) == art.ART_KERNEL_LOOKBACK
+    env.set("ART_SCHED", "lb")
     # pass counts above 2047 do not fit the look-back records: scanners
     assert art.art_decode_kernel_choice(_desc(), 1e-3, 1e-4, 2048) == art.ART_KERNEL_SCANNERS
     # full attention: the flag, or a zero threshold without ART_FLAG_KEEP_DETECTOR

@@ -3,8 +3,8 @@
 Bars: stop_block bit-exact except where the oracle's statistic lies within
 1e-5 of its threshold (feasible-stop rule, oracle/feasible.py); outputs within
 2e-3 max relative error at the compared stop; full-attention mode within the
-same tolerance.  Reduced sizes compare every head; full sizes compare sampled
-heads plus properties that hold at any size.
+same tolerance.  Every head is compared, at reduced sizes and at the full
+benchmark sizes, plus properties that hold at any size.
 """
 
 import math
@@ -215,16 +215,20 @@ def test_repeatable_and_workspace_reusable():
     assert np.array_equal(runs[0][0], runs[1][0]) and np.array_equal(runs[0][1], runs[1][1])
 
 
-# ---- full sizes (the benchmark shapes): sampled heads ----------------------------------------------------
+# ---- full sizes (the benchmark shapes): every head ------------------------------------------------------
 
 FULL_SIZES = [W.LLAMA3_8B, W.RAGGED, W.LONG, W.QWEN_FP8]
 
 
 @pytest.mark.parametrize("w", FULL_SIZES, ids=[w.name for w in FULL_SIZES])
-def test_full_size_sampled(w):
+def test_full_size_every_head(w):
+    """The benchmark shapes at full size, in the launch configuration bench.py times: every head's stop and
+    output against the oracle (ART mode stops early, so the float64 oracle finishes in seconds), and every
+    head's full-attention output."""
     case = synth.make_case(w)
-    check_art(case, sample=48)
-    check_full(case, sample=24)
+    rep, _, _, _ = check_art(case)
+    assert rep["checked"] == case["batch"] * case["num_q_heads"]
+    check_full(case)
 
 
 # ---- the workgroup schedulers ---------------------------------------------------------------------------
@@ -251,6 +255,14 @@ SCAN_VARIANTS = [
 ]
 
 
+STREAM_VARIANTS = [
+    dict(ART_SCHED="stream"),                                 # defaults: lookahead 16 + frontier / 2
+    dict(ART_SCHED="stream", ART_LA0="1", ART_LA_SHIFT="30"),   # the smallest lookahead (two chunks)
+    dict(ART_SCHED="stream", ART_LA0="100000", ART_LA_SHIFT="0"),  # the largest (ring and register ring)
+    dict(ART_SCHED="stream", ART_LA0="24", ART_LA_SHIFT="3"),
+]
+
+
 WIN_VARIANTS = [
     dict(ART_SCHED="win"),                                    # default: two fold workgroups when heads are few
     dict(ART_SCHED="win", ART_WIN_SPLIT="1"),                 # one fold workgroup per (stream, head)
@@ -263,10 +275,14 @@ WIN_VARIANTS = [
 
 
 def _with_env(env, fn):
+    """Run fn with the tuning variables in env set (the library re-reads them on each change)."""
     import os
+
+    from kv_cache_run_amd import art
 
     old = {k: os.environ.get(k) for k in env}
     os.environ.update(env)
+    art.reload_environment()
     try:
         return fn()
     finally:
@@ -275,13 +291,15 @@ def _with_env(env, fn):
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = v
+        art.reload_environment()
 
 
 SCHED_CASES = [(W.LLAMA3_8B, dict(batch=3, context=8192 - 40)), (W.RAGGED, dict(batch=3)),
                (W.QWEN_FP8, dict(batch=2, context=16384 - 3)), (W.LONG, dict(batch=1, context=131072 - 17))]
 
 
-@pytest.mark.parametrize("variants", [LB_VARIANTS, SCAN_VARIANTS, WIN_VARIANTS], ids=["lookback", "scanners", "windowed"])
+@pytest.mark.parametrize("variants", [LB_VARIANTS, SCAN_VARIANTS, WIN_VARIANTS, STREAM_VARIANTS],
+                         ids=["lookback", "scanners", "windowed", "stream"])
 @pytest.mark.parametrize("w,kw", SCHED_CASES, ids=["llama", "ragged", "fp8", "long"])
 def test_scheduler_variants_bit_identical(w, kw, variants):
     case = synth.make_case(w, **kw)
@@ -356,7 +374,7 @@ def test_scheduler_epoch_advances_and_no_error():
 # ART_SCHED=auto sends only few, long streams to the look-back kernel; these run the shape corners and the
 # edge cases through it explicitly.
 
-@pytest.mark.parametrize("sched", ["lb", "win"])
+@pytest.mark.parametrize("sched", ["lb", "win", "stream", "scan"])
 @pytest.mark.parametrize("w", SHAPES, ids=[w.name for w in SHAPES])
 def test_lookback_and_windowed_shape_matrix(w, sched):
     case = synth.make_case(w, batch=2, context=2000 + 9)
@@ -364,8 +382,9 @@ def test_lookback_and_windowed_shape_matrix(w, sched):
     _with_env(dict(ART_SCHED=sched), lambda: check_art(case))
 
 
-@pytest.mark.parametrize("env", [dict(ART_SCHED="lb", ART_WINDOW="2"), dict(ART_SCHED="win", ART_WIN_SPLIT="2")],
-                         ids=["lookback", "windowed"])
+@pytest.mark.parametrize("env", [dict(ART_SCHED="lb", ART_WINDOW="2"), dict(ART_SCHED="win", ART_WIN_SPLIT="2"),
+                                 dict(ART_SCHED="stream", ART_LA0="1", ART_LA_SHIFT="30"), dict(ART_SCHED="scan")],
+                         ids=["lookback", "windowed", "stream", "scanners"])
 def test_lookback_and_windowed_edge_cases(env):
     base = synth.make_case(W.LLAMA3_8B, batch=5, context=700)
     case = _with_lens(base, [0, 1, 15, 16, 17])
@@ -401,7 +420,8 @@ def test_lookback_and_windowed_edge_cases(env):
         assert _with_env(env, lambda: art.art_decode_kernel_choice(desc, 1e-3, 1e-4, 3000)) == art.ART_KERNEL_SCANNERS
         assert _with_env(env, lambda: art.art_decode_kernel_choice(desc, 1e-3, 1e-4, 30)) == art.ART_KERNEL_LOOKBACK
     else:
-        assert _with_env(env, lambda: art.art_decode_kernel_choice(desc, 1e-3, 1e-4, 3000)) == art.ART_KERNEL_WINDOWED
+        want = {"win": art.ART_KERNEL_WINDOWED, "stream": art.ART_KERNEL_STREAM, "scan": art.ART_KERNEL_SCANNERS}
+        assert _with_env(env, lambda: art.art_decode_kernel_choice(desc, 1e-3, 1e-4, 3000)) == want[env["ART_SCHED"]]
 
 
 # ---- detector ablation: one test switched off (threshold +inf) or patience 1 -----------------------------
@@ -418,7 +438,7 @@ def test_ablation_variants_parity(w, variant):
     check_art(case, eps_mag=em, eps_dir=ed, patience=p)
 
 
-@pytest.mark.parametrize("sched", ["lb", "win"])
+@pytest.mark.parametrize("sched", ["lb", "win", "stream"])
 def test_ablation_through_lookback_and_windowed(sched):
     case = synth.make_case(W.VALUE_HEAVY, batch=2, context=4096 - 5)
     _with_env(dict(ART_SCHED=sched), lambda: check_art(case, eps_dir=math.inf))
@@ -449,7 +469,7 @@ def _pruned_case():
     return case
 
 
-@pytest.mark.parametrize("sched", ["scan", "lb", "win"])
+@pytest.mark.parametrize("sched", ["scan", "lb", "win", "stream"])
 def test_pruned_cache_parity(sched):
     case = _pruned_case()
     print(f"[pruned] {sched}", flush=True)
@@ -474,7 +494,7 @@ def test_pruned_cache_full_attention():
 
 # ---- probe-vector detector: the statistics over the leading P output coordinates -------------------------
 
-@pytest.mark.parametrize("sched", ["scan", "lb", "win"])
+@pytest.mark.parametrize("sched", ["scan", "lb", "win", "stream"])
 @pytest.mark.parametrize("w,P", [(W.LLAMA3_8B, 8), (W.LLAMA3_8B, 32), (W.LLAMA3_8B, 64), (W.TINY, 16)],
                          ids=["llama-P8", "llama-P32", "llama-P64", "tiny-P16"])
 def test_probe_vector_parity(w, P, sched):
@@ -543,7 +563,7 @@ def test_importance_order_with_equal_scores_is_recency_first():
         assert list(order[s, :n]) == [0] + list(range(n - 1, 0, -1))
 
 
-@pytest.mark.parametrize("sched", ["scan", "lb", "win"])
+@pytest.mark.parametrize("sched", ["scan", "lb", "win", "stream"])
 def test_art_on_the_importance_order(sched):
     case = synth.make_case(W.LLAMA3_8B, batch=3, context=3000 - 5)
     _, order = _device_order(case)
@@ -559,7 +579,7 @@ def test_skip_statistics_flag_gives_full_attention_in_every_scheduler():
     case = synth.make_case(W.LLAMA3_8B, batch=2, context=1500)
     ref = _device_run(case, 0.0, 0.0, 4, flags=art.ART_FLAG_KEEP_DETECTOR)
     n = _nblocks(case)
-    for sched in ("scan", "lb", "win"):
+    for sched in ("scan", "lb", "win", "stream"):
         out, stop, fetched = _with_env(dict(ART_SCHED=sched),
                                        lambda: _device_run(case, 1e-3, 1e-4, 4, flags=art.ART_FLAG_SKIP_STATS))
         assert np.all(stop == n[:, None]), sched
@@ -624,7 +644,7 @@ def _random_case(seed):
     em = float(10 ** rng.uniform(-4, -1))
     ed = float(10 ** rng.uniform(-5, -2))
     p = int(rng.integers(1, 7))
-    sched = str(rng.choice(["scan", "lb", "win", "auto"]))
+    sched = str(rng.choice(["scan", "lb", "win", "auto", "stream"]))
     return case, em, ed, p, sched
 
 
@@ -756,7 +776,7 @@ def test_decoder_checks_inputs_when_asked():
 
 
 @pytest.mark.parametrize("w", [W.LLAMA3_8B, W.QWEN_FP8], ids=["bf16", "fp8"])
-@pytest.mark.parametrize("sched", ["scan", "lb", "win", "full"])
+@pytest.mark.parametrize("sched", ["scan", "lb", "win", "stream", "full"])
 def test_pages_past_4_gib(sched, w):
     """Page addressing is 64-bit: the same pages (and fp8 scales) placed past 4 GiB of K and of V (a pool
     of ≈4.3 GiB each) give the same bits as at low page ids, for each ART scheduler and for full attention."""
