@@ -202,6 +202,33 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
                              int32_t* blocks_fetched, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * art_decode without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The library itself allocates nothing either: full
+ * attention's per-split partial results (the only scratch this entry point
+ * uses) go to a static 8 MiB device array that every device holds until the
+ * process ends; its device address is looked up once per device, with that
+ * device current, at the first call there.  ART mode runs the kernels that
+ * need no scratch: the stream kernel for groups of up to 8 query heads, the
+ * per-stream scanners (without helper workgroups) for larger groups, whatever
+ * ART_SCHED says.  Results are those art_decode gives with ART_SCHED=stream
+ * (respectively scan with ART_HELPERS=0), bit for bit; full attention gives
+ * art_decode's full-attention bits.
+ * The static array is shared by every call on a device and keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that overlap
+ * in time on one device race, whatever their streams.
+ * Errors: as art_decode; ART_ERR_WORKSPACE when full attention's partials
+ * (streams x splits x GM x (D + 2) floats, GM = g rounded up to 4, 8 or 16)
+ * would pass 8 MiB -- use art_decode then; ART_ERR_HIP when the array's
+ * address cannot be looked up or a launch fails.
+ */
+art_status art_decode_noalloc(const art_decode_desc* desc, const void* q, const void* k_pages, const void* v_pages,
+                              const float* k_scale, const float* v_scale, const int32_t* block_table,
+                              const int32_t* block_order, const int32_t* seq_lens, float eps_mag, float eps_dir,
+                              int32_t patience, float* out, int32_t* stop_block, int32_t* blocks_fetched,
+                              void* stream);
+
+/*
  * Importance-first traversal (the ART explainer, Technical Summary 2.4,
  * names it beside recency-first as an order ART can take): a pre-pass that
  * writes block_order from a cheap per-block summary of the keys, after which

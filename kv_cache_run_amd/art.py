@@ -31,7 +31,7 @@ def art_flag_probe(p: int) -> int:
 EXPORTED = ("art_decode_workspace_bytes", "art_decode_workspace_init", "art_decode", "art_decode_visits",
             "art_status_string", "art_decode_version", "art_decode_kernel_choice", "art_block_key_summary",
             "art_importance_order_workspace_bytes", "art_importance_order", "art_check_inputs",
-            "art_decode_reload_environment")
+            "art_decode_reload_environment", "art_decode_noalloc")
 ART_KERNEL_FULL, ART_KERNEL_SCANNERS, ART_KERNEL_LOOKBACK, ART_KERNEL_WINDOWED, ART_KERNEL_STREAM = 0, 1, 2, 3, 4
 ART_CHECK_OK, ART_CHECK_SEQ_LEN, ART_CHECK_ORDER_RANGE, ART_CHECK_ORDER_REPEAT, ART_CHECK_PAGE_RANGE = 0, 1, 2, 3, 4
 CHECK_NAMES = {ART_CHECK_SEQ_LEN: "sequence length outside [0, max_blocks * block_size]",
@@ -102,6 +102,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.art_decode_version.restype = i32
     lib.art_decode_kernel_choice.argtypes = [ctypes.POINTER(ArtDecodeDesc), f32, f32, i32]
     lib.art_decode_kernel_choice.restype = i32
+    lib.art_decode_noalloc.argtypes = [ctypes.POINTER(ArtDecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, f32, f32, i32, vp,
+                                       vp, vp, vp]
+    lib.art_decode_noalloc.restype = ctypes.c_int
     lib.art_decode_reload_environment.argtypes = []
     lib.art_decode_reload_environment.restype = None
     if path is None:
@@ -202,6 +205,21 @@ def art_decode(q, k_pages, v_pages, block_table, block_order, seq_lens, eps_mag:
                                    _ptr(stop_block), _ptr(blocks_fetched), _ptr(workspace), nbytes,
                                    _stream(stream))
     _check(st)
+
+
+def art_decode_noalloc(q, k_pages, v_pages, block_table, block_order, seq_lens, eps_mag: float, eps_dir: float,
+                       patience: int, out, stop_block, *, k_scale=None, v_scale=None, blocks_fetched=None,
+                       flags: int = 0, stream=None) -> None:
+    """Enqueue art_decode_noalloc (no workspace: a static device scratch array, see include/art_decode.h)."""
+    for t in (q, k_pages, v_pages, block_table, block_order, seq_lens, out, stop_block, k_scale, v_scale,
+              blocks_fetched):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    desc = make_desc(q, k_pages, block_table, flags)
+    _check(load_library().art_decode_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
+                                             _ptr(v_scale), _ptr(block_table), _ptr(block_order), _ptr(seq_lens),
+                                             float(eps_mag), float(eps_dir), int(patience), _ptr(out),
+                                             _ptr(stop_block), _ptr(blocks_fetched), _stream(stream)))
 
 
 def block_key_summary(q, k_pages, block_table, seq_lens, *, k_scale=None, summary=None, stream=None):

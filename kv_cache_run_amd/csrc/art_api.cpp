@@ -280,11 +280,20 @@ art_status art_decode(const art_decode_desc* desc, const void* q, const void* k_
                            stream);
 }
 
-art_status art_decode_visits(const art_decode_desc* desc, const void* q, const void* k_pages, const void* v_pages,
-                             const float* k_scale, const float* v_scale, const int32_t* block_table,
-                             const int32_t* block_order, const int32_t* seq_lens, const int32_t* visit_lens,
-                             float eps_mag, float eps_dir, int32_t patience, float* out, int32_t* stop_block,
-                             int32_t* blocks_fetched, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// One decode call.  noalloc: no caller workspace; full attention's split
+// partials go to the static scratch (rejected when they would not fit) and
+// ART mode runs the kernels that need no scratch (the stream kernel for
+// groups of up to 8 heads, the scanners without helpers otherwise).
+art_status decode_impl(const art_decode_desc* desc, const void* q, const void* k_pages, const void* v_pages,
+                       const float* k_scale, const float* v_scale, const int32_t* block_table,
+                       const int32_t* block_order, const int32_t* seq_lens, const int32_t* visit_lens,
+                       float eps_mag, float eps_dir, int32_t patience, float* out, int32_t* stop_block,
+                       int32_t* blocks_fetched, void* workspace, size_t workspace_bytes, void* stream,
+                       bool noalloc) {
   const art_status ds = check_desc(desc);
   if (ds != ART_OK) return ds;
   if (!(eps_mag >= 0.f) || !(eps_dir >= 0.f) || patience < 1) return ART_ERR_INVALID_ARG;
@@ -298,14 +307,27 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
       (v_scale && !aligned(v_scale, 4)) || (visit_lens && !aligned(visit_lens, 4)))
     return ART_ERR_INVALID_ARG;
   const art::WorkspacePlan wp = plan_workspace(desc);
-  if (wp.total > 0) {
+  const bool full = full_mode(desc, eps_mag, eps_dir);
+  const int g = desc->num_q_heads / desc->num_kv_heads;
+  if (noalloc) {
+    // full attention's split partials are the only scratch this call uses
+    workspace = nullptr;
+    if (full && desc->batch > 0) {
+      const art::SplitPlan sp =
+          art::full_split_plan(desc->batch, desc->num_kv_heads, desc->max_blocks_per_seq, knobs().full_wgs);
+      if (sp.splits > 1) {
+        const size_t need = (size_t)desc->batch * desc->num_kv_heads * sp.splits * art::group_capacity(g) *
+                            (size_t)(desc->head_dim + 2) * sizeof(float);
+        if (need > art::noalloc_scratch_bytes()) return ART_ERR_WORKSPACE;
+        if (art::noalloc_scratch(&workspace) != hipSuccess) return ART_ERR_HIP;
+      }
+    }
+  } else if (wp.total > 0) {
     if (!workspace || workspace_bytes < wp.total) return ART_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return ART_ERR_INVALID_ARG;
   }
   if (desc->batch == 0) return ART_OK;
 
-  const bool full = full_mode(desc, eps_mag, eps_dir);
-  const int g = desc->num_q_heads / desc->num_kv_heads;
   art::Variant v;
   v.kv = desc->kv_dtype == ART_DTYPE_F32 ? art::KV_F32 : (fp8 ? art::KV_FP8 : art::KV_BF16);
   v.d = desc->head_dim;
@@ -352,34 +374,38 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
     const art::SplitPlan sp = art::full_split_plan(desc->batch, desc->num_kv_heads, desc->max_blocks_per_seq, knobs().full_wgs);
     p.splits = sp.splits;
     p.split_blocks = sp.split_blocks;
-    if (sp.splits > 1) p.ws_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + wp.data);
+    if (sp.splits > 1)
+      p.ws_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + (noalloc ? 0 : wp.data));
     e = v.kv == art::KV_F32 ? art::launch_full_f32(v, p, static_cast<hipStream_t>(stream))
         : v.kv == art::KV_BF16 ? art::launch_full_bf16(v, p, static_cast<hipStream_t>(stream))
                                : art::launch_full_fp8(v, p, static_cast<hipStream_t>(stream));
   } else {
     p.splits = 1;
     p.split_blocks = desc->max_blocks_per_seq;
+    // no-alloc calls (no workspace) run kernels that touch none of its regions: null views
     char* ws = static_cast<char*>(workspace);
+    auto at = [&](size_t off) { return ws ? ws + off : nullptr; };
     p.sched_ctrl = reinterpret_cast<uint32_t*>(ws);
-    p.sched_claim = reinterpret_cast<unsigned long long*>(ws + wp.claim);
-    p.sched_done = reinterpret_cast<unsigned long long*>(ws + wp.done);
-    p.sched_ready = reinterpret_cast<unsigned long long*>(ws + wp.ready);
-    p.sched_ring = reinterpret_cast<float*>(ws + wp.data);
+    p.sched_claim = reinterpret_cast<unsigned long long*>(at(wp.claim));
+    p.sched_done = reinterpret_cast<unsigned long long*>(at(wp.done));
+    p.sched_ready = reinterpret_cast<unsigned long long*>(at(wp.ready));
+    p.sched_ring = reinterpret_cast<float*>(at(wp.data));
     p.ring = wp.ring;
     p.slot_floats = wp.slot_floats;
     p.helpers = wp.helpers;
     p.lookahead = wp.lookahead;
     p.spin_limit = knobs().spin_limit;
-    p.lb_fetch = reinterpret_cast<uint32_t*>(ws + wp.lb_fetch);
-    p.lb_claim = reinterpret_cast<uint32_t*>(ws + wp.lb_claim);
-    p.lb_prog = reinterpret_cast<uint32_t*>(ws + wp.lb_prog);
-    p.lb_heads = reinterpret_cast<uint32_t*>(ws + wp.lb_heads);
-    p.lb_st = reinterpret_cast<unsigned long long*>(ws + wp.lb_st);
-    p.lb_rec = reinterpret_cast<float*>(ws + wp.data);
+    p.lb_fetch = reinterpret_cast<uint32_t*>(at(wp.lb_fetch));
+    p.lb_claim = reinterpret_cast<uint32_t*>(at(wp.lb_claim));
+    p.lb_prog = reinterpret_cast<uint32_t*>(at(wp.lb_prog));
+    p.lb_heads = reinterpret_cast<uint32_t*>(at(wp.lb_heads));
+    p.lb_st = reinterpret_cast<unsigned long long*>(at(wp.lb_st));
+    p.lb_rec = reinterpret_cast<float*>(at(wp.data));
     p.max_chunks = wp.max_chunks;
     p.rec_floats = wp.rec_floats;
     p.window = wp.window;
-    const Sched sched = terminating_kernel(desc, wp, patience);
+    const Sched sched = noalloc ? (g <= 8 ? SCHED_RUN_STREAM : SCHED_RUN_SCAN) : terminating_kernel(desc, wp, patience);
+    if (noalloc) p.helpers = 0;
     p.lb = sched == SCHED_RUN_LB ? 1 : 0;
     p.stream2 = sched == SCHED_RUN_STREAM ? 1 : 0;
     p.la0 = knobs().la0;
@@ -396,12 +422,12 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
       p.lb = 0;
       p.win_max = wp.win_max;
       p.win_slot = wp.win_slot;
-      p.win_slots = reinterpret_cast<float*>(ws + wp.data);
-      p.win_state = reinterpret_cast<float*>(ws + wp.win_state);
-      p.win_dead = reinterpret_cast<uint32_t*>(ws + wp.win_dead);
-      p.win_dwin = reinterpret_cast<uint32_t*>(ws + wp.win_dwin);
-      p.win_pass = reinterpret_cast<uint32_t*>(ws + wp.win_pass);
-      p.win_cnt = reinterpret_cast<uint32_t*>(ws + wp.win_cnt);
+      p.win_slots = reinterpret_cast<float*>(at(wp.data));
+      p.win_state = reinterpret_cast<float*>(at(wp.win_state));
+      p.win_dead = reinterpret_cast<uint32_t*>(at(wp.win_dead));
+      p.win_dwin = reinterpret_cast<uint32_t*>(at(wp.win_dwin));
+      p.win_pass = reinterpret_cast<uint32_t*>(at(wp.win_pass));
+      p.win_cnt = reinterpret_cast<uint32_t*>(at(wp.win_cnt));
       const Knobs& kn = knobs();
       // fold workgroups per (stream, head): ART_WIN_SPLIT, else 2 while the
       // doubled fold grid still fits two workgroups per CU (few heads: the
@@ -438,6 +464,29 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
     }
   }
   return e == hipSuccess ? ART_OK : ART_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+art_status art_decode_visits(const art_decode_desc* desc, const void* q, const void* k_pages, const void* v_pages,
+                             const float* k_scale, const float* v_scale, const int32_t* block_table,
+                             const int32_t* block_order, const int32_t* seq_lens, const int32_t* visit_lens,
+                             float eps_mag, float eps_dir, int32_t patience, float* out, int32_t* stop_block,
+                             int32_t* blocks_fetched, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(desc, q, k_pages, v_pages, k_scale, v_scale, block_table, block_order, seq_lens, visit_lens,
+                     eps_mag, eps_dir, patience, out, stop_block, blocks_fetched, workspace, workspace_bytes, stream,
+                     false);
+}
+
+art_status art_decode_noalloc(const art_decode_desc* desc, const void* q, const void* k_pages, const void* v_pages,
+                              const float* k_scale, const float* v_scale, const int32_t* block_table,
+                              const int32_t* block_order, const int32_t* seq_lens, float eps_mag, float eps_dir,
+                              int32_t patience, float* out, int32_t* stop_block, int32_t* blocks_fetched,
+                              void* stream) {
+  return decode_impl(desc, q, k_pages, v_pages, k_scale, v_scale, block_table, block_order, seq_lens, nullptr,
+                     eps_mag, eps_dir, patience, out, stop_block, blocks_fetched, nullptr, 0, stream, true);
 }
 
 art_status art_block_key_summary(const art_decode_desc* desc, const void* k_pages, const float* k_scale,

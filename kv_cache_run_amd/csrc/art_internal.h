@@ -125,6 +125,11 @@ hipError_t launch_full_f32(const Variant& v, const Params& p, hipStream_t stream
 hipError_t launch_full_bf16(const Variant& v, const Params& p, hipStream_t stream);
 hipError_t launch_full_fp8(const Variant& v, const Params& p, hipStream_t stream);
 
+// Static scratch of art_decode_noalloc (kern_noalloc.hip): its size, and its
+// device address on the current device (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** ptr);
+
 // Input-contract check (kern_check.hip).
 int check_max_blocks();
 hipError_t launch_check(const int32_t* block_table, const int32_t* block_order, const int32_t* seq_lens,

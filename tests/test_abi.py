@@ -210,3 +210,17 @@ def test_check_inputs_entry_point_validates(lib):
     assert call(d, FAKE, FAKE, FAKE, FAKE + 1, FAKE) == art.ART_ERR_INVALID_ARG
     assert call(_desc(max_blocks_per_seq=(1 << 18) + 1), FAKE, FAKE, FAKE, None, FAKE) == art.ART_ERR_UNSUPPORTED
     assert call(_desc(num_kv_heads=3), FAKE, FAKE, FAKE, None, FAKE) != art.ART_OK
+
+
+def test_noalloc_rejects_partials_past_the_static_scratch(lib):
+    """art_decode_noalloc: full attention whose split partials would pass the 8 MiB static array is refused
+    before any device call (one sequence of 65536 blocks, 8 kv-heads of 16 query heads: 256 splits of 256
+    blocks, 8 x 256 x 16 x 130 floats = 17 MB); the same descriptor in ART mode needs no scratch but the
+    call then reaches the device, which this host test does not do."""
+    d = _desc(batch=1, num_q_heads=128, num_kv_heads=8, max_blocks_per_seq=65536, num_pages=65536)
+    args = lambda em: (ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, em, em, 1, FAKE, FAKE, None,
+                       None)
+    assert lib.art_decode_noalloc(*args(0.0)) == art.ART_ERR_WORKSPACE
+    # argument checks come first, as in art_decode
+    assert lib.art_decode_noalloc(ctypes.byref(d), None, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 0.0, 0.0, 1,
+                                  FAKE, FAKE, None, None) == art.ART_ERR_INVALID_ARG
