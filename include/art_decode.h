@@ -98,7 +98,9 @@ typedef struct {
 
 /*
  * Bytes of device workspace art_decode needs for `desc` (0 = none).  Depends
- * only on the descriptor.  Returns 0 also for an invalid descriptor.
+ * on the descriptor and on the tuning variable ART_RING (slots per stream of
+ * the scanners' helper ring), read once per process (see
+ * art_decode_reload_environment).  Returns 0 also for an invalid descriptor.
  */
 size_t art_decode_workspace_bytes(const art_decode_desc* desc);
 
@@ -112,11 +114,28 @@ size_t art_decode_workspace_bytes(const art_decode_desc* desc);
  * workgroups: per-chunk records of the look-back scheduler, the partial
  * results helper workgroups hand to the per-stream scanners, or the
  * full-attention slices before their merge.  Calls that share a workspace
- * must not overlap.
+ * must not overlap.  The clearing is a small fill kernel, not a memset, so
+ * this call may be captured in a HIP graph as well.
  * Errors: ART_ERR_INVALID_ARG for NULL with bytes > 0 or a pointer that is
  * not 256-byte aligned, ART_ERR_HIP.
  */
 art_status art_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Whether a bounded wait gave up in any terminating-kernel call that used
+ * this workspace since art_decode_workspace_init: *failed = 1, else 0.  The
+ * waits between workgroups (look-back records, helper hand-offs) and between
+ * the waves of one workgroup (the stream kernel's ring) are bounded by
+ * ART_SPIN_LIMIT polls so that a fault in the hand-off can never hang the
+ * device; a call in which one gave up wrote stop_block = -1 or NaN output for
+ * the heads it had not finished, and art_decode still returned ART_OK (it
+ * returns before the kernels run).  The word is sticky until
+ * art_decode_workspace_init.  Reads the workspace back to the host and
+ * synchronizes `stream`: for diagnostics, not for the decode loop.
+ * Errors: ART_ERR_INVALID_ARG (NULL failed; NULL, misaligned or shorter than
+ * 16-byte workspace), ART_ERR_HIP.
+ */
+art_status art_decode_workspace_status(const void* workspace, size_t workspace_bytes, int32_t* failed, void* stream);
 
 /*
  * ART decode attention, one decode step of one layer.
@@ -141,7 +160,10 @@ art_status art_decode_workspace_init(void* workspace, size_t workspace_bytes, vo
  * out          [batch][Hq][D] float32: the head's normalized attention output
  *              over the blocks it folded (0 for an empty sequence).
  * stop_block   [batch][Hq] int32: number of folded blocks = visit positions
- *              0 .. stop-1 (n_s when the head never stopped, 0 when empty).
+ *              0 .. stop-1 (n_s when the head never stopped, 0 when empty;
+ *              -1 or NaN output, either of which marks the head, when a
+ *              bounded wait between the kernel's workgroups or waves gave
+ *              up: art_decode_workspace_status).
  * blocks_fetched  optional [batch][Hkv] int32 (NULL to skip): KV blocks the
  *              kernels actually read for each (sequence, kv-head), speculative
  *              reads (chunks fetched ahead of the stop) included.

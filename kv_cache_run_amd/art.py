@@ -31,7 +31,7 @@ def art_flag_probe(p: int) -> int:
 EXPORTED = ("art_decode_workspace_bytes", "art_decode_workspace_init", "art_decode", "art_decode_visits",
             "art_status_string", "art_decode_version", "art_decode_kernel_choice", "art_block_key_summary",
             "art_importance_order_workspace_bytes", "art_importance_order", "art_check_inputs",
-            "art_decode_reload_environment", "art_decode_noalloc")
+            "art_decode_reload_environment", "art_decode_noalloc", "art_decode_workspace_status")
 ART_KERNEL_FULL, ART_KERNEL_SCANNERS, ART_KERNEL_LOOKBACK, ART_KERNEL_WINDOWED, ART_KERNEL_STREAM = 0, 1, 2, 3, 4
 ART_CHECK_OK, ART_CHECK_SEQ_LEN, ART_CHECK_ORDER_RANGE, ART_CHECK_ORDER_REPEAT, ART_CHECK_PAGE_RANGE = 0, 1, 2, 3, 4
 CHECK_NAMES = {ART_CHECK_SEQ_LEN: "sequence length outside [0, max_blocks * block_size]",
@@ -67,6 +67,16 @@ class ArtError(RuntimeError):
 _lib = None
 
 
+def _mapped_hip_runtimes() -> list:
+    """Distinct HIP runtime files mapped into this process (Linux; empty where /proc is not readable)."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {line.split()[-1] for line in f if "libamdhip64.so" in line}
+    except OSError:
+        return []
+    return sorted({os.path.realpath(x) for x in paths})
+
+
 def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     """Load the HIP library (raises if it has not been built)."""
     global _lib
@@ -76,7 +86,15 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with `python -m kv_cache_run_amd.build` "
                            "(there is no non-HIP fallback)")
+    # torch first: it maps the HIP runtime it ships, and the library then binds to that one.  Loaded the
+    # other way round, the process would hold two HIP runtimes, and pointers and streams from torch's would be
+    # unknown to the library's.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(p)
+    runtimes = _mapped_hip_runtimes()
+    if len(runtimes) > 1:
+        raise RuntimeError(f"two HIP runtimes are mapped ({', '.join(runtimes)}): the library must share torch's")
     vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
     lib.art_decode_workspace_bytes.argtypes = [ctypes.POINTER(ArtDecodeDesc)]
     lib.art_decode_workspace_bytes.restype = sz
@@ -105,6 +123,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.art_decode_noalloc.argtypes = [ctypes.POINTER(ArtDecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, f32, f32, i32, vp,
                                        vp, vp, vp]
     lib.art_decode_noalloc.restype = ctypes.c_int
+    lib.art_decode_workspace_status.argtypes = [vp, sz, ctypes.POINTER(i32), vp]
+    lib.art_decode_workspace_status.restype = ctypes.c_int
     lib.art_decode_reload_environment.argtypes = []
     lib.art_decode_reload_environment.restype = None
     if path is None:
@@ -174,6 +194,14 @@ def _stream(stream) -> Optional[int]:
 
 def art_decode_workspace_bytes(desc: ArtDecodeDesc) -> int:
     return int(load_library().art_decode_workspace_bytes(ctypes.byref(desc)))
+
+
+def art_decode_workspace_status(workspace, stream=None) -> bool:
+    """True if a bounded wait gave up in a call that used this workspace (synchronizes the stream)."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    failed = ctypes.c_int32(0)
+    _check(load_library().art_decode_workspace_status(_ptr(workspace), nbytes, ctypes.byref(failed), _stream(stream)))
+    return bool(failed.value)
 
 
 def art_decode_workspace_init(workspace, stream=None) -> None:

@@ -112,7 +112,7 @@ Knobs read_knobs() {
                    env_int("ART_WORKERS", 0, 0, 1 << 20),       env_int("ART_WIN_SPLIT", 0, 0, art::art_win_split),
                    env_int("ART_WIN_FIRST", 0, 0, 64),          env_int("ART_WIN_GROWTH", 2, 2, 8),
                    env_int("ART_LA0", 16, 1, 1 << 20),          env_int("ART_LA_SHIFT", 1, 0, 30),
-                   env_int("ART_SPIN_LIMIT", 1 << 20, 64, 1 << 30), env_int("ART_FULL_WGS", 512, 1, 1 << 20)};
+                   env_int("ART_SPIN_LIMIT", 1 << 20, 1, 1 << 30), env_int("ART_FULL_WGS", 512, 1, 1 << 20)};
   return k;
 }
 // The knobs in effect; guarded by a flag so that the environment is read once.
@@ -262,10 +262,24 @@ size_t art_decode_workspace_bytes(const art_decode_desc* desc) {
   return plan_workspace(desc).total;
 }
 
+art_status art_decode_workspace_status(const void* workspace, size_t workspace_bytes, int32_t* failed, void* stream) {
+  if (!failed) return ART_ERR_INVALID_ARG;
+  *failed = 0;
+  if (!workspace || workspace_bytes < 16 || !aligned(workspace, 256)) return ART_ERR_INVALID_ARG;
+  uint32_t word = 0;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(&word, static_cast<const char*>(workspace) + 8, sizeof(word), hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return ART_ERR_HIP;
+  *failed = word != 0 ? 1 : 0;
+  return ART_OK;
+}
+
 art_status art_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
   if (workspace_bytes == 0) return ART_OK;
   if (!workspace || !aligned(workspace, 256)) return ART_ERR_INVALID_ARG;
-  if (hipMemsetAsync(workspace, 0, workspace_bytes, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (art::launch_zero_fill(workspace, workspace_bytes, static_cast<hipStream_t>(stream)) != hipSuccess)
     return ART_ERR_HIP;
   return ART_OK;
 }

@@ -135,6 +135,8 @@ int check_max_blocks();
 hipError_t launch_check(const int32_t* block_table, const int32_t* block_order, const int32_t* seq_lens,
                         const int32_t* visit_lens, int32_t* result, int batch, int max_blocks, int bs, int num_pages,
                         hipStream_t stream);
+// Zero a device range with a fill kernel (also valid under stream capture).
+hipError_t launch_zero_fill(void* ptr, size_t bytes, hipStream_t stream);
 
 // Importance-first order pre-pass (kern_order.hip).
 int order_max_blocks();

@@ -501,7 +501,12 @@ __global__ __launch_bounds__((64 * StreamCfg<KV, D, B, GM>::NW2)) void art_strea
       ART_TL(lane == 0, 8192 + 8 * (t0 / C) + 2 * w + 1);
       if (live == 0) break;
     }
-    if (failed && lane == 0) { lds_st(&sh.err, 1); lds_st(&sh.done, 1); lds_st(&sh.prog[w], STREAM_BIG); }
+    if (failed && lane == 0) {
+      lds_st(&sh.err, 1);
+      lds_st(&sh.done, 1);
+      lds_st(&sh.prog[w], STREAM_BIG);
+      if (p.sched_ctrl) st_dev32(p.sched_ctrl + 2, 1u);  // the workspace's sticky failure word
+    }
     // heads that never fired: the output after every visited block
 #pragma unroll
     for (int k = 0; k < HP; ++k) {
@@ -686,6 +691,7 @@ __global__ __launch_bounds__((64 * StreamCfg<KV, D, B, GM>::NW2)) void art_strea
     if (failed && lane == 0) {
       lds_st(&sh.err, 1);
       lds_st(&sh.done, 1);
+      if (p.sched_ctrl) st_dev32(p.sched_ctrl + 2, 1u);  // the workspace's sticky failure word
     }
 #ifdef ART_STREAM_TIMELINE
     if (lane == 0 && (int)blockIdx.x == art_timeline_stream) {

@@ -100,9 +100,28 @@ __global__ void check_final_kernel(const int32_t* table, const int32_t* order, c
   result[3] = val;
 }
 
+// Zero `bytes` bytes at a 16-byte aligned address: 16-byte stores over a
+// grid-stride loop, the remaining bytes one at a time.
+__global__ __launch_bounds__(256) void zero_fill_kernel(unsigned char* ptr, size_t bytes) {
+  const size_t words = bytes / 16;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += stride)
+    reinterpret_cast<uint4*>(ptr)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (blockIdx.x == 0 && threadIdx.x < bytes - 16 * words) ptr[16 * words + threadIdx.x] = 0;
+}
+
 }  // namespace
 
 int check_max_blocks() { return CHECK_MAX_BLOCKS; }
+
+hipError_t launch_zero_fill(void* ptr, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return hipSuccess;
+  const size_t words = (bytes + 15) / 16;
+  const size_t blocks = (words + 255) / 256;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256), 0, stream,
+                     static_cast<unsigned char*>(ptr), bytes);
+  return hipGetLastError();
+}
 
 hipError_t launch_check(const int32_t* block_table, const int32_t* block_order, const int32_t* seq_lens,
                         const int32_t* visit_lens, int32_t* result, int batch, int max_blocks, int bs, int num_pages,

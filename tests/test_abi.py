@@ -224,3 +224,16 @@ def test_noalloc_rejects_partials_past_the_static_scratch(lib):
     # argument checks come first, as in art_decode
     assert lib.art_decode_noalloc(ctypes.byref(d), None, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 0.0, 0.0, 1,
                                   FAKE, FAKE, None, None) == art.ART_ERR_INVALID_ARG
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loading the library (which imports torch first) leaves exactly one HIP runtime mapped, whatever was
+    imported before."""
+    import subprocess
+    import sys
+
+    code = ("from kv_cache_run_amd import art; art.load_library(); "
+            "import torch; print(len(art._mapped_hip_runtimes()))")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip().splitlines()[-1] == "1"

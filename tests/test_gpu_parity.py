@@ -818,3 +818,49 @@ def test_pages_past_4_gib(sched, w):
     assert np.array_equal(lo[0], hi[0]) and np.array_equal(lo[1], hi[1])
     del kb, vb
     torch.cuda.empty_cache()
+
+
+# ---- bounded waits that give up: forced from the host with the smallest spin limit -----------------------
+
+
+@pytest.mark.parametrize("sched", ["lb", "stream", "scan-helpers"])
+def test_bounded_waits_that_give_up_are_reported(sched):
+    """ART_SPIN_LIMIT=1 (two polls) makes waits between workgroups or waves give up; every wait is bounded, so
+    every kernel still exits.  A head whose result a give-up touched reads stop -1 or NaN output
+    (two workgroups of the look-back kernel may both write one head, so the two marks can mix); every other
+    head passes the oracle check, and any give-up sets the workspace's failure word."""
+    from kv_cache_run_amd import art
+
+    env = {"lb": dict(ART_SCHED="lb", ART_SPIN_LIMIT="1"), "stream": dict(ART_SCHED="stream", ART_SPIN_LIMIT="1"),
+           "scan-helpers": dict(ART_SCHED="scan", ART_HELPERS="256", ART_SPIN_LIMIT="1")}[sched]
+    case = synth.make_case(W.RAGGED, batch=4)
+
+    def run():
+        import torch
+
+        dev = art.case_to_device(case)
+        dec = art.Decoder(dev["q"], dev["k_pages"], dev["block_table"])
+        art.art_decode_workspace_init(dec.workspace) if dec.workspace is not None else None
+        assert dec.workspace is None or not art.art_decode_workspace_status(dec.workspace)
+        out, stop = dec(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"], dev["block_order"],
+                        dev["seq_lens"], case["eps_mag"], case["eps_dir"], case["patience"])
+        torch.cuda.synchronize()
+        failed = None if dec.workspace is None else art.art_decode_workspace_status(dec.workspace)
+        return out.cpu().numpy().astype(np.float64), stop.cpu().numpy(), failed
+
+    out, stop, failed = _with_env(env, run)
+    gave_up = (stop == -1) | np.isnan(out).any(axis=-1)
+    print(f"[give-up] {sched}: {int(gave_up.sum())} of {stop.size} heads gave up; status {failed}", flush=True)
+    if gave_up.any():
+        assert failed is True
+    if sched == "stream":
+        # the detectors' first wait (two polls) ends long before eight blocks' tiles can arrive
+        assert gave_up.any() and failed is True
+    ok = [(s, h) for s in range(case["batch"]) for h in range(case["num_q_heads"]) if not gave_up[s, h]]
+    if ok:
+        ref = oracle.art_reference(*synth.oracle_arrays(case), eps_mag=case["eps_mag"], eps_dir=case["eps_dir"],
+                                   patience=case["patience"], pairs=ok, **synth.oracle_kwargs(case),
+                                   **synth.oracle_detector_kwargs(case))
+        rep = oracle.compare_with_oracle(out, stop, case, ref, eps_mag=case["eps_mag"], eps_dir=case["eps_dir"],
+                                         patience=case["patience"], pairs=ok)
+        assert rep["bad"] == [] and rep["max_rel_err"] <= TOL, rep
