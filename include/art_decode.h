@@ -227,22 +227,25 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
  * art_decode without a workspace, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  The library itself allocates nothing either: full
- * attention's per-split partial results (the only scratch this entry point
- * uses) go to a static 8 MiB device array that every device holds until the
- * process ends; its device address is looked up once per device, with that
- * device current, at the first call there.  ART mode runs the kernels that
+ * attention's per-split partial results and per-stream slice counters (the
+ * only scratch this entry point uses) go to a static 8 MiB device array that
+ * every device holds until the process ends; its device address is looked up
+ * once per device, with that device current, at the first call there.  ART mode runs the kernels that
  * need no scratch: the stream kernel for groups of up to 8 query heads, the
  * per-stream scanners (without helper workgroups) for larger groups, whatever
  * ART_SCHED says.  Results are those art_decode gives with ART_SCHED=stream
  * (respectively scan with ART_HELPERS=0), bit for bit; full attention gives
  * art_decode's full-attention bits.
  * The static array is shared by every call on a device and keeps the last
- * call's contents (nothing in it needs to start at zero): calls that overlap
- * in time on one device race, whatever their streams.
- * Errors: as art_decode; ART_ERR_WORKSPACE when full attention's partials
- * (streams x splits x GM x (D + 2) floats, GM = g rounded up to 4, 8 or 16)
- * would pass 8 MiB -- use art_decode then; ART_ERR_HIP when the array's
- * address cannot be looked up or a launch fails.
+ * call's contents: the slice counters start at zero when the library is
+ * loaded and every full-attention call leaves them at zero; the partials need
+ * no clearing.  Calls that overlap in time on one device race, whatever their
+ * streams.
+ * Errors: as art_decode; ART_ERR_WORKSPACE when full attention splits the
+ * streams' blocks and either the streams (batch x Hkv) pass 16384 or 64 KiB of
+ * counters plus the partials (streams x splits x GM x (D + 2) floats, GM = g
+ * rounded up to 4, 8 or 16) pass 8 MiB -- use art_decode then; ART_ERR_HIP
+ * when the array's address cannot be looked up or a launch fails.
  */
 art_status art_decode_noalloc(const art_decode_desc* desc, const void* q, const void* k_pages, const void* v_pages,
                               const float* k_scale, const float* v_scale, const int32_t* block_table,
@@ -330,9 +333,11 @@ int32_t art_decode_version(void);
  *   ART_KERNEL_WINDOWED  the windowed scheduler,
  *   ART_KERNEL_STREAM    the stream kernel (one workgroup per stream,
  *                        producer and detector waves sharing an LDS ring),
+ *   ART_KERNEL_SEGMENTS  the segment kernel (segments of one stream on many
+ *                        workgroups, joined by decoupled look-back),
  * or minus the art_status art_decode would return for rejected arguments. */
 enum { ART_KERNEL_FULL = 0, ART_KERNEL_SCANNERS = 1, ART_KERNEL_LOOKBACK = 2, ART_KERNEL_WINDOWED = 3,
-       ART_KERNEL_STREAM = 4 };
+       ART_KERNEL_STREAM = 4, ART_KERNEL_SEGMENTS = 5 };
 int32_t art_decode_kernel_choice(const art_decode_desc* desc, float eps_mag, float eps_dir, int32_t patience);
 
 /* Re-read the tuning environment variables (ART_SCHED and the scheduler

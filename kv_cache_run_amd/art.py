@@ -33,6 +33,7 @@ EXPORTED = ("art_decode_workspace_bytes", "art_decode_workspace_init", "art_deco
             "art_importance_order_workspace_bytes", "art_importance_order", "art_check_inputs",
             "art_decode_reload_environment", "art_decode_noalloc", "art_decode_workspace_status")
 ART_KERNEL_FULL, ART_KERNEL_SCANNERS, ART_KERNEL_LOOKBACK, ART_KERNEL_WINDOWED, ART_KERNEL_STREAM = 0, 1, 2, 3, 4
+ART_KERNEL_SEGMENTS = 5
 ART_CHECK_OK, ART_CHECK_SEQ_LEN, ART_CHECK_ORDER_RANGE, ART_CHECK_ORDER_REPEAT, ART_CHECK_PAGE_RANGE = 0, 1, 2, 3, 4
 CHECK_NAMES = {ART_CHECK_SEQ_LEN: "sequence length outside [0, max_blocks * block_size]",
                ART_CHECK_ORDER_RANGE: "order entry outside [0, n_s)",
@@ -40,7 +41,7 @@ CHECK_NAMES = {ART_CHECK_SEQ_LEN: "sequence length outside [0, max_blocks * bloc
                ART_CHECK_PAGE_RANGE: "page outside [0, num_pages)"}
 KERNEL_NAMES = {ART_KERNEL_FULL: "full_split_kernel", ART_KERNEL_SCANNERS: "art_sched_kernel",
                 ART_KERNEL_LOOKBACK: "art_lb_kernel", ART_KERNEL_WINDOWED: "art_win_part_kernel",
-                ART_KERNEL_STREAM: "art_stream_kernel"}
+                ART_KERNEL_STREAM: "art_stream_kernel", ART_KERNEL_SEGMENTS: "art_seg_kernel"}
 
 
 class ArtDecodeDesc(ctypes.Structure):

@@ -66,15 +66,19 @@ art_status check_desc(const art_decode_desc* d) {
 // that needs them, and again whenever art_decode_reload_environment is
 // called; defaults when unset).  ART_SCHED selects the terminating kernel:
 // "stream" (one workgroup per stream: producer waves and detector waves
-// sharing an LDS ring), "scan" (one scanner workgroup per stream that folds
-// chunks in lock step, optional helpers), "lb" (the look-back scheduler),
-// "win" (the windowed scheduler) or "auto" (default): windows when the
-// streams are few (at most half the CUs) and long (at least 256 chunks),
-// where one workgroup per stream would leave most CUs idle for a long walk;
-// the stream kernel for groups of up to 4 query heads (one detector wave per
-// head); the look-back scheduler for larger groups with long streams (at
-// least 32 chunks); the stream kernel for groups of 5 to 8 heads otherwise,
-// scanners for larger groups.
+// sharing an LDS ring), "seg" (segments of a stream on many workgroups,
+// joined by decoupled look-back), "scan" (one scanner workgroup per stream
+// that folds chunks in lock step, optional helpers), "lb" (the look-back
+// scheduler), "win" (the windowed scheduler) or "auto" (default): for groups
+// of up to 8 query heads, segments when the streams are few (at most half
+// the CUs) and long (at least 256 chunks), where one workgroup per stream
+// would leave most CUs idle for a long walk, and for groups of 5 to 8 heads
+// with long streams (at least 32 chunks); the stream kernel otherwise.  For
+// larger groups: windows for few, long streams, the look-back scheduler for
+// long streams, scanners otherwise.
+// Segment kernel: ART_SEG_WIN (default 2) segments claimable past a stream's
+// resolved frontier, plus half the frontier; ART_SEG_WGS persistent
+// workgroups (0: one per CU).
 // Stream kernel: ART_LA0 and ART_LA_SHIFT set its lookahead, la0 +
 // (frontier >> la_shift) blocks (defaults 16 and 1).  Windowed:
 // ART_WIN_SPLIT fold workgroups per (stream, head) (1 .. 4; 0, the default:
@@ -96,9 +100,9 @@ int env_int(const char* name, int def, int lo, int hi) {
 }
 struct Knobs {
   int ring, lookahead, helpers, target, lb, window, workers, win_split, win_first, win_growth;
-  int la0, la_shift, spin_limit, full_wgs;
+  int la0, la_shift, spin_limit, full_wgs, seg_win, seg_wgs;
 };
-enum { SCHED_SCAN = 0, SCHED_LB = 1, SCHED_AUTO = 2, SCHED_WIN = 3, SCHED_STREAM = 4 };
+enum { SCHED_SCAN = 0, SCHED_LB = 1, SCHED_AUTO = 2, SCHED_WIN = 3, SCHED_STREAM = 4, SCHED_SEG = 5 };
 Knobs read_knobs() {
   const char* sched = getenv("ART_SCHED");
   int mode = SCHED_SCAN;
@@ -106,13 +110,15 @@ Knobs read_knobs() {
   else if (strcmp(sched, "lb") == 0) mode = SCHED_LB;
   else if (strcmp(sched, "win") == 0) mode = SCHED_WIN;
   else if (strcmp(sched, "stream") == 0) mode = SCHED_STREAM;
+  else if (strcmp(sched, "seg") == 0) mode = SCHED_SEG;
   const Knobs k = {env_int("ART_RING", 8, 1, 64),          env_int("ART_LOOKAHEAD", 3, 1, 64),
                    env_int("ART_HELPERS", 0, -1, 1 << 16), env_int("ART_TARGET_WGS", 512, 1, 1 << 16),
                    mode,                                    env_int("ART_WINDOW", 0, 0, 32),
                    env_int("ART_WORKERS", 0, 0, 1 << 20),       env_int("ART_WIN_SPLIT", 0, 0, art::art_win_split),
                    env_int("ART_WIN_FIRST", 0, 0, 64),          env_int("ART_WIN_GROWTH", 2, 2, 8),
                    env_int("ART_LA0", 16, 1, 1 << 20),          env_int("ART_LA_SHIFT", 1, 0, 30),
-                   env_int("ART_SPIN_LIMIT", 1 << 20, 1, 1 << 30), env_int("ART_FULL_WGS", 512, 1, 1 << 20)};
+                   env_int("ART_SPIN_LIMIT", 1 << 20, 1, 1 << 30), env_int("ART_FULL_WGS", 512, 1, 1 << 20),
+                   env_int("ART_SEG_WIN", 2, 1, 1 << 20),      env_int("ART_SEG_WGS", 0, 0, 1 << 20)};
   return k;
 }
 // The knobs in effect; guarded by a flag so that the environment is read once.
@@ -197,6 +203,8 @@ art::WorkspacePlan plan_workspace(const art_decode_desc* d) {
   }
   w.win_pass = off;
   off += round256(streams * (size_t)g * w.win_max * 4);
+  w.full_cnt = off;
+  off += round256(streams * 4);
   w.claim = off;
   off += round256(streams * 8);
   w.done = off;
@@ -221,7 +229,7 @@ art::WorkspacePlan plan_workspace(const art_decode_desc* d) {
 // counts up to 2047 and its claim sweep packs a stream index in 16 bits; the
 // windowed path carries the pass count as a float (exact to 2^24).  Either
 // falls back to the scanners outside those limits.
-enum Sched { SCHED_RUN_SCAN = 0, SCHED_RUN_LB = 1, SCHED_RUN_WIN = 2, SCHED_RUN_STREAM = 3 };
+enum Sched { SCHED_RUN_SCAN = 0, SCHED_RUN_LB = 1, SCHED_RUN_WIN = 2, SCHED_RUN_STREAM = 3, SCHED_RUN_SEG = 4 };
 Sched terminating_kernel(const art_decode_desc* d, const art::WorkspacePlan& wp, int32_t patience) {
   const Knobs& k = knobs();
   const long streams = (long)d->batch * d->num_kv_heads;
@@ -229,20 +237,26 @@ Sched terminating_kernel(const art_decode_desc* d, const art::WorkspacePlan& wp,
   int want = k.lb == SCHED_LB ? SCHED_RUN_LB
              : k.lb == SCHED_WIN ? SCHED_RUN_WIN
              : k.lb == SCHED_STREAM ? SCHED_RUN_STREAM
+             : k.lb == SCHED_SEG ? SCHED_RUN_SEG
                                     : SCHED_RUN_SCAN;
   if (k.lb == SCHED_AUTO) {
-    // few, long streams: windows; groups of up to 8 heads: the stream
-    // kernel; larger groups: look-back for long streams, else scanners
-    if (2 * streams <= cu_count() && wp.max_chunks >= 256)
-      want = SCHED_RUN_WIN;
-    else if (g <= 4)
-      want = SCHED_RUN_STREAM;
-    else if (wp.max_chunks >= 32)
-      want = SCHED_RUN_LB;
+    // groups of up to 8 heads: segments for few, long streams (at most half
+    // the CUs, at least 256 chunks) and for groups of more than 4 heads with
+    // long streams (at least 32 chunks), else the stream kernel; larger
+    // groups: windows for few, long streams, look-back for long streams,
+    // else scanners
+    const bool few_long = 2 * streams <= cu_count() && wp.max_chunks >= 256;
+    if (g <= 8 && (few_long || (g > 4 && wp.max_chunks >= 32)))
+      want = SCHED_RUN_SEG;
     else if (g <= 8)
       want = SCHED_RUN_STREAM;
+    else if (few_long)
+      want = SCHED_RUN_WIN;
+    else if (wp.max_chunks >= 32)
+      want = SCHED_RUN_LB;
   }
   if (want == SCHED_RUN_STREAM && g > 8) want = SCHED_RUN_SCAN;
+  if (want == SCHED_RUN_SEG && (g > 8 || patience > (1 << 26) - 1 || streams > 65535)) want = SCHED_RUN_SCAN;
   if (want == SCHED_RUN_LB && (patience > 2047 || streams > 65535)) want = SCHED_RUN_SCAN;
   if (want == SCHED_RUN_WIN && patience > (1 << 24)) want = SCHED_RUN_SCAN;
   return static_cast<Sched>(want);
@@ -330,9 +344,10 @@ art_status decode_impl(const art_decode_desc* desc, const void* q, const void* k
       const art::SplitPlan sp =
           art::full_split_plan(desc->batch, desc->num_kv_heads, desc->max_blocks_per_seq, knobs().full_wgs);
       if (sp.splits > 1) {
-        const size_t need = (size_t)desc->batch * desc->num_kv_heads * sp.splits * art::group_capacity(g) *
-                            (size_t)(desc->head_dim + 2) * sizeof(float);
-        if (need > art::noalloc_scratch_bytes()) return ART_ERR_WORKSPACE;
+        const size_t streams = (size_t)desc->batch * desc->num_kv_heads;
+        const size_t need = art::noalloc_part_offset() + streams * sp.splits * art::group_capacity(g) *
+                                                             (size_t)(desc->head_dim + 2) * sizeof(float);
+        if (streams > art::noalloc_max_streams() || need > art::noalloc_scratch_bytes()) return ART_ERR_WORKSPACE;
         if (art::noalloc_scratch(&workspace) != hipSuccess) return ART_ERR_HIP;
       }
     }
@@ -388,8 +403,11 @@ art_status decode_impl(const art_decode_desc* desc, const void* q, const void* k
     const art::SplitPlan sp = art::full_split_plan(desc->batch, desc->num_kv_heads, desc->max_blocks_per_seq, knobs().full_wgs);
     p.splits = sp.splits;
     p.split_blocks = sp.split_blocks;
-    if (sp.splits > 1)
-      p.ws_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + (noalloc ? 0 : wp.data));
+    if (sp.splits > 1) {
+      char* ws = static_cast<char*>(workspace);
+      p.ws_part = reinterpret_cast<float*>(ws + (noalloc ? art::noalloc_part_offset() : wp.data));
+      p.full_cnt = reinterpret_cast<uint32_t*>(ws + (noalloc ? 0 : wp.full_cnt));
+    }
     e = v.kv == art::KV_F32 ? art::launch_full_f32(v, p, static_cast<hipStream_t>(stream))
         : v.kv == art::KV_BF16 ? art::launch_full_bf16(v, p, static_cast<hipStream_t>(stream))
                                : art::launch_full_fp8(v, p, static_cast<hipStream_t>(stream));
@@ -422,6 +440,9 @@ art_status decode_impl(const art_decode_desc* desc, const void* q, const void* k
     if (noalloc) p.helpers = 0;
     p.lb = sched == SCHED_RUN_LB ? 1 : 0;
     p.stream2 = sched == SCHED_RUN_STREAM ? 1 : 0;
+    p.seg = sched == SCHED_RUN_SEG ? 1 : 0;
+    p.seg_win = knobs().seg_win;  // segments past the frontier: seg_win + frontier / 2
+    p.seg_wgs = knobs().seg_wgs > 0 ? knobs().seg_wgs : cu_count();
     p.la0 = knobs().la0;
     p.la_shift = knobs().la_shift;
     p.workers = knobs().workers;
@@ -590,6 +611,7 @@ int32_t art_decode_kernel_choice(const art_decode_desc* desc, float eps_mag, flo
     case SCHED_RUN_LB: return ART_KERNEL_LOOKBACK;
     case SCHED_RUN_WIN: return ART_KERNEL_WINDOWED;
     case SCHED_RUN_STREAM: return ART_KERNEL_STREAM;
+    case SCHED_RUN_SEG: return ART_KERNEL_SEGMENTS;
     default: return ART_KERNEL_SCANNERS;
   }
 }

@@ -38,6 +38,7 @@ struct Params {
   int32_t* stop_block;
   int32_t* blocks_fetched;  // may be null
   float* ws_part;           // full mode with splits: [streams][splits][GM][D + 2]
+  uint32_t* full_cnt;       // full mode with splits: [streams] slices finished (0 between calls)
   // ART scheduler (workspace): epoch-tagged control words and the ring of
   // partial-result slots helpers hand to scanners
   uint32_t* sched_ctrl;                // [0] stored epoch, [1] finished workgroups, [2] error flag, [3] epoch of a failed call
@@ -64,6 +65,9 @@ struct Params {
   int32_t window;                      // chunks claimable past the resolved frontier (1..32)
   int32_t lb;                          // 1: launch art_lb_kernel, 0: scanners (+ helpers)
   int32_t stream2;                     // 1: launch art_stream_kernel (one workgroup per stream)
+  int32_t seg;                         // 1: launch art_seg_kernel (segments of a stream on many workgroups)
+  int32_t seg_win;                     // segment kernel: segments claimable past a stream's resolved frontier
+  int32_t seg_wgs;                     // segment kernel: persistent workgroups
   int32_t la0, la_shift;               // stream kernel: lookahead la0 + (frontier >> la_shift) blocks
   int32_t workers;                     // art_lb_kernel workgroups (0: one per resident slot)
   // windowed path (art_win_kernel): per window, a launch in the partials
@@ -113,6 +117,7 @@ struct WorkspacePlan {
   size_t lb_fetch, lb_claim, lb_prog, lb_heads, lb_st;  // look-back scheduler
   size_t win_dead, win_dwin, win_state, win_pass, win_cnt;  // windowed path (its slots are in data)
   size_t claim, done, ready, data, total;               // scanner + helpers; data: ring | records | full partials
+  size_t full_cnt;                                      // full mode: per-stream count of finished slices
   int ring, slot_floats, helpers, lookahead, max_chunks, rec_floats, window, win_max, win_slot;
 };
 
@@ -128,6 +133,10 @@ hipError_t launch_full_fp8(const Variant& v, const Params& p, hipStream_t stream
 // Static scratch of art_decode_noalloc (kern_noalloc.hip): its size, and its
 // device address on the current device (looked up once per device).
 size_t noalloc_scratch_bytes();
+// Its layout: the full-mode slice counters [streams] at offset 0 (at most
+// noalloc_max_streams()), the split partials from noalloc_part_offset().
+constexpr size_t noalloc_part_offset() { return 64 << 10; }
+constexpr size_t noalloc_max_streams() { return noalloc_part_offset() / 4; }
 hipError_t noalloc_scratch(void** ptr);
 
 // Input-contract check (kern_check.hip).

@@ -32,7 +32,7 @@
 //  * full_split_kernel -- full attention (no detector).  Each workgroup owns
 //    a contiguous slice of one stream's blocks; each wave keeps its own
 //    online-softmax state with the next block's loads in flight; waves merge
-//    through LDS; slices are merged by full_merge_kernel (second launch).
+//    through LDS; the last slice of a stream to finish merges the slices.
 //
 // Data layout (HBM): k_pages/v_pages [page][kv_head][B][D], the (page, kvh)
 // tile contiguous, so one block of one stream is B*D*es contiguous bytes.
@@ -2678,83 +2678,81 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
       for (int j = 0; j < DPL; ++j) p.out[(head0 + h) * D + lane + 64 * j] = A[j] * rl;
       if (lane == 0) p.stop_block[head0 + h] = n;
     } else {
-      float* dst = p.ws_part + (((size_t)stream * p.splits + split) * GM + h) * (D + 2);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(p.ws_part + (((size_t)stream * p.splits + split) * GM + h) * (D + 2));
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) dst[lane + 64 * j] = A[j];
-      if (lane == 0) { dst[D] = M; dst[D + 1] = Ls; }
+      for (int j = 0; j < DPL; ++j) st_dev32(dst + lane + 64 * j, __float_as_uint(A[j]));
+      if (lane == 0) { st_dev32(dst + D, __float_as_uint(M)); st_dev32(dst + D + 1, __float_as_uint(Ls)); }
     }
   }
-  if (p.splits == 1 && threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[stream] = n;
-}
+  if (p.splits == 1) {
+    if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[stream] = n;
+    return;
+  }
 
-// Merge of the full-attention splits (a separate launch, so stream order
-// makes the partials visible without any device-scope fence).  One 64-lane
-// workgroup per (stream, query head): lanes first read the splits' (M, L) in
-// parallel and reduce the common maximum and the weights; then every lane
-// owns D/64 output elements and sums the weighted split numerators with
-// independent loads in flight.
-template <int D, int GM>
-__global__ __launch_bounds__(64) void full_merge_kernel(Params p) {
-  constexpr int DPL = D / 64;
-  const int lane = threadIdx.x;
-  const int g = p.g;
-  const int stream = blockIdx.x / g;
-  const int h = blockIdx.x - stream * g;
-  const int s = stream / p.hkv;
-  const int kvh = stream - s * p.hkv;
-  const int n = visit_count_b(p, s, p.seq_lens[s], p.block_size);
-  const size_t head = (size_t)s * p.hq + (size_t)kvh * g + h;
-  const size_t sstride = (size_t)GM * (D + 2);
-  const float* src = p.ws_part + ((size_t)stream * p.splits * GM + h) * (D + 2);
+  // The stream's last slice to finish merges all of them: every slice's
+  // partials are complete (device-coherent stores, waited for) before its
+  // count goes in; the slice that brings the count to `splits` resets it for
+  // the next call and folds the partials with device-coherent loads.
+  __shared__ int is_last;
+  wait_all_memory();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(p.full_cnt + stream, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = old == (uint32_t)(p.splits - 1) ? 1 : 0;
+    if (is_last) st_dev32(p.full_cnt + stream, 0u);
+  }
+  __syncthreads();
+  if (!is_last) return;
   const int S = p.splits;
-
-  // pass 1: common max over splits (lane-parallel, S may exceed 64)
-  float M = NEG_INF;
-  for (int sp = lane; sp < S; sp += 64) M = fmaxf(M, src[sp * sstride + D]);
-  M = rows_max(M);
-  M = fmaxf(M, dpp<DPP_ROW_MIRROR>(M));
-  M = fmaxf(M, dpp<DPP_HALF_MIRROR>(M));
-  M = fmaxf(M, dpp<DPP_XOR2>(M));
-  M = fmaxf(M, dpp<DPP_XOR1>(M));
-  // pass 2: weighted numerators; the weight of split sp is read by every lane
-  float Ls = 0.f;
-  float A[DPL];
+  const size_t sstride = (size_t)GM * (D + 2);
+  for (int h = w; h < g; h += NW) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(p.ws_part + ((size_t)stream * S * GM + h) * (D + 2));
+    // common maximum over the slices (lane-parallel, S may exceed 64)
+    float M = NEG_INF;
+    for (int sp = lane; sp < S; sp += 64) M = fmaxf(M, __uint_as_float(ld_dev32(src + sp * sstride + D)));
+    M = rows_max(M);
+    M = fmaxf(M, dpp<DPP_ROW_MIRROR>(M));
+    M = fmaxf(M, dpp<DPP_HALF_MIRROR>(M));
+    M = fmaxf(M, dpp<DPP_XOR2>(M));
+    M = fmaxf(M, dpp<DPP_XOR1>(M));
+    // weighted numerators: every lane owns D/64 output elements
+    float Ls = 0.f;
+    float A[DPL];
 #pragma unroll
-  for (int j = 0; j < DPL; ++j) A[j] = 0.f;
-  int sp = 0;
-  for (; sp + 8 <= S; sp += 8) {
-    float ms[8], ls[8], a[8][DPL];
+    for (int j = 0; j < DPL; ++j) A[j] = 0.f;
+    int sp = 0;
+    for (; sp + 4 <= S; sp += 4) {
+      float ms[4], ls[4], a[4][DPL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float* q = src + (size_t)(sp + u) * sstride;
-      ms[u] = q[D];
-      ls[u] = q[D + 1];
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t* q = src + (size_t)(sp + u) * sstride;
+        ms[u] = __uint_as_float(ld_dev32(q + D));
+        ls[u] = __uint_as_float(ld_dev32(q + D + 1));
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) a[u][j] = q[lane + 64 * j];
+        for (int j = 0; j < DPL; ++j) a[u][j] = __uint_as_float(ld_dev32(q + lane + 64 * j));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float f = (ms[u] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - M);
+        Ls = fmaf(f, ls[u], Ls);
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) A[j] = fmaf(f, a[u][j], A[j]);
+      }
     }
+    for (; sp < S; ++sp) {
+      const uint32_t* q = src + (size_t)sp * sstride;
+      const float ms = __uint_as_float(ld_dev32(q + D));
+      const float f = (ms == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+      Ls = fmaf(f, __uint_as_float(ld_dev32(q + D + 1)), Ls);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float f = (ms[u] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - M);
-      Ls = fmaf(f, ls[u], Ls);
-#pragma unroll
-      for (int j = 0; j < DPL; ++j) A[j] = fmaf(f, a[u][j], A[j]);
+      for (int j = 0; j < DPL; ++j) A[j] = fmaf(f, __uint_as_float(ld_dev32(q + lane + 64 * j)), A[j]);
     }
-  }
-  for (; sp < S; ++sp) {
-    const float* q = src + (size_t)sp * sstride;
-    const float ms = q[D];
-    const float f = (ms == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    Ls = fmaf(f, q[D + 1], Ls);
+    const float rl = Ls > 0.f ? 1.0f / Ls : 0.f;
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) A[j] = fmaf(f, q[lane + 64 * j], A[j]);
+    for (int j = 0; j < DPL; ++j) p.out[(head0 + h) * D + lane + 64 * j] = A[j] * rl;
+    if (lane == 0) p.stop_block[head0 + h] = n;
   }
-  const float rl = Ls > 0.f ? 1.0f / Ls : 0.f;
-#pragma unroll
-  for (int j = 0; j < DPL; ++j) p.out[head * D + lane + 64 * j] = A[j] * rl;
-  if (lane == 0) {
-    p.stop_block[head] = n;
-    if (h == 0 && p.blocks_fetched) p.blocks_fetched[stream] = n;
-  }
+  if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[stream] = n;
 }
 
 }  // namespace kern

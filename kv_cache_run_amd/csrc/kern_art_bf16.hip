@@ -2,6 +2,7 @@
 // storage type and kernel so that the build runs in parallel).
 #include "art_kernels_impl.h"
 #include "art_stream.h"
+#include "art_seg.h"
 
 namespace art {
 namespace {
@@ -25,6 +26,14 @@ int resident_slots(K kernel, int threads) {
 template <int D, int B, int GM>
 hipError_t go(const Params& p, hipStream_t st) {
   constexpr int threads = 64 * kern::Cfg<KV_BF16, D, B, GM>::NWA;
+  if (p.seg) {
+    if constexpr (GM <= 8) {
+      hipLaunchKernelGGL((kern::art_seg_kernel<KV_BF16, D, B, GM>), dim3((unsigned)p.seg_wgs),
+                         dim3(64 * kern::SegCfg<KV_BF16, D, B, GM>::NW3), 0, st, p);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   if (p.stream2) {
     if constexpr (GM <= 8) {
       hipLaunchKernelGGL((kern::art_stream_kernel<KV_BF16, D, B, GM>), dim3(p.batch * p.hkv),

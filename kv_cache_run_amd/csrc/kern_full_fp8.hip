@@ -1,4 +1,4 @@
-// Instantiations of full_split_kernel (+ full_merge_kernel) for KV storage FP8 (one translation unit per
+// Instantiations of full_split_kernel for KV storage FP8 (one translation unit per
 // storage type and kernel so that the build runs in parallel).
 #include "art_kernels_impl.h"
 
@@ -8,9 +8,6 @@ namespace {
 template <int D, int B, int GM>
 hipError_t go(const Params& p, hipStream_t st) {
   hipLaunchKernelGGL((kern::full_split_kernel<KV_FP8, D, B, GM>), dim3(p.batch * p.hkv * p.splits), dim3(kern::WG), 0, st, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL((kern::full_merge_kernel<D, GM>), dim3(p.batch * p.hkv * p.g), dim3(64), 0, st, p);
   return hipGetLastError();
 }
 

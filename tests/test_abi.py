@@ -118,12 +118,12 @@ def test_kernel_choice_follows_the_knob_and_the_mode(lib, env):
     long_desc = _desc(batch=4, num_q_heads=64, num_kv_heads=8, block_size=32, max_blocks_per_seq=4096)
     qwen_desc = _desc(batch=64, num_q_heads=28, num_kv_heads=4, max_blocks_per_seq=1024,
                       kv_dtype=art.ART_DTYPE_FP8_E4M3FN)
-    # auto (no device here: 256 CUs assumed): few long streams -> windows, groups of up to 4 heads -> the
-    # stream kernel, larger groups -> look-back for long streams, else the stream kernel (up to 8 heads) or
-    # scanners
+    # auto (no device here: 256 CUs assumed), groups of up to 8 heads: segments for few long streams and for
+    # groups of more than 4 heads with long streams, else the stream kernel; larger groups: windows for few
+    # long streams, look-back for long streams, else scanners
     env.unset("ART_SCHED")
-    assert art.art_decode_kernel_choice(long_desc, 5e-4, 5e-5, 6) == art.ART_KERNEL_WINDOWED
-    assert art.art_decode_kernel_choice(qwen_desc, 1e-3, 1e-4, 4) == art.ART_KERNEL_LOOKBACK
+    assert art.art_decode_kernel_choice(long_desc, 5e-4, 5e-5, 6) == art.ART_KERNEL_SEGMENTS
+    assert art.art_decode_kernel_choice(qwen_desc, 1e-3, 1e-4, 4) == art.ART_KERNEL_SEGMENTS
     assert art.art_decode_kernel_choice(_desc(num_q_heads=56, max_blocks_per_seq=64), 1e-3, 1e-4, 4) == \
         art.ART_KERNEL_STREAM
     assert art.art_decode_kernel_choice(_desc(), 1e-3, 1e-4, 4) == art.ART_KERNEL_STREAM
@@ -131,7 +131,14 @@ def test_kernel_choice_follows_the_knob_and_the_mode(lib, env):
         art.ART_KERNEL_LOOKBACK
     assert art.art_decode_kernel_choice(_desc(num_q_heads=128, max_blocks_per_seq=16), 1e-3, 1e-4, 4) == \
         art.ART_KERNEL_SCANNERS
-    assert art.art_decode_kernel_choice(_desc(max_blocks_per_seq=8192), 1e-3, 1e-4, 4) == art.ART_KERNEL_WINDOWED
+    assert art.art_decode_kernel_choice(_desc(max_blocks_per_seq=8192), 1e-3, 1e-4, 4) == art.ART_KERNEL_SEGMENTS
+    assert art.art_decode_kernel_choice(_desc(num_q_heads=128, max_blocks_per_seq=8192), 1e-3, 1e-4, 4) == \
+        art.ART_KERNEL_WINDOWED
+    env.set("ART_SCHED", "seg")
+    assert art.art_decode_kernel_choice(_desc(), 1e-3, 1e-4, 4) == art.ART_KERNEL_SEGMENTS
+    # groups of more than 8 heads, or pass counts past what its status words hold: scanners
+    assert art.art_decode_kernel_choice(_desc(num_q_heads=128), 1e-3, 1e-4, 4) == art.ART_KERNEL_SCANNERS
+    assert art.art_decode_kernel_choice(_desc(), 1e-3, 1e-4, 1 << 26) == art.ART_KERNEL_SCANNERS
     env.set("ART_SCHED", "stream")
     assert art.art_decode_kernel_choice(long_desc, 1e-3, 1e-4, 4) == art.ART_KERNEL_STREAM
     # groups of more than 8 heads: the stream kernel takes none, scanners instead

@@ -263,6 +263,15 @@ STREAM_VARIANTS = [
 ]
 
 
+SEG_VARIANTS = [
+    dict(ART_SCHED="seg"),                                    # defaults: two segments past the frontier + half of it
+    dict(ART_SCHED="seg", ART_SEG_WIN="1"),                   # the smallest window
+    dict(ART_SCHED="seg", ART_SEG_WIN="64"),                  # every segment at once
+    dict(ART_SCHED="seg", ART_SEG_WGS="7"),                   # few workgroups: long queues of items each
+    dict(ART_SCHED="seg", ART_SEG_WGS="1000"),                # more workgroups than CUs
+]
+
+
 WIN_VARIANTS = [
     dict(ART_SCHED="win"),                                    # default: two fold workgroups when heads are few
     dict(ART_SCHED="win", ART_WIN_SPLIT="1"),                 # one fold workgroup per (stream, head)
@@ -298,8 +307,8 @@ SCHED_CASES = [(W.LLAMA3_8B, dict(batch=3, context=8192 - 40)), (W.RAGGED, dict(
                (W.QWEN_FP8, dict(batch=2, context=16384 - 3)), (W.LONG, dict(batch=1, context=131072 - 17))]
 
 
-@pytest.mark.parametrize("variants", [LB_VARIANTS, SCAN_VARIANTS, WIN_VARIANTS, STREAM_VARIANTS],
-                         ids=["lookback", "scanners", "windowed", "stream"])
+@pytest.mark.parametrize("variants", [LB_VARIANTS, SCAN_VARIANTS, WIN_VARIANTS, STREAM_VARIANTS, SEG_VARIANTS],
+                         ids=["lookback", "scanners", "windowed", "stream", "segments"])
 @pytest.mark.parametrize("w,kw", SCHED_CASES, ids=["llama", "ragged", "fp8", "long"])
 def test_scheduler_variants_bit_identical(w, kw, variants):
     case = synth.make_case(w, **kw)
@@ -374,7 +383,7 @@ def test_scheduler_epoch_advances_and_no_error():
 # ART_SCHED=auto sends only few, long streams to the look-back kernel; these run the shape corners and the
 # edge cases through it explicitly.
 
-@pytest.mark.parametrize("sched", ["lb", "win", "stream", "scan"])
+@pytest.mark.parametrize("sched", ["lb", "win", "stream", "seg", "scan"])
 @pytest.mark.parametrize("w", SHAPES, ids=[w.name for w in SHAPES])
 def test_lookback_and_windowed_shape_matrix(w, sched):
     case = synth.make_case(w, batch=2, context=2000 + 9)
@@ -383,8 +392,9 @@ def test_lookback_and_windowed_shape_matrix(w, sched):
 
 
 @pytest.mark.parametrize("env", [dict(ART_SCHED="lb", ART_WINDOW="2"), dict(ART_SCHED="win", ART_WIN_SPLIT="2"),
-                                 dict(ART_SCHED="stream", ART_LA0="1", ART_LA_SHIFT="30"), dict(ART_SCHED="scan")],
-                         ids=["lookback", "windowed", "stream", "scanners"])
+                                 dict(ART_SCHED="stream", ART_LA0="1", ART_LA_SHIFT="30"), dict(ART_SCHED="scan"),
+                                 dict(ART_SCHED="seg", ART_SEG_WIN="1")],
+                         ids=["lookback", "windowed", "stream", "scanners", "segments"])
 def test_lookback_and_windowed_edge_cases(env):
     base = synth.make_case(W.LLAMA3_8B, batch=5, context=700)
     case = _with_lens(base, [0, 1, 15, 16, 17])
@@ -420,7 +430,8 @@ def test_lookback_and_windowed_edge_cases(env):
         assert _with_env(env, lambda: art.art_decode_kernel_choice(desc, 1e-3, 1e-4, 3000)) == art.ART_KERNEL_SCANNERS
         assert _with_env(env, lambda: art.art_decode_kernel_choice(desc, 1e-3, 1e-4, 30)) == art.ART_KERNEL_LOOKBACK
     else:
-        want = {"win": art.ART_KERNEL_WINDOWED, "stream": art.ART_KERNEL_STREAM, "scan": art.ART_KERNEL_SCANNERS}
+        want = {"win": art.ART_KERNEL_WINDOWED, "stream": art.ART_KERNEL_STREAM, "scan": art.ART_KERNEL_SCANNERS,
+                "seg": art.ART_KERNEL_SEGMENTS}
         assert _with_env(env, lambda: art.art_decode_kernel_choice(desc, 1e-3, 1e-4, 3000)) == want[env["ART_SCHED"]]
 
 
@@ -438,7 +449,7 @@ def test_ablation_variants_parity(w, variant):
     check_art(case, eps_mag=em, eps_dir=ed, patience=p)
 
 
-@pytest.mark.parametrize("sched", ["lb", "win", "stream"])
+@pytest.mark.parametrize("sched", ["lb", "win", "stream", "seg"])
 def test_ablation_through_lookback_and_windowed(sched):
     case = synth.make_case(W.VALUE_HEAVY, batch=2, context=4096 - 5)
     _with_env(dict(ART_SCHED=sched), lambda: check_art(case, eps_dir=math.inf))
@@ -469,7 +480,7 @@ def _pruned_case():
     return case
 
 
-@pytest.mark.parametrize("sched", ["scan", "lb", "win", "stream"])
+@pytest.mark.parametrize("sched", ["scan", "lb", "win", "stream", "seg"])
 def test_pruned_cache_parity(sched):
     case = _pruned_case()
     print(f"[pruned] {sched}", flush=True)
@@ -494,7 +505,7 @@ def test_pruned_cache_full_attention():
 
 # ---- probe-vector detector: the statistics over the leading P output coordinates -------------------------
 
-@pytest.mark.parametrize("sched", ["scan", "lb", "win", "stream"])
+@pytest.mark.parametrize("sched", ["scan", "lb", "win", "stream", "seg"])
 @pytest.mark.parametrize("w,P", [(W.LLAMA3_8B, 8), (W.LLAMA3_8B, 32), (W.LLAMA3_8B, 64), (W.TINY, 16)],
                          ids=["llama-P8", "llama-P32", "llama-P64", "tiny-P16"])
 def test_probe_vector_parity(w, P, sched):
@@ -563,7 +574,7 @@ def test_importance_order_with_equal_scores_is_recency_first():
         assert list(order[s, :n]) == [0] + list(range(n - 1, 0, -1))
 
 
-@pytest.mark.parametrize("sched", ["scan", "lb", "win", "stream"])
+@pytest.mark.parametrize("sched", ["scan", "lb", "win", "stream", "seg"])
 def test_art_on_the_importance_order(sched):
     case = synth.make_case(W.LLAMA3_8B, batch=3, context=3000 - 5)
     _, order = _device_order(case)
@@ -579,7 +590,7 @@ def test_skip_statistics_flag_gives_full_attention_in_every_scheduler():
     case = synth.make_case(W.LLAMA3_8B, batch=2, context=1500)
     ref = _device_run(case, 0.0, 0.0, 4, flags=art.ART_FLAG_KEEP_DETECTOR)
     n = _nblocks(case)
-    for sched in ("scan", "lb", "win", "stream"):
+    for sched in ("scan", "lb", "win", "stream", "seg"):
         out, stop, fetched = _with_env(dict(ART_SCHED=sched),
                                        lambda: _device_run(case, 1e-3, 1e-4, 4, flags=art.ART_FLAG_SKIP_STATS))
         assert np.all(stop == n[:, None]), sched
@@ -644,7 +655,7 @@ def _random_case(seed):
     em = float(10 ** rng.uniform(-4, -1))
     ed = float(10 ** rng.uniform(-5, -2))
     p = int(rng.integers(1, 7))
-    sched = str(rng.choice(["scan", "lb", "win", "auto", "stream"]))
+    sched = str(rng.choice(["scan", "lb", "win", "auto", "stream", "seg"]))
     return case, em, ed, p, sched
 
 
@@ -776,7 +787,7 @@ def test_decoder_checks_inputs_when_asked():
 
 
 @pytest.mark.parametrize("w", [W.LLAMA3_8B, W.QWEN_FP8], ids=["bf16", "fp8"])
-@pytest.mark.parametrize("sched", ["scan", "lb", "win", "stream", "full"])
+@pytest.mark.parametrize("sched", ["scan", "lb", "win", "stream", "seg", "full"])
 def test_pages_past_4_gib(sched, w):
     """Page addressing is 64-bit: the same pages (and fp8 scales) placed past 4 GiB of K and of V (a pool
     of ≈4.3 GiB each) give the same bits as at low page ids, for each ART scheduler and for full attention."""
@@ -823,7 +834,7 @@ def test_pages_past_4_gib(sched, w):
 # ---- bounded waits that give up: forced from the host with the smallest spin limit -----------------------
 
 
-@pytest.mark.parametrize("sched", ["lb", "stream", "scan-helpers"])
+@pytest.mark.parametrize("sched", ["lb", "stream", "seg", "scan-helpers"])
 def test_bounded_waits_that_give_up_are_reported(sched):
     """ART_SPIN_LIMIT=1 (two polls) makes waits between workgroups or waves give up; every wait is bounded, so
     every kernel still exits.  A head whose result a give-up touched reads stop -1 or NaN output
@@ -832,6 +843,7 @@ def test_bounded_waits_that_give_up_are_reported(sched):
     from kv_cache_run_amd import art
 
     env = {"lb": dict(ART_SCHED="lb", ART_SPIN_LIMIT="1"), "stream": dict(ART_SCHED="stream", ART_SPIN_LIMIT="1"),
+           "seg": dict(ART_SCHED="seg", ART_SPIN_LIMIT="1"),
            "scan-helpers": dict(ART_SCHED="scan", ART_HELPERS="256", ART_SPIN_LIMIT="1")}[sched]
     case = synth.make_case(W.RAGGED, batch=4)
 
