@@ -227,7 +227,7 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
  * art_decode without a workspace, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  The library itself allocates nothing either: full
- * attention's per-split partial results and per-stream slice counters (the
+ * attention's per-piece partial results and per-stream piece counters (the
  * only scratch this entry point uses) go to a static 8 MiB device array that
  * every device holds until the process ends; its device address is looked up
  * once per device, with that device current, at the first call there.  ART mode runs the kernels that
@@ -237,15 +237,16 @@ art_status art_decode_visits(const art_decode_desc* desc, const void* q, const v
  * (respectively scan with ART_HELPERS=0), bit for bit; full attention gives
  * art_decode's full-attention bits.
  * The static array is shared by every call on a device and keeps the last
- * call's contents: the slice counters start at zero when the library is
+ * call's contents: the piece counters start at zero when the library is
  * loaded and every full-attention call leaves them at zero; the partials need
  * no clearing.  Calls that overlap in time on one device race, whatever their
  * streams.
- * Errors: as art_decode; ART_ERR_WORKSPACE when full attention splits the
- * streams' blocks and either the streams (batch x Hkv) pass 16384 or 64 KiB of
- * counters plus the partials (streams x splits x GM x (D + 2) floats, GM = g
- * rounded up to 4, 8 or 16) pass 8 MiB -- use art_decode then; ART_ERR_HIP
- * when the array's address cannot be looked up or a launch fails.
+ * Errors: as art_decode; ART_ERR_WORKSPACE in full-attention mode when the
+ * streams (batch x Hkv) pass 16384 or 64 KiB of counters plus the partials
+ * ((streams + workgroups) x GM x (D + 2) floats, GM = g rounded up to 4, 8
+ * or 16, workgroups = ART_FULL_WGS, default 256, 512 for fp8 KV) pass 8 MiB -- use
+ * art_decode then; ART_ERR_HIP when the array's address cannot be looked up
+ * or a launch fails.
  */
 art_status art_decode_noalloc(const art_decode_desc* desc, const void* q, const void* k_pages, const void* v_pages,
                               const float* k_scale, const float* v_scale, const int32_t* block_table,

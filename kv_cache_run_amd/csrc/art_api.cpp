@@ -10,25 +10,6 @@
 
 namespace art {
 
-SplitPlan full_split_plan(int batch, int hkv, int max_blocks, int target) {
-  const long streams = (long)batch * hkv;
-  // about two workgroups per CU on 256 CUs (measured against 256 … 3072:
-  // fewer, longer slices avoid a tail of partly filled CUs and shrink the
-  // merge); ART_FULL_WGS overrides
-  const long target_wgs = target;
-  long splits = streams > 0 ? (target_wgs + streams - 1) / streams : 1;
-  const long by_len = (max_blocks + 7) / 8;  // at least 8 blocks (2 per wave) per split
-  if (splits > by_len) splits = by_len;
-  if (splits < 1) splits = 1;
-  long per = (max_blocks + splits - 1) / splits;
-  per = (per + 3) / 4 * 4;
-  if (per < 4) per = 4;
-  if (per > 256) per = 256;  // at most 64 blocks per wave (one lane-held page table)
-  splits = (max_blocks + per - 1) / per;
-  if (splits < 1) splits = 1;
-  return SplitPlan{(int)splits, (int)per};
-}
-
 }  // namespace art
 
 namespace {
@@ -117,7 +98,7 @@ Knobs read_knobs() {
                    env_int("ART_WORKERS", 0, 0, 1 << 20),       env_int("ART_WIN_SPLIT", 0, 0, art::art_win_split),
                    env_int("ART_WIN_FIRST", 0, 0, 64),          env_int("ART_WIN_GROWTH", 2, 2, 8),
                    env_int("ART_LA0", 16, 1, 1 << 20),          env_int("ART_LA_SHIFT", 1, 0, 30),
-                   env_int("ART_SPIN_LIMIT", 1 << 20, 1, 1 << 30), env_int("ART_FULL_WGS", 512, 1, 1 << 20),
+                   env_int("ART_SPIN_LIMIT", 1 << 20, 1, 1 << 30), env_int("ART_FULL_WGS", 0, 0, 1 << 20),
                    env_int("ART_SEG_WIN", 2, 1, 1 << 20),      env_int("ART_SEG_WGS", 0, 0, 1 << 20)};
   return k;
 }
@@ -145,6 +126,16 @@ int cu_count() {
 }
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workgroups of the full-attention kernel: ART_FULL_WGS, else 256 (one per
+// CU: measured fastest for bf16 on the Llama-3-8B, ragged and 128k shapes)
+// and 512 for fp8 KV (two per CU: its block math needs the second wave per
+// SIMD to keep the loads flowing).  Fixed per descriptor, so that the
+// workspace size needs no device query.
+int full_wgs(const art_decode_desc* d) {
+  const int k = knobs().full_wgs;
+  return k > 0 ? k : (d->kv_dtype == ART_DTYPE_FP8_E4M3FN ? 512 : 256);
+}
 
 art::WorkspacePlan plan_workspace(const art_decode_desc* d) {
   art::WorkspacePlan w;
@@ -214,8 +205,7 @@ art::WorkspacePlan plan_workspace(const art_decode_desc* d) {
   w.data = off;
   const size_t ring_bytes = streams * (size_t)w.ring * w.slot_floats * sizeof(float);
   const size_t rec_bytes = streams * (size_t)max_chunks * g * w.rec_floats * sizeof(float);
-  const art::SplitPlan sp = art::full_split_plan(d->batch, d->num_kv_heads, d->max_blocks_per_seq, knobs().full_wgs);
-  const size_t part = sp.splits > 1 ? streams * sp.splits * gm * (size_t)(d->head_dim + 2) * sizeof(float) : 0;
+  const size_t part = art::full_part_floats((long)streams, full_wgs(d), gm, d->head_dim) * sizeof(float);
   size_t data = ring_bytes > part ? ring_bytes : part;
   if (rec_bytes > data) data = rec_bytes;
   const size_t win_bytes = streams * (size_t)w.win_max * w.win_slot * sizeof(float);
@@ -338,18 +328,15 @@ art_status decode_impl(const art_decode_desc* desc, const void* q, const void* k
   const bool full = full_mode(desc, eps_mag, eps_dir);
   const int g = desc->num_q_heads / desc->num_kv_heads;
   if (noalloc) {
-    // full attention's split partials are the only scratch this call uses
+    // full attention's piece partials and counters are the only scratch this call uses
     workspace = nullptr;
     if (full && desc->batch > 0) {
-      const art::SplitPlan sp =
-          art::full_split_plan(desc->batch, desc->num_kv_heads, desc->max_blocks_per_seq, knobs().full_wgs);
-      if (sp.splits > 1) {
-        const size_t streams = (size_t)desc->batch * desc->num_kv_heads;
-        const size_t need = art::noalloc_part_offset() + streams * sp.splits * art::group_capacity(g) *
-                                                             (size_t)(desc->head_dim + 2) * sizeof(float);
-        if (streams > art::noalloc_max_streams() || need > art::noalloc_scratch_bytes()) return ART_ERR_WORKSPACE;
-        if (art::noalloc_scratch(&workspace) != hipSuccess) return ART_ERR_HIP;
-      }
+      const size_t streams = (size_t)desc->batch * desc->num_kv_heads;
+      const size_t need = art::noalloc_part_offset() +
+                          art::full_part_floats((long)streams, full_wgs(desc), art::group_capacity(g), desc->head_dim) *
+                              sizeof(float);
+      if (streams > art::noalloc_max_streams() || need > art::noalloc_scratch_bytes()) return ART_ERR_WORKSPACE;
+      if (art::noalloc_scratch(&workspace) != hipSuccess) return ART_ERR_HIP;
     }
   } else if (wp.total > 0) {
     if (!workspace || workspace_bytes < wp.total) return ART_ERR_WORKSPACE;
@@ -400,20 +387,15 @@ art_status decode_impl(const art_decode_desc* desc, const void* q, const void* k
 
   hipError_t e;
   if (full) {
-    const art::SplitPlan sp = art::full_split_plan(desc->batch, desc->num_kv_heads, desc->max_blocks_per_seq, knobs().full_wgs);
-    p.splits = sp.splits;
-    p.split_blocks = sp.split_blocks;
-    if (sp.splits > 1) {
-      char* ws = static_cast<char*>(workspace);
-      p.ws_part = reinterpret_cast<float*>(ws + (noalloc ? art::noalloc_part_offset() : wp.data));
-      p.full_cnt = reinterpret_cast<uint32_t*>(ws + (noalloc ? 0 : wp.full_cnt));
-    }
+    p.splits = full_wgs(desc);
+    char* ws = static_cast<char*>(workspace);
+    p.ws_part = reinterpret_cast<float*>(ws + (noalloc ? art::noalloc_part_offset() : wp.data));
+    p.full_cnt = reinterpret_cast<uint32_t*>(ws + (noalloc ? 0 : wp.full_cnt));
     e = v.kv == art::KV_F32 ? art::launch_full_f32(v, p, static_cast<hipStream_t>(stream))
         : v.kv == art::KV_BF16 ? art::launch_full_bf16(v, p, static_cast<hipStream_t>(stream))
                                : art::launch_full_fp8(v, p, static_cast<hipStream_t>(stream));
   } else {
     p.splits = 1;
-    p.split_blocks = desc->max_blocks_per_seq;
     // no-alloc calls (no workspace) run kernels that touch none of its regions: null views
     char* ws = static_cast<char*>(workspace);
     auto at = [&](size_t off) { return ws ? ws + off : nullptr; };

@@ -37,8 +37,8 @@ struct Params {
   float* out;
   int32_t* stop_block;
   int32_t* blocks_fetched;  // may be null
-  float* ws_part;           // full mode with splits: [streams][splits][GM][D + 2]
-  uint32_t* full_cnt;       // full mode with splits: [streams] slices finished (0 between calls)
+  float* ws_part;           // full mode: piece partials [streams + workgroups][GM][D + 2]
+  uint32_t* full_cnt;       // full mode: [streams] pieces finished (0 between calls)
   // ART scheduler (workspace): epoch-tagged control words and the ring of
   // partial-result slots helpers hand to scanners
   uint32_t* sched_ctrl;                // [0] stored epoch, [1] finished workgroups, [2] error flag, [3] epoch of a failed call
@@ -86,8 +86,7 @@ struct Params {
   int32_t batch, hq, hkv, g;
   int32_t block_size;
   int32_t max_blocks;
-  int32_t splits;           // full mode: splits per stream (1 = no merge)
-  int32_t split_blocks;     // full mode: blocks per split
+  int32_t splits;           // full mode: workgroups over the flattened blocks
   float eps_mag, eps_dir;
   int32_t patience;
   int32_t probe;            // the detector's statistics use coordinates [0, probe) of O (D: all)
@@ -106,11 +105,9 @@ struct Variant {
 inline int group_capacity(int g) { return g <= 4 ? 4 : (g <= 8 ? 8 : 16); }
 
 // Full-attention split plan (depends only on the descriptor).
-struct SplitPlan {
-  int splits;
-  int split_blocks;
-};
-SplitPlan full_split_plan(int batch, int hkv, int max_blocks, int target_wgs);
+// Full attention's partials: one slot per (stream, workgroup) piece, at most
+// streams + workgroups of them.
+inline size_t full_part_floats(long streams, int wgs, int gm, int d) { return (size_t)(streams + wgs) * gm * (d + 2); }
 
 // Workspace layout (bytes from the workspace base, each region 256-B aligned).
 struct WorkspacePlan {

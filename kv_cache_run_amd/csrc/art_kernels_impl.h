@@ -123,6 +123,13 @@ struct Cfg {
   static constexpr int CH = EPL >= 4 ? 1 : 2;         // independent accumulator chains
   static constexpr int VN = B * R / 256;              // V dwords per lane per block (either layout)
   static constexpr int NACC = PV4 ? HG * CH * EPL : DT;
+  // Full attention with fp8 V: P V on v_mfma_f32_16x16x16_bf16 instead of
+  // the fp32 4x4x1 product (fp8 values are exact in bf16; P goes in as two
+  // bf16 parts, hi + lo, so the products keep about 16 bits of P), with V
+  // transposed through a per-wave LDS buffer [D][VTS] of bf16.
+  static constexpr bool PVB = KV == KV_FP8 && PV4 && D == 128;
+  static constexpr int NACCF = PVB ? D / 16 : NACC;   // accumulators of the full-attention kernel
+  static constexpr int VTS = B + 2;                   // bf16 per d-row of V^T (an odd number of dwords)
   static_assert(BPB * NBW == C && HWV <= NWA, "one block wave per block of a chunk");
   static_assert(!PV4 || NLD % 4 == 0, "P is read four tokens at a time");
   static_assert(2 * C <= 64, "stat reduction holds at most 64 values");
@@ -249,14 +256,14 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float (&o)[4]) {
   o[0] = a.x; o[1] = a.y; o[2] = b.x; o[3] = b.y;
 }
 
-// 4 fp8 bytes -> 2 dwords of packed bf16 (exact: E4M3 values fit bf16).
+// 4 fp8 bytes -> 2 dwords of packed bf16 (exact: E4M3 values fit bf16), one
+// v_cvt_scalef32_pk_bf16_fp8 per pair with unit scale (checked bit for bit
+// against converting through f32 and truncating, for every byte value).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
-  float f[4];
-  fp8x4_to_f32(w, f);
-  uint2 r;
-  r.x = (__float_as_uint(f[1]) & 0xffff0000u) | (__float_as_uint(f[0]) >> 16);
-  r.y = (__float_as_uint(f[3]) & 0xffff0000u) | (__float_as_uint(f[2]) >> 16);
-  return r;
+  const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
 // One KV load of 16, 8 or 4 bytes; NT: non-temporal (streamed past the
@@ -2523,10 +2530,71 @@ __global__ __launch_bounds__(64 * WNW) void art_win_scan_kernel(Params p) {
 // ---------------------------------------------------------------------------
 // Full-attention split kernel
 // ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// fp8 V of one block, transposed into this wave's LDS buffer vt[d][token]
+// as bf16.  Lane l holds token row 2u + l / 32, elements d0 .. d0 + 3 with
+// d0 = 4 (l % 32), of load u; one lane swap pairs rows 2u and 2u + 1, so
+// every store writes two tokens of one d.
+template <class Cf>
+__device__ __forceinline__ void vt_store_fp8(const BlockRegs<Cf>& r, uint32_t* vt, int lane) {
+  static_assert(Cf::RPL == 2 && Cf::VW == 1, "fp8 rows of 128 bytes: two rows per load, one dword per lane");
+  constexpr int VTW = Cf::VTS / 2;  // dwords per d-row
+  const int da = 4 * (lane & 31) + (lane >= 32 ? 2 : 0);
+#pragma unroll
+  for (int u = 0; u < Cf::NLD; ++u) {
+    const uint2 bb = fp8x4_to_bf16x4(r.v[u]);
+    float x = bitsf(bb.x), y = bitsf(bb.y);
+    // lanes < 32: x = (row 2u: d0, d0+1), y <- (row 2u+1: d0, d0+1) of lane + 32;
+    // lanes >= 32: x <- (row 2u: d0+2, d0+3) of lane - 32, y = (row 2u+1: d0+2, d0+3)
+    swap32(x, y);
+    const uint32_t X = fbits(x), Y = fbits(y);
+    vt[da * VTW + u] = (X & 0xffffu) | (Y << 16);
+    vt[(da + 1) * VTW + u] = (X >> 16) | (Y & 0xffff0000u);
+  }
+}
+
+// P V for one block on bf16 MFMA: acc[j] (d-tile j, 16 d) holds, in lane
+// (c, q) component i, head c at d = 16 j + 4 q + i.  A = V^T tile (lane: d =
+// 16 j + c, tokens 4q .. 4q+3 from vt), B = P^T (lane: head c, tokens 4q ..
+// 4q+3: the score layout itself), P split into bf16 hi + lo (truncation: P =
+// hi + lo + O(2^-16 P)).
+template <class Cf>
+__device__ __forceinline__ void pvb_block(const BlockRegs<Cf>& r, const float (&pq)[Cf::T][4], uint32_t* vt, int lane,
+                                          f32x4 (&acc)[Cf::NACCF]) {
+  constexpr int VTW = Cf::VTS / 2;
+  vt_store_fp8<Cf>(r, vt, lane);
+  const int c = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < Cf::T; ++t) {
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t b = fbits(pq[t][i]);
+      hi[i] = b & 0xffff0000u;
+      lo[i] = fbits(pq[t][i] - bitsf(hi[i])) & 0xffff0000u;
+    }
+    s16x4 ph, pl;
+    {
+      const uint32_t h0 = (hi[0] >> 16) | hi[1], h1 = (hi[2] >> 16) | hi[3];
+      const uint32_t l0 = (lo[0] >> 16) | lo[1], l1 = (lo[2] >> 16) | lo[3];
+      ph = __builtin_bit_cast(s16x4, make_uint2(h0, h1));
+      pl = __builtin_bit_cast(s16x4, make_uint2(l0, l1));
+    }
+#pragma unroll
+    for (int j = 0; j < Cf::D / 16; ++j) {
+      const uint32_t* src = vt + (16 * j + c) * VTW + 8 * t + 2 * q;
+      const s16x4 a = __builtin_bit_cast(s16x4, make_uint2(src[0], src[1]));
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ph, acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pl, acc[j], 0, 0, 0);
+    }
+  }
+}
+
 template <class Cf>
 __device__ __forceinline__ void full_block(const BlockRegs<Cf>& r, int nvalid, float ksc, float vsc,
                                            const uint4 (&qf)[Cf::QF], float qk_log2, int lane, float& m_run,
-                                           float& l_run, f32x4 (&acc)[Cf::NACC], float* pbuf) {
+                                           float& l_run, f32x4 (&acc)[Cf::NACCF], float* pbuf, uint32_t* vt) {
   f32x4 S[Cf::T];
   qk_scores<Cf>(r, qf, S);
   float x[Cf::T][4];
@@ -2546,10 +2614,35 @@ __device__ __forceinline__ void full_block(const BlockRegs<Cf>& r, int nvalid, f
   ls = rows_sum(ls);
   l_run = fmaf(al, l_run, ls);
   m_run = mn;
-  pv_rescale<Cf>(acc, al);
-  pv_block<Cf>(r, pq, pbuf, lane, acc);
+  if constexpr (Cf::PVB) {
+#pragma unroll
+    for (int j = 0; j < Cf::NACCF; ++j) acc[j] *= al;  // lane (c, q) holds head c
+    pvb_block<Cf>(r, pq, vt, lane, acc);
+  } else {
+    pv_rescale<Cf>(acc, al);
+    pv_block<Cf>(r, pq, pbuf, lane, acc);
+  }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ long long wave_incl_scan(long long x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Full attention over a balanced partition: the blocks of all streams
+// (sequence, kv-head), kv-head fastest and in logical order within a
+// stream, form one flattened list of W blocks; workgroup i of G folds
+// positions [floor(i W / G), floor((i + 1) W / G)), whatever streams they
+// belong to, so every workgroup gets the same number of blocks however
+// ragged the sequences are.  Each piece (a workgroup's part of one stream)
+// leaves a partial (max, sum, numerator per head) in slot s + i of the
+// workspace (injective: stream s's pieces take consecutive workgroups), and
+// the stream's last piece to finish merges its pieces in order.
 template <int KV, int D, int B, int GM>
 __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
   using Cf = Cfg<KV, D, B, GM>;
@@ -2557,202 +2650,280 @@ __global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) float mw_a[NW][GM][D];
   __shared__ float mw_m[NW][GM];
   __shared__ float mw_l[NW][GM];
-  __shared__ __attribute__((aligned(16))) float pbuf_all[NW][Cf::PV4 ? GM * B : 4];
+  __shared__ __attribute__((aligned(16))) float pbuf_all[NW][Cf::PV4 && !Cf::PVB ? GM * B : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t vt_all[NW][Cf::PVB ? D * Cf::VTS / 2 : 4];
+  __shared__ long long plan[4];  // W, first position, end position, flattened start of the first sequence
+  __shared__ int plan_sq;        // the sequence holding the first position
+  __shared__ int is_last;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Workgroup i takes slice i / streams of stream i % streams (streams =
-  // (sequence, kv-head), kv-head fastest).  Workgroups are dealt to the 8
-  // XCDs round-robin: slice-major keeps each XCD's share of a ragged batch
-  // equal (stream-major with 8 slices per stream would give XCD k every
-  // slice k, and late slices of short sequences are empty), puts the
-  // slices that always hold blocks first, and lets adjacent workgroups read
-  // the adjacent kv-head tiles of the same pages together.
-  const int streams = p.batch * p.hkv;
-  const int split = blockIdx.x / streams;
-  const int stream = blockIdx.x - split * streams;
-  const int s = stream / p.hkv;
-  const int kvh = stream - s * p.hkv;
+  const int G = gridDim.x;
+  const int wg = blockIdx.x;
+  const int hkv = p.hkv;
+  const int streams = p.batch * hkv;
   const int g = p.g;
-  const int L = p.seq_lens[s];
-  const int n = visit_count<B>(p, s, L);
-  const size_t head0 = (size_t)s * p.hq + (size_t)kvh * g;
-  const int b0 = split * p.split_blocks;
-  const int b1 = min(n, b0 + p.split_blocks);
-  // this wave folds the blocks at positions b0 + w + NW * k, k < cnt (cnt <= 64
-  // by the split plan): logical blocks in order, or, for a pruned cache, the
-  // visited blocks block_order[s][t] (the order does not change the result)
-  const int cnt = b0 + w < b1 ? (b1 - b0 - w + NW - 1) / NW : 0;
+
+  // streams without visits: out = 0, stop = 0 (no position belongs to them)
+  for (int st = wg; st < streams; st += G) {
+    const int sq = st / hkv;
+    if (visit_count<B>(p, sq, p.seq_lens[sq]) <= 0) {
+      const size_t head0 = (size_t)sq * p.hq + (size_t)(st - sq * hkv) * g;
+      for (int i = threadIdx.x; i < g * D; i += blockDim.x) p.out[head0 * D + i] = 0.f;
+      if ((int)threadIdx.x < g) p.stop_block[head0 + threadIdx.x] = 0;
+      if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[st] = 0;
+    }
+  }
+
+  // wave 0: the total W, this workgroup's range and the sequence holding its
+  // first position (two sweeps over the sequences, 64 at a time)
+  if (w == 0) {
+    long long tot = 0;
+    for (int base = 0; base < p.batch; base += 64) {
+      const int sq = base + lane;
+      const long long nb = sq < p.batch ? (long long)visit_count<B>(p, sq, p.seq_lens[sq]) * hkv : 0;
+      tot += __shfl(wave_incl_scan(nb, lane), 63);
+    }
+    // with fewer blocks than workgroups, the first W workgroups take one each
+    const long long Ge = tot < G ? tot : G;
+    const long long a = wg < Ge ? tot * wg / Ge : 0, e = wg < Ge ? tot * (wg + 1) / Ge : 0;
+    long long before = 0;
+    int found = -1;
+    long long fstart = 0;
+    for (int base = 0; base < p.batch && found < 0 && a < e; base += 64) {
+      const int sq = base + lane;
+      const long long nb = sq < p.batch ? (long long)visit_count<B>(p, sq, p.seq_lens[sq]) * hkv : 0;
+      const long long inc = before + wave_incl_scan(nb, lane);
+      const unsigned long long hit = __ballot(sq < p.batch && nb > 0 && inc > a && inc - nb <= a);
+      if (hit != 0ull) {
+        const int l = __builtin_ctzll(hit);
+        found = base + l;
+        fstart = __shfl(inc - nb, l);
+      }
+      before = __shfl(inc, 63);
+    }
+    if (lane == 0) {
+      plan[0] = tot;
+      plan[1] = a;
+      plan[2] = e;
+      plan[3] = fstart;
+      plan_sq = found;
+    }
+  }
+  __syncthreads();
+  const long long W = plan[0];
+  long long pos = plan[1];
+  const long long end = plan[2];
+  if (pos >= end || plan_sq < 0) return;
+  const long long Ge = W < G ? W : G;  // workgroups with a non-empty range
+  // the workgroup holding flattened position x: the largest i with floor(i W / Ge) <= x
+  auto wg_of = [&](long long x) { return (int)(((x + 1) * Ge - 1) / W); };
+
+  int sq = plan_sq;
+  int L = p.seq_lens[sq];
+  int n = visit_count<B>(p, sq, L);
+  int kvh = (int)((pos - plan[3]) / n);
+  int off = (int)(pos - plan[3] - (long long)kvh * n);
 
   uint4 qf[Cf::QF];
-  load_q<Cf>(p, s, kvh, lane, qf);
-
   const size_t tile = (size_t)B * Cf::R;
   const char* kbase = static_cast<const char*>(p.k_pages);
   const char* vbase = static_cast<const char*>(p.v_pages);
-  const int32_t* trow = p.block_table + (size_t)s * p.max_blocks;
-
-  // lane k holds the logical block, the page (and fp8 scales) of the wave's
-  // k-th block
-  int tab = 0, blk = 0;
-  float ks_t = 1.f, vs_t = 1.f;
-  if (cnt > 0) {
-    const int t = b0 + w + NW * min(lane, cnt - 1);
-    blk = p.visit_lens ? p.block_order[(size_t)s * p.max_blocks + t] : t;
-    tab = trow[blk];
-    if constexpr (KV == KV_FP8) {
-      ks_t = p.k_scale[(size_t)tab * p.hkv + kvh];
-      vs_t = p.v_scale[(size_t)tab * p.hkv + kvh];
-    }
-  }
-
-  float m_run = NEG_INF, l_run = 0.f;
-  f32x4 acc[Cf::NACC];
-  pv_zero<Cf>(acc);
   float* pbuf = pbuf_all[w];
+  uint32_t* vt = vt_all[w];
 
-  auto nvalid_of = [&](int k) { return min(B, L - readlane(blk, k) * B); };
-  auto tile_of = [&](int k) { return ((size_t)readlane(tab, k) * p.hkv + kvh) * tile; };
-  auto fold = [&](const BlockRegs<Cf>& r, int k) {
-    float ks = 1.f, vs = 1.f;
-    if constexpr (KV == KV_FP8) { ks = readlanef(ks_t, k); vs = readlanef(vs_t, k); }
-    full_block<Cf>(r, nvalid_of(k), ks, vs, qf, p.qk_log2, lane, m_run, l_run, acc, pbuf);
-  };
+  while (pos < end) {
+    const int s = sq * hkv + kvh;
+    const int len = (int)min((long long)(n - off), end - pos);
+    const size_t head0 = (size_t)sq * p.hq + (size_t)kvh * g;
+    const int32_t* trow = p.block_table + (size_t)sq * p.max_blocks;
+    load_q<Cf>(p, sq, kvh, lane, qf);
 
-  // Register ring of PF block buffers: while block k is folded, blocks
-  // k+1 .. k+PF-1 are in flight.  Loads are unconditional (past the wave's
-  // last block they re-read that block, a cache hit), so every fold site has
-  // the same PF-1 blocks of younger loads outstanding and the waits are exact.
-  if (cnt > 0) {
-    constexpr int PF = FULL_PREFETCH;
-    BlockRegs<Cf> ring[PF];
+    // ---- this wave's blocks of the piece: off + w + NW k, in sub-ranges of
+    // 64 (one lane-held page table each), the state carried across them
+    float m_run = NEG_INF, l_run = 0.f;
+    f32x4 acc[Cf::NACCF];
 #pragma unroll
-    for (int j = 0; j < PF - 1; ++j) {
-      const int kk = min(j, cnt - 1);
-      const size_t o = tile_of(kk);
-      load_block<Cf, true>(ring[j], kbase + o, vbase + o, lane, nvalid_of(kk));
-    }
-    for (int k = 0; k < cnt; k += PF) {
+    for (int jj = 0; jj < Cf::NACCF; ++jj) acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int cnt_all = w < len ? (len - w + NW - 1) / NW : 0;
+    for (int k0 = 0; k0 < cnt_all; k0 += 64) {
+      const int cnt = min(64, cnt_all - k0);
+      int tab = 0, blk = 0;
+      float ks_t = 1.f, vs_t = 1.f;
+      {
+        const int t = off + w + NW * (k0 + min(lane, cnt - 1));
+        blk = p.visit_lens ? p.block_order[(size_t)sq * p.max_blocks + t] : t;
+        tab = trow[blk];
+        if constexpr (KV == KV_FP8) {
+          ks_t = p.k_scale[(size_t)tab * hkv + kvh];
+          vs_t = p.v_scale[(size_t)tab * hkv + kvh];
+        }
+      }
+      auto nvalid_of = [&](int k) { return min(B, L - readlane(blk, k) * B); };
+      auto tile_of = [&](int k) { return ((size_t)readlane(tab, k) * hkv + kvh) * tile; };
+      auto fold = [&](const BlockRegs<Cf>& r, int k) {
+        float ks = 1.f, vs = 1.f;
+        if constexpr (KV == KV_FP8) { ks = readlanef(ks_t, k); vs = readlanef(vs_t, k); }
+        full_block<Cf>(r, nvalid_of(k), ks, vs, qf, p.qk_log2, lane, m_run, l_run, acc, pbuf, vt);
+      };
+      // Register ring of PF block buffers: while block k is folded, blocks
+      // k+1 .. k+PF-1 are in flight.  Loads are unconditional (past the last
+      // block they re-read that block, a cache hit), so every fold site has
+      // the same PF-1 blocks of younger loads outstanding and the waits are exact.
+      constexpr int PF = FULL_PREFETCH;
+      BlockRegs<Cf> ring[PF];
 #pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        const int kk = min(k + j + PF - 1, cnt - 1);
+      for (int jj = 0; jj < PF - 1; ++jj) {
+        const int kk = min(jj, cnt - 1);
         const size_t o = tile_of(kk);
-        load_block<Cf, true>(ring[(j + PF - 1) % PF], kbase + o, vbase + o, lane, nvalid_of(kk));
-        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
-        if (k + j < cnt) fold(ring[j], k + j);
+        load_block<Cf, true>(ring[jj], kbase + o, vbase + o, lane, nvalid_of(kk));
+      }
+      for (int k = 0; k < cnt; k += PF) {
+#pragma unroll
+        for (int jj = 0; jj < PF; ++jj) {
+          const int kk = min(k + jj + PF - 1, cnt - 1);
+          const size_t o = tile_of(kk);
+          load_block<Cf, true>(ring[(jj + PF - 1) % PF], kbase + o, vbase + o, lane, nvalid_of(kk));
+          __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
+          if (k + jj < cnt) fold(ring[jj], k + jj);
+        }
       }
     }
-  }
 
-  // merge the four waves
-  {
-    const int c = lane & 15;
-    pv_finish<Cf>(acc);
-    pv_store<Cf>(&mw_a[w][0][0], lane, acc, 1.f);
-    if (c < GM && (lane >> 4) == 0) { mw_m[w][c] = m_run; mw_l[w][c] = l_run; }
-  }
-  __syncthreads();
-
+    // ---- merge the four waves
+    {
+      const int c = lane & 15;
+      if constexpr (Cf::PVB) {
+        if (c < GM) {
 #pragma unroll
-  for (int k = 0; k < HPW; ++k) {
-    const int h = w + NW * k;
-    if (h >= g) continue;
-    float M = NEG_INF;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mw_m[ww][h]);
-    float Ls = 0.f;
-    float A[DPL];
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) A[j] = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const float mw = mw_m[ww][h];
-      const float f = (mw == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      Ls = fmaf(f, mw_l[ww][h], Ls);
-#pragma unroll
-      for (int j = 0; j < DPL; ++j) A[j] = fmaf(f, mw_a[ww][h][lane + 64 * j], A[j]);
+          for (int jj = 0; jj < Cf::NACCF; ++jj)
+            *reinterpret_cast<f32x4*>(&mw_a[w][c][16 * jj + 4 * (lane >> 4)]) = acc[jj];
+        }
+      } else {
+        pv_finish<Cf>(acc);
+        pv_store<Cf>(&mw_a[w][0][0], lane, acc, 1.f);
+      }
+      if (c < GM && (lane >> 4) == 0) { mw_m[w][c] = m_run; mw_l[w][c] = l_run; }
     }
-    if (p.splits == 1) {
-      const float rl = Ls > 0.f ? 1.0f / Ls : 0.f;
+    __syncthreads();
+    const long long sstart = pos - off;  // flattened start of stream s
+    const int first = wg_of(sstart), last = wg_of(sstart + n - 1);
+    const bool alone = first == last;  // the whole stream is this piece
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) p.out[(head0 + h) * D + lane + 64 * j] = A[j] * rl;
-      if (lane == 0) p.stop_block[head0 + h] = n;
+    for (int k = 0; k < HPW; ++k) {
+      const int h = w + NW * k;
+      if (h >= g) continue;
+      float M = NEG_INF;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mw_m[ww][h]);
+      float Ls = 0.f;
+      float A[DPL];
+#pragma unroll
+      for (int jj = 0; jj < DPL; ++jj) A[jj] = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float mw = mw_m[ww][h];
+        const float f = (mw == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+        Ls = fmaf(f, mw_l[ww][h], Ls);
+#pragma unroll
+        for (int jj = 0; jj < DPL; ++jj) A[jj] = fmaf(f, mw_a[ww][h][lane + 64 * jj], A[jj]);
+      }
+      if (alone) {
+        const float rl = Ls > 0.f ? 1.0f / Ls : 0.f;
+#pragma unroll
+        for (int jj = 0; jj < DPL; ++jj) p.out[(head0 + h) * D + lane + 64 * jj] = A[jj] * rl;
+        if (lane == 0) p.stop_block[head0 + h] = n;
+      } else {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(p.ws_part + ((size_t)(s + wg) * GM + h) * (D + 2));
+#pragma unroll
+        for (int jj = 0; jj < DPL; ++jj) st_dev32(dst + lane + 64 * jj, __float_as_uint(A[jj]));
+        if (lane == 0) { st_dev32(dst + D, __float_as_uint(M)); st_dev32(dst + D + 1, __float_as_uint(Ls)); }
+      }
+    }
+    if (alone) {
+      if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[s] = n;
     } else {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(p.ws_part + (((size_t)stream * p.splits + split) * GM + h) * (D + 2));
+      // The stream's last piece to finish merges all of them: every piece's
+      // partials are complete (device-coherent stores, waited for) before
+      // its count goes in; the piece that brings the count to the number of
+      // pieces resets it for the next call and folds the partials, in piece
+      // order, with device-coherent loads.
+      const int pieces = last - first + 1;
+      wait_all_memory();
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(p.full_cnt + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = old == (uint32_t)(pieces - 1) ? 1 : 0;
+        if (is_last) st_dev32(p.full_cnt + s, 0u);
+      }
+      __syncthreads();
+      if (is_last) {
+        const size_t sstride = (size_t)GM * (D + 2);
+        for (int h = w; h < g; h += NW) {
+          const uint32_t* src = reinterpret_cast<const uint32_t*>(p.ws_part + ((size_t)(s + first) * GM + h) * (D + 2));
+          // common maximum over the pieces (lane-parallel, they may exceed 64)
+          float M = NEG_INF;
+          for (int sp = lane; sp < pieces; sp += 64) M = fmaxf(M, __uint_as_float(ld_dev32(src + sp * sstride + D)));
+          M = rows_max(M);
+          M = fmaxf(M, dpp<DPP_ROW_MIRROR>(M));
+          M = fmaxf(M, dpp<DPP_HALF_MIRROR>(M));
+          M = fmaxf(M, dpp<DPP_XOR2>(M));
+          M = fmaxf(M, dpp<DPP_XOR1>(M));
+          // weighted numerators: every lane owns D/64 output elements
+          float Ls = 0.f;
+          float A[DPL];
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) st_dev32(dst + lane + 64 * j, __float_as_uint(A[j]));
-      if (lane == 0) { st_dev32(dst + D, __float_as_uint(M)); st_dev32(dst + D + 1, __float_as_uint(Ls)); }
+          for (int jj = 0; jj < DPL; ++jj) A[jj] = 0.f;
+          int sp = 0;
+          for (; sp + 4 <= pieces; sp += 4) {
+            float ms[4], ls[4], a[4][DPL];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const uint32_t* q = src + (size_t)(sp + u) * sstride;
+              ms[u] = __uint_as_float(ld_dev32(q + D));
+              ls[u] = __uint_as_float(ld_dev32(q + D + 1));
+#pragma unroll
+              for (int jj = 0; jj < DPL; ++jj) a[u][jj] = __uint_as_float(ld_dev32(q + lane + 64 * jj));
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float f = (ms[u] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - M);
+              Ls = fmaf(f, ls[u], Ls);
+#pragma unroll
+              for (int jj = 0; jj < DPL; ++jj) A[jj] = fmaf(f, a[u][jj], A[jj]);
+            }
+          }
+          for (; sp < pieces; ++sp) {
+            const uint32_t* q = src + (size_t)sp * sstride;
+            const float ms = __uint_as_float(ld_dev32(q + D));
+            const float f = (ms == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+            Ls = fmaf(f, __uint_as_float(ld_dev32(q + D + 1)), Ls);
+#pragma unroll
+            for (int jj = 0; jj < DPL; ++jj) A[jj] = fmaf(f, __uint_as_float(ld_dev32(q + lane + 64 * jj)), A[jj]);
+          }
+          const float rl = Ls > 0.f ? 1.0f / Ls : 0.f;
+#pragma unroll
+          for (int jj = 0; jj < DPL; ++jj) p.out[(head0 + h) * D + lane + 64 * jj] = A[jj] * rl;
+          if (lane == 0) p.stop_block[head0 + h] = n;
+        }
+        if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[s] = n;
+      }
     }
-  }
-  if (p.splits == 1) {
-    if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[stream] = n;
-    return;
-  }
+    __syncthreads();  // mw_* are rewritten by the next piece
 
-  // The stream's last slice to finish merges all of them: every slice's
-  // partials are complete (device-coherent stores, waited for) before its
-  // count goes in; the slice that brings the count to `splits` resets it for
-  // the next call and folds the partials with device-coherent loads.
-  __shared__ int is_last;
-  wait_all_memory();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(p.full_cnt + stream, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = old == (uint32_t)(p.splits - 1) ? 1 : 0;
-    if (is_last) st_dev32(p.full_cnt + stream, 0u);
-  }
-  __syncthreads();
-  if (!is_last) return;
-  const int S = p.splits;
-  const size_t sstride = (size_t)GM * (D + 2);
-  for (int h = w; h < g; h += NW) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(p.ws_part + ((size_t)stream * S * GM + h) * (D + 2));
-    // common maximum over the slices (lane-parallel, S may exceed 64)
-    float M = NEG_INF;
-    for (int sp = lane; sp < S; sp += 64) M = fmaxf(M, __uint_as_float(ld_dev32(src + sp * sstride + D)));
-    M = rows_max(M);
-    M = fmaxf(M, dpp<DPP_ROW_MIRROR>(M));
-    M = fmaxf(M, dpp<DPP_HALF_MIRROR>(M));
-    M = fmaxf(M, dpp<DPP_XOR2>(M));
-    M = fmaxf(M, dpp<DPP_XOR1>(M));
-    // weighted numerators: every lane owns D/64 output elements
-    float Ls = 0.f;
-    float A[DPL];
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) A[j] = 0.f;
-    int sp = 0;
-    for (; sp + 4 <= S; sp += 4) {
-      float ms[4], ls[4], a[4][DPL];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t* q = src + (size_t)(sp + u) * sstride;
-        ms[u] = __uint_as_float(ld_dev32(q + D));
-        ls[u] = __uint_as_float(ld_dev32(q + D + 1));
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) a[u][j] = __uint_as_float(ld_dev32(q + lane + 64 * j));
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float f = (ms[u] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - M);
-        Ls = fmaf(f, ls[u], Ls);
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) A[j] = fmaf(f, a[u][j], A[j]);
-      }
+    // ---- the next stream (kv-head fastest; sequences without visits hold no position)
+    pos += len;
+    off = 0;
+    if (pos >= end) break;
+    if (++kvh == hkv) {
+      kvh = 0;
+      do {
+        ++sq;
+        L = p.seq_lens[sq];
+        n = visit_count<B>(p, sq, L);
+      } while (n <= 0);
     }
-    for (; sp < S; ++sp) {
-      const uint32_t* q = src + (size_t)sp * sstride;
-      const float ms = __uint_as_float(ld_dev32(q + D));
-      const float f = (ms == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-      Ls = fmaf(f, __uint_as_float(ld_dev32(q + D + 1)), Ls);
-#pragma unroll
-      for (int j = 0; j < DPL; ++j) A[j] = fmaf(f, __uint_as_float(ld_dev32(q + lane + 64 * j)), A[j]);
-    }
-    const float rl = Ls > 0.f ? 1.0f / Ls : 0.f;
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) p.out[(head0 + h) * D + lane + 64 * j] = A[j] * rl;
-    if (lane == 0) p.stop_block[head0 + h] = n;
   }
-  if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[stream] = n;
 }
 
 }  // namespace kern

@@ -7,7 +7,7 @@ namespace {
 
 template <int D, int B, int GM>
 hipError_t go(const Params& p, hipStream_t st) {
-  hipLaunchKernelGGL((kern::full_split_kernel<KV_F32, D, B, GM>), dim3(p.batch * p.hkv * p.splits), dim3(kern::WG), 0, st, p);
+  hipLaunchKernelGGL((kern::full_split_kernel<KV_F32, D, B, GM>), dim3(p.splits), dim3(kern::WG), 0, st, p);
   return hipGetLastError();
 }
 

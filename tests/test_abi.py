@@ -220,11 +220,11 @@ def test_check_inputs_entry_point_validates(lib):
 
 
 def test_noalloc_rejects_partials_past_the_static_scratch(lib):
-    """art_decode_noalloc: full attention whose split partials would pass the 8 MiB static array is refused
-    before any device call (one sequence of 65536 blocks, 8 kv-heads of 16 query heads: 256 splits of 256
-    blocks, 8 x 256 x 16 x 130 floats = 17 MB); the same descriptor in ART mode needs no scratch but the
-    call then reaches the device, which this host test does not do."""
-    d = _desc(batch=1, num_q_heads=128, num_kv_heads=8, max_blocks_per_seq=65536, num_pages=65536)
+    """art_decode_noalloc: full attention whose piece partials would pass the 8 MiB static array is refused
+    before any device call (128 sequences x 8 kv-heads of 16 query heads with 256 workgroups: (1024 + 256)
+    pieces x 16 x 130 floats = 10.6 MB, past 8 MiB less the 64 KiB of counters); the same descriptor in ART
+    mode needs no scratch but the call then reaches the device, which this host test does not do."""
+    d = _desc(batch=128, num_q_heads=128, num_kv_heads=8, max_blocks_per_seq=64, num_pages=65536)
     args = lambda em: (ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, em, em, 1, FAKE, FAKE, None,
                        None)
     assert lib.art_decode_noalloc(*args(0.0)) == art.ART_ERR_WORKSPACE
