@@ -61,7 +61,7 @@ art_status check_desc(const art_decode_desc* d) {
 // resolved frontier, plus half the frontier; ART_SEG_WGS persistent
 // workgroups (0: one per CU).
 // Stream kernel: ART_LA0 and ART_LA_SHIFT set its lookahead, la0 +
-// (frontier >> la_shift) blocks (defaults 16 and 1).  Windowed:
+// (frontier >> la_shift) blocks (defaults 32 and 1).  Windowed:
 // ART_WIN_SPLIT fold workgroups per (stream, head) (1 .. 4; 0, the default:
 // 2 when there are few heads, else 1), ART_WIN_FIRST chunks in the first
 // window (0, the default: 1/8 of the longest stream's chunks, 2 .. 64) and
@@ -97,7 +97,7 @@ Knobs read_knobs() {
                    mode,                                    env_int("ART_WINDOW", 0, 0, 32),
                    env_int("ART_WORKERS", 0, 0, 1 << 20),       env_int("ART_WIN_SPLIT", 0, 0, art::art_win_split),
                    env_int("ART_WIN_FIRST", 0, 0, 64),          env_int("ART_WIN_GROWTH", 2, 2, 8),
-                   env_int("ART_LA0", 16, 1, 1 << 20),          env_int("ART_LA_SHIFT", 1, 0, 30),
+                   env_int("ART_LA0", 32, 1, 1 << 20),          env_int("ART_LA_SHIFT", 1, 0, 30),
                    env_int("ART_SPIN_LIMIT", 1 << 20, 1, 1 << 30), env_int("ART_FULL_WGS", 0, 0, 1 << 20),
                    env_int("ART_SEG_WIN", 2, 1, 1 << 20),      env_int("ART_SEG_WGS", 0, 0, 1 << 20)};
   return k;

@@ -65,7 +65,12 @@ struct StreamCfg : Cfg<KV_, D_, B_, GM_> {
 #ifdef ART_STREAM_NP
   static constexpr int NP2 = ART_STREAM_NP;
 #else
-  static constexpr int NP2 = TILE_V >= 64 ? 4 : 8;      // producer waves
+  // producer waves: ten for bf16/f32 16-token blocks of groups up to 4
+  // heads (with the four detector waves, 14 waves at up to 128 VGPRs each;
+  // measured faster than 8 and 12 on the Llama-3-8B and ragged shapes),
+  // eight for the other small tiles (whose math needs more registers), four
+  // for large ones
+  static constexpr int NP2 = TILE_V >= 64 ? 4 : (GM_ <= 4 && KV_ != KV_FP8 && B_ == 16 ? 10 : 8);
 #endif
   static constexpr int NW2 = NS2 + NP2;
   static constexpr int SLOTF = GM_ * D_ + 2 * GM_;     // floats per ring slot: o[GM][D], m[GM], l[GM]

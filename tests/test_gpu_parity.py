@@ -256,7 +256,7 @@ SCAN_VARIANTS = [
 
 
 STREAM_VARIANTS = [
-    dict(ART_SCHED="stream"),                                 # defaults: lookahead 16 + frontier / 2
+    dict(ART_SCHED="stream"),                                 # defaults: lookahead 32 + frontier / 2
     dict(ART_SCHED="stream", ART_LA0="1", ART_LA_SHIFT="30"),   # the smallest lookahead (two chunks)
     dict(ART_SCHED="stream", ART_LA0="100000", ART_LA_SHIFT="0"),  # the largest (ring and register ring)
     dict(ART_SCHED="stream", ART_LA0="24", ART_LA_SHIFT="3"),
