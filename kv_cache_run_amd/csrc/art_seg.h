@@ -242,51 +242,78 @@ __device__ __forceinline__ uint32_t seg_probe(const u64* st0, int g, int j, uint
   return jj >= 0 ? tag_val(ld_dev(st0 + (size_t)jj * g), E, 0u) : (LB_FIN | SG_RUN);
 }
 
-// One query head of one item: aggregate, look back, detect, resolve.  Returns
-// false if a wait ran past the spin limit (the head then reads stop -1 and
-// NaN output).
+// The query heads h0 + NS k (k < HP) of one item, in one detector wave:
+// aggregate, look back, detect, resolve.  The heads go through every phase
+// together, so their waits on other workgroups overlap: a poll reads the
+// status words of both heads at once (lanes [k LPH, (k + 1) LPH) examine head
+// k's segments j-1-(lane - k LPH)).  A wait that runs past the spin limit
+// fails every head of the wave (stop -1, NaN output).
 template <class Cf>
-__device__ bool seg_head(const Params& p, uint32_t E, int s, int j, int n, int ns, int h, const float* slots,
-                         const int2* ent, int lane) {
+__device__ void seg_heads(const Params& p, uint32_t E, int s, int j, int n, int ns, int h0, const float* slots,
+                          const int2* ent, int lane) {
   constexpr int S = Cf::S, C = Cf::C3, DPL = Cf::DPL, D = Cf::D, GM = Cf::GM, SLOTF = Cf::SLOTF, NCH = Cf::NCH;
+  constexpr int HP = Cf::HP3, NS = Cf::NS3;
+  constexpr int LPH = 64 / HP;  // lanes per head in a poll (segments examined per head)
   const int g = p.g;
   const int t0 = j * S;
   const bool last = t0 + ns >= n;
-  const u64* st0 = p.lb_st + (size_t)s * p.max_chunks * g + h;  // segment stride g
-  u64* stw = p.lb_st + ((size_t)s * p.max_chunks + j) * g + h;
   const size_t rstride = (size_t)g * p.rec_floats;
-  const float* rec0 = p.lb_rec + ((size_t)s * p.max_chunks * g + h) * p.rec_floats;
-  float* rec = p.lb_rec + (((size_t)s * p.max_chunks + j) * g + h) * p.rec_floats;
   const int incl = D + 4;  // the inclusive state follows the aggregate
-  const size_t head = (size_t)(s / p.hkv) * p.hq + (size_t)(s % p.hkv) * g + h;
-  float* out_row = p.out + head * D;
   const int cap = min(p.patience, SG_CNT_MAX);
+  const int kh = lane / LPH;  // the head this lane examines in a poll
+  const int li = lane - kh * LPH;
+  auto head_of = [&](int k) { return h0 + NS * k; };
+  auto stw_of = [&](int k) { return p.lb_st + ((size_t)s * p.max_chunks + j) * g + head_of(k); };
+  auto rec_of = [&](int k) { return p.lb_rec + (((size_t)s * p.max_chunks + j) * g + head_of(k)) * p.rec_floats; };
+  auto rec0_of = [&](int k) { return p.lb_rec + ((size_t)s * p.max_chunks * g + head_of(k)) * p.rec_floats; };
+  auto part = [&](unsigned long long b, int k) -> unsigned long long {
+    return HP == 1 ? b : (b >> (k * LPH)) & ((1ull << LPH) - 1ull);
+  };
+  // status of segment j-1-li of head kh (lanes of inactive heads read "resolved, running")
+  auto probe = [&](const bool (&act)[HP]) {
+    bool a = false;
+#pragma unroll
+    for (int k = 0; k < HP; ++k) a = (kh == k) ? act[k] : a;
+    const int h = min(head_of(kh), g - 1);
+    const int jj = j - 1 - li;
+    if (!a || jj < 0) return (uint32_t)(LB_FIN | SG_RUN);
+    return tag_val(ld_dev(p.lb_st + ((size_t)s * p.max_chunks + jj) * g + h), E, 0u);
+  };
 
-  // ---- the segment's own aggregate
-  float gm, gl, ga[DPL];
+  bool act[HP];  // heads of the group, not yet dead
+#pragma unroll
+  for (int k = 0; k < HP; ++k) act[k] = head_of(k) < g;
+
+  // ---- each head's own aggregate of the segment
+  float gm[HP], gl[HP], ga[HP][DPL];
   {
-    const float mt = lane < ns ? slots[(size_t)min(lane, S - 1) * SLOTF + GM * D + h] : NEG_INF;
-    const float lt = lane < ns ? slots[(size_t)min(lane, S - 1) * SLOTF + GM * D + GM + h] : 0.f;
-    gm = wave_max(mt);
-    float e[1] = {lane < ns ? __builtin_amdgcn_exp2f(mt - gm) * lt : 0.f};
-    const float el = e[0];
-    gl = xreduce<1>(e, lane);
+    const int tl = min(lane, S - 1);
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) ga[k] = 0.f;
-    // eight positions' loads at a time, then their products in order
-    for (int t0c = 0; t0c < ns; t0c += 8) {
-      float v[8][DPL];
+    for (int k = 0; k < HP; ++k) {
+      const int h = min(head_of(k), GM - 1);
+      const float mt = lane < ns ? slots[(size_t)tl * SLOTF + GM * D + h] : NEG_INF;
+      const float lt = lane < ns ? slots[(size_t)tl * SLOTF + GM * D + GM + h] : 0.f;
+      gm[k] = wave_max(mt);
+      float e[1] = {lane < ns ? __builtin_amdgcn_exp2f(mt - gm[k]) * lt : 0.f};
+      const float el = e[0];
+      gl[k] = xreduce<1>(e, lane);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float* src = slots + (size_t)min(t0c + u, S - 1) * SLOTF + h * D + DPL * lane;
+      for (int q = 0; q < DPL; ++q) ga[k][q] = 0.f;
+      // eight positions' loads at a time, then their products in order
+      for (int t0c = 0; t0c < ns; t0c += 8) {
+        float v[8][DPL];
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) v[u][k] = src[k];
-      }
+        for (int u = 0; u < 8; ++u) {
+          const float* src = slots + (size_t)min(t0c + u, S - 1) * SLOTF + h * D + DPL * lane;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float et = t0c + u < ns ? readlanef(el, t0c + u) : 0.f;
+          for (int q = 0; q < DPL; ++q) v[u][q] = src[q];
+        }
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) ga[k] = fmaf(et, v[u][k], ga[k]);
+        for (int u = 0; u < 8; ++u) {
+          const float et = t0c + u < ns ? readlanef(el, t0c + u) : 0.f;
+#pragma unroll
+          for (int q = 0; q < DPL; ++q) ga[k][q] = fmaf(et, v[u][q], ga[k][q]);
+        }
       }
     }
   }
@@ -298,45 +325,68 @@ __device__ bool seg_head(const Params& p, uint32_t E, int s, int j, int n, int n
   // stop before this segment (once the pass bits are out, a bit may come
   // from a later stop, so the mask is not consulted after that).  Dead heads
   // publish SG_DEAD and nothing else.
-  auto mask_dead = [&]() { return ((ld_dev32(p.lb_heads + s) >> h) & 1u) != 0u; };
-  auto publish_dead = [&]() {
-    if (lane == 0) st_dev(stw, tag_word(E, SG_DEAD));
-  };
-  if (mask_dead()) {
-    publish_dead();
-    return true;
-  }
-
-  // ---- state entering the segment: nearest published inclusive state (lane
-  // f examines segment j-1-f), then the aggregates after it in segment order;
-  // the aggregate is published first unless that state can be had at once
-  LbState<Cf> x;
-  x.M = NEG_INF;
-  x.L = 0.f;
+  auto kill_dead = [&](uint32_t mword, unsigned long long dead_ballot) {
 #pragma unroll
-  for (int k = 0; k < DPL; ++k) x.A[k] = 0.f;
+    for (int k = 0; k < HP; ++k)
+      if (act[k] && ((((mword >> head_of(k)) & 1u) != 0u) || part(dead_ballot, k) != 0ull)) {
+        if (lane == 0) st_dev(stw_of(k), tag_word(E, SG_DEAD));
+        act[k] = false;
+      }
+  };
+  kill_dead(ld_dev32(p.lb_heads + s), 0ull);
+
+  // ---- state entering the segment: nearest published inclusive state, then
+  // the aggregates after it in segment order; a head publishes its aggregate
+  // first unless that state can be had at once
+  LbState<Cf> x[HP];
+#pragma unroll
+  for (int k = 0; k < HP; ++k) {
+    x[k].M = NEG_INF;
+    x[k].L = 0.f;
+#pragma unroll
+    for (int q = 0; q < DPL; ++q) x[k].A[q] = 0.f;
+  }
   bool ok = true;
   if (j > 0) {
-    bool published = false;
-    int f = 0;
+    bool found[HP], pub[HP];
+    int f[HP];
+#pragma unroll
+    for (int k = 0; k < HP; ++k) { found[k] = !act[k]; pub[k] = false; f[k] = 0; }
     for (int spin = 0;; ++spin) {
-      const uint32_t v = seg_probe(st0, g, j, E, lane);
+      const uint32_t v = probe(act);
       const uint32_t lvl = v & LB_LEVEL;
-      if (__ballot(lvl == SG_DEAD) != 0ull || mask_dead()) {
-        publish_dead();
-        return true;
+      const uint32_t mword = ld_dev32(p.lb_heads + s);
+      kill_dead(mword, __ballot(lvl == SG_DEAD));
+      const unsigned long long inc = __ballot(lvl >= LB_INCL && lvl <= LB_FIN);
+      const unsigned long long agg = __ballot(lvl >= LB_AGG && lvl <= LB_FIN);
+      bool all = true;
+#pragma unroll
+      for (int k = 0; k < HP; ++k) {
+        if (!act[k]) { found[k] = true; continue; }
+        if (!found[k]) {
+          const unsigned long long ik = part(inc, k);
+          if (ik != 0ull) {
+            const int fk = __builtin_ctzll(ik);
+            const unsigned long long need = (1ull << fk) - 1ull;
+            if ((part(agg, k) & need) == need) { found[k] = true; f[k] = fk; }
+          }
+        }
+        all = all && found[k];
       }
-      const u64 inc = __ballot(lvl >= LB_INCL);
-      if (inc != 0ull) {
-        f = __builtin_ctzll(inc);
-        const u64 need = (1ull << f) - 1ull;
-        if ((__ballot(lvl >= LB_AGG) & need) == need) break;
-      }
-      if (!published) {
-        lb_store<Cf>(rec, lane, gm, gl, ga);
+      if (all) break;
+      bool stored = false;
+#pragma unroll
+      for (int k = 0; k < HP; ++k)
+        if (!found[k] && !pub[k]) {
+          lb_store<Cf>(rec_of(k), lane, gm[k], gl[k], ga[k]);
+          pub[k] = true;
+          stored = true;
+        }
+      if (stored) {
         wait_all_memory();
-        if (lane == 0) st_dev(stw, tag_word(E, LB_AGG));
-        published = true;
+#pragma unroll
+        for (int k = 0; k < HP; ++k)
+          if (pub[k] && !found[k] && lane == 0) st_dev(stw_of(k), tag_word(E, LB_AGG));
       }
       if (lb_give_up(p, E, spin)) {
         ok = false;
@@ -345,78 +395,120 @@ __device__ bool seg_head(const Params& p, uint32_t E, int s, int j, int n, int n
       __builtin_amdgcn_s_sleep(1);
     }
     if (ok) {
-      const int jb = j - 1 - f;
-      if (jb >= 0) lb_load<Cf>(rec0 + (size_t)jb * rstride + incl, lane, x.M, x.L, x.A);
-      for (int i = f - 1; i >= 0; --i) {
-        float m, l, a[DPL];
-        lb_load<Cf>(rec0 + (size_t)(j - 1 - i) * rstride, lane, m, l, a);
-        lb_combine<Cf>(x, m, l, a);
+#pragma unroll
+      for (int k = 0; k < HP; ++k) {
+        if (!act[k]) continue;
+        const float* rec0 = rec0_of(k);
+        const int jb = j - 1 - f[k];
+        if (jb >= 0) lb_load<Cf>(rec0 + (size_t)jb * rstride + incl, lane, x[k].M, x[k].L, x[k].A);
+        for (int i = f[k] - 1; i >= 0; --i) {
+          float m, l, a[DPL];
+          lb_load<Cf>(rec0 + (size_t)(j - 1 - i) * rstride, lane, m, l, a);
+          lb_combine<Cf>(x[k], m, l, a);
+        }
       }
     }
   }
   if (ok) {
-    LbState<Cf> xi = x;
-    lb_combine<Cf>(xi, gm, gl, ga);
-    lb_store<Cf>(rec + incl, lane, xi.M, xi.L, xi.A);
+#pragma unroll
+    for (int k = 0; k < HP; ++k) {
+      if (!act[k]) continue;
+      LbState<Cf> xi = x[k];
+      lb_combine<Cf>(xi, gm[k], gl[k], ga[k]);
+      lb_store<Cf>(rec_of(k) + incl, lane, xi.M, xi.L, xi.A);
+    }
     wait_all_memory();
-    if (lane == 0) st_dev(stw, tag_word(E, LB_INCL));
+#pragma unroll
+    for (int k = 0; k < HP; ++k)
+      if (act[k] && lane == 0) st_dev(stw_of(k), tag_word(E, LB_INCL));
   }
 
   // ---- statistics of every position, from X_j (a head found dead here is
   // resolved as stopped; the mask is read before the statistics and looked at
   // after them, so its latency hides behind them)
-  const uint32_t mword = ld_dev32(p.lb_heads + s);
-  uint32_t passb = 0u;
-  SegCarry<Cf> hc;
+  const uint32_t mword2 = ld_dev32(p.lb_heads + s);
   // the carry entering the segment, from X_j
-  auto enter = [&](SegCarry<Cf>& e) {
-    const float rl = x.L > 0.f ? __builtin_amdgcn_rcpf(x.L) : 0.f;
+  auto enter = [&](SegCarry<Cf>& e, const LbState<Cf>& xs) {
+    const float rl = xs.L > 0.f ? __builtin_amdgcn_rcpf(xs.L) : 0.f;
     float sq[1] = {0.f};
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) {
-      e.O[k] = x.L > 0.f ? x.A[k] * rl : 0.f;
-      const float op = DPL * lane + k < p.probe ? e.O[k] : 0.f;
+    for (int q = 0; q < DPL; ++q) {
+      e.O[q] = xs.L > 0.f ? xs.A[q] * rl : 0.f;
+      const float op = DPL * lane + q < p.probe ? e.O[q] : 0.f;
       sq[0] = fmaf(op, op, sq[0]);
     }
-    e.M = x.M;
-    e.L = x.L;
+    e.M = xs.M;
+    e.L = xs.L;
     e.Np = xreduce<1>(sq, lane);
   };
-  enter(hc);
+  SegCarry<Cf> hc[HP];
+  uint32_t passb[HP];
+#pragma unroll
+  for (int k = 0; k < HP; ++k) {
+    enter(hc[k], x[k]);
+    passb[k] = 0u;
+  }
   if (ok) {
     float oo_unused[C][DPL];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       if (c * C < ns) {
-        const u64 pb = seg_chunk<Cf, false>(hc, slots, h, c * C, min(C, ns - c * C), t0 + c * C, p, lane, oo_unused);
-        passb |= (uint32_t)pb << (c * C);
+#pragma unroll
+        for (int k = 0; k < HP; ++k)
+          if (act[k]) {
+            const u64 pb = seg_chunk<Cf, false>(hc[k], slots, head_of(k), c * C, min(C, ns - c * C), t0 + c * C, p,
+                                                lane, oo_unused);
+            passb[k] |= (uint32_t)pb << (c * C);
+          }
       }
     }
   }
-  const bool dead = ((mword >> h) & 1u) != 0u;
-  if (dead) passb = 0u;
+  bool dead[HP];
+#pragma unroll
+  for (int k = 0; k < HP; ++k) {
+    dead[k] = act[k] && ((mword2 >> head_of(k)) & 1u) != 0u;
+    if (dead[k]) passb[k] = 0u;
+  }
   const uint32_t sinkb = (uint32_t)__ballot(lane < ns && ent[min(lane, S - 1)].x == 0);
   if (ok) {
-    if (lane == 0) st_dev(reinterpret_cast<u64*>(rec + D + 2), ((u64)sinkb << 32) | passb);
+#pragma unroll
+    for (int k = 0; k < HP; ++k)
+      if (act[k] && lane == 0) st_dev(reinterpret_cast<u64*>(rec_of(k) + D + 2), ((u64)sinkb << 32) | passb[k]);
     wait_all_memory();
-    if (lane == 0) st_dev(stw, tag_word(E, LB_PASS));
+#pragma unroll
+    for (int k = 0; k < HP; ++k)
+      if (act[k] && lane == 0) st_dev(stw_of(k), tag_word(E, LB_PASS));
   }
 
   // ---- pass count, block-0 flag and running flag entering the segment
-  int cnt = 0;
-  bool sink = false, run = true;
+  int cnt[HP];
+  bool sink[HP], run[HP];
+#pragma unroll
+  for (int k = 0; k < HP; ++k) { cnt[k] = 0; sink[k] = false; run[k] = act[k]; }
   if (ok && j > 0) {
     uint32_t v = 0u;
-    int f = 0;
+    int f[HP];
+#pragma unroll
+    for (int k = 0; k < HP; ++k) f[k] = 0;
     for (int spin = 0;; ++spin) {
-      v = seg_probe(st0, g, j, E, lane);
+      v = probe(act);
       const uint32_t lvl = v & LB_LEVEL;
-      const u64 fin = __ballot(lvl == LB_FIN || lvl == SG_DEAD);
-      if (fin != 0ull) {
-        f = __builtin_ctzll(fin);
-        const u64 need = (1ull << f) - 1ull;
-        if ((__ballot(lvl == LB_PASS) & need) == need) break;
+      const unsigned long long fin = __ballot(lvl == LB_FIN || lvl == SG_DEAD);
+      const unsigned long long pas = __ballot(lvl == LB_PASS);
+      bool all = true;
+#pragma unroll
+      for (int k = 0; k < HP; ++k) {
+        if (!act[k]) continue;
+        const unsigned long long fk = part(fin, k);
+        bool got = false;
+        if (fk != 0ull) {
+          f[k] = __builtin_ctzll(fk);
+          const unsigned long long need = (1ull << f[k]) - 1ull;
+          got = (part(pas, k) & need) == need;
+        }
+        all = all && got;
       }
+      if (all) break;
       if (lb_give_up(p, E, spin)) {
         ok = false;
         break;
@@ -424,79 +516,95 @@ __device__ bool seg_head(const Params& p, uint32_t E, int s, int j, int n, int n
       __builtin_amdgcn_s_sleep(1);
     }
     if (ok) {
-      const uint32_t wf = (uint32_t)readlane((int)v, f);
-      cnt = (int)(wf >> SG_CNT_SH);
-      sink = (wf & SG_SINK) != 0u;
-      run = (wf & LB_LEVEL) == LB_FIN && (wf & SG_RUN) != 0u;
-      // bits of segments j-f .. j-1 (lane i: segment j-1-i), read together
-      u64 bits = 0ull;
-      if (lane < f) bits = ld_dev(reinterpret_cast<const u64*>(rec0 + (size_t)(j - 1 - lane) * rstride + D + 2));
-      for (int i = f - 1; i >= 0 && run; --i) {
-        const uint32_t pw = (uint32_t)readlane((int)(uint32_t)bits, i);
-        const uint32_t kw = (uint32_t)readlane((int)(uint32_t)(bits >> 32), i);
-        int unused = -1;
-        seg_apply(cnt, sink, run, pw, kw, S, cap, p.patience, lane, unused);
+#pragma unroll
+      for (int k = 0; k < HP; ++k) {
+        if (!act[k]) continue;
+        const uint32_t wf = (uint32_t)readlane((int)v, k * LPH + f[k]);
+        cnt[k] = (int)(wf >> SG_CNT_SH);
+        sink[k] = (wf & SG_SINK) != 0u;
+        run[k] = (wf & LB_LEVEL) == LB_FIN && (wf & SG_RUN) != 0u;
+        // bits of segments j-f .. j-1 (lane i: segment j-1-i), read together
+        u64 bits = 0ull;
+        if (lane < f[k]) bits = ld_dev(reinterpret_cast<const u64*>(rec0_of(k) + (size_t)(j - 1 - lane) * rstride + D + 2));
+        for (int i = f[k] - 1; i >= 0 && run[k]; --i) {
+          const uint32_t pw = (uint32_t)readlane((int)(uint32_t)bits, i);
+          const uint32_t kw = (uint32_t)readlane((int)(uint32_t)(bits >> 32), i);
+          int unused = -1;
+          seg_apply(cnt[k], sink[k], run[k], pw, kw, S, cap, p.patience, lane, unused);
+        }
       }
     }
   }
-  // ---- the segment's own positions
-  int fire_at = -1;
-  if (ok && run && !dead) seg_apply(cnt, sink, run, passb, sinkb, ns, cap, p.patience, lane, fire_at);
-  if (ok && dead) run = false;
-  if (ok && lane == 0)
-    st_dev(stw, tag_word(E, LB_FIN | (run ? SG_RUN : 0u) | (sink ? SG_SINK : 0u) |
-                                ((uint32_t)min(cnt, cap) << SG_CNT_SH)));
 
-  // ---- outputs
-  bool stopped = false;
-  if (ok && fire_at >= 0) {
-    // fold the segment again up to the chunk holding the stop (the same
-    // arithmetic, so the same output as the statistics saw)
-    const int c = fire_at / C;
-    SegCarry<Cf> h2;
-    enter(h2);
-    float oo[C][DPL];
-    for (int cc = 0; cc < c; ++cc)
-      (void)seg_chunk<Cf, false>(h2, slots, h, cc * C, C, t0 + cc * C, p, lane, oo);
-    (void)seg_chunk<Cf, true>(h2, slots, h, c * C, min(C, ns - c * C), t0 + c * C, p, lane, oo);
-    const int k = fire_at - c * C;
-    float ov[DPL];
+  // ---- the segment's own positions, the resolved states, the outputs
+  bool stopped[HP];
 #pragma unroll
-    for (int q = 0; q < DPL; ++q) ov[q] = oo[0][q];
+  for (int k = 0; k < HP; ++k) {
+    stopped[k] = false;
+    if (!act[k]) continue;
+    const int h = head_of(k);
+    const size_t head = (size_t)(s / p.hkv) * p.hq + (size_t)(s % p.hkv) * g + h;
+    float* out_row = p.out + head * D;
+    int fire_at = -1;
+    if (ok && run[k] && !dead[k]) seg_apply(cnt[k], sink[k], run[k], passb[k], sinkb, ns, cap, p.patience, lane, fire_at);
+    if (ok && dead[k]) run[k] = false;
+    if (ok && lane == 0)
+      st_dev(stw_of(k), tag_word(E, LB_FIN | (run[k] ? SG_RUN : 0u) | (sink[k] ? SG_SINK : 0u) |
+                                        ((uint32_t)min(cnt[k], cap) << SG_CNT_SH)));
+    if (ok && fire_at >= 0) {
+      // fold the segment again up to the chunk holding the stop (the same
+      // arithmetic, so the same output as the statistics saw)
+      const int c = fire_at / C;
+      SegCarry<Cf> h2;
+      enter(h2, x[k]);
+      float oo[C][DPL];
+      for (int cc = 0; cc < c; ++cc)
+        (void)seg_chunk<Cf, false>(h2, slots, h, cc * C, C, t0 + cc * C, p, lane, oo);
+      (void)seg_chunk<Cf, true>(h2, slots, h, c * C, min(C, ns - c * C), t0 + c * C, p, lane, oo);
+      const int kk = fire_at - c * C;
+      float ov[DPL];
 #pragma unroll
-    for (int t = 1; t < C; ++t)
-      if (k == t)
+      for (int q = 0; q < DPL; ++q) ov[q] = oo[0][q];
 #pragma unroll
-        for (int q = 0; q < DPL; ++q) ov[q] = oo[t][q];
+      for (int t = 1; t < C; ++t)
+        if (kk == t)
 #pragma unroll
-    for (int q = 0; q < DPL; ++q) out_row[DPL * lane + q] = ov[q];
-    if (lane == 0) p.stop_block[head] = t0 + fire_at + 1;
-    stopped = true;
-  } else if (ok && run && last) {
-    // never stopped: the output after all n blocks
+          for (int q = 0; q < DPL; ++q) ov[q] = oo[t][q];
 #pragma unroll
-    for (int q = 0; q < DPL; ++q) out_row[DPL * lane + q] = hc.O[q];
-    if (lane == 0) p.stop_block[head] = n;
-    stopped = true;  // its result is written
-  }
-  if (!ok) {
+      for (int q = 0; q < DPL; ++q) out_row[DPL * lane + q] = ov[q];
+      if (lane == 0) p.stop_block[head] = t0 + fire_at + 1;
+      stopped[k] = true;
+    } else if (ok && run[k] && last) {
+      // never stopped: the output after all n blocks
 #pragma unroll
-    for (int q = 0; q < DPL; ++q) out_row[DPL * lane + q] = __builtin_nanf("");
-    if (lane == 0) {
-      p.stop_block[head] = -1;
-      lb_fail(p, E);
+      for (int q = 0; q < DPL; ++q) out_row[DPL * lane + q] = hc[k].O[q];
+      if (lane == 0) p.stop_block[head] = n;
+      stopped[k] = true;  // its result is written
     }
-    stopped = true;
+    if (!ok) {
+#pragma unroll
+      for (int q = 0; q < DPL; ++q) out_row[DPL * lane + q] = __builtin_nanf("");
+      if (lane == 0) {
+        p.stop_block[head] = -1;
+        lb_fail(p, E);
+      }
+      stopped[k] = true;
+    }
   }
-  if (stopped) wait_all_memory();  // the resolved status is out before the mask bit
-  if (stopped && lane == 0) {
-    // mark the head finished; close the stream when the whole group is
-    const uint32_t bit = 1u << h;
-    const uint32_t was = __hip_atomic_fetch_or(p.lb_heads + s, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((was | bit) == (1u << g) - 1u && was != (was | bit))
+  bool any = false;
+#pragma unroll
+  for (int k = 0; k < HP; ++k) any = any || stopped[k];
+  if (any) wait_all_memory();  // the resolved statuses are out before the mask bits
+  if (any && lane == 0) {
+    // mark the heads finished; close the stream when the whole group is
+    uint32_t bits = 0u;
+#pragma unroll
+    for (int k = 0; k < HP; ++k)
+      if (stopped[k]) bits |= 1u << head_of(k);
+    const uint32_t was = __hip_atomic_fetch_or(p.lb_heads + s, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((was | bits) == (1u << g) - 1u && was != (was | bits))
       __hip_atomic_fetch_or(p.lb_claim + s, CLAIM_FIN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  return ok;
 }
 
 // Claim the next item (whole wave 0): a segment of the current stream while
@@ -800,11 +908,7 @@ __global__ __launch_bounds__((64 * SegCfg<KV, D, B, GM>::NW3)) void art_seg_kern
         // every head stopped in an earlier segment
         if (dw == 0 && lane < g) st_dev(p.lb_st + ((size_t)s * p.max_chunks + j) * g + lane, tag_word(E, SG_DEAD));
       } else {
-#pragma unroll
-        for (int q = 0; q < HP; ++q) {
-          const int h = dw + NS * q;
-          if (h < g) (void)seg_head<Cf>(p, E, s, j, n, ns, h, slots[b], ent[b], lane);
-        }
+        if (dw < g) seg_heads<Cf>(p, E, s, j, n, ns, dw, slots[b], ent[b], lane);
       }
       lds_wait();  // this wave's reads of the buffer are complete
       if (lane == 0 && lds_add(&sh.ddone[b], 1) == NS - 1) {
