@@ -167,6 +167,22 @@ def test_empty_short_and_single_token_sequences():
     assert np.all(out[0] == 0.0) and np.all(stop[0] == 0) and np.all(fetched[0] == 0)
 
 
+@pytest.mark.parametrize("wgs", ["1", "3", "7", "256", "1000", "5000"])
+def test_full_attention_over_any_workgroup_count(wgs):
+    """Full attention partitions the flattened block list over ART_FULL_WGS workgroups: one workgroup
+    folding every stream, counts that cut streams at odd places, more workgroups than blocks (some get none)
+    and many pieces per stream all match the oracle on every head, with empty and one-block sequences mixed
+    into a ragged batch."""
+    base = synth.make_case(W.RAGGED, batch=6)
+    lens = [int(x) for x in base["seq_lens"]]
+    lens[1] = 0
+    lens[3] = 1
+    case = _with_lens(base, lens)
+    _with_env(dict(ART_FULL_WGS=wgs), lambda: check_full(case))
+    out, stop, fetched = _with_env(dict(ART_FULL_WGS=wgs), lambda: _device_run(case, 0.0, 0.0, 1))
+    assert np.all(out[1] == 0.0) and np.all(stop[1] == 0) and np.all(fetched[1] == 0)
+
+
 def test_sink_not_first_and_random_orders():
     case = synth.make_case(W.LLAMA3_8B, batch=3, context=3000)
     rng = np.random.default_rng(11)
