@@ -693,10 +693,7 @@ __device__ void seg_claim(const Params& p, uint32_t E, int* info, int* pclaim, i
     const int ob = orow[t0 + lane];
     ent[lane] = make_int2(ob, trow[ob]);
   }
-  const char* qsrc = static_cast<const char*>(p.q) + ((size_t)sq * p.hq + (size_t)kvh * p.g) * QROWB;
-  const int qwords = p.g * QROWB / 16;
-  for (int i = lane; i < qwords; i += 64)
-    *reinterpret_cast<uint4*>(qdst + 16 * i) = *reinterpret_cast<const uint4*>(qsrc + 16 * i);
+  q_to_lds<Cf>(static_cast<const char*>(p.q) + ((size_t)sq * p.hq + (size_t)kvh * p.g) * QROWB, qdst, p.g, lane, 64);
   // a group whose heads have all stopped needs nothing more (the stops lie
   // in earlier segments: a segment resolves only after this one's pass bits)
   const bool done = ld_dev32(p.lb_heads + got_s) == (1u << p.g) - 1u;
@@ -719,7 +716,7 @@ __global__ __launch_bounds__((64 * SegCfg<KV, D, B, GM>::NW3)) void art_seg_kern
   constexpr int QROWB = KV == KV_FP8 ? 2 * D : Cf::R;
   __shared__ __attribute__((aligned(16))) float slots[2][S * SLOTF];
   __shared__ __attribute__((aligned(16))) float pbuf_all[NP][PD][GM * B];
-  __shared__ __attribute__((aligned(16))) char qs[2][GM * QROWB];
+  __shared__ __attribute__((aligned(16))) char qs[2][GM * QLds<Cf>::STRIDE];
   __shared__ int2 ent[2][S];
   __shared__ SegShared sh;
 

@@ -152,12 +152,31 @@ __device__ __forceinline__ void lds_wait() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// The group's query rows in LDS: ROWB bytes each (fp8 K: q stays bf16), rows
+// STRIDE bytes apart; the 16 extra bytes put the rows on different banks, so
+// that the lanes of different heads reading the same column do not collide.
+template <class Cf>
+struct QLds {
+  static constexpr int ROWB = Cf::KV == KV_FP8 ? 2 * Cf::D : Cf::R;
+  static constexpr int STRIDE = ROWB + 16;
+};
+
+// Copy the g query rows starting at src into the padded LDS rows (thread
+// `tid` of `nthreads`).
+template <class Cf>
+__device__ __forceinline__ void q_to_lds(const char* src, char* dst, int g, int tid, int nthreads) {
+  constexpr int W = QLds<Cf>::ROWB / 16;  // 16-byte words per row
+  for (int i = tid; i < g * W; i += nthreads) {
+    const int r = i / W, c = i - r * W;
+    *reinterpret_cast<uint4*>(dst + r * QLds<Cf>::STRIDE + 16 * c) = reinterpret_cast<const uint4*>(src)[i];
+  }
+}
+
 // q fragments of the group from its LDS copy (rows past the group repeat the
 // last head: their columns are never read back).
 template <class Cf>
 __device__ __forceinline__ void q_from_lds(const char* qs, int g, int lane, uint4 (&qf)[Cf::QF]) {
-  constexpr int QROWB = Cf::KV == KV_FP8 ? 2 * Cf::D : Cf::R;
-  const char* row = qs + min(lane & 15, g - 1) * QROWB;
+  const char* row = qs + min(lane & 15, g - 1) * QLds<Cf>::STRIDE;
   const int base = (lane >> 4) * 16;
   if constexpr (Cf::KV == KV_FP8) {
 #pragma unroll
@@ -417,8 +436,8 @@ __global__ __launch_bounds__((64 * StreamCfg<KV, D, B, GM>::NW2)) void art_strea
   __shared__ __attribute__((aligned(16))) float ring[RING * SLOTF];
   __shared__ __attribute__((aligned(16))) float pbuf_all[NP][PD][GM * B];
   __shared__ StreamShared sh;
-  constexpr int QROWB = KV == KV_FP8 ? 2 * D : Cf::R;  // bytes of one query row (fp8 K: q stays bf16)
-  __shared__ __attribute__((aligned(16))) char qs[GM * QROWB];
+  constexpr int QROWB = QLds<Cf>::ROWB;  // bytes of one query row (fp8 K: q stays bf16)
+  __shared__ __attribute__((aligned(16))) char qs[GM * QLds<Cf>::STRIDE];
   __shared__ int2 ent[STREAM_ENT];
 
   const int stream = blockIdx.x;
@@ -449,9 +468,7 @@ __global__ __launch_bounds__((64 * StreamCfg<KV, D, B, GM>::NW2)) void art_strea
     if (threadIdx.x < 8) sh.win[threadIdx.x] = threadIdx.x + 1;
   }
   // the group's query rows, for the producers' MFMA operands
-  for (int i = threadIdx.x; i < g * QROWB / 16; i += 64 * Cf::NW2)
-    reinterpret_cast<uint4*>(qs)[i] =
-        reinterpret_cast<const uint4*>(static_cast<const char*>(p.q) + head0 * QROWB)[i];
+  q_to_lds<Cf>(static_cast<const char*>(p.q) + head0 * QROWB, qs, g, threadIdx.x, 64 * Cf::NW2);
   if (threadIdx.x < NS) sh.prog[threadIdx.x] = (int)threadIdx.x < g ? 0 : STREAM_BIG;
   if (threadIdx.x == 0) { sh.done = 0; sh.nfired = 0; sh.fsum = 0; sh.pfin = 0; sh.err = 0; sh.claim = 0; }
   lds_barrier();
