@@ -2643,8 +2643,16 @@ __device__ __forceinline__ long long wave_incl_scan(long long x, int lane) {
 // leaves a partial (max, sum, numerator per head) in slot s + i of the
 // workspace (injective: stream s's pieces take consecutive workgroups), and
 // the stream's last piece to finish merges its pieces in order.
+// Waves per SIMD the full-attention kernel is compiled for: three for fp8 KV
+// with 16-token blocks (the register budget then drops from 178 to 136, no
+// spills; 212-243 -> 204 us on the fp8 Qwen shape, box to box), else what
+// the compiler picks.
+template <int KV, int B>
+struct FullWaves {
+  static constexpr int v = (KV == KV_FP8 && B == 16) ? 3 : 1;
+};
 template <int KV, int D, int B, int GM>
-__global__ __launch_bounds__(WG) void full_split_kernel(Params p) {
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(FullWaves<KV, B>::v))) void full_split_kernel(Params p) {
   using Cf = Cfg<KV, D, B, GM>;
   constexpr int HPW = (GM + NW - 1) / NW, DPL = Cf::DPL;
   __shared__ __attribute__((aligned(16))) float mw_a[NW][GM][D];
