@@ -42,7 +42,7 @@ import numpy as np  # noqa: E402
 PEAK_GBPS = 8000.0
 METRIC = "decode-attn µs/step + achieved HBM GB/s (frac of peak) + KV fraction read, 1 GPU"
 KERNEL_SOURCES = ["kv_cache_run_amd/csrc/art_kernels_impl.h", "kv_cache_run_amd/csrc/art_stream.h",
-                  "kv_cache_run_amd/csrc/art_internal.h", "kv_cache_run_amd/csrc/kern_art_bf16.hip",
+                  "kv_cache_run_amd/csrc/art_seg.h", "kv_cache_run_amd/csrc/art_internal.h", "kv_cache_run_amd/csrc/kern_art_bf16.hip",
                   "kv_cache_run_amd/csrc/kern_art_fp8.hip", "kv_cache_run_amd/csrc/kern_art_f32.hip",
                   "kv_cache_run_amd/csrc/kern_full_bf16.hip", "kv_cache_run_amd/csrc/kern_full_fp8.hip",
                   "kv_cache_run_amd/csrc/kern_full_f32.hip", "kv_cache_run_amd/csrc/art_api.cpp"]

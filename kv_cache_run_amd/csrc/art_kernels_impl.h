@@ -126,10 +126,9 @@ struct Cfg {
   // Full attention with fp8 V: P V on v_mfma_f32_16x16x16_bf16 instead of
   // the fp32 4x4x1 product (fp8 values are exact in bf16; P goes in as two
   // bf16 parts, hi + lo, so the products keep about 16 bits of P), with V
-  // transposed through a per-wave LDS buffer [D][VTS] of bf16.
+  // loaded four token rows per lane and transposed in registers.
   static constexpr bool PVB = KV == KV_FP8 && PV4 && D == 128;
   static constexpr int NACCF = PVB ? D / 16 : NACC;   // accumulators of the full-attention kernel
-  static constexpr int VTS = B + 2;                   // bf16 per d-row of V^T (an odd number of dwords)
   static_assert(BPB * NBW == C && HWV <= NWA, "one block wave per block of a chunk");
   static_assert(!PV4 || NLD % 4 == 0, "P is read four tokens at a time");
   static_assert(2 * C <= 64, "stat reduction holds at most 64 values");
@@ -306,7 +305,11 @@ __device__ __forceinline__ uint32_t ld_kv4(const char* a) {
 // and streams them (measured: 0.82 instead of 0.73 of HBM peak on 8 KiB
 // tiles); the terminating kernels keep the default, since their clamped
 // re-reads of a chunk past a stream's end are meant to hit in the cache.
-template <class Cf, bool NT = false>
+// VQ: V in the full-attention kernel's fp8 layout for the bf16 P V product
+// (Cf::PVB): lane (c, q) holds, in v[8 t + 2 r] and v[8 t + 2 r + 1], bytes
+// 8 c .. 8 c + 7 of token row 16 t + 4 q + r (one 8-byte load per row: the
+// 16 lanes of a q read a whole 128-byte row).
+template <class Cf, bool NT = false, bool VQ = false>
 __device__ __forceinline__ void load_block(BlockRegs<Cf>& r, const char* kt, const char* vt, int lane, int nvalid) {
   const int c = lane & 15;
   const int q = lane >> 4;
@@ -315,7 +318,25 @@ __device__ __forceinline__ void load_block(BlockRegs<Cf>& r, const char* kt, con
 #pragma unroll
     for (int i = 0; i < Cf::NKL; ++i)
       r.k[t][i] = ld_kv16<NT>(kt + (size_t)(16 * t + c) * Cf::R + q * 16 + 64 * i);
-  if constexpr (Cf::PV4) {
+  if constexpr (VQ) {
+    static_assert(Cf::PVB && Cf::R == 128 && Cf::VN == 8 * Cf::T, "fp8 rows of 128 bytes");
+    const char* src = vt + (size_t)(4 * q) * Cf::R + 8 * c;
+#pragma unroll
+    for (int t = 0; t < Cf::T; ++t)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const uint2 x = ld_kv8<NT>(src + (size_t)(16 * t + rr) * Cf::R);
+        r.v[8 * t + 2 * rr] = x.x;
+        r.v[8 * t + 2 * rr + 1] = x.y;
+      }
+    if (nvalid < Cf::B) {
+#pragma unroll
+      for (int t = 0; t < Cf::T; ++t)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          if (16 * t + 4 * q + rr >= nvalid) r.v[8 * t + 2 * rr] = r.v[8 * t + 2 * rr + 1] = 0u;
+    }
+  } else if constexpr (Cf::PV4) {
     // load u covers token rows u*RPL .. u*RPL+RPL-1; lane: row u*RPL + lane/LPR,
     // bytes (lane % LPR) * BPL .. +BPL of it
     const int rg = lane / Cf::LPR;
@@ -2532,39 +2553,22 @@ __global__ __launch_bounds__(64 * WNW) void art_win_scan_kernel(Params p) {
 // ---------------------------------------------------------------------------
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// fp8 V of one block, transposed into this wave's LDS buffer vt[d][token]
-// as bf16.  Lane l holds token row 2u + l / 32, elements d0 .. d0 + 3 with
-// d0 = 4 (l % 32), of load u; one lane swap pairs rows 2u and 2u + 1, so
-// every store writes two tokens of one d.
-template <class Cf>
-__device__ __forceinline__ void vt_store_fp8(const BlockRegs<Cf>& r, uint32_t* vt, int lane) {
-  static_assert(Cf::RPL == 2 && Cf::VW == 1, "fp8 rows of 128 bytes: two rows per load, one dword per lane");
-  constexpr int VTW = Cf::VTS / 2;  // dwords per d-row
-  const int da = 4 * (lane & 31) + (lane >= 32 ? 2 : 0);
-#pragma unroll
-  for (int u = 0; u < Cf::NLD; ++u) {
-    const uint2 bb = fp8x4_to_bf16x4(r.v[u]);
-    float x = bitsf(bb.x), y = bitsf(bb.y);
-    // lanes < 32: x = (row 2u: d0, d0+1), y <- (row 2u+1: d0, d0+1) of lane + 32;
-    // lanes >= 32: x <- (row 2u: d0+2, d0+3) of lane - 32, y = (row 2u+1: d0+2, d0+3)
-    swap32(x, y);
-    const uint32_t X = fbits(x), Y = fbits(y);
-    vt[da * VTW + u] = (X & 0xffffu) | (Y << 16);
-    vt[(da + 1) * VTW + u] = (X >> 16) | (Y & 0xffff0000u);
-  }
+// P V for one block on bf16 MFMA, V as load_block<Cf, NT, true> holds it.
+// Four of a lane's dwords (token rows 4q .. 4q+3, bytes 8c + 4k .. 8c + 4k
+// + 3, k = 0, 1) form a 4x4 byte matrix; two byte permutations pair the
+// rows' bytes so that each bf16 conversion yields two consecutive tokens of
+// one d.  So d-tile j = 4 k + e (e = 0..3) takes, in row m = c, the element
+// d = 8 c + j: A = that V^T tile (lane (c, q): tokens 4q .. 4q+3), B = P^T
+// (lane: head c, tokens 4q .. 4q+3: the score layout itself), P split into
+// bf16 hi + lo (truncation: P = hi + lo + O(2^-16 P)).  acc[j] then holds,
+// in lane (c, q) component i, head c at d = 8 (4 q + i) + j.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
-
-// P V for one block on bf16 MFMA: acc[j] (d-tile j, 16 d) holds, in lane
-// (c, q) component i, head c at d = 16 j + 4 q + i.  A = V^T tile (lane: d =
-// 16 j + c, tokens 4q .. 4q+3 from vt), B = P^T (lane: head c, tokens 4q ..
-// 4q+3: the score layout itself), P split into bf16 hi + lo (truncation: P =
-// hi + lo + O(2^-16 P)).
 template <class Cf>
-__device__ __forceinline__ void pvb_block(const BlockRegs<Cf>& r, const float (&pq)[Cf::T][4], uint32_t* vt, int lane,
-                                          f32x4 (&acc)[Cf::NACCF]) {
-  constexpr int VTW = Cf::VTS / 2;
-  vt_store_fp8<Cf>(r, vt, lane);
-  const int c = lane & 15, q = lane >> 4;
+__device__ __forceinline__ void pvb_block(const BlockRegs<Cf>& r, const float (&pq)[Cf::T][4], f32x4 (&acc)[Cf::NACCF]) {
+  static_assert(Cf::NACCF == 8, "eight d-tiles of 16");
 #pragma unroll
   for (int t = 0; t < Cf::T; ++t) {
     uint32_t hi[4], lo[4];
@@ -2582,11 +2586,23 @@ __device__ __forceinline__ void pvb_block(const BlockRegs<Cf>& r, const float (&
       pl = __builtin_bit_cast(s16x4, make_uint2(l0, l1));
     }
 #pragma unroll
-    for (int j = 0; j < Cf::D / 16; ++j) {
-      const uint32_t* src = vt + (16 * j + c) * VTW + 8 * t + 2 * q;
-      const s16x4 a = __builtin_bit_cast(s16x4, make_uint2(src[0], src[1]));
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ph, acc[j], 0, 0, 0);
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pl, acc[j], 0, 0, 0);
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t w[4] = {r.v[8 * t + k], r.v[8 * t + 2 + k], r.v[8 * t + 4 + k], r.v[8 * t + 6 + k]};
+      // bytes (row 0, row 1) of columns 0 and 2, of columns 1 and 3; likewise rows 2, 3
+      const uint32_t a01 = __builtin_amdgcn_perm(w[1], w[0], 0x06020400u);
+      const uint32_t b01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030501u);
+      const uint32_t a23 = __builtin_amdgcn_perm(w[3], w[2], 0x06020400u);
+      const uint32_t b23 = __builtin_amdgcn_perm(w[3], w[2], 0x07030501u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = (e & 1) ? b01 : a01, y = (e & 1) ? b23 : a23;
+        const uint2 xy = e >= 2 ? make_uint2(fp8x2_to_bf16x2<true>(x), fp8x2_to_bf16x2<true>(y))
+                                : make_uint2(fp8x2_to_bf16x2<false>(x), fp8x2_to_bf16x2<false>(y));
+        const s16x4 a = __builtin_bit_cast(s16x4, xy);
+        f32x4& o = acc[4 * k + e];
+        o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ph, o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pl, o, 0, 0, 0);
+      }
     }
   }
 }
@@ -2594,7 +2610,7 @@ __device__ __forceinline__ void pvb_block(const BlockRegs<Cf>& r, const float (&
 template <class Cf>
 __device__ __forceinline__ void full_block(const BlockRegs<Cf>& r, int nvalid, float ksc, float vsc,
                                            const uint4 (&qf)[Cf::QF], float qk_log2, int lane, float& m_run,
-                                           float& l_run, f32x4 (&acc)[Cf::NACCF], float* pbuf, uint32_t* vt) {
+                                           float& l_run, f32x4 (&acc)[Cf::NACCF], float* pbuf) {
   f32x4 S[Cf::T];
   qk_scores<Cf>(r, qf, S);
   float x[Cf::T][4];
@@ -2614,12 +2630,18 @@ __device__ __forceinline__ void full_block(const BlockRegs<Cf>& r, int nvalid, f
   ls = rows_sum(ls);
   l_run = fmaf(al, l_run, ls);
   m_run = mn;
+  // Once the running maxima settle, every factor is exactly 2^0 = 1 and the
+  // rescale would leave the accumulators unchanged bit for bit: it is skipped
+  // unless some head's maximum moved (a wave-uniform test).
+  const bool rescale = __ballot((lane & 15) < Cf::GM && al != 1.f) != 0ull;
   if constexpr (Cf::PVB) {
+    if (rescale) {
 #pragma unroll
-    for (int j = 0; j < Cf::NACCF; ++j) acc[j] *= al;  // lane (c, q) holds head c
-    pvb_block<Cf>(r, pq, vt, lane, acc);
+      for (int j = 0; j < Cf::NACCF; ++j) acc[j] *= al;  // lane (c, q) holds head c
+    }
+    pvb_block<Cf>(r, pq, acc);
   } else {
-    pv_rescale<Cf>(acc, al);
+    if (rescale) pv_rescale<Cf>(acc, al);
     pv_block<Cf>(r, pq, pbuf, lane, acc);
   }
 }
@@ -2659,7 +2681,6 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(FullWaves<KV
   __shared__ float mw_m[NW][GM];
   __shared__ float mw_l[NW][GM];
   __shared__ __attribute__((aligned(16))) float pbuf_all[NW][Cf::PV4 && !Cf::PVB ? GM * B : 4];
-  __shared__ __attribute__((aligned(16))) uint32_t vt_all[NW][Cf::PVB ? D * Cf::VTS / 2 : 4];
   __shared__ long long plan[4];  // W, first position, end position, flattened start of the first sequence
   __shared__ int plan_sq;        // the sequence holding the first position
   __shared__ int is_last;
@@ -2738,7 +2759,6 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(FullWaves<KV
   const char* kbase = static_cast<const char*>(p.k_pages);
   const char* vbase = static_cast<const char*>(p.v_pages);
   float* pbuf = pbuf_all[w];
-  uint32_t* vt = vt_all[w];
 
   while (pos < end) {
     const int s = sq * hkv + kvh;
@@ -2772,7 +2792,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(FullWaves<KV
       auto fold = [&](const BlockRegs<Cf>& r, int k) {
         float ks = 1.f, vs = 1.f;
         if constexpr (KV == KV_FP8) { ks = readlanef(ks_t, k); vs = readlanef(vs_t, k); }
-        full_block<Cf>(r, nvalid_of(k), ks, vs, qf, p.qk_log2, lane, m_run, l_run, acc, pbuf, vt);
+        full_block<Cf>(r, nvalid_of(k), ks, vs, qf, p.qk_log2, lane, m_run, l_run, acc, pbuf);
       };
       // Register ring of PF block buffers: while block k is folded, blocks
       // k+1 .. k+PF-1 are in flight.  Loads are unconditional (past the last
@@ -2784,14 +2804,14 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(FullWaves<KV
       for (int jj = 0; jj < PF - 1; ++jj) {
         const int kk = min(jj, cnt - 1);
         const size_t o = tile_of(kk);
-        load_block<Cf, true>(ring[jj], kbase + o, vbase + o, lane, nvalid_of(kk));
+        load_block<Cf, true, Cf::PVB>(ring[jj], kbase + o, vbase + o, lane, nvalid_of(kk));
       }
       for (int k = 0; k < cnt; k += PF) {
 #pragma unroll
         for (int jj = 0; jj < PF; ++jj) {
           const int kk = min(k + jj + PF - 1, cnt - 1);
           const size_t o = tile_of(kk);
-          load_block<Cf, true>(ring[(jj + PF - 1) % PF], kbase + o, vbase + o, lane, nvalid_of(kk));
+          load_block<Cf, true, Cf::PVB>(ring[(jj + PF - 1) % PF], kbase + o, vbase + o, lane, nvalid_of(kk));
           __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
           if (k + jj < cnt) fold(ring[jj], k + jj);
         }
@@ -2803,9 +2823,13 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(FullWaves<KV
       const int c = lane & 15;
       if constexpr (Cf::PVB) {
         if (c < GM) {
+          const int q = lane >> 4;
 #pragma unroll
-          for (int jj = 0; jj < Cf::NACCF; ++jj)
-            *reinterpret_cast<f32x4*>(&mw_a[w][c][16 * jj + 4 * (lane >> 4)]) = acc[jj];
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+              *reinterpret_cast<f32x4*>(&mw_a[w][c][8 * (4 * q + i) + 4 * k]) =
+                  f32x4{acc[4 * k][i], acc[4 * k + 1][i], acc[4 * k + 2][i], acc[4 * k + 3][i]};
         }
       } else {
         pv_finish<Cf>(acc);
