@@ -58,7 +58,10 @@ art_status check_desc(const art_decode_desc* d) {
 // larger groups: windows for few, long streams, the look-back scheduler for
 // long streams, scanners otherwise.
 // Segment kernel: ART_SEG_WIN (default 2) segments claimable past a stream's
-// resolved frontier, plus half the frontier; ART_SEG_WGS persistent
+// resolved frontier, plus half the frontier; ART_SEG_EXT (default 2): a
+// workgroup that finds every stream at its window claims on the
+// longest-running stream up to (ART_SEG_EXT + 1) x frontier + 2 ART_SEG_WIN
+// segments (0: never; 4096: without bound); ART_SEG_WGS persistent
 // workgroups (0: one per CU).
 // Stream kernel: ART_LA0 and ART_LA_SHIFT set its lookahead, la0 +
 // (frontier >> la_shift) blocks (defaults 32 and 1).  Windowed:
@@ -81,7 +84,7 @@ int env_int(const char* name, int def, int lo, int hi) {
 }
 struct Knobs {
   int ring, lookahead, helpers, target, lb, window, workers, win_split, win_first, win_growth;
-  int la0, la_shift, spin_limit, full_wgs, seg_win, seg_wgs;
+  int la0, la_shift, spin_limit, full_wgs, seg_win, seg_wgs, seg_ext;
 };
 enum { SCHED_SCAN = 0, SCHED_LB = 1, SCHED_AUTO = 2, SCHED_WIN = 3, SCHED_STREAM = 4, SCHED_SEG = 5 };
 Knobs read_knobs() {
@@ -99,7 +102,8 @@ Knobs read_knobs() {
                    env_int("ART_WIN_FIRST", 0, 0, 64),          env_int("ART_WIN_GROWTH", 2, 2, 8),
                    env_int("ART_LA0", 32, 1, 1 << 20),          env_int("ART_LA_SHIFT", 1, 0, 30),
                    env_int("ART_SPIN_LIMIT", 1 << 20, 1, 1 << 30), env_int("ART_FULL_WGS", 0, 0, 1 << 20),
-                   env_int("ART_SEG_WIN", 2, 1, 1 << 20),      env_int("ART_SEG_WGS", 0, 0, 1 << 20)};
+                   env_int("ART_SEG_WIN", 2, 1, 1 << 20),      env_int("ART_SEG_WGS", 0, 0, 1 << 20),
+                   env_int("ART_SEG_EXT", 2, 0, 4096)};
   return k;
 }
 // The knobs in effect; guarded by a flag so that the environment is read once.
@@ -425,6 +429,7 @@ art_status decode_impl(const art_decode_desc* desc, const void* q, const void* k
     p.seg = sched == SCHED_RUN_SEG ? 1 : 0;
     p.seg_win = knobs().seg_win;  // segments past the frontier: seg_win + frontier / 2
     p.seg_wgs = knobs().seg_wgs > 0 ? knobs().seg_wgs : cu_count();
+    p.seg_ext = knobs().seg_ext;
     p.la0 = knobs().la0;
     p.la_shift = knobs().la_shift;
     p.workers = knobs().workers;

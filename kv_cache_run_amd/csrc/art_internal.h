@@ -68,6 +68,7 @@ struct Params {
   int32_t seg;                         // 1: launch art_seg_kernel (segments of a stream on many workgroups)
   int32_t seg_win;                     // segment kernel: segments claimable past a stream's resolved frontier
   int32_t seg_wgs;                     // segment kernel: persistent workgroups
+  int32_t seg_ext;                     // segment kernel: idle claims up to (seg_ext + 1) x frontier + 2 seg_win (0: none)
   int32_t la0, la_shift;               // stream kernel: lookahead la0 + (frontier >> la_shift) blocks
   int32_t workers;                     // art_lb_kernel workgroups (0: one per resident slot)
   // windowed path (art_win_kernel): per window, a launch in the partials

@@ -10,8 +10,14 @@
 // 2.3 (patience), 2.4 (visit order, block 0 folded before any stop).
 //
 // Persistent workgroups claim items (stream, segment j) in segment order per
-// stream, at most `seg_win` segments past the stream's resolved frontier, so
-// the KV read past a stop is bounded.  Per item:
+// stream, at most `seg_win` + frontier / 2 segments past the stream's resolved
+// frontier, so the KV read past a stop is bounded; a workgroup that would
+// otherwise wait (every stream at its window) claims further ahead on the
+// stream that has run longest without stopping (up to (seg_ext + 1) x
+// frontier + 2 seg_win segments), so that idle CUs shorten the long streams.
+// Every wait is on an item claimed earlier (a predecessor segment of the same
+// stream, or an earlier item of the same workgroup), so no claim order can
+// deadlock, and the results do not depend on the claim order.  Per item:
 //  1. producer waves turn the segment's blocks into per-block results
 //     (o_b = block-normalised output, m_b, l_b per head) in LDS, as the stream
 //     kernel's producers do;
@@ -609,7 +615,9 @@ __device__ void seg_heads(const Params& p, uint32_t E, int s, int j, int n, int 
 
 // Claim the next item (whole wave 0): a segment of the current stream while
 // its window has room, else of the stream with the most unclaimed segments
-// (counted up to 16; ties spread over the workgroups).  Loads the segment's
+// (counted up to 16; ties spread over the workgroups), else (every stream at
+// its window) past the window of the longest-running stream, within
+// p.seg_ext's bound.  Loads the segment's
 // (order entry, page) pairs and the group's query rows into LDS.
 template <class Cf>
 __device__ void seg_claim(const Params& p, uint32_t E, int* info, int* pclaim, int2* ent, char* qdst, int& cur,
@@ -642,27 +650,45 @@ __device__ void seg_claim(const Params& p, uint32_t E, int* info, int* pclaim, i
     }
     if (got_s < 0) {
       uint32_t best = 0u;  // (min(remaining, 16) << 24) | (hash << 16) | stream, 0 = none
+      // idle speculation: every live stream is at its window, so this
+      // workgroup would wait; claim past the window of the stream that has
+      // run longest without stopping, up to (seg_ext + 1) x frontier +
+      // 2 seg_win segments.  Key (min(frontier, 255) << 24) | (hash << 16) |
+      // stream.
+      uint32_t best2 = 0u;
       bool live_any = false;
       const uint32_t hw = (blockIdx.x * 2654435761u) >> 24;
+      auto ext_window = [&](uint32_t prog) {
+        return p.seg_ext <= 0 ? 0u
+               : p.seg_ext >= 4096 ? 0xFFFFFFFFu
+                                   : (uint32_t)(p.seg_ext + 1) * prog + 2u * (uint32_t)p.seg_win;
+      };
       for (int base = 0; base < NSTR; base += 64) {
         const int st = base + lane;
-        uint32_t key = 0u;
+        uint32_t key = 0u, key2 = 0u;
         if (st < NSTR) {
           const uint32_t cv = ld_dev32(p.lb_claim + st);
           const uint32_t prog = ld_dev32(p.lb_prog + st);
           const int ns = nseg_of(st);
           const bool live = !(cv & CLAIM_FIN) && (int)cv < ns;
           live_any |= live;
+          const uint32_t hash = ((((uint32_t)st * 40503u) ^ hw) & 0xFFu) << 16;
           if (live && cv < window(prog))
-            key = ((uint32_t)min(ns - (int)cv, 16) << 24) | ((((uint32_t)st * 40503u) ^ hw) & 0xFFu) << 16 |
-                  (uint32_t)st;
+            key = ((uint32_t)min(ns - (int)cv, 16) << 24) | hash | (uint32_t)st;
+          else if (live && cv < ext_window(prog))
+            key2 = (min(prog, 255u) << 24) | hash | (uint32_t)st;
         }
-        uint32_t mk = key;
+        uint32_t mk = key, mk2 = key2;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) mk = max(mk, (uint32_t)__shfl_xor((int)mk, o));
+        for (int o = 32; o >= 1; o >>= 1) {
+          mk = max(mk, (uint32_t)__shfl_xor((int)mk, o));
+          mk2 = max(mk2, (uint32_t)__shfl_xor((int)mk2, o));
+        }
         best = max(best, mk);
+        best2 = max(best2, mk2);
       }
       live_any = __ballot(live_any) != 0ull;
+      if (best == 0u) best = best2;
       if (best != 0u) {
         const int st = (int)(best & 0xFFFFu);
         const int k = take(st);

@@ -457,13 +457,30 @@ __global__ __launch_bounds__((64 * StreamCfg<KV, D, B, GM>::NW2)) void art_strea
     return;
   }
   if (threadIdx.x < 64) sh.rdy[threadIdx.x] = 0;
-  // entries (order entry, page) of the first STREAM_ENT visit positions
+  // entries (order entry, page) of the first STREAM_ENT visit positions: a
+  // thread's order entries are all loaded before its page lookups, so the
+  // table costs two dependent loads whatever its length
   {
     const int32_t* trow = p.block_table + (size_t)s * p.max_blocks;
     const int32_t* orow = p.block_order + (size_t)s * p.max_blocks;
-    for (int t = threadIdx.x; t < min(n, STREAM_ENT); t += 64 * Cf::NW2) {
-      const int ob = orow[t];
-      ent[t] = make_int2(ob, trow[ob]);
+    constexpr int NT = 64 * Cf::NW2;
+    constexpr int IT = (STREAM_ENT + NT - 1) / NT;
+    const int nent = min(n, STREAM_ENT);
+    int ob[IT], pg[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int t = (int)threadIdx.x + i * NT;
+      ob[i] = t < nent ? orow[t] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int t = (int)threadIdx.x + i * NT;
+      pg[i] = t < nent ? trow[ob[i]] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int t = (int)threadIdx.x + i * NT;
+      if (t < nent) ent[t] = make_int2(ob[i], pg[i]);
     }
     if (threadIdx.x < 8) sh.win[threadIdx.x] = threadIdx.x + 1;
   }

@@ -285,6 +285,9 @@ SEG_VARIANTS = [
     dict(ART_SCHED="seg", ART_SEG_WIN="64"),                  # every segment at once
     dict(ART_SCHED="seg", ART_SEG_WGS="7"),                   # few workgroups: long queues of items each
     dict(ART_SCHED="seg", ART_SEG_WGS="1000"),                # more workgroups than CUs
+    dict(ART_SCHED="seg", ART_SEG_EXT="0"),                   # no claims past the window
+    dict(ART_SCHED="seg", ART_SEG_EXT="4096", ART_SEG_WIN="1"),   # idle claims without bound
+    dict(ART_SCHED="seg", ART_SEG_EXT="4096", ART_SEG_WGS="7"),   # few workgroups, unbounded idle claims
 ]
 
 
