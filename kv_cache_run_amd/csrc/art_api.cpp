@@ -58,7 +58,7 @@ art_status check_desc(const art_decode_desc* d) {
 // larger groups: windows for few, long streams, the look-back scheduler for
 // long streams, scanners otherwise.
 // Segment kernel: ART_SEG_WIN (default 2) segments claimable past a stream's
-// resolved frontier, plus half the frontier; ART_SEG_EXT (default 2): a
+// resolved frontier, plus half the frontier; ART_SEG_EXT (default 8): a
 // workgroup that finds every stream at its window claims on the
 // longest-running stream up to (ART_SEG_EXT + 1) x frontier + 2 ART_SEG_WIN
 // segments (0: never; 4096: without bound); ART_SEG_WGS persistent
@@ -103,7 +103,7 @@ Knobs read_knobs() {
                    env_int("ART_LA0", 32, 1, 1 << 20),          env_int("ART_LA_SHIFT", 1, 0, 30),
                    env_int("ART_SPIN_LIMIT", 1 << 20, 1, 1 << 30), env_int("ART_FULL_WGS", 0, 0, 1 << 20),
                    env_int("ART_SEG_WIN", 2, 1, 1 << 20),      env_int("ART_SEG_WGS", 0, 0, 1 << 20),
-                   env_int("ART_SEG_EXT", 2, 0, 4096)};
+                   env_int("ART_SEG_EXT", 8, 0, 4096)};
   return k;
 }
 // The knobs in effect; guarded by a flag so that the environment is read once.

@@ -407,10 +407,21 @@ __device__ void seg_heads(const Params& p, uint32_t E, int s, int j, int n, int 
         const float* rec0 = rec0_of(k);
         const int jb = j - 1 - f[k];
         if (jb >= 0) lb_load<Cf>(rec0 + (size_t)jb * rstride + incl, lane, x[k].M, x[k].L, x[k].A);
-        for (int i = f[k] - 1; i >= 0; --i) {
-          float m, l, a[DPL];
-          lb_load<Cf>(rec0 + (size_t)(j - 1 - i) * rstride, lane, m, l, a);
-          lb_combine<Cf>(x[k], m, l, a);
+        // the aggregates after it, folded in segment order; their loads go
+        // out LB at a time (the fold order, and so the bits, is unchanged)
+#ifdef ART_SEG_LB
+        constexpr int LB = ART_SEG_LB;
+#else
+        constexpr int LB = 8;
+#endif
+        for (int i0 = f[k] - 1; i0 >= 0; i0 -= LB) {
+          float mb[LB], lb[LB], ab[LB][DPL];
+#pragma unroll
+          for (int u = 0; u < LB; ++u)
+            if (i0 - u >= 0) lb_load<Cf>(rec0 + (size_t)(j - 1 - (i0 - u)) * rstride, lane, mb[u], lb[u], ab[u]);
+#pragma unroll
+          for (int u = 0; u < LB; ++u)
+            if (i0 - u >= 0) lb_combine<Cf>(x[k], mb[u], lb[u], ab[u]);
         }
       }
     }
