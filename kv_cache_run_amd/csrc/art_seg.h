@@ -85,6 +85,21 @@ constexpr uint32_t SG_RUN = 1u << 3, SG_SINK = 1u << 4;
 constexpr uint32_t SG_DEAD = 5u;
 constexpr int SG_CNT_SH = 5;
 constexpr int SG_CNT_MAX = (1 << 26) - 1;
+// Segments of at most 16 positions publish their pass bits inside the status
+// word (level LB_PASS): bit 3 + t for position t, and at bit 19 one plus the
+// position holding logical block 0 (0: none; block 0 occurs once in an
+// order row).  One 64-bit store then carries the level and its bits, so the
+// store needs no wait before it and the replay no load after its poll.
+// Longer segments keep the bits in the record after the inclusive state.
+constexpr int SG_PB_SH = 3, SG_PK_SH = 19;
+__device__ __forceinline__ uint32_t sg_pass_word(uint32_t pass, uint32_t sinkb) {
+  return LB_PASS | (pass << SG_PB_SH) | ((sinkb ? (uint32_t)__builtin_ctz(sinkb) + 1u : 0u) << SG_PK_SH);
+}
+__device__ __forceinline__ void sg_pass_bits(uint32_t w, uint32_t& pass, uint32_t& sinkb) {
+  pass = (w >> SG_PB_SH) & 0xFFFFu;
+  const uint32_t k = (w >> SG_PK_SH) & 31u;
+  sinkb = k ? 1u << (k - 1u) : 0u;
+}
 constexpr int SEG_END = -1, SEG_BUBBLE = -2;
 
 // LDS words of the segment kernel; [b]: item buffer b.  Item k of the
@@ -487,14 +502,21 @@ __device__ void seg_heads(const Params& p, uint32_t E, int s, int j, int n, int 
     if (dead[k]) passb[k] = 0u;
   }
   const uint32_t sinkb = (uint32_t)__ballot(lane < ns && ent[min(lane, S - 1)].x == 0);
+  constexpr bool BITS_IN_STATUS = S <= 16;
   if (ok) {
+    if constexpr (BITS_IN_STATUS) {
 #pragma unroll
-    for (int k = 0; k < HP; ++k)
-      if (act[k] && lane == 0) st_dev(reinterpret_cast<u64*>(rec_of(k) + D + 2), ((u64)sinkb << 32) | passb[k]);
-    wait_all_memory();
+      for (int k = 0; k < HP; ++k)
+        if (act[k] && lane == 0) st_dev(stw_of(k), tag_word(E, sg_pass_word(passb[k], sinkb)));
+    } else {
 #pragma unroll
-    for (int k = 0; k < HP; ++k)
-      if (act[k] && lane == 0) st_dev(stw_of(k), tag_word(E, LB_PASS));
+      for (int k = 0; k < HP; ++k)
+        if (act[k] && lane == 0) st_dev(reinterpret_cast<u64*>(rec_of(k) + D + 2), ((u64)sinkb << 32) | passb[k]);
+      wait_all_memory();
+#pragma unroll
+      for (int k = 0; k < HP; ++k)
+        if (act[k] && lane == 0) st_dev(stw_of(k), tag_word(E, LB_PASS));
+    }
   }
 
   // ---- pass count, block-0 flag and running flag entering the segment
@@ -540,12 +562,19 @@ __device__ void seg_heads(const Params& p, uint32_t E, int s, int j, int n, int 
         cnt[k] = (int)(wf >> SG_CNT_SH);
         sink[k] = (wf & SG_SINK) != 0u;
         run[k] = (wf & LB_LEVEL) == LB_FIN && (wf & SG_RUN) != 0u;
-        // bits of segments j-f .. j-1 (lane i: segment j-1-i), read together
+        // bits of segments j-f .. j-1 (lane i: segment j-1-i): in the
+        // status words of the last poll, or read together from the records
         u64 bits = 0ull;
-        if (lane < f[k]) bits = ld_dev(reinterpret_cast<const u64*>(rec0_of(k) + (size_t)(j - 1 - lane) * rstride + D + 2));
+        if constexpr (!BITS_IN_STATUS)
+          if (lane < f[k]) bits = ld_dev(reinterpret_cast<const u64*>(rec0_of(k) + (size_t)(j - 1 - lane) * rstride + D + 2));
         for (int i = f[k] - 1; i >= 0 && run[k]; --i) {
-          const uint32_t pw = (uint32_t)readlane((int)(uint32_t)bits, i);
-          const uint32_t kw = (uint32_t)readlane((int)(uint32_t)(bits >> 32), i);
+          uint32_t pw, kw;
+          if constexpr (BITS_IN_STATUS) {
+            sg_pass_bits((uint32_t)readlane((int)v, k * LPH + i), pw, kw);
+          } else {
+            pw = (uint32_t)readlane((int)(uint32_t)bits, i);
+            kw = (uint32_t)readlane((int)(uint32_t)(bits >> 32), i);
+          }
           int unused = -1;
           seg_apply(cnt[k], sink[k], run[k], pw, kw, S, cap, p.patience, lane, unused);
         }
