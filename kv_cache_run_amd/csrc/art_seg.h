@@ -673,14 +673,29 @@ __device__ void seg_claim(const Params& p, uint32_t E, int* info, int* pclaim, i
     k = (uint32_t)readlane((int)k, 0);
     return ((k & CLAIM_FIN) || (int)k >= nseg_of(st)) ? -1 : (int)k;
   };
-  if (!ended && ld_dev32(p.sched_ctrl + 3) == E) ended = true;  // a bounded wait of this call gave up
+  // the words the current stream's claim decides on are loaded together:
+  // the call's failure word, the stream's claim count and frontier, its length
+  const uint32_t failw = ld_dev32(p.sched_ctrl + 3);
+  uint32_t cv0 = CLAIM_FIN, prog0 = 0u;
+  int n0 = 0;
+  if (cur >= 0) {
+    cv0 = ld_dev32(p.lb_claim + cur);
+    prog0 = ld_dev32(p.lb_prog + cur);
+    n0 = visit_count<Cf::B>(p, cur / p.hkv, p.seq_lens[cur / p.hkv]);
+  }
+  // the order entries of the segment this claim most likely takes (the one
+  // the claim count names) are loaded with the claim itself
+  int pred_s = -1, pred_j = -1, ob_pred = 0;
+  if (!ended && failw == E) ended = true;  // a bounded wait of this call gave up
   if (!ended) {
     // segments claimable past the resolved frontier: seg_win + frontier / 2
     auto window = [&](uint32_t prog) { return prog + (uint32_t)p.seg_win + (prog >> 1); };
     if (cur >= 0) {
-      const uint32_t cv = ld_dev32(p.lb_claim + cur);
-      const uint32_t prog = ld_dev32(p.lb_prog + cur);
-      if (!(cv & CLAIM_FIN) && (int)cv < nseg_of(cur) && cv < window(prog)) {
+      if (!(cv0 & CLAIM_FIN) && (int)cv0 < (n0 + S - 1) / S && cv0 < window(prog0)) {
+        pred_s = cur;
+        pred_j = (int)cv0;
+        const int tp = pred_j * S + lane;
+        if (lane < S && tp < n0) ob_pred = p.block_order[(size_t)(cur / p.hkv) * p.max_blocks + tp];
         const int k = take(cur);
         if (k >= 0) {
           got_s = cur;
@@ -756,7 +771,7 @@ __device__ void seg_claim(const Params& p, uint32_t E, int* info, int* pclaim, i
   const int32_t* orow = p.block_order + (size_t)sq * p.max_blocks;
   const int32_t* trow = p.block_table + (size_t)sq * p.max_blocks;
   if (lane < ns) {
-    const int ob = orow[t0 + lane];
+    const int ob = got_s == pred_s && got_j == pred_j ? ob_pred : orow[t0 + lane];
     ent[lane] = make_int2(ob, trow[ob]);
   }
   q_to_lds<Cf>(static_cast<const char*>(p.q) + ((size_t)sq * p.hq + (size_t)kvh * p.g) * QROWB, qdst, p.g, lane, 64);
